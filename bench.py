@@ -1,0 +1,321 @@
+#!/usr/bin/env python3
+"""Draft + verify cycles per second on one MI355X.
+
+One step = one whole cycle of the hot path on one batch:
+    len[b] <- C_b (hold the context at the workload's length, a D2D copy)
+    dflash_inject_kv   (features of the tau_b rows accepted last cycle)
+    dflash_draft_block (anchor + gamma-1 masks -> gamma-1 draft tokens)
+    dflash_verify      (against planted target tokens -> tau_b, next anchor)
+Inputs are seeded synthetic tensors already resident in HBM.  The target's own
+forward pass is outside the cycle: its outputs (the features of accepted rows
+and its greedy tokens at the block positions) are synthetic inputs, planted so
+that each cycle accepts a truncated-geometric number of drafts (mean ~6 at
+gamma 16).  Drafting is deterministic, so an untimed planning pass records the
+drafts of every cycle and builds the target tokens; the timed pass replays the
+identical sequence and must reproduce every planted accept length.
+
+Prints one JSON line.  `roofline` is for the dominant kernel (the fused final
+norm + LM head + argmax launch), timed per launch with HIP events recorded by
+the library around that launch inside the timed cycles.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "draft+verify cycles/sec and % HBM roofline, Qwen3-8B shape, gamma=16"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class Hip:
+    """Minimal ctypes access to HIP events (the library records them)."""
+
+    def __init__(self):
+        self.h = ctypes.CDLL("libamdhip64.so")
+        self.h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.h.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.h.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def elapsed_ms(self, a, b):
+        f = ctypes.c_float()
+        assert self.h.hipEventSynchronize(b) == 0
+        assert self.h.hipEventElapsedTime(ctypes.byref(f), a, b) == 0
+        return f.value
+
+    def destroy(self, e):
+        self.h.hipEventDestroy(e)
+
+
+def algorithmic_bytes(cfg, B, C_mean, tau_mean):
+    """Bytes one cycle must move: each weight once (W_k/W_v once for injection and
+    drafting together), the context K/V once, feature rows read, new K/V written."""
+    e = cfg.elem_bytes
+    H, F, D, L = cfg.hidden, cfg.n_feat, cfg.head_dim, cfg.n_layers
+    parts = {
+        "w_fuse": H * F * H * e,
+        "w_k_w_v": L * 2 * cfg.n_kv * D * H * e,
+        "w_q_w_o": L * 2 * cfg.n_q * D * H * e,
+        "mlp": L * 3 * cfg.inter * H * e,
+        "lm_head": cfg.vocab * H * e,
+        "ctx_kv": L * B * cfg.n_kv * C_mean * D * 2 * e,
+        "features_kv_rows": B * tau_mean * (F * H + L * 2 * cfg.n_kv * D) * e,
+    }
+    return parts, sum(parts.values())
+
+
+def cpu_oracle_baseline(cfg, W, K, V, lengths, feats, anchors, plant_k, gamma, budget_s):
+    """The oracle (fp64 numpy) on a bounded sample of the same workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    from oracle import dflash as O
+    from synth import gen
+
+    t0 = time.time()
+    m = O.DraftModel(cfg, W)
+    kv = O.KVCache.from_storage(cfg, K, V, lengths)
+    log(f"oracle set-up {time.time() - t0:.1f}s")
+    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    B = len(lengths)
+    n = 0
+    tau = [int(k) + 1 for k in plant_k[0]]
+    anchor = [int(a) for a in anchors]
+    start = time.time()
+    while True:
+        for b in range(B):
+            kv.len[b] = lengths[b]
+            f = O.decode_storage(feats[n % len(feats)][b, : tau[b]])
+            O.inject(m, kv, b, f)
+            d = O.draft(m, kv, b, anchor[b], gamma)
+            y = gen.planted_targets(cfg, d[None, :], np.array([plant_k[n % len(plant_k)][b]]), tag=f"cpu.{n}.{b}")[0]
+            t, _, nxt = O.verify(d, y)
+            tau[b], anchor[b] = t, nxt
+        n += 1
+        if time.time() - start >= budget_s:
+            break
+    el = time.time() - start
+    return {"value": n / el, "unit": "cycles/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} whole cycles (inject accepted rows + draft + verify) of the same workload, "
+                      f"batch {B}, fp64 numpy oracle, {el:.1f}s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="C3")
+    ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--reps", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--trace-cycles", type=int, default=20)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import block_diffusion_drafter_states_amd as dfl
+    from block_diffusion_drafter_states_amd import _abi
+    import synth
+    from synth import gen
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dfl.lib()
+
+    cfg = synth.get_config(args.config)
+    B = args.batch
+    cfg = cfg.with_(batch=B)
+    gamma = cfg.gamma
+    lengths = gen.context_lengths(cfg)
+    cap = (int(lengths.max()) + 2 * cfg.gamma_max + 63) // 64 * 64
+    dev = "cuda"
+    K_steps, W_steps = args.steps, args.warmup
+
+    t0 = time.time()
+    W = gen.weights(cfg)
+    log(f"weights generated {time.time() - t0:.1f}s")
+    model = dfl.Model(cfg, W, device=dev, max_batch=B, kv_capacity=cap)
+    cache = dfl.Cache(model)
+    Kc, Vc = gen.context_kv(cfg, lengths, int(lengths.max()), tag="bench.ctx")
+    cache.set_context(Kc, Vc, lengths)
+    ws = dfl.Workspace(model, B, gamma)
+    log(f"uploaded {time.time() - t0:.1f}s; workspace {ws.nbytes / 2**20:.1f} MiB, cap {cap}")
+
+    NP = 8
+    feats_host = [gen.features(cfg, B, gamma, tag=f"bench.feat.{i}") for i in range(NP)]
+    feats = [dfl.to_device(f, dev) for f in feats_host]
+    plant_k = [gen.planted_accept(cfg, (B,), gamma, tag=f"bench.k.{i}") for i in range(K_steps)]
+    anchor0 = gen.anchors(cfg, B, tag="bench.anchor")
+    len_base = torch.as_tensor(lengths, dtype=torch.int32, device=dev)
+    acc = torch.zeros((K_steps + 1, B), dtype=torch.int32, device=dev)      # accept_len per cycle
+    nxt = torch.zeros((K_steps + 1, B), dtype=torch.int32, device=dev)      # next anchor per cycle
+    drafts = torch.zeros((K_steps, B, gamma - 1), dtype=torch.int32, device=dev)
+    ytgt = torch.zeros((K_steps, B, gamma), dtype=torch.int32, device=dev)
+    committed = torch.zeros((B, gamma), dtype=torch.int32, device=dev)
+    tau0 = torch.as_tensor(plant_k[-1] + 1, dtype=torch.int32, device=dev)
+
+    def reset():
+        acc[0].copy_(tau0)
+        nxt[0].copy_(torch.as_tensor(anchor0, device=dev))
+
+    def cycle(i, trace=None):
+        cache.len[:B].copy_(len_base)
+        if trace is None:
+            dfl.inject_kv(model, cache, feats[i % NP], acc[i], ws)
+            dfl.draft_block(model, cache, gamma, nxt[i], drafts[i], ws)
+        else:
+            _abi.check(dfl.lib().dflash_inject_kv_traced(
+                ctypes.byref(model.c), ctypes.byref(model.w), ctypes.byref(cache.s), B, feats[i % NP].data_ptr(),
+                gamma, acc[i].data_ptr(), ws.ptr(), ws.nbytes, dfl._stream_ptr(None), ctypes.byref(trace[0])),
+                "inject_traced")
+            _abi.check(dfl.lib().dflash_draft_block_traced(
+                ctypes.byref(model.c), ctypes.byref(model.w), ctypes.byref(cache.s), B, gamma, nxt[i].data_ptr(),
+                drafts[i].data_ptr(), None, None, ws.ptr(), ws.nbytes, dfl._stream_ptr(None),
+                ctypes.byref(trace[1])), "draft_traced")
+        dfl.verify(drafts[i], ytgt[i], acc[i + 1], committed, nxt[i + 1])
+
+    # ---- planning pass (untimed): record drafts, plant target tokens
+    t1 = time.time()
+    reset()
+    for i in range(K_steps):
+        cache.len[:B].copy_(len_base)
+        dfl.inject_kv(model, cache, feats[i % NP], acc[i], ws)
+        dfl.draft_block(model, cache, gamma, nxt[i], drafts[i], ws)
+        d = drafts[i].cpu().numpy()
+        ytgt[i].copy_(torch.as_tensor(gen.planted_targets(cfg, d, plant_k[i], tag=f"bench.y.{i}")))
+        dfl.verify(drafts[i], ytgt[i], acc[i + 1], committed, nxt[i + 1])
+    torch.cuda.synchronize()
+    status = int(cache.status.item())
+    assert status == 0, f"device status {status}"
+    log(f"planning pass {time.time() - t1:.1f}s")
+
+    # ---- warm-up + timed repetitions
+    reset()
+    for i in range(min(W_steps, K_steps)):
+        cycle(i)
+    torch.cuda.synchronize()
+    times = []
+    for r in range(args.reps):
+        reset()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(K_steps):
+            cycle(i)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+        taus = acc[1:].cpu().numpy()
+        want = np.stack(plant_k) + 1
+        assert np.array_equal(taus, want), "timed pass did not reproduce the planted accept lengths"
+    ms_total = statistics.median(times)
+    ms_per = ms_total / K_steps
+    cps = 1000.0 / ms_per
+    tau_mean = float(np.mean(np.stack(plant_k) + 1))
+    log(f"cycles: {ms_per * 1000:.1f} us/cycle ({cps:.1f} cycles/s), reps {[round(t / K_steps * 1000, 1) for t in times]}")
+
+    # ---- per-launch timing with library-recorded events
+    hip = Hip()
+    CAP = 64
+    names_arr = [(ctypes.c_char_p * CAP)(), (ctypes.c_char_p * CAP)()]
+    probe = [_abi.dflash_trace(events=None, capacity=CAP, count=0,
+                               names=ctypes.cast(names_arr[k], ctypes.POINTER(ctypes.c_char_p))) for k in range(2)]
+    reset()
+    cycle(0, trace=probe)
+    torch.cuda.synchronize()
+    names = [[names_arr[k][i].decode() for i in range(probe[k].count)] for k in range(2)]
+    NT = min(args.trace_cycles, K_steps)
+    per_cycle = []
+    for i in range(NT):
+        tr = []
+        for k in range(2):
+            n = probe[k].count
+            evs = (ctypes.c_void_p * (2 * n))(*[hip.event() for _ in range(2 * n)])
+            t = _abi.dflash_trace(events=ctypes.cast(evs, ctypes.POINTER(ctypes.c_void_p)), capacity=n, count=0,
+                                  names=None)
+            t._evs = evs
+            tr.append(t)
+        per_cycle.append(tr)
+    reset()
+    for i in range(NT):
+        cycle(i, trace=per_cycle[i])
+    torch.cuda.synchronize()
+    kern = {}
+    for i in range(NT):
+        for k in range(2):
+            evs = per_cycle[i][k]._evs
+            for j, nm in enumerate(names[k]):
+                kern.setdefault(nm, []).append(hip.elapsed_ms(evs[2 * j], evs[2 * j + 1]))
+            for e in evs:
+                hip.destroy(e)
+    kern_us = {nm: round(1000.0 * sum(v) / NT, 2) for nm, v in kern.items()}     # per cycle (all launches)
+    lm = kern["lm_head_argmax"]
+    lm_avg_ms = sum(lm) / len(lm)
+    lm_bytes = cfg.vocab * cfg.hidden * cfg.elem_bytes + B * gamma * cfg.hidden * 4
+    lm_gbs = lm_bytes / (lm_avg_ms * 1e-3) / 1e9
+    log(f"lm_head_argmax {lm_avg_ms * 1000:.1f} us -> {lm_gbs:.0f} GB/s; per-cycle kernel us {kern_us}")
+
+    parts, bytes_cycle = algorithmic_bytes(cfg, B, float(np.mean(lengths)), tau_mean)
+    result = {
+        "metric": METRIC,
+        "value": round(cps, 2),
+        "unit": "cycles/s",
+        "n_gpus": 1,
+        "steps": K_steps,
+        "warmup": W_steps,
+        "ms_per_step": round(ms_per, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded random-init drafter weights, N(0,1) target features and context K/V, "
+                "planted target tokens)",
+        "config": {"workload": f"{cfg.name}: Qwen3-8B-shaped drafter, batch {B}, gamma {gamma}, "
+                               f"context {int(lengths.mean())}",
+                   "batch": B, "gamma": gamma, "context": int(lengths.mean()), "hidden": cfg.hidden,
+                   "layers": cfg.n_layers, "vocab": cfg.vocab, "parallelism": "single GPU"},
+        "draft_tokens_per_s": round(cps * B * (gamma - 1), 1),
+        "committed_tokens_per_s": round(cps * B * tau_mean, 1),
+        "planted_mean_accept_len": round(tau_mean, 3),
+        "bytes_per_cycle": int(bytes_cycle),
+        "hbm_roofline_frac": round(bytes_cycle * cps / (HBM_PEAK_GBS * 1e9), 4),
+        "roofline": {"bound": "hbm", "kernel": "lm_head_argmax", "achieved": round(lm_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(lm_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "avg_launch_us": round(lm_avg_ms * 1000, 2)},
+        "kernels_us_per_cycle": kern_us,
+    }
+    if not args.no_cpu_baseline:
+        Kh, Vh = gen.context_kv(cfg, lengths, cap, tag="bench.ctx")
+        result["cpu_baseline"] = cpu_oracle_baseline(cfg, W, Kh, Vh, lengths, feats_host, anchor0, plant_k, gamma,
+                                                     args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

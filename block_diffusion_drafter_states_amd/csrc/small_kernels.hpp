@@ -1,0 +1,67 @@
+// Small kernels of the cycle: block embedding, greedy verification, copies.
+#pragma once
+
+#include "common.hpp"
+
+namespace dflash {
+
+// x[b*gamma + j][:] = E[id] with id = anchor[b] (j == 0) or the mask id; also the
+// row's sum of squares (one partial tile) for the first layer's RMSNorm.
+template <typename T>
+__global__ __launch_bounds__(256) void embed_block_kernel(const T* __restrict__ embed, const int* __restrict__ anchor,
+                                                          int mask_id, int vocab, int gamma, int H,
+                                                          float* __restrict__ x, float* __restrict__ ssq,
+                                                          unsigned* status) {
+    __shared__ float red[4];
+    const int m = blockIdx.x;
+    const int b = m / gamma, j = m % gamma;
+    int id = (j == 0) ? anchor[b] : mask_id;
+    if (id < 0 || id >= vocab) {
+        if (threadIdx.x == 0) atomicOr(status, STATUS_BAD_TOKEN);
+        id = 0;
+    }
+    const T* e = embed + (long long)id * H;
+    float* xr = x + (long long)m * H;
+    float s = 0.f;
+    for (int k = threadIdx.x; k < H; k += 256) {
+        const float v = Elem<T>::to_f(e[k]);
+        xr[k] = v;
+        s += v * v;
+    }
+    s = wave_sum(s);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) ssq[m] = (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// One wavefront per sequence: k = leading matches of draft[j] == target[j].
+__global__ __launch_bounds__(64) void verify_kernel(int batch, int gamma, const int* __restrict__ draft,
+                                                    const int* __restrict__ target, int* __restrict__ accept_len,
+                                                    int* __restrict__ committed, int* __restrict__ next_anchor) {
+    const int b = blockIdx.x;
+    const int lane = threadIdx.x;
+    const int* d = draft + (long long)b * (gamma - 1);
+    const int* y = target + (long long)b * gamma;
+    int k = gamma - 1;
+    for (int base = 0; base < gamma - 1; base += 64) {
+        const int j = base + lane;
+        const bool mism = (j < gamma - 1) && (d[j] != y[j]);
+        const unsigned long long ball = __ballot(mism);
+        if (ball) {
+            k = base + __ffsll((long long)ball) - 1;
+            break;
+        }
+    }
+    for (int j = lane; j < gamma; j += 64) committed[(long long)b * gamma + j] = (j <= k) ? y[j] : -1;
+    if (lane == 0) {
+        accept_len[b] = k + 1;
+        next_anchor[b] = y[k];
+    }
+}
+
+__global__ __launch_bounds__(256) void copy_f32_kernel(const float* __restrict__ src, float* __restrict__ dst,
+                                                       long long n) {
+    for (long long i = blockIdx.x * 256ll + threadIdx.x; i < n; i += (long long)gridDim.x * 256) dst[i] = src[i];
+}
+
+}  // namespace dflash

@@ -1,0 +1,208 @@
+/* dflash.h - C ABI of the DFlash drafting + verification cycle for AMD gfx950.
+ *
+ * Source of the method: "DFlash: Block Diffusion for Flash Speculative
+ * Decoding" (technical summary on gist.science, Japanese and Dutch pages;
+ * abstract on the fugumt.com paper page).  The three calls follow the
+ * summary's statement of the inference path (section 2.2):
+ *   - dflash_inject_kv:   context-feature fusion (first bullet) and KV injection
+ *                         into every draft layer's cache (second bullet);
+ *   - dflash_draft_block: one forward pass of the drafter over a block made of
+ *                         a clean anchor token plus gamma-1 mask tokens (third
+ *                         bullet; anchor from section 2.3), ending in the
+ *                         target's shared LM head (section 2.3, architecture);
+ *   - dflash_verify:      greedy verification - the longest prefix of drafts
+ *                         equal to the target's greedy tokens plus one bonus
+ *                         token (sections 1, 4 and 5: lossless vs. greedy).
+ *
+ * General rules
+ *   - Pointers are device pointers unless marked [host].  The library never
+ *     allocates, frees or synchronises; every call is enqueued on `stream`
+ *     (a hipStream_t; NULL = the default stream) and returns immediately.
+ *   - The caller owns every buffer; buffers must stay alive until the queued
+ *     work has finished.  The library keeps no global mutable state: calls on
+ *     different streams are safe when they use disjoint buffers (including
+ *     disjoint workspaces).
+ *   - Errors the host can see (NULL pointers, sizes out of range, unsupported
+ *     shapes, a workspace that is too small) return a negative dflash_status
+ *     and enqueue nothing.  Errors only the device can see (a cache that would
+ *     overflow, a token id outside the vocabulary, a negative row count) set a
+ *     sticky bit in *kv->status and skip the offending write; nothing is ever
+ *     written out of bounds.  The library never prints or aborts.
+ *
+ * Storage types: every weight, the K/V cache and the input features use the
+ * configuration's dtype (DFLASH_F32 or DFLASH_BF16, bf16 = raw bit patterns).
+ * Activations between layers are fp32; every GEMM input is rounded to the
+ * storage type (round-to-nearest-even), as are q, k and v.
+ *
+ * Layouts (row-major, innermost last):
+ *   weight matrices           [out][in]   (as torch.nn.Linear.weight)
+ *   w_fuse                    [H][F*H]    (input = the F feature rows concatenated,
+ *                                          shallowest tapped layer first)
+ *   K cache  kv->k            [L][max_batch][n_kv][kv_capacity][D]
+ *   V cache  kv->v            [L][max_batch][n_kv][D][kv_capacity]   (transposed)
+ *   kv->len                   int32 [max_batch]: rows of context held per sequence
+ *   rope_cos / rope_sin       fp32 [rope_rows][D/2]: cos/sin of p * theta^(-2i/D)
+ *                             for position p (rotate-half pairs (i, i+D/2))
+ */
+#ifndef DFLASH_H_
+#define DFLASH_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DFLASH_OK = 0,
+    DFLASH_EINVAL = -1,        /* NULL pointer or size out of range */
+    DFLASH_EUNSUPPORTED = -2,  /* shape or dtype this build does not handle */
+    DFLASH_EWORKSPACE = -3,    /* workspace NULL or smaller than dflash_workspace_bytes() */
+    DFLASH_ELAUNCH = -4        /* the HIP runtime rejected a launch */
+} dflash_status;
+
+typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
+
+/* Device-side sticky status bits (OR-ed into *kv->status). */
+#define DFLASH_STATUS_KV_OVERFLOW 1u  /* len + new rows (or block) exceeds kv_capacity / rope_rows */
+#define DFLASH_STATUS_BAD_TOKEN   2u  /* anchor id outside [0, vocab) (id 0 used instead) */
+#define DFLASH_STATUS_BAD_COUNT   4u  /* n_new outside [0, rows_stride] or len < 0 */
+
+/* Model shape [host].  Supported: head_dim*sizeof(dtype) == 256 (bf16 D=128,
+ * f32 D=64); n_q_heads % n_kv_heads == 0; hidden, inter, n_feat*hidden and
+ * n_q_heads*head_dim multiples of 256 (bf16) / 128 (f32); n_kv_heads*head_dim
+ * a multiple of 128; inter a multiple of 64; 2 <= gamma_max <= 16;
+ * kv_capacity a multiple of 64. */
+typedef struct {
+    int32_t hidden;         /* H */
+    int32_t n_q_heads;
+    int32_t n_kv_heads;
+    int32_t head_dim;       /* D */
+    int32_t inter;          /* SwiGLU intermediate size I */
+    int32_t n_layers;       /* L draft layers */
+    int32_t n_feat;         /* F target layers fused */
+    int32_t vocab;          /* V */
+    int32_t gamma_max;      /* largest block size used with this cache/workspace */
+    int32_t mask_token_id;  /* embedding row used for the gamma-1 mask positions */
+    int32_t max_batch;      /* sequences held by the cache */
+    int32_t kv_capacity;    /* cache rows per (layer, sequence, kv head) */
+    float rms_eps;
+    int32_t dtype;          /* dflash_dtype */
+} dflash_config;
+
+/* One draft layer (all [host] struct, device pointers inside). */
+typedef struct {
+    const void *in_norm;    /* [H]        input RMSNorm scale (also applied to context rows) */
+    const void *wq;         /* [n_q*D][H] */
+    const void *wk;         /* [n_kv*D][H] */
+    const void *wv;         /* [n_kv*D][H] */
+    const void *q_norm;     /* [D]        per-head RMSNorm scale of q */
+    const void *k_norm;     /* [D]        per-head RMSNorm scale of k */
+    const void *wo;         /* [H][n_q*D] */
+    const void *post_norm;  /* [H]        RMSNorm before the MLP */
+    const void *w_gate;     /* [I][H] */
+    const void *w_up;       /* [I][H] */
+    const void *w_down;     /* [H][I] */
+} dflash_layer_weights;
+
+typedef struct {
+    const void *w_fuse;      /* [H][F*H] */
+    const void *embed;       /* [V][H]   the target's frozen token embedding */
+    const void *final_norm;  /* [H] */
+    const void *lm_head;     /* [V][H]   the target's frozen LM head (may alias embed) */
+    const float *rope_cos;   /* [rope_rows][D/2] */
+    const float *rope_sin;   /* [rope_rows][D/2] */
+    int32_t rope_rows;       /* must be >= kv_capacity + gamma_max */
+    const dflash_layer_weights *layers;  /* [host] array of n_layers */
+} dflash_weights;
+
+typedef struct {
+    void *k;           /* K cache, layout above */
+    void *v;           /* V cache (transposed), layout above */
+    int32_t *len;      /* [max_batch] */
+    uint32_t *status;  /* [1] sticky device status bits */
+} dflash_kv;
+
+/* Bytes of workspace needed by dflash_inject_kv / dflash_draft_block for up to
+ * `batch` sequences and up to `max_rows_per_seq` injected rows per sequence per
+ * call.  The workspace must be zero-filled once before its first use (it holds
+ * self-resetting counters); every call leaves those counters at zero again.
+ * Calls that share a workspace must be ordered (e.g. on one stream).
+ * Returns 0 for an invalid or unsupported configuration. */
+size_t dflash_workspace_bytes(const dflash_config *cfg, int32_t batch, int32_t max_rows_per_seq);
+
+/* Stages 1-2 (summary section 2.2): for every sequence b < batch and row
+ * i < n_new[b], fuse feat[b][i][0..F-1][0..H-1] with W_fuse, pass the fused
+ * feature through every layer's input RMSNorm, W_k / W_v, per-head k RMSNorm
+ * and RoPE at position len[b] + i, and store the rounded k and v rows at that
+ * position of each layer's cache; then len[b] += n_new[b].
+ *   feat     [batch][rows_stride][F][H] in the storage dtype
+ *   n_new    device int32 [batch], each in [0, rows_stride] (the accept_len of
+ *            dflash_verify can be passed straight in)
+ * If len[b] + n_new[b] > kv_capacity nothing is written for b, len[b] is
+ * unchanged and DFLASH_STATUS_KV_OVERFLOW is set.
+ * 1 <= rows_stride <= max_rows_per_seq given to dflash_workspace_bytes. */
+int dflash_inject_kv(const dflash_config *cfg, const dflash_weights *w, const dflash_kv *kv,
+                     int32_t batch, const void *feat, int32_t rows_stride, const int32_t *n_new,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/* Stage 3 (summary section 2.2, third bullet): for each sequence b, one
+ * forward pass over ids [anchor[b], MASK x (gamma-1)] at positions
+ * len[b] .. len[b]+gamma-1 with attention over [cached context (len[b] rows)
+ * ; the block's own keys/values], no mask inside the block; then the final
+ * RMSNorm, the LM head and a row-wise argmax (ties -> lowest id) on the gamma-1
+ * mask rows.  The block's own K/V are not written to the cache and len is not
+ * changed.  Requires len[b] + gamma <= rope_rows.
+ *   anchor      int32 [batch]
+ *   draft       int32 [batch][gamma-1]   d_1 .. d_{gamma-1}
+ *   dbg_hidden  nullable fp32 [batch][gamma][H]: final residual stream (before the final norm)
+ *   dbg_logits  nullable fp32 [batch][gamma-1][V]: logits of the mask rows
+ * 2 <= gamma <= gamma_max, 1 <= batch <= max_batch. */
+int dflash_draft_block(const dflash_config *cfg, const dflash_weights *w, const dflash_kv *kv,
+                       int32_t batch, int32_t gamma, const int32_t *anchor, int32_t *draft,
+                       float *dbg_hidden, float *dbg_logits,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/* Stage 4 (summary sections 1, 4, 5): per sequence, k = the number of leading
+ * j in 1..gamma-1 with draft[b][j-1] == target[b][j-1]; accept_len[b] = k + 1;
+ * committed[b][0..k] = target[b][0..k], the rest -1; next_anchor[b] =
+ * target[b][k].  target[b][j] is the target's greedy token at block position j
+ * (its choice for the position that draft d_{j+1} filled).
+ *   draft  int32 [batch][gamma-1];  target int32 [batch][gamma]
+ * 2 <= gamma <= 1024, batch >= 1.  Exact integer work. */
+int dflash_verify(int32_t batch, int32_t gamma, const int32_t *draft, const int32_t *target,
+                  int32_t *accept_len, int32_t *committed, int32_t *next_anchor, void *stream);
+
+/* Tracing (optional per-launch timing).  The caller creates hipEvents and
+ * passes their handles; the *_traced variants record events[2*i] before and
+ * events[2*i+1] after the i-th kernel launch of the call, on `stream`, for
+ * every i < capacity whose handles are non-NULL.  On return `count` holds the
+ * number of launches the call made and, when `names` is non-NULL, names[i]
+ * points to a static string naming launch i (e.g. "lm_head_argmax").  A call
+ * with events == NULL records nothing; launch order is the same as for the
+ * untraced call, so a first call can be used to learn count and names. */
+typedef struct {
+    void **events;         /* [host] 2*capacity hipEvent_t handles, entries may be NULL */
+    int32_t capacity;      /* launch slots described by events / names */
+    int32_t count;         /* [out] launches made */
+    const char **names;    /* [host, optional] [capacity] out: launch names */
+} dflash_trace;
+
+int dflash_inject_kv_traced(const dflash_config *cfg, const dflash_weights *w, const dflash_kv *kv,
+                            int32_t batch, const void *feat, int32_t rows_stride, const int32_t *n_new,
+                            void *workspace, size_t workspace_bytes, void *stream, dflash_trace *trace);
+
+int dflash_draft_block_traced(const dflash_config *cfg, const dflash_weights *w, const dflash_kv *kv,
+                              int32_t batch, int32_t gamma, const int32_t *anchor, int32_t *draft,
+                              float *dbg_hidden, float *dbg_logits,
+                              void *workspace, size_t workspace_bytes, void *stream, dflash_trace *trace);
+
+/* Human-readable name of a dflash_status value (static string). */
+const char *dflash_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DFLASH_H_ */

@@ -1,0 +1,112 @@
+"""Shared set-up for the GPU parity tests: the same seeded inputs go to the HIP
+path (through the C ABI) and to the CPU oracle; results are compared here."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import synth
+from synth import gen
+import oracle
+from oracle import dflash as O
+
+
+def log(msg: str) -> None:
+    print(f"[gpu] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def rel_err(got, ref) -> float:
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    return float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+
+
+def decode(a):
+    return O.decode_storage(a, np.float64)
+
+
+def top2_gap(z: np.ndarray) -> np.ndarray:
+    s = np.sort(z, axis=-1)
+    return s[..., -1] - s[..., -2]
+
+
+def tol(cfg) -> float:
+    """Relative-error bound for floating outputs: 1e-4 for fp32 storage, 2e-2 for bf16."""
+    return 1e-4 if cfg.dtype == "f32" else 2e-2
+
+
+class Pair:
+    """One configuration instantiated on both sides."""
+
+    def __init__(self, cfg, batch: int, cap: int, max_rows: int, device: str = "cuda", overrides=None):
+        import block_diffusion_drafter_states_amd as dfl
+        import torch
+        self.torch = torch
+        self.dfl = dfl
+        self.cfg = cfg
+        self.batch = batch
+        self.cap = cap
+        self.W = gen.weights(cfg, overrides)
+        self.om = O.DraftModel(cfg, self.W)
+        self.model = dfl.Model(cfg, self.W, device=device, max_batch=batch, kv_capacity=cap,
+                               gamma_max=cfg.gamma_max)
+        self.cache = dfl.Cache(self.model)
+        self.okv = O.KVCache(cfg, batch, cap)
+        self.ws = dfl.Workspace(self.model, batch, max_rows)
+        self.device = device
+
+    # ---------------------------------------------------------------- inputs
+    def dev_i32(self, a):
+        return self.torch.as_tensor(np.asarray(a, dtype=np.int32), device=self.device).contiguous()
+
+    def dev_storage(self, a):
+        return self.dfl.to_device(a, self.device)
+
+    # ---------------------------------------------------------------- steps
+    def inject(self, feat_storage: np.ndarray, n_new) -> None:
+        """feat_storage [B][rows][F][H] storage; both sides append n_new[b] rows."""
+        self.dfl.inject_kv(self.model, self.cache, self.dev_storage(feat_storage), self.dev_i32(n_new), self.ws)
+        f = decode(feat_storage)
+        for b in range(self.batch):
+            O.inject(self.om, self.okv, b, f[b, : int(n_new[b])])
+
+    def set_context(self, lengths, tag="ctx"):
+        K, V = gen.context_kv(self.cfg, np.asarray(lengths), self.cap, tag=tag)
+        self.cache.set_context(K, V, lengths)
+        self.okv = O.KVCache.from_storage(self.cfg, K, V, lengths)
+
+    def draft(self, anchors, gamma):
+        torch = self.torch
+        B = self.batch
+        d = torch.full((B, gamma - 1), -7, dtype=torch.int32, device=self.device)
+        hid = torch.full((B, gamma, self.cfg.hidden), float("nan"), dtype=torch.float32, device=self.device)
+        lg = torch.full((B, gamma - 1, self.cfg.vocab), float("nan"), dtype=torch.float32, device=self.device)
+        self.dfl.draft_block(self.model, self.cache, gamma, self.dev_i32(anchors), d, self.ws, hid, lg)
+        torch.cuda.synchronize()
+        return d.cpu().numpy(), hid.cpu().numpy(), lg.cpu().numpy()
+
+    def oracle_draft(self, anchors, gamma):
+        ds, xs, zs = [], [], []
+        for b in range(self.batch):
+            d, x, z = O.draft(self.om, self.okv, b, int(anchors[b]), gamma, return_all=True)
+            ds.append(d); xs.append(x); zs.append(z)
+        return np.stack(ds), np.stack(xs), np.stack(zs)
+
+    def status(self) -> int:
+        return int(self.cache.status.item())
+
+
+def check_draft(cfg, got, ref, gap_min=1e-2):
+    """Compare (draft, hidden, logits) of GPU vs oracle; returns a dict of metrics."""
+    d, x, z = got
+    dr, xr, zr = ref
+    assert np.isfinite(x).all() and np.isfinite(z).all()
+    ex = rel_err(x, xr)
+    ez = rel_err(z, zr)
+    gap = top2_gap(zr)
+    sure = gap >= gap_min
+    mism = int(((d != dr) & sure).sum())
+    return {"hidden_rel": ex, "logits_rel": ez, "draft_checked": int(sure.sum()), "draft_mismatch": mism,
+            "logit_maxabs": float(np.abs(z - zr).max())}

@@ -1,0 +1,183 @@
+"""The C-ABI library loads, exports every symbol include/dflash.h declares, its
+ctypes structs match the header, and every host-detectable error returns its
+code without touching a device (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_diffusion_drafter_states_amd import _abi
+from block_diffusion_drafter_states_amd._abi import (dflash_config, dflash_kv, dflash_layer_weights, dflash_weights,
+                                                     dflash_trace, DFLASH_EINVAL, DFLASH_EUNSUPPORTED,
+                                                     DFLASH_EWORKSPACE)
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dflash.h")
+
+
+def _lib():
+    if not os.path.exists(_abi.LIB_PATH):
+        pytest.skip("libdflash.so not built (run __graft_entry__.build())")
+    return _abi.lib()
+
+
+def _header_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(dflash_[a-z_]+)\s*\(", txt)))
+
+
+def test_header_declares_the_entry_points():
+    assert _header_functions() == sorted(_abi.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib()
+    for name in _header_functions():
+        assert hasattr(L, name), name
+    out = os.popen(f"nm -D --defined-only {_abi.LIB_PATH}").read()
+    for name in _header_functions():
+        assert re.search(rf"\bT {name}\b", out), name
+
+
+def _struct_fields(name):
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    end = re.search(r"\}\s*" + name + ";", txt).start()
+    body = txt[txt.rindex("typedef struct {", 0, end) + len("typedef struct {"):end]
+    fields = []
+    for decl in body.split(";"):
+        decl = decl.strip()
+        if not decl:
+            continue
+        names = decl.split()[-1] if "," not in decl else None
+        if names is None:
+            # "const void *in_norm, *wq, ..." style
+            parts = decl.split(",")
+            first = parts[0].split()[-1].lstrip("*")
+            fields += [first] + [p.strip().lstrip("*") for p in parts[1:]]
+        else:
+            fields.append(names.lstrip("*"))
+    return fields
+
+
+@pytest.mark.parametrize("cname,pyt", [("dflash_config", dflash_config), ("dflash_layer_weights", dflash_layer_weights),
+                                       ("dflash_weights", dflash_weights), ("dflash_kv", dflash_kv),
+                                       ("dflash_trace", dflash_trace)])
+def test_ctypes_structs_match_header(cname, pyt):
+    assert _struct_fields(cname) == [f[0] for f in pyt._fields_]
+
+
+def _cfg(**kw):
+    c = synth.get_config("C1")
+    d = dict(hidden=c.hidden, n_q_heads=c.n_q, n_kv_heads=c.n_kv, head_dim=c.head_dim, inter=c.inter,
+             n_layers=c.n_layers, n_feat=c.n_feat, vocab=c.vocab, gamma_max=c.gamma, mask_token_id=c.mask_id,
+             max_batch=1, kv_capacity=128, rms_eps=1e-6, dtype=0)
+    d.update(kw)
+    return dflash_config(**d)
+
+
+def test_workspace_bytes_validates_config():
+    L = _lib()
+    ok = L.dflash_workspace_bytes(ctypes.byref(_cfg()), 1, 16)
+    assert ok > 0
+    assert L.dflash_workspace_bytes(ctypes.byref(_cfg()), 2, 16) == 0          # batch > max_batch
+    assert L.dflash_workspace_bytes(ctypes.byref(_cfg(head_dim=128)), 1, 16) == 0   # fp32 needs D=64
+    assert L.dflash_workspace_bytes(ctypes.byref(_cfg(gamma_max=17)), 1, 16) == 0
+    assert L.dflash_workspace_bytes(ctypes.byref(_cfg(kv_capacity=100)), 1, 16) == 0
+    assert L.dflash_workspace_bytes(ctypes.byref(_cfg(dtype=7)), 1, 16) == 0
+    assert L.dflash_workspace_bytes(None, 1, 16) == 0
+    bf = _cfg(dtype=1, head_dim=128, n_q_heads=4, n_kv_heads=2, hidden=512, inter=512)
+    assert L.dflash_workspace_bytes(ctypes.byref(bf), 1, 16) > 0
+
+
+FAKE = 0x1000   # never dereferenced: every call below fails validation first
+
+
+def _weights(L_layers=2, null_field=None):
+    arr = (dflash_layer_weights * L_layers)()
+    for l in range(L_layers):
+        for f, _ in dflash_layer_weights._fields_:
+            setattr(arr[l], f, None if f == null_field else FAKE)
+    w = dflash_weights(w_fuse=FAKE, embed=FAKE, final_norm=FAKE, lm_head=FAKE, rope_cos=FAKE, rope_sin=FAKE,
+                       rope_rows=1024, layers=ctypes.cast(arr, ctypes.POINTER(dflash_layer_weights)))
+    w._keep = arr
+    return w
+
+
+def _kv():
+    return dflash_kv(k=FAKE, v=FAKE, len=FAKE, status=FAKE)
+
+
+def test_inject_host_errors():
+    L = _lib()
+    c, w, kv = _cfg(), _weights(), _kv()
+    ws_need = L.dflash_workspace_bytes(ctypes.byref(c), 1, 8)
+    call = lambda **k: L.dflash_inject_kv(ctypes.byref(k.get("c", c)), ctypes.byref(k.get("w", w)),
+                                          ctypes.byref(k.get("kv", kv)), k.get("batch", 1), k.get("feat", FAKE),
+                                          k.get("rows", 8), k.get("n_new", FAKE), k.get("ws", FAKE),
+                                          k.get("wsb", ws_need), None)
+    assert call(batch=0) == DFLASH_EINVAL
+    assert call(batch=2) == DFLASH_EINVAL
+    assert call(rows=0) == DFLASH_EINVAL
+    assert call(feat=None) == DFLASH_EINVAL
+    assert call(n_new=None) == DFLASH_EINVAL
+    assert call(kv=dflash_kv(k=FAKE, v=FAKE, len=None, status=FAKE)) == DFLASH_EINVAL
+    assert call(w=_weights(null_field="wk")) == DFLASH_EINVAL
+    assert call(ws=None) == DFLASH_EWORKSPACE
+    assert call(wsb=ws_need - 1) == DFLASH_EWORKSPACE
+    assert call(rows=9) == DFLASH_EWORKSPACE        # workspace sized for 8 rows
+    assert call(c=_cfg(head_dim=32)) == DFLASH_EUNSUPPORTED
+    small = _weights()
+    small.rope_rows = 10
+    assert call(w=small) == DFLASH_EINVAL
+
+
+def test_draft_host_errors():
+    L = _lib()
+    c, w, kv = _cfg(), _weights(), _kv()
+    ws_need = L.dflash_workspace_bytes(ctypes.byref(c), 1, 0)
+    call = lambda **k: L.dflash_draft_block(ctypes.byref(k.get("c", c)), ctypes.byref(w), ctypes.byref(kv),
+                                            k.get("batch", 1), k.get("gamma", 8), k.get("anchor", FAKE),
+                                            k.get("draft", FAKE), None, None, k.get("ws", FAKE),
+                                            k.get("wsb", ws_need), None)
+    assert call(gamma=1) == DFLASH_EINVAL
+    assert call(gamma=9) == DFLASH_EINVAL           # > gamma_max
+    assert call(batch=0) == DFLASH_EINVAL
+    assert call(anchor=None) == DFLASH_EINVAL
+    assert call(draft=None) == DFLASH_EINVAL
+    assert call(wsb=ws_need - 256) == DFLASH_EWORKSPACE
+    assert call(c=_cfg(mask_token_id=5000)) == DFLASH_EINVAL
+    assert call(c=_cfg(n_q_heads=3)) == DFLASH_EUNSUPPORTED
+
+
+def test_verify_host_errors():
+    L = _lib()
+    assert L.dflash_verify(0, 4, FAKE, FAKE, FAKE, FAKE, FAKE, None) == DFLASH_EINVAL
+    assert L.dflash_verify(1, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None) == DFLASH_EINVAL
+    assert L.dflash_verify(1, 1025, FAKE, FAKE, FAKE, FAKE, FAKE, None) == DFLASH_EINVAL
+    assert L.dflash_verify(1, 4, None, FAKE, FAKE, FAKE, FAKE, None) == DFLASH_EINVAL
+    assert L.dflash_verify(1, 4, FAKE, FAKE, FAKE, None, FAKE, None) == DFLASH_EINVAL
+
+
+def test_status_strings():
+    L = _lib()
+    for code in (0, -1, -2, -3, -4):
+        assert L.dflash_status_str(code).startswith(b"DFLASH_")
+    assert L.dflash_status_str(99) == b"unknown dflash status"
+
+
+def test_traced_variants_validate_like_the_plain_calls():
+    L = _lib()
+    c, w, kv = _cfg(), _weights(), _kv()
+    ws_need = L.dflash_workspace_bytes(ctypes.byref(c), 1, 8)
+    bad = dflash_trace(events=None, capacity=-1, count=0, names=None)
+    good = dflash_trace(events=None, capacity=0, count=0, names=None)
+    assert L.dflash_inject_kv_traced(ctypes.byref(c), ctypes.byref(w), ctypes.byref(kv), 1, FAKE, 8, FAKE, FAKE,
+                                     ws_need, None, ctypes.byref(bad)) == DFLASH_EINVAL
+    assert L.dflash_inject_kv_traced(ctypes.byref(c), ctypes.byref(w), ctypes.byref(kv), 0, FAKE, 8, FAKE, FAKE,
+                                     ws_need, None, ctypes.byref(good)) == DFLASH_EINVAL
+    assert L.dflash_draft_block_traced(ctypes.byref(c), ctypes.byref(w), ctypes.byref(kv), 1, 1, FAKE, FAKE,
+                                       None, None, FAKE, ws_need, None, ctypes.byref(good)) == DFLASH_EINVAL
