@@ -29,13 +29,18 @@ constexpr int ATT_THREADS = 256;
 struct AttnArgs {
     const void* kcache;     // this layer: T [Bmax][n_kv][cap][D]
     const void* vcache;     // this layer: T [Bmax][n_kv][D][cap]
-    const void* qbuf;       // T [B][n_kv][rpad][D]
-    const void* kblk;       // T [B][n_kv][32][D]
-    const void* vblk;       // T [B][n_kv][D][32]
+    const float* qkv;       // raw projections fp32 [B*gamma][qkv_ld]: q heads, then k heads, then v heads
+    int qkv_ld;
+    const void* q_norm;     // T [D]
+    const void* k_norm;     // T [D]
+    const float* rope_cos;  // [rope_rows][D/2]
+    const float* rope_sin;
+    int rope_rows;
+    float eps;
     const int* len;         // [B]
     float* opart;           // [B][n_kv][nch_max][rpad][D]
     float* mlpart;          // [B][n_kv][nch_max][rpad][2]  (m in log2 units, l)
-    int n_kv, cap, rpad, nch_max, chunk;   // chunk = CH context keys per chunk
+    int n_q, n_kv, cap, rpad, nch_max, chunk;   // chunk = CH context keys per chunk
     int gamma, group;       // rows = group * gamma
     int qg, kg;             // waves = qg query groups x kg key groups (qg*kg <= 4)
     float scale_log2;       // log2(e) / sqrt(D)
@@ -100,27 +105,107 @@ __device__ __forceinline__ void pv_mfma<float>(f32x4_t& acc, const float (&p)[8]
     for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(p[j], v[j], acc, 0, 0, 0);
 }
 
-// Process keys [kb, kb+32) of which the first `nvalid` are real.
-// krow(key) gives the K row pointer, vrow(d) the V^T row pointer for key kb.
-template <typename T, class KRow, class VRow>
-__device__ __forceinline__ void attn_subblock(WaveAttn<T>& w, int nqt, int kb, int nvalid, float scale_log2,
-                                              KRow krow, VRow vrow) {
+// Load the K fragments (two S^T tiles) and V^T fragments of keys [kb, kb+32) from
+// the cache; keys at or beyond `nvalid` are clamped on load and masked later.
+template <typename T>
+__device__ __forceinline__ void load_ctx_frags(Frag64 (&kf)[2], float (&vf)[WaveAttn<T>::DT][8], const T* kc,
+                                               const T* vc, int cap, int kb, int nvalid) {
     constexpr int D = WaveAttn<T>::D, DT = WaveAttn<T>::DT, STEP = Elem<T>::STEP;
     const int lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
-    // key rows for the two S^T tiles: lane row r -> key (r/4)*8 + t*4 + r%4
-    Frag64 kf[2];
+    // key rows of the two S^T tiles: lane row r -> key (r/4)*8 + t*4 + r%4
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         int key = (r >> 2) * 8 + t * 4 + (r & 3);
-        key = key < nvalid ? key : (nvalid - 1);      // stay on a real row; masked below
-        load_frag64(kf[t], krow(kb + key) + g * (STEP / 4));
+        key = key < nvalid ? key : (nvalid - 1);
+        load_frag64(kf[t], kc + (long long)(kb + key) * D + g * Elem<T>::PER16);
     }
     // V^T fragments: lane (g,r), d = dt*16 + r, keys kb + g*8 .. +8
-    float vf[DT][8];
     const int vvalid = nvalid - g * 8;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) vfrag_load<T>(vf[dt], vrow(dt * 16 + r) + g * 8, vvalid);
+    for (int dt = 0; dt < DT; ++dt) vfrag_load<T>(vf[dt], vc + (long long)(dt * 16 + r) * cap + kb + g * 8, vvalid);
+}
 
+// A head row as held by one lane in the fragment layout: piece i (0..3) holds
+// elements d = 4*PER*i + PER*g + j (j < PER, PER = 16 bytes / element size).
+// Rotate-half RoPE pairs d with d + D/2, i.e. piece i with piece i + 2 of the
+// same lane; the four lanes of a row (g = 0..3) are 16 lanes apart.
+template <typename T>
+__device__ __forceinline__ void load_row_raw(float (&x)[4][Elem<T>::PER16], const float* row, bool valid) {
+    constexpr int PER = Elem<T>::PER16;
+    const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int h = 0; h < PER / 4; ++h) {
+            const float4 v = valid ? *reinterpret_cast<const float4*>(row + i * 4 * PER + g * PER + h * 4)
+                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+            x[i][h * 4 + 0] = v.x; x[i][h * 4 + 1] = v.y; x[i][h * 4 + 2] = v.z; x[i][h * 4 + 3] = v.w;
+        }
+}
+
+// Per-head RMSNorm (over the D elements spread over the row's four lanes) then
+// rotate-half RoPE, rounded to the storage type, into an MFMA fragment.
+template <typename T>
+__device__ __forceinline__ void norm_rope_frag(Frag64& out, const float (&x)[4][Elem<T>::PER16], const T* wn,
+                                               float eps, const float* cosr, const float* sinr) {
+    constexpr int PER = Elem<T>::PER16;
+    constexpr int D = 16 * PER;
+    const int g = (threadIdx.x & 63) >> 4;
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < PER; ++j) ss += x[i][j] * x[i][j];
+    ss += __shfl_xor(ss, 16, WAVE);
+    ss += __shfl_xor(ss, 32, WAVE);
+    const float rs = 1.0f / sqrtf(ss / (float)D + eps);
+    Frag64 wf;
+    load_frag64(wf, wn + g * PER);
+    float y[4][PER];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const T* wp = reinterpret_cast<const T*>(&wf.q[i]);
+#pragma unroll
+        for (int j = 0; j < PER; ++j) y[i][j] = x[i][j] * rs * Elem<T>::to_f(wp[j]);
+    }
+    float o[4][PER];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        float c[PER], sn[PER];
+#pragma unroll
+        for (int h = 0; h < PER / 4; ++h) {
+            const float4 c4 = *reinterpret_cast<const float4*>(cosr + i * 4 * PER + g * PER + h * 4);
+            const float4 s4 = *reinterpret_cast<const float4*>(sinr + i * 4 * PER + g * PER + h * 4);
+            c[h * 4 + 0] = c4.x; c[h * 4 + 1] = c4.y; c[h * 4 + 2] = c4.z; c[h * 4 + 3] = c4.w;
+            sn[h * 4 + 0] = s4.x; sn[h * 4 + 1] = s4.y; sn[h * 4 + 2] = s4.z; sn[h * 4 + 3] = s4.w;
+        }
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            o[i][j] = y[i][j] * c[j] - y[i + 2][j] * sn[j];
+            o[i + 2][j] = y[i + 2][j] * c[j] + y[i][j] * sn[j];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if constexpr (sizeof(T) == 2) {
+            uint32_t w4[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                w4[k] = (uint32_t)f32_to_bf16(o[i][2 * k]) | ((uint32_t)f32_to_bf16(o[i][2 * k + 1]) << 16);
+            out.q[i] = u32x4_t{w4[0], w4[1], w4[2], w4[3]};
+        } else {
+            out.q[i] = u32x4_t{__float_as_uint(o[i][0]), __float_as_uint(o[i][1]), __float_as_uint(o[i][2]),
+                               __float_as_uint(o[i][3])};
+        }
+    }
+}
+
+// Process keys [kb, kb+32) of which the first `nvalid` are real.
+template <typename T>
+__device__ __forceinline__ void attn_subblock(WaveAttn<T>& w, int nqt, int nvalid, float scale_log2,
+                                              const Frag64 (&kf)[2], const float (&vf)[WaveAttn<T>::DT][8]) {
+    constexpr int DT = WaveAttn<T>::DT;
+    const int lane = threadIdx.x & 63, g = lane >> 4;
 #pragma unroll
     for (int qi = 0; qi < 4; ++qi) {
         if (qi < nqt) {
@@ -188,39 +273,69 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_partial_kernel(const AttnArg
     const int nqt = active_wave ? max(0, min(4, nqt_all - qt0)) : 0;
 
     WaveAttn<T> w;
-    const T* qbase = reinterpret_cast<const T*>(a.qbuf) + ((long long)b * a.n_kv + h) * a.rpad * D;
+    constexpr int PER = Elem<T>::PER16;
+    const T* qn = reinterpret_cast<const T*>(a.q_norm);
+    const T* kn = reinterpret_cast<const T*>(a.k_norm);
+    const int G = a.gamma;
 #pragma unroll
     for (int qi = 0; qi < 4; ++qi) {
+        // query row R = hq*gamma + j of q head (h*group + hq) at block position j
         const int R = (qt0 + qi) * 16 + r;
-        if (qi < nqt && R < rows) load_frag64(w.qf[qi], qbase + (long long)R * D + g * (STEP / 4));
-        else zero_frag64(w.qf[qi]);
+        const bool valid = qi < nqt && R < rows;
+        const int hq = valid ? R / G : 0, j = valid ? R % G : 0;
+        float x[4][PER];
+        load_row_raw<T>(x, a.qkv + (long long)(b * G + j) * a.qkv_ld + (h * a.group + hq) * D, valid);
+        int pos = len + j;
+        pos = pos < a.rope_rows ? pos : a.rope_rows - 1;
+        norm_rope_frag<T>(w.qf[qi], x, qn, a.eps, a.rope_cos + (long long)pos * (D / 2),
+                          a.rope_sin + (long long)pos * (D / 2));
+        if (!valid) zero_frag64(w.qf[qi]);
         w.m[qi] = -INFINITY;
         w.l[qi] = 0.f;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) w.o[qi][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 
-    if (nqt > 0) {
-        if (c == 0) {
-            if (kgi == 0) {
-                const T* kb_ = reinterpret_cast<const T*>(a.kblk) + ((long long)b * a.n_kv + h) * 32 * D;
-                const T* vb_ = reinterpret_cast<const T*>(a.vblk) + ((long long)b * a.n_kv + h) * D * 32;
-                attn_subblock<T>(w, nqt, 0, a.gamma, a.scale_log2,
-                                 [&](int key) { return kb_ + (long long)key * D; },
-                                 [&](int d) { return vb_ + (long long)d * 32; });
+    if (c == 0) {
+        // the block's own keys/values, from the raw projections (k: norm + RoPE; v: rounded)
+        if (nqt > 0 && kgi == 0) {
+            Frag64 kf[2];
+            float vf[DT][8];
+            const float* kraw = a.qkv + (long long)(b * G) * a.qkv_ld + (a.n_q + h) * D;
+            const float* vraw = a.qkv + (long long)(b * G) * a.qkv_ld + (a.n_q + a.n_kv + h) * D;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int key = (r >> 2) * 8 + t * 4 + (r & 3);
+                const bool valid = key < G;
+                float x[4][PER];
+                load_row_raw<T>(x, kraw + (long long)(valid ? key : 0) * a.qkv_ld, valid);
+                int pos = len + (valid ? key : 0);
+                pos = pos < a.rope_rows ? pos : a.rope_rows - 1;
+                norm_rope_frag<T>(kf[t], x, kn, a.eps, a.rope_cos + (long long)pos * (D / 2),
+                                  a.rope_sin + (long long)pos * (D / 2));
             }
-        } else {
-            const int per_wave = a.chunk / a.kg;
-            const int k_lo = (c - 1) * a.chunk + kgi * per_wave;
-            const int k_hi = min(k_lo + per_wave, len);
-            const T* kc = reinterpret_cast<const T*>(a.kcache) + ((long long)b * a.n_kv + h) * (long long)a.cap * D;
-            const T* vc = reinterpret_cast<const T*>(a.vcache) + ((long long)b * a.n_kv + h) * (long long)D * a.cap;
-            for (int kb = k_lo; kb < k_hi; kb += 32) {
-                const int nvalid = min(32, k_hi - kb);
-                attn_subblock<T>(w, nqt, kb, nvalid, a.scale_log2,
-                                 [&](int key) { return kc + (long long)key * D; },
-                                 [&](int d) { return vc + (long long)d * a.cap + kb; });
-            }
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) {
+                    const int key = g * 8 + jj;
+                    const float v = vraw[(long long)(key < G ? key : 0) * a.qkv_ld + dt * 16 + r];
+                    vf[dt][jj] = key < G ? Elem<T>::rho(v) : 0.f;
+                }
+            attn_subblock<T>(w, nqt, G, a.scale_log2, kf, vf);
+        }
+    } else if (nqt > 0) {
+        const int per_wave = a.chunk / a.kg;
+        const int k_lo = (c - 1) * a.chunk + kgi * per_wave;
+        const int k_hi = min(k_lo + per_wave, len);
+        const T* kc = reinterpret_cast<const T*>(a.kcache) + ((long long)b * a.n_kv + h) * (long long)a.cap * D;
+        const T* vc = reinterpret_cast<const T*>(a.vcache) + ((long long)b * a.n_kv + h) * (long long)D * a.cap;
+        for (int kb = k_lo; kb < k_hi; kb += 32) {
+            const int nvalid = min(32, k_hi - kb);
+            Frag64 kf[2];
+            float vf[DT][8];
+            load_ctx_frags<T>(kf, vf, kc, vc, a.cap, kb, nvalid);
+            attn_subblock<T>(w, nqt, nvalid, a.scale_log2, kf, vf);
         }
     }
 
@@ -324,29 +439,49 @@ struct MergeArgs {
     int n_kv, group, gamma, rpad, nch_max, chunk, cap, head_dim;
 };
 
+constexpr int MERGE_MAX_CHUNKS = 1024;
+
 template <typename T>
-__global__ __launch_bounds__(128) void attn_merge_kernel(const MergeArgs a) {
-    // blockIdx.x = row (b*gamma + j), blockIdx.y = q head
+__global__ __launch_bounds__(64) void attn_merge_kernel(const MergeArgs a) {
+    // blockIdx.x = row (b*gamma + j), blockIdx.y = q head; one wavefront
+    __shared__ float wts[MERGE_MAX_CHUNKS];
     const int m = blockIdx.x, hq_all = blockIdx.y;
     const int b = m / a.gamma, j = m % a.gamma;
     const int h = hq_all / a.group, hq = hq_all % a.group;
     const int R = hq * a.gamma + j;
     const int D = a.head_dim;
+    const int lane = threadIdx.x;
     int len = a.len[b];
     len = len < 0 ? 0 : (len > a.cap ? a.cap : len);
     const int nch = 1 + (len + a.chunk - 1) / a.chunk;
     const long long base = ((long long)b * a.n_kv + h) * a.nch_max;
     float mmax = -INFINITY;
-    for (int c = 0; c < nch; ++c) mmax = fmaxf(mmax, a.mlpart[((base + c) * a.rpad + R) * 2]);
-    for (int d = threadIdx.x; d < D; d += blockDim.x) {
-        float num = 0.f, den = 0.f;
-        for (int c = 0; c < nch; ++c) {
-            const long long row = (base + c) * a.rpad + R;
-            const float mc = a.mlpart[row * 2], lc = a.mlpart[row * 2 + 1];
-            const float wgt = (mc == -INFINITY) ? 0.f : exp2f(mc - mmax);
-            num += wgt * a.opart[row * D + d];
-            den += wgt * lc;
+    for (int c = lane; c < nch; c += 64) mmax = fmaxf(mmax, a.mlpart[((base + c) * a.rpad + R) * 2]);
+    mmax = wave_max(mmax);
+    float den = 0.f;
+    for (int c = lane; c < nch; c += 64) {
+        const long long row = (base + c) * a.rpad + R;
+        const float mc = a.mlpart[row * 2];
+        const float wc = (mc == -INFINITY) ? 0.f : exp2f(mc - mmax);
+        wts[c] = wc;
+        den += wc * a.mlpart[row * 2 + 1];
+    }
+    den = wave_sum(den);
+    __syncthreads();
+    for (int d = lane; d < D; d += 64) {
+        float num = 0.f;
+        int c = 0;
+        for (; c + 4 <= nch; c += 4) {
+            const float o0 = a.opart[((base + c) * a.rpad + R) * D + d];
+            const float o1 = a.opart[((base + c + 1) * a.rpad + R) * D + d];
+            const float o2 = a.opart[((base + c + 2) * a.rpad + R) * D + d];
+            const float o3 = a.opart[((base + c + 3) * a.rpad + R) * D + d];
+            num += wts[c] * o0;
+            num += wts[c + 1] * o1;
+            num += wts[c + 2] * o2;
+            num += wts[c + 3] * o3;
         }
+        for (; c < nch; ++c) num += wts[c] * a.opart[((base + c) * a.rpad + R) * D + d];
         reinterpret_cast<T*>(a.out)[(long long)m * (gridDim.y * D) + (long long)hq_all * D + d] =
             Elem<T>::from_f(num / den);
     }

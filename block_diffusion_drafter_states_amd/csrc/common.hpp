@@ -6,10 +6,11 @@
 //    B[k=g*8+j][n=r] for j = 0..7 and receives C[m=g*4+v][n=r] for v = 0..3;
 //  * MFMA 16x16x4 f32 layout: lane (g,r) supplies A[m=r][k=g], B[k=g][n=r] and
 //    receives the same C layout.
-//  A "k-step" is 256 bytes of every operand row: each lane reads 64 contiguous
-//  bytes of a row (32 bf16 or 16 f32), which feed 4 (bf16) or 16 (f32) MFMAs.
-//  The reduction index is permuted consistently on both operands, so any
-//  assignment of k to MFMA slots gives the same dot products.
+//  A "k-step" is 256 bytes of every operand row, read as four 64-byte lines:
+//  in load i the four lanes of row r (g = 0..3) read bytes [64 i + 16 g, +16),
+//  so every load instruction covers whole 64-byte lines.  Piece i feeds MFMA i
+//  (bf16: k = 32 i + 8 g + j, the native 16x16x32 layout) or MFMAs 4i..4i+3
+//  (f32).  Both operands use the same assignment of k to MFMA slots.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -20,6 +21,7 @@ namespace dflash {
 typedef uint16_t bf16_t;  // bf16 bit pattern
 typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4_t;
 
 constexpr int WAVE = 64;
 
@@ -55,26 +57,62 @@ template <> struct Elem<float> {
     __device__ static float rho(float v) { return v; }
 };
 
-// 64 bytes of one operand row held by one lane: 4 x 16-byte pieces.
+// 64 bytes of one operand row held by one lane: 4 x 16-byte pieces, 64 bytes apart.
 struct Frag64 {
-    uint4 q[4];
+    u32x4_t q[4];
 };
 
+// p = row start + 16*g bytes (the lane's first piece); pieces follow every 64 bytes.
 __device__ __forceinline__ void load_frag64(Frag64& f, const void* p) {
-    const uint4* s = reinterpret_cast<const uint4*>(p);
+    const u32x4_t* s = reinterpret_cast<const u32x4_t*>(p);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) f.q[i] = s[i];
+    for (int i = 0; i < 4; ++i) f.q[i] = s[4 * i];
 }
 
 __device__ __forceinline__ void zero_frag64(Frag64& f) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) f.q[i] = make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < 4; ++i) f.q[i] = u32x4_t{0u, 0u, 0u, 0u};
 }
 
-__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) {
+__device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4_t& v) {
     bf16x8_t r;
     __builtin_memcpy(&r, &v, 16);
     return r;
+}
+
+// ---- explicitly scheduled vector-memory operations (streaming loops) ----------------------
+// These are opaque to the compiler's wait-count pass: the caller issues them in a
+// fixed order and waits with vm_wait<N>() (loads complete in issue order), then
+// ties the destination registers so that no use is scheduled before the wait.
+
+// LDS byte offset of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// 16 bytes per lane from global memory straight into LDS at lds + 16 * lane
+// (lds must be wave-uniform).
+__device__ __forceinline__ void dma_b128(const void* g, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(g), "s"(lds)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ void vload_b128(u32x4_t& d, const void* g) {
+    asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(d) : "v"(g) : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+__device__ __forceinline__ void tie(u32x4_t& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void tie(Frag64& f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tie(f.q[i]);
 }
 
 // acc += A_frag . B_frag over one k-step (64 bytes per lane of each operand).
@@ -92,11 +130,10 @@ template <>
 __device__ __forceinline__ void mfma_kstep<float>(f32x4_t& acc, const Frag64& a, const Frag64& b) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const uint4 av = a.q[i], bv = b.q[i];
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(av.x), __uint_as_float(bv.x), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(av.y), __uint_as_float(bv.y), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(av.z), __uint_as_float(bv.z), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(av.w), __uint_as_float(bv.w), acc, 0, 0, 0);
+        const u32x4_t av = a.q[i], bv = b.q[i];
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(av[c]), __uint_as_float(bv[c]), acc, 0, 0, 0);
     }
 }
 

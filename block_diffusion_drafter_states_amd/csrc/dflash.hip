@@ -16,7 +16,7 @@ using namespace dflash;
 namespace {
 
 constexpr size_t ALIGN = 256;
-constexpr size_t COUNTER_SLOTS = 65536;   // fixed-size, self-resetting counters at workspace offset 0
+constexpr size_t GEMM_MAX_LDS = 160 * 1024 - 4096;   // dynamic LDS per workgroup (static LDS needs the rest)
 
 inline size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
@@ -66,8 +66,7 @@ int make_shape(const dflash_config* c, Shape& s) {
     if (s.cap % 64) return DFLASH_EUNSUPPORTED;
     if (s.H % s.step || s.I % s.step || (s.nq * s.D) % s.step || ((long long)s.F * s.H) % s.step)
         return DFLASH_EUNSUPPORTED;
-    if (s.H % GEMM_TILE_N || (s.nq * s.D) % GEMM_TILE_N || (s.nkv * s.D) % GEMM_TILE_N || s.I % 64)
-        return DFLASH_EUNSUPPORTED;
+    if (s.H % 128 || (s.nq * s.D) % 128 || (s.nkv * s.D) % 128 || s.I % 64) return DFLASH_EUNSUPPORTED;
     s.group = s.nq / s.nkv;
     if (s.group * s.gmax > 256) return DFLASH_EUNSUPPORTED;
     s.rpad = cdiv(s.group * s.gmax, 16) * 16;
@@ -82,34 +81,62 @@ int make_shape(const dflash_config* c, Shape& s) {
     while (ch > 256 && (long long)s.Bmax * s.nkv * cdiv(s.cap, ch) < 512) ch >>= 1;
     s.chunk = ch;
     s.nch_max = 1 + cdiv(s.cap, ch);
+    if (s.nch_max > MERGE_MAX_CHUNKS) return DFLASH_EUNSUPPORTED;
     return DFLASH_OK;
 }
 
 struct GemmPlan {
-    int n_tiles, n_mgroups, S, kw, layers;
-    size_t partial_floats;
-    size_t counters;
-    int mpad;
+    int ns, ks, kw, n_tiles, mt, mgroups, layers, ntw, epi, amode;
+    bool prenorm;   // RMSNorm applied by rmsnorm_rows_kernel first (A_NORM request with several M-tiles)
+    size_t lds;
 };
 
-GemmPlan plan_gemm(const Shape& s, int n_tiles, int M, int K, int layers) {
+// Geometry of one projection.  wrows = weight rows (EPI_SWIGLU: rows of each of
+// gate/up).  Every workgroup owns complete output columns (no cross-workgroup
+// reduction); its waves split K (ks) and rows (ns).  Choices follow a sweep on
+// MI355X: A_PLAIN streams best with 4 waves splitting K and a 4-deep ring,
+// A_NORM (more A registers, 2-deep ring) with 2 or 1 waves along K; one
+// workgroup's LDS rings must fit the 160 KB of a CU.
+GemmPlan plan_gemm(const Shape& s, int epi, int amode, int wrows, int K, int M, int layers) {
     GemmPlan p;
-    p.n_tiles = n_tiles;
-    p.n_mgroups = cdiv(M, GEMM_MAX_M);
+    p.epi = epi;
     p.layers = layers;
-    const int base = n_tiles * p.n_mgroups * layers;
-    const int maxS = K / s.step;
-    const int mrows = std::min(M, GEMM_MAX_M);
-    const int capS = std::max(1, (int)((long long)K * s.esize / (32LL * std::max(16, mrows))));
-    int S = 1;
-    while ((long long)base * S < 512 && S < maxS && S < capS) ++S;
-    int kw = cdiv(cdiv(K, S), s.step) * s.step;
-    S = cdiv(K, kw);
-    p.S = S;
-    p.kw = kw;
-    p.partial_floats = S > 1 ? (size_t)layers * n_tiles * S * (size_t)M * GEMM_TILE_N : 0;
-    p.counters = (size_t)layers * p.n_mgroups * n_tiles + 1;
-    p.mpad = std::min(GEMM_MAX_M, cdiv(M, 16) * 16);
+    p.ntw = GEMM_NT;
+    p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+    p.mgroups = cdiv(M, 16 * p.mt);
+    // normalising on load keeps fp32 rows of every M-tile in registers; beyond one
+    // M-tile the rows are normalised once up front and streamed as plain A
+    p.prenorm = amode == A_NORM && p.mt > 1;
+    if (p.prenorm) amode = A_PLAIN;
+    p.amode = amode;
+    const int ring = gemm_ring_depth(amode, p.mt, p.ntw);
+    int ks;
+    if (epi == EPI_KV_INJECT) {
+        p.ns = s.D / (GEMM_NT * 16);            // one head per workgroup
+        p.n_tiles = 2 * s.nkv;
+        ks = 1;
+    } else if (epi == EPI_ARGMAX) {
+        p.ns = 1;
+        p.n_tiles = cdiv(wrows, p.ns * p.ntw * 16);
+        ks = 1;
+    } else if (epi == EPI_SWIGLU) {
+        p.ns = 1;
+        p.n_tiles = cdiv(wrows, p.ns * 16);         // 16 output columns (gate + up tiles) per wave group
+        ks = 2;
+    } else {
+        p.ns = 1;
+        p.n_tiles = cdiv(wrows, p.ns * p.ntw * 16);
+        ks = amode == A_PLAIN ? 4 : 2;
+    }
+    while (ks > 1 && K / s.step < 2 * ks) ks /= 2;        // at least two k-steps per wave
+    while (ks > 1 && gemm_lds_bytes_host(p.ns, ks, p.mt, p.ntw, ring) > GEMM_MAX_LDS) ks /= 2;
+    while (p.ns > 1 && gemm_lds_bytes_host(p.ns, ks, p.mt, p.ntw, ring) > GEMM_MAX_LDS) {
+        p.ns /= 2;
+        p.n_tiles *= 2;
+    }
+    p.ks = ks;
+    p.kw = cdiv(cdiv(K, ks), s.step) * s.step;
+    p.lds = gemm_lds_bytes_host(p.ns, p.ks, p.mt, p.ntw, ring);
     return p;
 }
 
@@ -125,107 +152,94 @@ AttnPlan plan_attn(const Shape& s, int gamma) {
     return a;
 }
 
-// Workspace carving.  Offsets of the counters and argmax slots are fixed (they
-// persist between calls); everything after them is per-call scratch.
+// Workspace carving.  Everything is per-call scratch: no state survives a call.
 struct Layout {
-    size_t counters, slots;
     // draft
-    size_t x, ssq_x, qbuf, kblk, vblk, opart, mlpart, obuf, hbuf, dpartial, draft_end;
+    size_t x, ssq_x, qkv, opart, mlpart, obuf, hbuf, amax, nbuf, draft_end;
     // inject
-    size_t c, ssq_c, ipartial, inject_end;
-    size_t dpartial_floats, ipartial_floats;
+    size_t c, ssq_c, cnorm, inject_end;
 };
 
-void draft_plans(const Shape& s, int batch, GemmPlan* g) {
-    const int M = batch * s.gmax;
-    g[0] = plan_gemm(s, (s.nq * s.D + 2 * s.nkv * s.D) / GEMM_TILE_N, M, s.H, 1);   // qkv
-    g[1] = plan_gemm(s, s.H / GEMM_TILE_N, M, s.nq * s.D, 1);                      // o
-    g[2] = plan_gemm(s, s.I / 64, M, s.H, 1);                                       // gate/up
-    g[3] = plan_gemm(s, s.H / GEMM_TILE_N, M, s.I, 1);                              // down
-    g[4] = plan_gemm(s, cdiv(s.V, GEMM_TILE_N), M, s.H, 1);                         // lm head
-}
-
-void inject_plans(const Shape& s, int batch, int rows, GemmPlan* g) {
-    const int M = batch * rows;
-    g[0] = plan_gemm(s, s.H / GEMM_TILE_N, M, s.F * s.H, 1);                     // fuse
-    g[1] = plan_gemm(s, 2 * s.nkv * s.D / GEMM_TILE_N, M, s.H, s.L);            // kv (all layers)
-}
+int lm_tiles(const Shape& s) { return cdiv(s.V, 8 * GEMM_NT * 16); }
 
 Layout make_layout(const Shape& s, int batch, int rows) {
     Layout l;
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
-    l.counters = take(COUNTER_SLOTS * sizeof(unsigned));
-    l.slots = take((size_t)s.Bmax * (s.gmax - 1) * sizeof(unsigned long long));
     const size_t M = (size_t)batch * s.gmax;
+    const int ntH = s.H / (GEMM_NT * 16);
     l.x = take(M * s.H * 4);
-    l.ssq_x = take((size_t)(s.H / GEMM_TILE_N) * M * 4);
-    l.qbuf = take((size_t)batch * s.nkv * s.rpad * s.D * s.esize);
-    l.kblk = take((size_t)batch * s.nkv * 32 * s.D * s.esize);
-    l.vblk = take((size_t)batch * s.nkv * 32 * s.D * s.esize);
+    l.ssq_x = take((size_t)ntH * M * 4);
+    l.qkv = take(M * (size_t)(s.nq + 2 * s.nkv) * s.D * 4);
     l.opart = take((size_t)batch * s.nkv * s.nch_max * s.rpad * s.D * 4);
     l.mlpart = take((size_t)batch * s.nkv * s.nch_max * s.rpad * 2 * 4);
     l.obuf = take(M * s.nq * s.D * s.esize);
     l.hbuf = take(M * s.I * s.esize);
-    GemmPlan dp[5];
-    draft_plans(s, batch, dp);
-    l.dpartial_floats = 0;
-    for (auto& p : dp) l.dpartial_floats = std::max(l.dpartial_floats, p.partial_floats);
-    l.dpartial = take(l.dpartial_floats * 4);
+    l.amax = take((size_t)lm_tiles(s) * M * 8);
+    l.nbuf = take(M > 16 ? M * s.H * s.esize : 0);            // normalised rows (batch > 1)
     l.draft_end = off;
-    l.c = l.ssq_c = l.ipartial = 0;
-    l.ipartial_floats = 0;
+    l.c = l.ssq_c = l.cnorm = 0;
     if (rows > 0) {
         const size_t Mi = (size_t)batch * rows;
         l.c = take(Mi * s.H * 4);
-        l.ssq_c = take((size_t)(s.H / GEMM_TILE_N) * Mi * 4);
-        GemmPlan ip[2];
-        inject_plans(s, batch, rows, ip);
-        l.ipartial_floats = std::max(ip[0].partial_floats, ip[1].partial_floats);
-        l.ipartial = take(l.ipartial_floats * 4);
+        l.ssq_c = take((size_t)ntH * Mi * 4);
+        l.cnorm = take(Mi > 16 ? (size_t)s.L * Mi * s.H * s.esize : 0);   // per-layer normalised rows
     }
     l.inject_end = off;
     return l;
 }
 
-template <typename T, int EPI>
-int launch_gemm(const GemmArgs& a, const GemmPlan& p, size_t lds, hipStream_t st, Tracer& tr, const char* name) {
-    dim3 grid(8 * cdiv(p.n_tiles, 8) * p.S, p.n_mgroups, p.layers);
+template <typename T, int EPI, int AMODE, int MT>
+int launch_gemm(const GemmArgs& a, const GemmPlan& p, hipStream_t st, Tracer& tr, const char* name) {
+    constexpr int P = gemm_ring_depth(AMODE, MT, GEMM_NT);
+    dim3 grid(p.n_tiles, p.mgroups, p.layers);
     tr.begin(name);
-    hipLaunchKernelGGL((gemm_kernel<T, EPI>), grid, dim3(GEMM_THREADS), lds, st, a);
+    hipLaunchKernelGGL((gemm_kernel<T, EPI, AMODE, MT, P>), grid, dim3(64 * p.ns * p.ks), p.lds, st, a);
     const bool ok = hipGetLastError() == hipSuccess;
     tr.end();
     return ok ? DFLASH_OK : DFLASH_ELAUNCH;
 }
 
-template <typename T>
-int gemm_dispatch(int epi, const GemmArgs& a, const GemmPlan& p, const Shape& s, hipStream_t st, Tracer& tr,
-                  const char* name) {
-    const size_t lds = gemm_lds_bytes_host(s.esize, p.mpad);
-    switch (epi) {
-        case EPI_STORE: return launch_gemm<T, EPI_STORE>(a, p, lds, st, tr, name);
-        case EPI_QKV: return launch_gemm<T, EPI_QKV>(a, p, lds, st, tr, name);
-        case EPI_SWIGLU: return launch_gemm<T, EPI_SWIGLU>(a, p, lds, st, tr, name);
-        case EPI_ARGMAX: return launch_gemm<T, EPI_ARGMAX>(a, p, lds, st, tr, name);
-        case EPI_KV_INJECT: return launch_gemm<T, EPI_KV_INJECT>(a, p, lds, st, tr, name);
+template <typename T, int EPI, int AMODE>
+int launch_gemm_mt(const GemmArgs& a, const GemmPlan& p, hipStream_t st, Tracer& tr, const char* name) {
+    if constexpr (AMODE == A_NORM) {
+        return p.mt == 1 ? launch_gemm<T, EPI, A_NORM, 1>(a, p, st, tr, name) : DFLASH_EINVAL;
+    } else {
+        switch (p.mt) {
+            case 1: return launch_gemm<T, EPI, AMODE, 1>(a, p, st, tr, name);
+            case 2: return launch_gemm<T, EPI, AMODE, 2>(a, p, st, tr, name);
+            case 4: return launch_gemm<T, EPI, AMODE, 4>(a, p, st, tr, name);
+        }
+        return DFLASH_EINVAL;
     }
+}
+
+template <typename T>
+int gemm_dispatch(const GemmArgs& a, const GemmPlan& p, hipStream_t st, Tracer& tr, const char* name) {
+    if (p.epi == EPI_STORE && p.amode == A_PLAIN) return launch_gemm_mt<T, EPI_STORE, A_PLAIN>(a, p, st, tr, name);
+    if (p.epi == EPI_SWIGLU && p.amode == A_PLAIN) return launch_gemm_mt<T, EPI_SWIGLU, A_PLAIN>(a, p, st, tr, name);
+    if (p.epi == EPI_ARGMAX && p.amode == A_PLAIN) return launch_gemm_mt<T, EPI_ARGMAX, A_PLAIN>(a, p, st, tr, name);
+    if (p.epi == EPI_KV_INJECT && p.amode == A_PLAIN)
+        return launch_gemm_mt<T, EPI_KV_INJECT, A_PLAIN>(a, p, st, tr, name);
+    if (p.epi == EPI_STORE && p.amode == A_NORM) return launch_gemm_mt<T, EPI_STORE, A_NORM>(a, p, st, tr, name);
+    if (p.epi == EPI_SWIGLU && p.amode == A_NORM) return launch_gemm_mt<T, EPI_SWIGLU, A_NORM>(a, p, st, tr, name);
+    if (p.epi == EPI_ARGMAX && p.amode == A_NORM) return launch_gemm_mt<T, EPI_ARGMAX, A_NORM>(a, p, st, tr, name);
+    if (p.epi == EPI_KV_INJECT && p.amode == A_NORM)
+        return launch_gemm_mt<T, EPI_KV_INJECT, A_NORM>(a, p, st, tr, name);
     return DFLASH_EINVAL;
 }
 
-GemmArgs gemm_base(const Shape& s, const GemmPlan& p, int M, int K, void* ws, const Layout& lay, float* partial) {
+GemmArgs gemm_base(const Shape& s, const GemmPlan& p, int M, int K) {
     GemmArgs a;
     std::memset(&a, 0, sizeof(a));
     a.M = M;
     a.K = K;
     a.eps = s.eps;
-    a.S = p.S;
+    a.ns = p.ns;
+    a.ks = p.ks;
     a.kw = p.kw;
     a.n_tiles = p.n_tiles;
-    a.n_mgroups = p.n_mgroups;
     a.n_layers = p.layers;
-    a.partial = partial;
-    a.counters = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + lay.counters);
-    a.n_q = s.nq;
     a.n_kv = s.nkv;
     a.head_dim = s.D;
     a.cap = s.cap;
@@ -245,45 +259,97 @@ bool weights_ok(const Shape& s, const dflash_weights* w) {
     return true;
 }
 
+struct InjectPlans {
+    GemmPlan fuse, kv;
+};
+
+InjectPlans inject_plans(const Shape& s, int batch, int rows) {
+    const int M = batch * rows;
+    return {plan_gemm(s, EPI_STORE, A_PLAIN, s.H, s.F * s.H, M, 1),
+            plan_gemm(s, EPI_KV_INJECT, A_NORM, 2 * s.nkv * s.D, s.H, M, s.L)};
+}
+
+struct DraftPlans {
+    GemmPlan qkv, o, gateup, down, lm;
+};
+
+DraftPlans draft_plans(const Shape& s, int M) {
+    return {plan_gemm(s, EPI_STORE, A_NORM, (s.nq + 2 * s.nkv) * s.D, s.H, M, 1),
+            plan_gemm(s, EPI_STORE, A_PLAIN, s.H, s.nq * s.D, M, 1),
+            plan_gemm(s, EPI_SWIGLU, A_NORM, s.I, s.H, M, 1),
+            plan_gemm(s, EPI_STORE, A_PLAIN, s.H, s.I, M, 1),
+            plan_gemm(s, EPI_ARGMAX, A_NORM, s.V, s.H, M, 1)};
+}
+
+// A operand = RMSNorm(x; w): normalised on load (one M-tile), or normalised once
+// into nbuf by rmsnorm_rows_kernel and then streamed as plain A.
+template <typename T>
+int set_norm_a(GemmArgs& a, const GemmPlan& p, const Shape& s, const float* x, int M, const float* ssq, int n_ssq,
+               const void* w, void* nbuf, hipStream_t st, Tracer& tr) {
+    if (!p.prenorm) {
+        a.a = x;
+        a.lda = s.H;
+        a.ssq = ssq;
+        a.n_ssq = n_ssq;
+        a.ssq_ld = M;
+        a.layer[0].norm_w = w;
+        return DFLASH_OK;
+    }
+    NormWeights nw{};
+    nw.w[0] = w;
+    tr.begin("rmsnorm");
+    hipLaunchKernelGGL((rmsnorm_rows_kernel<T>), dim3(M, cdiv(s.H, 1024), 1), dim3(256), 0, st, x, s.H, ssq, n_ssq, M,
+                       nw, s.H, s.eps, static_cast<T*>(nbuf), s.H, 0LL);
+    tr.end();
+    a.a = nbuf;
+    a.lda = s.H;
+    return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_ELAUNCH;
+}
+
 template <typename T>
 int run_inject(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int batch, const void* feat,
                int rows, const int* n_new, void* ws, const Layout& lay, hipStream_t st, Tracer& tr) {
     char* wsb = static_cast<char*>(ws);
-    GemmPlan pl[2];
-    inject_plans(s, batch, rows, pl);
+    const InjectPlans pl = inject_plans(s, batch, rows);
     const int M = batch * rows;
     float* c = reinterpret_cast<float*>(wsb + lay.c);
     float* ssq_c = reinterpret_cast<float*>(wsb + lay.ssq_c);
-    float* part = reinterpret_cast<float*>(wsb + lay.ipartial);
     int rc;
     {   // stage 1: c = W_fuse . concat(feat)
-        GemmArgs a = gemm_base(s, pl[0], M, s.F * s.H, ws, lay, part);
-        a.a_mode = A_PLAIN;
+        GemmArgs a = gemm_base(s, pl.fuse, M, s.F * s.H);
         a.a = feat;
         a.lda = (long long)s.F * s.H;
-        a.n_seg = 1;
-        a.seg_n[0] = s.H;
         a.N = s.H;
+        a.seg_end[0] = a.seg_end[1] = a.seg_end[2] = s.H;
         a.layer[0].w[0] = w->w_fuse;
         a.out = c;
         a.ldo = s.H;
         a.residual = 0;
         a.ssq_out = ssq_c;
         a.ssq_out_ld = M;
-        if ((rc = gemm_dispatch<T>(EPI_STORE, a, pl[0], s, st, tr, "fuse"))) return rc;
+        if ((rc = gemm_dispatch<T>(a, pl.fuse, st, tr, "fuse"))) return rc;
     }
     {   // stage 2: every layer's RMSNorm -> W_k | W_v -> k-norm + RoPE -> cache
-        GemmArgs a = gemm_base(s, pl[1], M, s.H, ws, lay, part);
-        a.a_mode = A_NORM;
+        GemmArgs a = gemm_base(s, pl.kv, M, s.H);
         a.a = c;
         a.lda = s.H;
         a.ssq = ssq_c;
-        a.n_ssq = s.H / GEMM_TILE_N;
+        a.n_ssq = pl.fuse.n_tiles;
         a.ssq_ld = M;
-        a.n_seg = 2;
-        a.seg_n[0] = s.nkv * s.D;
-        a.seg_n[1] = s.nkv * s.D;
+        if (pl.kv.prenorm) {   // one normalised copy of c per layer (each layer has its own scale)
+            NormWeights nw{};
+            for (int l = 0; l < s.L; ++l) nw.w[l] = w->layers[l].in_norm;
+            T* cn = reinterpret_cast<T*>(wsb + lay.cnorm);
+            tr.begin("rmsnorm");
+            hipLaunchKernelGGL((rmsnorm_rows_kernel<T>), dim3(M, cdiv(s.H, 1024), s.L), dim3(256), 0, st, c, s.H,
+                               ssq_c, pl.fuse.n_tiles, M, nw, s.H, s.eps, cn, s.H, (long long)M * s.H);
+            tr.end();
+            if (hipGetLastError() != hipSuccess) return DFLASH_ELAUNCH;
+            for (int l = 0; l < s.L; ++l) a.layer[l].a = cn + (size_t)l * M * s.H;
+        }
         a.N = 2 * s.nkv * s.D;
+        a.seg_end[0] = s.nkv * s.D;
+        a.seg_end[1] = a.seg_end[2] = 2 * s.nkv * s.D;
         const size_t layer_elems = (size_t)s.Bmax * s.nkv * s.cap * s.D;
         for (int l = 0; l < s.L; ++l) {
             const dflash_layer_weights& lw = w->layers[l];
@@ -301,10 +367,13 @@ int run_inject(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int
         a.rope_sin = w->rope_sin;
         a.rope_rows = w->rope_rows;
         a.status = kv->status;
-        a.batch = batch;
-        if ((rc = gemm_dispatch<T>(EPI_KV_INJECT, a, pl[1], s, st, tr, "inject_kv"))) return rc;
+        if ((rc = gemm_dispatch<T>(a, pl.kv, st, tr, "inject_kv"))) return rc;
     }
-    return DFLASH_OK;
+    tr.begin("inject_finish");
+    hipLaunchKernelGGL(inject_finish_kernel, dim3(1), dim3(64), 0, st, batch, rows, s.cap, w->rope_rows, kv->len,
+                       n_new, kv->status);
+    tr.end();
+    return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_ELAUNCH;
 }
 
 template <typename T>
@@ -313,29 +382,17 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
               hipStream_t st, Tracer& tr) {
     char* wsb = static_cast<char*>(ws);
     const int M = batch * gamma;
-    GemmPlan pl[5];
-    {
-        // plans for the call's gamma (workspace was sized for gamma_max)
-        const int Mg = M;
-        pl[0] = plan_gemm(s, (s.nq * s.D + 2 * s.nkv * s.D) / GEMM_TILE_N, Mg, s.H, 1);
-        pl[1] = plan_gemm(s, s.H / GEMM_TILE_N, Mg, s.nq * s.D, 1);
-        pl[2] = plan_gemm(s, s.I / 64, Mg, s.H, 1);
-        pl[3] = plan_gemm(s, s.H / GEMM_TILE_N, Mg, s.I, 1);
-        pl[4] = plan_gemm(s, cdiv(s.V, GEMM_TILE_N), Mg, s.H, 1);
-        for (auto& p : pl)
-            if (p.partial_floats > lay.dpartial_floats || p.counters > COUNTER_SLOTS) return DFLASH_EUNSUPPORTED;
-    }
+    const DraftPlans pl = draft_plans(s, M);
     float* x = reinterpret_cast<float*>(wsb + lay.x);
     float* ssq_x = reinterpret_cast<float*>(wsb + lay.ssq_x);
-    float* part = reinterpret_cast<float*>(wsb + lay.dpartial);
-    void* qbuf = wsb + lay.qbuf;
-    void* kblk = wsb + lay.kblk;
-    void* vblk = wsb + lay.vblk;
+    float* qkv = reinterpret_cast<float*>(wsb + lay.qkv);
     float* opart = reinterpret_cast<float*>(wsb + lay.opart);
     float* mlpart = reinterpret_cast<float*>(wsb + lay.mlpart);
     void* obuf = wsb + lay.obuf;
     void* hbuf = wsb + lay.hbuf;
-    const int ntH = s.H / GEMM_TILE_N;
+    unsigned long long* amax = reinterpret_cast<unsigned long long*>(wsb + lay.amax);
+    void* nbuf = wsb + lay.nbuf;
+    const int qkv_ld = (s.nq + 2 * s.nkv) * s.D;
     int rc;
 
     tr.begin("embed");
@@ -351,49 +408,37 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
 
     for (int l = 0; l < s.L; ++l) {
         const dflash_layer_weights& lw = w->layers[l];
-        {   // q, k, v of the block (+ per-head norm, RoPE)
-            GemmArgs a = gemm_base(s, pl[0], M, s.H, ws, lay, part);
-            a.a_mode = A_NORM;
-            a.a = x;
-            a.lda = s.H;
-            a.ssq = ssq_x;
-            a.n_ssq = n_ssq;
-            a.ssq_ld = M;
-            a.n_seg = 3;
-            a.seg_n[0] = s.nq * s.D;
-            a.seg_n[1] = s.nkv * s.D;
-            a.seg_n[2] = s.nkv * s.D;
-            a.N = (s.nq + 2 * s.nkv) * s.D;
+        {   // raw q | k | v of the block (three weight tensors, one launch)
+            GemmArgs a = gemm_base(s, pl.qkv, M, s.H);
+            if ((rc = set_norm_a<T>(a, pl.qkv, s, x, M, ssq_x, n_ssq, lw.in_norm, nbuf, st, tr))) return rc;
+            a.N = qkv_ld;
+            a.seg_end[0] = s.nq * s.D;
+            a.seg_end[1] = (s.nq + s.nkv) * s.D;
+            a.seg_end[2] = qkv_ld;
             a.layer[0].w[0] = lw.wq;
             a.layer[0].w[1] = lw.wk;
             a.layer[0].w[2] = lw.wv;
-            a.layer[0].norm_w = lw.in_norm;
-            a.layer[0].head_norm = lw.q_norm;
-            a.layer[0].head_norm2 = lw.k_norm;
-            a.qbuf = qbuf;
-            a.kblk = kblk;
-            a.vblk = vblk;
-            a.rpad = s.rpad;
-            a.gamma = gamma;
-            a.len = kv->len;
-            a.rope_cos = w->rope_cos;
-            a.rope_sin = w->rope_sin;
-            a.rope_rows = w->rope_rows;
-            a.status = kv->status;
-            a.batch = batch;
-            if ((rc = gemm_dispatch<T>(EPI_QKV, a, pl[0], s, st, tr, "qkv"))) return rc;
+            a.out = qkv;
+            a.ldo = qkv_ld;
+            if ((rc = gemm_dispatch<T>(a, pl.qkv, st, tr, "qkv_proj"))) return rc;
         }
         {   // attention over [context ; block]
             AttnArgs a;
             std::memset(&a, 0, sizeof(a));
             a.kcache = static_cast<const T*>(kv->k) + l * layer_elems;
             a.vcache = static_cast<const T*>(kv->v) + l * layer_elems;
-            a.qbuf = qbuf;
-            a.kblk = kblk;
-            a.vblk = vblk;
+            a.qkv = qkv;
+            a.qkv_ld = qkv_ld;
+            a.q_norm = lw.q_norm;
+            a.k_norm = lw.k_norm;
+            a.rope_cos = w->rope_cos;
+            a.rope_sin = w->rope_sin;
+            a.rope_rows = w->rope_rows;
+            a.eps = s.eps;
             a.len = kv->len;
             a.opart = opart;
             a.mlpart = mlpart;
+            a.n_q = s.nq;
             a.n_kv = s.nkv;
             a.cap = s.cap;
             a.rpad = s.rpad;
@@ -423,61 +468,50 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
             mgr.cap = s.cap;
             mgr.head_dim = s.D;
             tr.begin("attn_merge");
-            hipLaunchKernelGGL((attn_merge_kernel<T>), dim3(M, s.nq), dim3(128), 0, st, mgr);
+            hipLaunchKernelGGL((attn_merge_kernel<T>), dim3(M, s.nq), dim3(64), 0, st, mgr);
             tr.end();
             if (hipGetLastError() != hipSuccess) return DFLASH_ELAUNCH;
         }
         {   // x += W_o o
-            GemmArgs a = gemm_base(s, pl[1], M, s.nq * s.D, ws, lay, part);
-            a.a_mode = A_PLAIN;
+            GemmArgs a = gemm_base(s, pl.o, M, s.nq * s.D);
             a.a = obuf;
             a.lda = s.nq * s.D;
-            a.n_seg = 1;
-            a.seg_n[0] = s.H;
             a.N = s.H;
+            a.seg_end[0] = a.seg_end[1] = a.seg_end[2] = s.H;
             a.layer[0].w[0] = lw.wo;
             a.out = x;
             a.ldo = s.H;
             a.residual = 1;
             a.ssq_out = ssq_x;
             a.ssq_out_ld = M;
-            if ((rc = gemm_dispatch<T>(EPI_STORE, a, pl[1], s, st, tr, "o_proj"))) return rc;
-            n_ssq = ntH;
+            if ((rc = gemm_dispatch<T>(a, pl.o, st, tr, "o_proj"))) return rc;
+            n_ssq = pl.o.n_tiles;
         }
         {   // h = silu(W_gate a2) * (W_up a2)
-            GemmArgs a = gemm_base(s, pl[2], M, s.H, ws, lay, part);
-            a.a_mode = A_NORM;
-            a.a = x;
-            a.lda = s.H;
-            a.ssq = ssq_x;
-            a.n_ssq = n_ssq;
-            a.ssq_ld = M;
-            a.n_seg = 2;
-            a.seg_n[0] = s.I;
-            a.seg_n[1] = s.I;
-            a.N = 2 * s.I;
+            GemmArgs a = gemm_base(s, pl.gateup, M, s.H);
+            if ((rc = set_norm_a<T>(a, pl.gateup, s, x, M, ssq_x, n_ssq, lw.post_norm, nbuf, st, tr))) return rc;
+            a.N = s.I;
+            a.seg_end[0] = a.seg_end[1] = a.seg_end[2] = s.I;
             a.layer[0].w[0] = lw.w_gate;
             a.layer[0].w[1] = lw.w_up;
-            a.layer[0].norm_w = lw.post_norm;
             a.out_t = hbuf;
             a.ldo = s.I;
-            if ((rc = gemm_dispatch<T>(EPI_SWIGLU, a, pl[2], s, st, tr, "gate_up"))) return rc;
+            if ((rc = gemm_dispatch<T>(a, pl.gateup, st, tr, "gate_up"))) return rc;
         }
         {   // x += W_down h
-            GemmArgs a = gemm_base(s, pl[3], M, s.I, ws, lay, part);
-            a.a_mode = A_PLAIN;
+            GemmArgs a = gemm_base(s, pl.down, M, s.I);
             a.a = hbuf;
             a.lda = s.I;
-            a.n_seg = 1;
-            a.seg_n[0] = s.H;
             a.N = s.H;
+            a.seg_end[0] = a.seg_end[1] = a.seg_end[2] = s.H;
             a.layer[0].w[0] = lw.w_down;
             a.out = x;
             a.ldo = s.H;
             a.residual = 1;
             a.ssq_out = ssq_x;
             a.ssq_out_ld = M;
-            if ((rc = gemm_dispatch<T>(EPI_STORE, a, pl[3], s, st, tr, "down_proj"))) return rc;
+            if ((rc = gemm_dispatch<T>(a, pl.down, st, tr, "down_proj"))) return rc;
+            n_ssq = pl.down.n_tiles;
         }
     }
     if (dbg_hidden) {
@@ -488,27 +522,22 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
         tr.end();
         if (hipGetLastError() != hipSuccess) return DFLASH_ELAUNCH;
     }
-    {   // final norm -> LM head -> argmax over the vocabulary
-        GemmArgs a = gemm_base(s, pl[4], M, s.H, ws, lay, part);
-        a.a_mode = A_NORM;
-        a.a = x;
-        a.lda = s.H;
-        a.ssq = ssq_x;
-        a.n_ssq = n_ssq;
-        a.ssq_ld = M;
-        a.n_seg = 1;
-        a.seg_n[0] = s.V;
+    {   // final norm -> LM head -> per-tile argmax
+        GemmArgs a = gemm_base(s, pl.lm, M, s.H);
+        if ((rc = set_norm_a<T>(a, pl.lm, s, x, M, ssq_x, n_ssq, w->final_norm, nbuf, st, tr))) return rc;
         a.N = s.V;
+        a.seg_end[0] = a.seg_end[1] = a.seg_end[2] = s.V;
         a.layer[0].w[0] = w->lm_head;
-        a.layer[0].norm_w = w->final_norm;
         a.gamma = gamma;
-        a.batch = batch;
-        a.slots = reinterpret_cast<unsigned long long*>(wsb + lay.slots);
-        a.draft = draft;
+        a.amax = amax;
         a.dbg_logits = dbg_logits;
-        if ((rc = gemm_dispatch<T>(EPI_ARGMAX, a, pl[4], s, st, tr, "lm_head_argmax"))) return rc;
+        if ((rc = gemm_dispatch<T>(a, pl.lm, st, tr, "lm_head_argmax"))) return rc;
     }
-    return DFLASH_OK;
+    tr.begin("argmax_finish");
+    hipLaunchKernelGGL(argmax_finish_kernel, dim3(batch * (gamma - 1)), dim3(256), 0, st, amax, pl.lm.n_tiles, M,
+                       gamma, draft);
+    tr.end();
+    return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_ELAUNCH;
 }
 
 }  // namespace
@@ -537,9 +566,6 @@ int dflash_inject_kv_traced(const dflash_config* cfg, const dflash_weights* w, c
     if (!workspace) return DFLASH_EWORKSPACE;
     const Layout lay = make_layout(s, batch, rows_stride);
     if (workspace_bytes < lay.inject_end) return DFLASH_EWORKSPACE;
-    GemmPlan ip[2];
-    inject_plans(s, batch, rows_stride, ip);
-    if (ip[0].counters > COUNTER_SLOTS || ip[1].counters > COUNTER_SLOTS) return DFLASH_EUNSUPPORTED;
     hipStream_t st = static_cast<hipStream_t>(stream);
     Tracer tr{trace, st};
     if (trace) trace->count = 0;

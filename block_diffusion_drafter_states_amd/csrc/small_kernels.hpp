@@ -59,6 +59,36 @@ __global__ __launch_bounds__(64) void verify_kernel(int batch, int gamma, const 
     }
 }
 
+// out[z][m][k] = rho(x[m][k] * rstd_m * w_z[k]); rstd_m from the per-tile sums of
+// squares of row m.  blockIdx.x = row, blockIdx.y = 1024-column chunk,
+// blockIdx.z = weight set (one per layer when the same rows feed every layer).
+struct NormWeights {
+    const void* w[16];
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const float* __restrict__ x, int ldx,
+                                                           const float* __restrict__ ssq, int n_ssq, int ssq_ld,
+                                                           const NormWeights wz, int K, float eps,
+                                                           T* __restrict__ out, int ldo, long long out_z) {
+    __shared__ float rs_sh;
+    const int m = blockIdx.x;
+    if (threadIdx.x < 64) {
+        float s = 0.f;
+        for (int t = threadIdx.x; t < n_ssq; t += 64) s += ssq[(long long)t * ssq_ld + m];
+        s = wave_sum(s);
+        if (threadIdx.x == 0) rs_sh = 1.0f / sqrtf(s / (float)K + eps);
+    }
+    __syncthreads();
+    const float rs = rs_sh;
+    const T* w = reinterpret_cast<const T*>(wz.w[blockIdx.z]);
+    T* o = out + (long long)blockIdx.z * out_z + (long long)m * ldo;
+    const float* xr = x + (long long)m * ldx;
+    const int kend = min(K, (int)(blockIdx.y + 1) * 1024);
+    for (int k = blockIdx.y * 1024 + threadIdx.x; k < kend; k += 256)
+        o[k] = Elem<T>::from_f(xr[k] * rs * Elem<T>::to_f(w[k]));
+}
+
 __global__ __launch_bounds__(256) void copy_f32_kernel(const float* __restrict__ src, float* __restrict__ dst,
                                                        long long n) {
     for (long long i = blockIdx.x * 256ll + threadIdx.x; i < n; i += (long long)gridDim.x * 256) dst[i] = src[i];
