@@ -7,17 +7,23 @@
 //
 // Work split ("split-K" over keys): chunk 0 of each (b,h) holds the block
 // rows, chunks 1.. hold CH context rows each.  A workgroup of 4 wavefronts
-// takes one chunk; its waves split the chunk's keys (and, for g*gamma > 64,
-// the query rows).  Each wave streams keys in sub-blocks of 32:
-//   S^T = K . Q^T   (A = key rows read straight from the cache, B = queries)
-// with the key rows permuted so that every lane ends up holding 8 consecutive
-// keys of one query - exactly the A-operand layout of the following
-//   O  += P . V     (B = V^T rows, read straight from the transposed V cache).
-// Online softmax in base 2 (log2(e)/sqrt(D) folded into the scale); for bf16
-// the PV product takes P as a hi + lo pair of bf16 values.  The waves of a workgroup
-// merge through LDS; the workgroup writes (m, l, O) for its chunk, and
-// attn_merge combines the chunks of a (b,h) with log-sum-exp weights in fixed
-// chunk order.
+// takes one chunk:
+//  * prologue: the query rows get the per-head q RMSNorm and RoPE once per
+//    workgroup (wave w builds query tiles w, w+4, ...) and are kept as MFMA
+//    fragments in LDS; chunk 0 also builds the block's keys (k RMSNorm + RoPE)
+//    and values (rounded, transposed to [d][key]) in LDS;
+//  * the waves split the chunk's keys (and, for g*gamma > 64, the query rows)
+//    and stream keys in sub-blocks of 32, loading the next sub-block while the
+//    current one is computed:
+//      S^T = K . Q^T   (A = key rows, B = queries)
+//    with the key rows permuted so that every lane ends up holding 8
+//    consecutive keys of one query - exactly the A-operand layout of
+//      O  += P . V     (B = V^T rows, read straight from the transposed V cache);
+//  * online softmax in base 2 (log2(e)/sqrt(D) folded into the scale); for
+//    bf16 the PV product takes P as a hi + lo pair of bf16 values;
+//  * the waves merge through LDS; the workgroup writes (m, l, O) for its chunk
+//    and attn_merge combines the chunks with log-sum-exp weights in fixed
+//    chunk order.
 #pragma once
 
 #include "common.hpp"
@@ -46,83 +52,87 @@ struct AttnArgs {
     float scale_log2;       // log2(e) / sqrt(D)
 };
 
-// Per-wave attention state for up to 4 query tiles.
+// Per-wave attention state for up to 4 query tiles (the query fragments
+// themselves stay in LDS).
 template <typename T>
 struct WaveAttn {
     static constexpr int D = 256 / (int)sizeof(T);   // head_dim (one k-step)
     static constexpr int DT = D / 16;                 // d tiles
-    Frag64 qf[4];
     float m[4], l[4];     // per query column r of tile qi (replicated over g)
     f32x4_t o[4][DT];     // O[q = qi*16 + g*4 + v][d = dt*16 + r]
 };
 
+// 8 consecutive keys of one V^T row (d fixed): the MFMA B operand of O += P.V.
+template <typename T> struct VFrag;
+template <> struct VFrag<bf16_t> { u32x4_t q; };        // 8 bf16
+template <> struct VFrag<float> { u32x4_t q[2]; };      // 8 f32
+
+// Keys [kb + g*8, +8) of V^T row p (p points at key kb + g*8).  The load is
+// unconditional (no per-lane branch, so that loads of a sub-block stay in
+// flight together); keys beyond the real ones are cleared by vfrag_mask.
 template <typename T>
-__device__ __forceinline__ void vfrag_load(float (&v)[8], const T* p, int valid);   // 8 consecutive keys
+__device__ __forceinline__ void vfrag_load(VFrag<T>& v, const T* p);
 
 template <>
-__device__ __forceinline__ void vfrag_load<bf16_t>(float (&v)[8], const bf16_t* p, int valid) {
-    const uint4 u = *reinterpret_cast<const uint4*>(p);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+__device__ __forceinline__ void vfrag_load<bf16_t>(VFrag<bf16_t>& v, const bf16_t* p) {
+    v.q = *reinterpret_cast<const u32x4_t*>(p);
+}
+
+template <>
+__device__ __forceinline__ void vfrag_load<float>(VFrag<float>& v, const float* p) {
+    v.q[0] = *reinterpret_cast<const u32x4_t*>(p);
+    v.q[1] = *reinterpret_cast<const u32x4_t*>(p + 4);
+}
+
+// Zero keys >= valid of the fragment (valid may be <= 0 or >= 8).  Stale cache
+// rows may hold any bits, and 0 * NaN would poison O, so they are cleared.
+__device__ __forceinline__ void vfrag_mask(VFrag<bf16_t>& v, int valid) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        v[2 * j] = (2 * j < valid) ? __uint_as_float(w[j] << 16) : 0.f;
-        v[2 * j + 1] = (2 * j + 1 < valid) ? __uint_as_float(w[j] & 0xFFFF0000u) : 0.f;
+        const uint32_t keep = ((2 * j < valid) ? 0x0000FFFFu : 0u) | ((2 * j + 1 < valid) ? 0xFFFF0000u : 0u);
+        v.q[j] &= keep;
     }
 }
 
-template <>
-__device__ __forceinline__ void vfrag_load<float>(float (&v)[8], const float* p, int valid) {
-    const float4 a = *reinterpret_cast<const float4*>(p);
-    const float4 b = *reinterpret_cast<const float4*>(p + 4);
-    const float t[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+__device__ __forceinline__ void vfrag_mask(VFrag<float>& v, int valid) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = (j < valid) ? t[j] : 0.f;
-}
-
-// O[qi][dt] += P(8 keys of this lane's group) . V(8 keys x 16 d)
-template <typename T>
-__device__ __forceinline__ void pv_mfma(f32x4_t& acc, const float (&p)[8], const float (&v)[8]);
-
-// P is split into hi + lo bf16 parts (|P - hi - lo| <= 2^-17 |P|), so the bf16
-// MFMA does not add the rounding of P to the result; V is bf16-exact already.
-template <>
-__device__ __forceinline__ void pv_mfma<bf16_t>(f32x4_t& acc, const float (&p)[8], const float (&v)[8]) {
-    bf16x8_t hi, lo, b;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const bf16_t h = f32_to_bf16(p[j]);
-        hi[j] = (short)h;
-        lo[j] = (short)f32_to_bf16(p[j] - bf16_to_f32(h));
-        b[j] = (short)f32_to_bf16(v[j]);
+    for (int j = 0; j < 4; ++j) {
+        v.q[0][j] = (j < valid) ? v.q[0][j] : 0u;
+        v.q[1][j] = (j + 4 < valid) ? v.q[1][j] : 0u;
     }
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, b, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, b, acc, 0, 0, 0);
 }
 
-template <>
-__device__ __forceinline__ void pv_mfma<float>(f32x4_t& acc, const float (&p)[8], const float (&v)[8]) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(p[j], v[j], acc, 0, 0, 0);
-}
+// P of one lane (8 consecutive keys of one query) as the MFMA A operand.
+template <typename T> struct PFrag;
+// bf16: P = hi + lo with both parts bf16 (|P - hi - lo| <= 2^-17 |P|), so the
+// bf16 MFMA does not add the rounding of P to the result; V is bf16-exact.
+template <> struct PFrag<bf16_t> { u32x4_t hi, lo; };
+template <> struct PFrag<float> { float p[8]; };
 
-// Load the K fragments (two S^T tiles) and V^T fragments of keys [kb, kb+32) from
-// the cache; keys at or beyond `nvalid` are clamped on load and masked later.
-template <typename T>
-__device__ __forceinline__ void load_ctx_frags(Frag64 (&kf)[2], float (&vf)[WaveAttn<T>::DT][8], const T* kc,
-                                               const T* vc, int cap, int kb, int nvalid) {
-    constexpr int D = WaveAttn<T>::D, DT = WaveAttn<T>::DT, STEP = Elem<T>::STEP;
-    const int lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
-    // key rows of the two S^T tiles: lane row r -> key (r/4)*8 + t*4 + r%4
+__device__ __forceinline__ void make_pfrag(PFrag<bf16_t>& f, const float (&p)[8]) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        int key = (r >> 2) * 8 + t * 4 + (r & 3);
-        key = key < nvalid ? key : (nvalid - 1);
-        load_frag64(kf[t], kc + (long long)(kb + key) * D + g * Elem<T>::PER16);
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t h = pack2_bf16(p[2 * j], p[2 * j + 1]);
+        f.hi[j] = h;
+        f.lo[j] = pack2_bf16(p[2 * j] - __uint_as_float(h << 16), p[2 * j + 1] - __uint_as_float(h & 0xFFFF0000u));
     }
-    // V^T fragments: lane (g,r), d = dt*16 + r, keys kb + g*8 .. +8
-    const int vvalid = nvalid - g * 8;
+}
+
+__device__ __forceinline__ void make_pfrag(PFrag<float>& f, const float (&p)[8]) {
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) vfrag_load<T>(vf[dt], vc + (long long)(dt * 16 + r) * cap + kb + g * 8, vvalid);
+    for (int j = 0; j < 8; ++j) f.p[j] = p[j];
+}
+
+// acc[q][d] += P(q, 8 keys of this lane group) . V(8 keys, 16 d)
+__device__ __forceinline__ void pv_mfma(f32x4_t& acc, const PFrag<bf16_t>& p, const VFrag<bf16_t>& v) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(p.hi), as_bf16x8(v.q), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(p.lo), as_bf16x8(v.q), acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ void pv_mfma(f32x4_t& acc, const PFrag<float>& p, const VFrag<float>& v) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(p.p[j], __uint_as_float(v.q[j >> 2][j & 3]), acc, 0, 0, 0);
 }
 
 // A head row as held by one lane in the fragment layout: piece i (0..3) holds
@@ -188,11 +198,8 @@ __device__ __forceinline__ void norm_rope_frag(Frag64& out, const float (&x)[4][
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         if constexpr (sizeof(T) == 2) {
-            uint32_t w4[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-                w4[k] = (uint32_t)f32_to_bf16(o[i][2 * k]) | ((uint32_t)f32_to_bf16(o[i][2 * k + 1]) << 16);
-            out.q[i] = u32x4_t{w4[0], w4[1], w4[2], w4[3]};
+            out.q[i] = u32x4_t{pack2_bf16(o[i][0], o[i][1]), pack2_bf16(o[i][2], o[i][3]),
+                               pack2_bf16(o[i][4], o[i][5]), pack2_bf16(o[i][6], o[i][7])};
         } else {
             out.q[i] = u32x4_t{__float_as_uint(o[i][0]), __float_as_uint(o[i][1]), __float_as_uint(o[i][2]),
                                __float_as_uint(o[i][3])};
@@ -200,20 +207,48 @@ __device__ __forceinline__ void norm_rope_frag(Frag64& out, const float (&x)[4][
     }
 }
 
-// Process keys [kb, kb+32) of which the first `nvalid` are real.
+// LDS operand tiles: rows of 256 bytes; the 16-byte chunk c of row R sits at
+// position c ^ (R & 15), so that the fragment reads of 16 rows hit distinct banks.
+__device__ __forceinline__ int lds_swz(int R, int c) { return R * 256 + ((c ^ (R & 15)) * 16); }
+
+__device__ __forceinline__ void store_frag_lds(unsigned char* base, int R, const Frag64& f) {
+    const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4_t*>(base + lds_swz(R, 4 * i + g)) = f.q[i];
+}
+
+__device__ __forceinline__ void load_frag_lds(Frag64& f, const unsigned char* base, int R) {
+    const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.q[i] = *reinterpret_cast<const u32x4_t*>(base + lds_swz(R, 4 * i + g));
+}
+
+// Key of lane row r in S^T tile t of a 32-key sub-block: (r/4)*8 + t*4 + r%4,
+// so that lane group g of the result holds keys g*8 .. g*8+7.
+__device__ __forceinline__ int subblock_key(int t, int r) { return (r >> 2) * 8 + t * 4 + (r & 3); }
+
+// One 32-key sub-block of which the first `nvalid` keys are real.
+// qlds holds the query fragments of this wave's tiles (rows qt0*16 ..).
 template <typename T>
-__device__ __forceinline__ void attn_subblock(WaveAttn<T>& w, int nqt, int nvalid, float scale_log2,
-                                              const Frag64 (&kf)[2], const float (&vf)[WaveAttn<T>::DT][8]) {
+__device__ __forceinline__ void attn_subblock(WaveAttn<T>& w, const unsigned char* qlds, int qt0, int nqt, int nvalid,
+                                              float scale_log2, const Frag64 (&kf)[2],
+                                              VFrag<T> (&vf)[WaveAttn<T>::DT]) {
     constexpr int DT = WaveAttn<T>::DT;
-    const int lane = threadIdx.x & 63, g = lane >> 4;
+    const int lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
+    if (nvalid < 32) {   // wave-uniform: only the last sub-block of a sequence
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) vfrag_mask(vf[dt], nvalid - g * 8);
+    }
 #pragma unroll
     for (int qi = 0; qi < 4; ++qi) {
         if (qi < nqt) {
+            Frag64 qf;
+            load_frag_lds(qf, qlds, (qt0 + qi) * 16 + r);
             f32x4_t st[2];
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 st[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                mfma_kstep<T>(st[t], kf[t], w.qf[qi]);
+                mfma_kstep<T>(st[t], kf[t], qf);
             }
             // lane holds S[q = qi*16 + r][key = g*8 + t*4 + v]
             float s[8];
@@ -232,12 +267,12 @@ __device__ __forceinline__ void attn_subblock(WaveAttn<T>& w, int nqt, int nvali
             const float mnew = fmaxf(w.m[qi], mx);
             const bool dead = (mnew == -INFINITY);
             const float alpha = dead ? 1.f : exp2f(w.m[qi] - mnew);
-            float pv[8];
+            float p[8];
             float psum = 0.f;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                pv[j] = dead ? 0.f : exp2f(s[j] - mnew);
-                psum += pv[j];
+                p[j] = dead ? 0.f : exp2f(s[j] - mnew);
+                psum += p[j];
             }
             w.l[qi] = w.l[qi] * alpha + psum;
             w.m[qi] = mnew;
@@ -248,15 +283,48 @@ __device__ __forceinline__ void attn_subblock(WaveAttn<T>& w, int nqt, int nvali
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt) w.o[qi][dt][v] *= av;
             }
+            PFrag<T> pf;
+            make_pfrag(pf, p);
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) pv_mfma<T>(w.o[qi][dt], pv, vf[dt]);
+            for (int dt = 0; dt < DT; ++dt) pv_mfma(w.o[qi][dt], pf, vf[dt]);
         }
     }
 }
 
+// Context keys [kb, kb+32) of one (b,h): K rows clamped to the last real key
+// (their scores are masked); V is read whole (kb + 32 <= cap) and masked at use.
+template <typename T>
+__device__ __forceinline__ void fetch_ctx(Frag64 (&kf)[2], VFrag<T> (&vf)[WaveAttn<T>::DT], const T* kc, const T* vc,
+                                          int cap, int kb, int nvalid) {
+    constexpr int D = WaveAttn<T>::D, DT = WaveAttn<T>::DT, PER = Elem<T>::PER16;
+    const int lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        int key = subblock_key(t, r);
+        key = key < nvalid ? key : (nvalid - 1);
+        load_frag64(kf[t], kc + (long long)(kb + key) * D + g * PER);
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+        vfrag_load<T>(vf[dt], vc + (long long)(dt * 16 + r) * cap + kb + g * 8);
+}
+
+// LDS of a workgroup: query fragments [16 * qtiles rows][256 B], block keys
+// [32][256 B], block V^T [D][32 keys]; the wave merge later reuses the space.
+__host__ __device__ inline size_t attn_q_lds_bytes(int qtiles) { return (size_t)qtiles * 16 * 256; }
+static inline size_t attn_slot_floats(int elem_bytes) {
+    const int DT = 256 / elem_bytes / 16;
+    return (size_t)4 * DT * 64 * 4 + 2 * 4 * 4 * 64;
+}
+static inline size_t attn_lds_bytes_host(int elem_bytes, int qtiles, int kg) {
+    const size_t prologue = attn_q_lds_bytes(qtiles) + 32 * 256 + (size_t)(256 / elem_bytes) * 32 * elem_bytes;
+    const size_t slot = kg >= 2 ? attn_slot_floats(elem_bytes) * sizeof(float) : 0;
+    return prologue > slot ? prologue : slot;
+}
+
 template <typename T>
 __global__ __launch_bounds__(ATT_THREADS) void attn_partial_kernel(const AttnArgs a) {
-    constexpr int D = WaveAttn<T>::D, DT = WaveAttn<T>::DT, STEP = Elem<T>::STEP;
+    constexpr int D = WaveAttn<T>::D, DT = WaveAttn<T>::DT, PER = Elem<T>::PER16;
     extern __shared__ __align__(16) unsigned char smem[];
     const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     int len = a.len[b];
@@ -267,29 +335,72 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_partial_kernel(const AttnArg
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, g = lane >> 4, r = lane & 15;
     const int qgi = wv / a.kg, kgi = wv % a.kg;
     const bool active_wave = wv < a.qg * a.kg;
-    const int rows = a.group * a.gamma;
+    const int G = a.gamma;
+    const int rows = a.group * G;
     const int nqt_all = (rows + 15) >> 4;
     const int qt0 = qgi * 4;
     const int nqt = active_wave ? max(0, min(4, nqt_all - qt0)) : 0;
+    unsigned char* qlds = smem;
+    unsigned char* klds = qlds + attn_q_lds_bytes(nqt_all);
+    T* vlds = reinterpret_cast<T*>(klds + 32 * 256);   // [D][32]
 
-    WaveAttn<T> w;
-    constexpr int PER = Elem<T>::PER16;
-    const T* qn = reinterpret_cast<const T*>(a.q_norm);
-    const T* kn = reinterpret_cast<const T*>(a.k_norm);
-    const int G = a.gamma;
-#pragma unroll
-    for (int qi = 0; qi < 4; ++qi) {
-        // query row R = hq*gamma + j of q head (h*group + hq) at block position j
-        const int R = (qt0 + qi) * 16 + r;
-        const bool valid = qi < nqt && R < rows;
+    // ---- prologue: query fragments, normalised and rotated once per workgroup
+    for (int qt = wv; qt < nqt_all; qt += 4) {
+        const int R = qt * 16 + r;
+        const bool valid = R < rows;
         const int hq = valid ? R / G : 0, j = valid ? R % G : 0;
         float x[4][PER];
         load_row_raw<T>(x, a.qkv + (long long)(b * G + j) * a.qkv_ld + (h * a.group + hq) * D, valid);
         int pos = len + j;
         pos = pos < a.rope_rows ? pos : a.rope_rows - 1;
-        norm_rope_frag<T>(w.qf[qi], x, qn, a.eps, a.rope_cos + (long long)pos * (D / 2),
+        Frag64 f;
+        norm_rope_frag<T>(f, x, reinterpret_cast<const T*>(a.q_norm), a.eps, a.rope_cos + (long long)pos * (D / 2),
                           a.rope_sin + (long long)pos * (D / 2));
-        if (!valid) zero_frag64(w.qf[qi]);
+        if (!valid) zero_frag64(f);
+        store_frag_lds(qlds, R, f);
+    }
+    if (c == 0) {
+        // the block's own keys (waves 0,1: keys 0..31, k RMSNorm + RoPE) and values (rounded)
+        if (wv < 2) {
+            const int key = wv * 16 + r;
+            const bool valid = key < G;
+            float x[4][PER];
+            load_row_raw<T>(x, a.qkv + (long long)(b * G + (valid ? key : 0)) * a.qkv_ld + (a.n_q + h) * D, valid);
+            int pos = len + (valid ? key : 0);
+            pos = pos < a.rope_rows ? pos : a.rope_rows - 1;
+            Frag64 f;
+            norm_rope_frag<T>(f, x, reinterpret_cast<const T*>(a.k_norm), a.eps,
+                              a.rope_cos + (long long)pos * (D / 2), a.rope_sin + (long long)pos * (D / 2));
+            if (!valid) zero_frag64(f);
+            store_frag_lds(klds, key, f);
+        }
+        // V^T of the block: all float4 loads of a thread are independent (one latency)
+        constexpr int NV4 = 32 * D / 4;
+        static_assert(NV4 % ATT_THREADS == 0, "block V tile split");
+        float4 vv[NV4 / ATT_THREADS];
+#pragma unroll
+        for (int it = 0; it < NV4 / ATT_THREADS; ++it) {
+            const int e4 = it * ATT_THREADS + threadIdx.x;
+            const int key = e4 / (D / 4), d4 = e4 % (D / 4);
+            vv[it] = key < G ? *reinterpret_cast<const float4*>(a.qkv + (long long)(b * G + key) * a.qkv_ld +
+                                                                (a.n_q + a.n_kv + h) * D + d4 * 4)
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int it = 0; it < NV4 / ATT_THREADS; ++it) {
+            const int e4 = it * ATT_THREADS + threadIdx.x;
+            const int key = e4 / (D / 4), d = (e4 % (D / 4)) * 4;
+            vlds[(d + 0) * 32 + key] = Elem<T>::from_f(vv[it].x);
+            vlds[(d + 1) * 32 + key] = Elem<T>::from_f(vv[it].y);
+            vlds[(d + 2) * 32 + key] = Elem<T>::from_f(vv[it].z);
+            vlds[(d + 3) * 32 + key] = Elem<T>::from_f(vv[it].w);
+        }
+    }
+    __syncthreads();
+
+    WaveAttn<T> w;
+#pragma unroll
+    for (int qi = 0; qi < 4; ++qi) {
         w.m[qi] = -INFINITY;
         w.l[qi] = 0.f;
 #pragma unroll
@@ -297,32 +408,14 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_partial_kernel(const AttnArg
     }
 
     if (c == 0) {
-        // the block's own keys/values, from the raw projections (k: norm + RoPE; v: rounded)
         if (nqt > 0 && kgi == 0) {
             Frag64 kf[2];
-            float vf[DT][8];
-            const float* kraw = a.qkv + (long long)(b * G) * a.qkv_ld + (a.n_q + h) * D;
-            const float* vraw = a.qkv + (long long)(b * G) * a.qkv_ld + (a.n_q + a.n_kv + h) * D;
+            VFrag<T> vf[DT];
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const int key = (r >> 2) * 8 + t * 4 + (r & 3);
-                const bool valid = key < G;
-                float x[4][PER];
-                load_row_raw<T>(x, kraw + (long long)(valid ? key : 0) * a.qkv_ld, valid);
-                int pos = len + (valid ? key : 0);
-                pos = pos < a.rope_rows ? pos : a.rope_rows - 1;
-                norm_rope_frag<T>(kf[t], x, kn, a.eps, a.rope_cos + (long long)pos * (D / 2),
-                                  a.rope_sin + (long long)pos * (D / 2));
-            }
+            for (int t = 0; t < 2; ++t) load_frag_lds(kf[t], klds, subblock_key(t, r));
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-                for (int jj = 0; jj < 8; ++jj) {
-                    const int key = g * 8 + jj;
-                    const float v = vraw[(long long)(key < G ? key : 0) * a.qkv_ld + dt * 16 + r];
-                    vf[dt][jj] = key < G ? Elem<T>::rho(v) : 0.f;
-                }
-            attn_subblock<T>(w, nqt, G, a.scale_log2, kf, vf);
+            for (int dt = 0; dt < DT; ++dt) vfrag_load<T>(vf[dt], vlds + (dt * 16 + r) * 32 + g * 8);
+            attn_subblock<T>(w, qlds, qt0, nqt, G, a.scale_log2, kf, vf);
         }
     } else if (nqt > 0) {
         const int per_wave = a.chunk / a.kg;
@@ -330,12 +423,17 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_partial_kernel(const AttnArg
         const int k_hi = min(k_lo + per_wave, len);
         const T* kc = reinterpret_cast<const T*>(a.kcache) + ((long long)b * a.n_kv + h) * (long long)a.cap * D;
         const T* vc = reinterpret_cast<const T*>(a.vcache) + ((long long)b * a.n_kv + h) * (long long)D * a.cap;
-        for (int kb = k_lo; kb < k_hi; kb += 32) {
-            const int nvalid = min(32, k_hi - kb);
-            Frag64 kf[2];
-            float vf[DT][8];
-            load_ctx_frags<T>(kf, vf, kc, vc, a.cap, kb, nvalid);
-            attn_subblock<T>(w, nqt, nvalid, a.scale_log2, kf, vf);
+        // two register buffers: sub-block kb+32 loads while kb is computed
+        Frag64 kfa[2], kfb[2];
+        VFrag<T> vfa[DT], vfb[DT];
+        if (k_lo < k_hi) fetch_ctx<T>(kfa, vfa, kc, vc, a.cap, k_lo, min(32, k_hi - k_lo));
+        for (int kb = k_lo; kb < k_hi; kb += 64) {
+            const int kb1 = kb + 32, kb2 = kb + 64;
+            if (kb1 < k_hi) fetch_ctx<T>(kfb, vfb, kc, vc, a.cap, kb1, min(32, k_hi - kb1));
+            attn_subblock<T>(w, qlds, qt0, nqt, min(32, k_hi - kb), a.scale_log2, kfa, vfa);
+            if (kb1 >= k_hi) break;
+            if (kb2 < k_hi) fetch_ctx<T>(kfa, vfa, kc, vc, a.cap, kb2, min(32, k_hi - kb2));
+            attn_subblock<T>(w, qlds, qt0, nqt, min(32, k_hi - kb1), a.scale_log2, kfb, vfb);
         }
     }
 
@@ -355,6 +453,7 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_partial_kernel(const AttnArg
 
     // ---- merge the key-group waves of each query group through one LDS slot
     // (pairwise rounds; the exchanges of a round run one after another)
+    __syncthreads();   // the prologue tiles are dead: the slot reuses their space
     float* s = reinterpret_cast<float*>(smem);
     float* sm = s + 4 * DT * 64 * 4;
     for (int span = a.kg >> 1; span >= 1; span >>= 1) {
@@ -423,13 +522,6 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_partial_kernel(const AttnArg
     }
 }
 
-static inline size_t attn_lds_bytes_host(int elem_bytes, int qg, int kg) {
-    (void)qg;
-    const int D = 256 / elem_bytes, DT = D / 16;
-    const int slot_floats = 4 * DT * 64 * 4 + 2 * 4 * 4 * 64;
-    return kg >= 2 ? (size_t)slot_floats * sizeof(float) : 0;
-}
-
 // o[b*gamma + j][(h*g + hq)*D + d] = rho( sum_c w_c O_c / sum_c w_c l_c ),  w_c = 2^(m_c - max m)
 struct MergeArgs {
     const float* opart;
@@ -440,16 +532,18 @@ struct MergeArgs {
 };
 
 constexpr int MERGE_MAX_CHUNKS = 1024;
+constexpr int MERGE_BATCH = 16;   // chunk partials loaded together per lane
 
 template <typename T>
 __global__ __launch_bounds__(64) void attn_merge_kernel(const MergeArgs a) {
-    // blockIdx.x = row (b*gamma + j), blockIdx.y = q head; one wavefront
+    // blockIdx.x = row (b*gamma + j), blockIdx.y = q head; one wavefront, lane
+    // owns d = lane*DPL .. +DPL.  Chunks are summed in ascending order.
+    constexpr int D = 256 / (int)sizeof(T), DPL = D / 64;
     __shared__ float wts[MERGE_MAX_CHUNKS];
     const int m = blockIdx.x, hq_all = blockIdx.y;
     const int b = m / a.gamma, j = m % a.gamma;
     const int h = hq_all / a.group, hq = hq_all % a.group;
     const int R = hq * a.gamma + j;
-    const int D = a.head_dim;
     const int lane = threadIdx.x;
     int len = a.len[b];
     len = len < 0 ? 0 : (len > a.cap ? a.cap : len);
@@ -468,23 +562,31 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(const MergeArgs a) {
     }
     den = wave_sum(den);
     __syncthreads();
-    for (int d = lane; d < D; d += 64) {
-        float num = 0.f;
-        int c = 0;
-        for (; c + 4 <= nch; c += 4) {
-            const float o0 = a.opart[((base + c) * a.rpad + R) * D + d];
-            const float o1 = a.opart[((base + c + 1) * a.rpad + R) * D + d];
-            const float o2 = a.opart[((base + c + 2) * a.rpad + R) * D + d];
-            const float o3 = a.opart[((base + c + 3) * a.rpad + R) * D + d];
-            num += wts[c] * o0;
-            num += wts[c + 1] * o1;
-            num += wts[c + 2] * o2;
-            num += wts[c + 3] * o3;
+    const float* op = a.opart + (base * a.rpad + R) * (long long)D + lane * DPL;
+    const long long cstride = (long long)a.rpad * D;
+    float num[DPL];
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) num[k] = 0.f;
+    for (int c0 = 0; c0 < nch; c0 += MERGE_BATCH) {
+        float ov[MERGE_BATCH][DPL];
+#pragma unroll
+        for (int u = 0; u < MERGE_BATCH; ++u) {
+            const int c = min(c0 + u, nch - 1);
+#pragma unroll
+            for (int k = 0; k < DPL; ++k) ov[u][k] = op[c * cstride + k];
         }
-        for (; c < nch; ++c) num += wts[c] * a.opart[((base + c) * a.rpad + R) * D + d];
-        reinterpret_cast<T*>(a.out)[(long long)m * (gridDim.y * D) + (long long)hq_all * D + d] =
-            Elem<T>::from_f(num / den);
+#pragma unroll
+        for (int u = 0; u < MERGE_BATCH; ++u) {
+            if (c0 + u < nch) {
+                const float wc = wts[c0 + u];
+#pragma unroll
+                for (int k = 0; k < DPL; ++k) num[k] += wc * ov[u][k];
+            }
+        }
     }
+    T* out = reinterpret_cast<T*>(a.out) + (long long)m * (gridDim.y * D) + (long long)hq_all * D + lane * DPL;
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) out[k] = Elem<T>::from_f(num[k] / den);
 }
 
 }  // namespace dflash

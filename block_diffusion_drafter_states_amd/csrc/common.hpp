@@ -38,6 +38,16 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
 
 __device__ __forceinline__ float round_bf16(float f) { return bf16_to_f32(f32_to_bf16(f)); }
 
+// Two floats -> two bf16 (round to nearest even) packed low/high in one dword,
+// with gfx950's packed conversion instruction.
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_hw_t;
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
+    const bf16x2_hw_t v = {(__bf16)lo, (__bf16)hi};
+    uint32_t u;
+    __builtin_memcpy(&u, &v, 4);
+    return u;
+}
+
 // Element storage type traits: bf16 (bit patterns) or f32.
 template <typename T> struct Elem;
 template <> struct Elem<bf16_t> {

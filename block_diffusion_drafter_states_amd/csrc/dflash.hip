@@ -403,7 +403,7 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
     int n_ssq = 1;
 
     const AttnPlan ap = plan_attn(s, gamma);
-    const size_t attn_lds = attn_lds_bytes_host(s.esize, ap.qg, ap.kg);
+    const size_t attn_lds = attn_lds_bytes_host(s.esize, cdiv(s.group * gamma, 16), ap.kg);
     const size_t layer_elems = (size_t)s.Bmax * s.nkv * s.cap * s.D;
 
     for (int l = 0; l < s.L; ++l) {
