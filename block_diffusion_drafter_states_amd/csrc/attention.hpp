@@ -6,31 +6,30 @@
 // mask inside the block and the whole context is visible (bidirectional).
 //
 // Work split ("split-K" over keys): chunk 0 of each (b,h) holds the block
-// rows, chunks 1.. hold CH context rows each.  A workgroup of 4 wavefronts
-// takes one chunk:
-//  * prologue: the query rows get the per-head q RMSNorm and RoPE once per
-//    workgroup (wave w builds query tiles w, w+4, ...) and are kept as MFMA
-//    fragments in LDS; chunk 0 also builds the block's keys (k RMSNorm + RoPE)
-//    and values (rounded, transposed to [d][key]) in LDS;
-//  * the waves split the chunk's keys (and, for g*gamma > 64, the query rows)
-//    and stream keys in sub-blocks of 32, loading the next sub-block while the
-//    current one is computed:
-//      S^T = K . Q^T   (A = key rows, B = queries)
+// rows, chunks 1.. hold CH context rows each.  A workgroup takes one chunk and
+// up to 8 query tiles of 16 rows; it has KG waves per query tile, which split
+// the chunk's keys.  A wave owns one query tile:
+//  * it builds the tile's q fragments itself (per-head RMSNorm + RoPE);
+//  * the waves of a key group stream their keys through LDS in sub-blocks of
+//    32 (direct-to-LDS loads of whole 1 KB spans, double-buffered, each byte
+//    fetched once per workgroup) and every wave computes from LDS:
+//      S^T = K . Q^T    (A = key rows, B = queries)
 //    with the key rows permuted so that every lane ends up holding 8
-//    consecutive keys of one query - exactly the A-operand layout of
-//      O  += P . V     (B = V^T rows, read straight from the transposed V cache);
+//    consecutive keys of one query - exactly the B-operand layout of
+//      O^T += V^T . P^T (A = V^T rows of the transposed V cache),
+//    whose result leaves every lane with output columns of the same query as its
+//    scores, so the online-softmax rescaling needs no data exchange;
 //  * online softmax in base 2 (log2(e)/sqrt(D) folded into the scale); for
-//    bf16 the PV product takes P as a hi + lo pair of bf16 values;
-//  * the waves merge through LDS; the workgroup writes (m, l, O) for its chunk
-//    and attn_merge combines the chunks with log-sum-exp weights in fixed
-//    chunk order.
+//    bf16 the PV product takes P as a hi + lo pair of bf16 values.
+// Chunk 0's workgroup first builds the block's keys (k RMSNorm + RoPE) and
+// values (rounded, transposed) in LDS.  The KG waves of a tile merge through
+// LDS (all tiles at once); the workgroup writes (m, l, O) per chunk and
+// attn_merge combines the chunks with log-sum-exp weights in fixed chunk order.
 #pragma once
 
 #include "common.hpp"
 
 namespace dflash {
-
-constexpr int ATT_THREADS = 256;
 
 struct AttnArgs {
     const void* kcache;     // this layer: T [Bmax][n_kv][cap][D]
@@ -48,41 +47,24 @@ struct AttnArgs {
     float* mlpart;          // [B][n_kv][nch_max][rpad][2]  (m in log2 units, l)
     int n_q, n_kv, cap, rpad, nch_max, chunk;   // chunk = CH context keys per chunk
     int gamma, group;       // rows = group * gamma
-    int qg, kg;             // waves = qg query groups x kg key groups (qg*kg <= 4)
+    int qtw, kg, nqs;       // query tiles per workgroup, waves per tile, workgroups per (b,h,chunk)
     float scale_log2;       // log2(e) / sqrt(D)
 };
 
-// Per-wave attention state for up to 4 query tiles (the query fragments
-// themselves stay in LDS).
+// Per-wave attention state for one query tile.
 template <typename T>
 struct WaveAttn {
     static constexpr int D = 256 / (int)sizeof(T);   // head_dim (one k-step)
     static constexpr int DT = D / 16;                 // d tiles
-    float m[4], l[4];     // per query column r of tile qi (replicated over g)
-    f32x4_t o[4][DT];     // O[q = qi*16 + g*4 + v][d = dt*16 + r]
+    Frag64 qf;            // B operand: lane (g,r) holds query r
+    float m, l;           // running max (log2 units) of query r; this lane's share of its sum
+    f32x4_t o[DT];        // O^T[d = dt*16 + g*4 + v][q = r]
 };
 
 // 8 consecutive keys of one V^T row (d fixed): the MFMA B operand of O += P.V.
 template <typename T> struct VFrag;
 template <> struct VFrag<bf16_t> { u32x4_t q; };        // 8 bf16
 template <> struct VFrag<float> { u32x4_t q[2]; };      // 8 f32
-
-// Keys [kb + g*8, +8) of V^T row p (p points at key kb + g*8).  The load is
-// unconditional (no per-lane branch, so that loads of a sub-block stay in
-// flight together); keys beyond the real ones are cleared by vfrag_mask.
-template <typename T>
-__device__ __forceinline__ void vfrag_load(VFrag<T>& v, const T* p);
-
-template <>
-__device__ __forceinline__ void vfrag_load<bf16_t>(VFrag<bf16_t>& v, const bf16_t* p) {
-    v.q = *reinterpret_cast<const u32x4_t*>(p);
-}
-
-template <>
-__device__ __forceinline__ void vfrag_load<float>(VFrag<float>& v, const float* p) {
-    v.q[0] = *reinterpret_cast<const u32x4_t*>(p);
-    v.q[1] = *reinterpret_cast<const u32x4_t*>(p + 4);
-}
 
 // Zero keys >= valid of the fragment (valid may be <= 0 or >= 8).  Stale cache
 // rows may hold any bits, and 0 * NaN would poison O, so they are cleared.
@@ -123,16 +105,16 @@ __device__ __forceinline__ void make_pfrag(PFrag<float>& f, const float (&p)[8])
     for (int j = 0; j < 8; ++j) f.p[j] = p[j];
 }
 
-// acc[q][d] += P(q, 8 keys of this lane group) . V(8 keys, 16 d)
+// acc[d][q] += V^T(16 d, 8 keys of this lane group) . P^T(8 keys, q)
 __device__ __forceinline__ void pv_mfma(f32x4_t& acc, const PFrag<bf16_t>& p, const VFrag<bf16_t>& v) {
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(p.hi), as_bf16x8(v.q), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(p.lo), as_bf16x8(v.q), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(v.q), as_bf16x8(p.hi), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(v.q), as_bf16x8(p.lo), acc, 0, 0, 0);
 }
 
 __device__ __forceinline__ void pv_mfma(f32x4_t& acc, const PFrag<float>& p, const VFrag<float>& v) {
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(p.p[j], __uint_as_float(v.q[j >> 2][j & 3]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.q[j >> 2][j & 3]), p.p[j], acc, 0, 0, 0);
 }
 
 // A head row as held by one lane in the fragment layout: piece i (0..3) holds
@@ -207,20 +189,42 @@ __device__ __forceinline__ void norm_rope_frag(Frag64& out, const float (&x)[4][
     }
 }
 
-// LDS operand tiles: rows of 256 bytes; the 16-byte chunk c of row R sits at
-// position c ^ (R & 15), so that the fragment reads of 16 rows hit distinct banks.
-__device__ __forceinline__ int lds_swz(int R, int c) { return R * 256 + ((c ^ (R & 15)) * 16); }
+// K tile of a sub-block in LDS: key row at key*256 B, 16-byte chunk c at
+// position c ^ kswz(key); the 16 rows read by one fragment load hit 16
+// different bank groups.
+__device__ __forceinline__ int kswz(int key) { return ((key >> 1) & 12) | (key & 3); }
+__device__ __forceinline__ int k_lds_off(int key, int c) { return key * 256 + ((c ^ kswz(key)) << 4); }
 
-__device__ __forceinline__ void store_frag_lds(unsigned char* base, int R, const Frag64& f) {
+// V^T tile of a sub-block in LDS: row d holds the 32 keys (32 * element bytes);
+// bf16 rows (64 B) put chunk c at position c ^ ((d >> 2) & 3), f32 rows are plain.
+template <typename T> __device__ __forceinline__ int v_lds_off(int d, int c);
+template <> __device__ __forceinline__ int v_lds_off<bf16_t>(int d, int c) { return d * 64 + ((c ^ ((d >> 2) & 3)) << 4); }
+template <> __device__ __forceinline__ int v_lds_off<float>(int d, int c) { return d * 128 + (c << 4); }
+
+constexpr int ATT_STAGE_BYTES = 16384;   // K (32 x 256 B) then V^T (8 KB)
+constexpr int ATT_V_OFF = 8192;
+
+__device__ __forceinline__ void store_frag_lds(unsigned char* kt, int key, const Frag64& f) {
     const int g = (threadIdx.x & 63) >> 4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4_t*>(base + lds_swz(R, 4 * i + g)) = f.q[i];
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4_t*>(kt + k_lds_off(key, 4 * i + g)) = f.q[i];
 }
 
-__device__ __forceinline__ void load_frag_lds(Frag64& f, const unsigned char* base, int R) {
+__device__ __forceinline__ void load_frag_lds(Frag64& f, const unsigned char* kt, int key) {
     const int g = (threadIdx.x & 63) >> 4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) f.q[i] = *reinterpret_cast<const u32x4_t*>(base + lds_swz(R, 4 * i + g));
+    for (int i = 0; i < 4; ++i) f.q[i] = *reinterpret_cast<const u32x4_t*>(kt + k_lds_off(key, 4 * i + g));
+}
+
+// Keys g*8 .. g*8+7 of V^T row d of a staged sub-block.
+__device__ __forceinline__ void vfrag_lds(VFrag<bf16_t>& v, const unsigned char* vt, int d) {
+    const int g = (threadIdx.x & 63) >> 4;
+    v.q = *reinterpret_cast<const u32x4_t*>(vt + v_lds_off<bf16_t>(d, g));
+}
+__device__ __forceinline__ void vfrag_lds(VFrag<float>& v, const unsigned char* vt, int d) {
+    const int g = (threadIdx.x & 63) >> 4;
+    v.q[0] = *reinterpret_cast<const u32x4_t*>(vt + v_lds_off<float>(d, 2 * g));
+    v.q[1] = *reinterpret_cast<const u32x4_t*>(vt + v_lds_off<float>(d, 2 * g + 1));
 }
 
 // Key of lane row r in S^T tile t of a 32-key sub-block: (r/4)*8 + t*4 + r%4,
@@ -228,124 +232,135 @@ __device__ __forceinline__ void load_frag_lds(Frag64& f, const unsigned char* ba
 __device__ __forceinline__ int subblock_key(int t, int r) { return (r >> 2) * 8 + t * 4 + (r & 3); }
 
 // One 32-key sub-block of which the first `nvalid` keys are real.
-// qlds holds the query fragments of this wave's tiles (rows qt0*16 ..).
+// One 32-key sub-block of which the first `nvalid` keys are real.
 template <typename T>
-__device__ __forceinline__ void attn_subblock(WaveAttn<T>& w, const unsigned char* qlds, int qt0, int nqt, int nvalid,
-                                              float scale_log2, const Frag64 (&kf)[2],
+__device__ __forceinline__ void attn_subblock(WaveAttn<T>& w, int nvalid, float scale_log2, const Frag64 (&kf)[2],
                                               VFrag<T> (&vf)[WaveAttn<T>::DT]) {
     constexpr int DT = WaveAttn<T>::DT;
-    const int lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
+    const int g = (threadIdx.x & 63) >> 4;
     if (nvalid < 32) {   // wave-uniform: only the last sub-block of a sequence
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) vfrag_mask(vf[dt], nvalid - g * 8);
     }
+    f32x4_t st[2];
 #pragma unroll
-    for (int qi = 0; qi < 4; ++qi) {
-        if (qi < nqt) {
-            Frag64 qf;
-            load_frag_lds(qf, qlds, (qt0 + qi) * 16 + r);
-            f32x4_t st[2];
+    for (int t = 0; t < 2; ++t) {
+        st[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        mfma_kstep<T>(st[t], kf[t], w.qf);
+    }
+    // lane holds S[q = r][key = g*8 + t*4 + v]
+    float s[8];
+    float mx = -INFINITY;
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                st[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                mfma_kstep<T>(st[t], kf[t], qf);
-            }
-            // lane holds S[q = qi*16 + r][key = g*8 + t*4 + v]
-            float s[8];
-            float mx = -INFINITY;
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+        for (int v = 0; v < 4; ++v) {
+            const float x = (g * 8 + t * 4 + v) < nvalid ? st[t][v] * scale_log2 : -INFINITY;
+            s[t * 4 + v] = x;
+            mx = fmaxf(mx, x);
+        }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
+    const float mnew = fmaxf(w.m, mx);
+    const bool dead = (mnew == -INFINITY);
+    const float alpha = dead ? 1.f : exp2f(w.m - mnew);
+    float p[8];
+    float psum = 0.f;
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int key = g * 8 + t * 4 + v;
-                    const float x = key < nvalid ? st[t][v] * scale_log2 : -INFINITY;
-                    s[t * 4 + v] = x;
-                    mx = fmaxf(mx, x);
-                }
-            mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
-            mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
-            const float mnew = fmaxf(w.m[qi], mx);
-            const bool dead = (mnew == -INFINITY);
-            const float alpha = dead ? 1.f : exp2f(w.m[qi] - mnew);
-            float p[8];
-            float psum = 0.f;
+    for (int j = 0; j < 8; ++j) {
+        p[j] = dead ? 0.f : exp2f(s[j] - mnew);
+        psum += p[j];
+    }
+    w.l = w.l * alpha + psum;
+    w.m = mnew;
+    PFrag<T> pf;
+    make_pfrag(pf, p);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                p[j] = dead ? 0.f : exp2f(s[j] - mnew);
-                psum += p[j];
-            }
-            w.l[qi] = w.l[qi] * alpha + psum;
-            w.m[qi] = mnew;
-            // rescale O rows q = g*4 + v by alpha of that query (held by lane g*4+v)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const float av = __shfl(alpha, g * 4 + v, WAVE);
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) w.o[qi][dt][v] *= av;
-            }
-            PFrag<T> pf;
-            make_pfrag(pf, p);
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) pv_mfma(w.o[qi][dt], pf, vf[dt]);
+    for (int dt = 0; dt < DT; ++dt) {
+        w.o[dt] *= alpha;
+        pv_mfma(w.o[dt], pf, vf[dt]);
+    }
+}
+
+// Direct-to-LDS loads of context keys [kb, kb+32) of one (b,h) into a stage:
+// 8 instructions of 1 KB for K (rows beyond the real keys repeat the last real
+// one; their scores are masked) and 8 for V^T (whole rows: kb + 32 <= cap; keys
+// beyond the real ones are cleared at use).  Instruction j goes to the wave
+// with j % nw == iw; the loop is wave-uniform.
+template <typename T>
+__device__ __forceinline__ void stage_issue(uint32_t stage, const T* kc, const T* vc, int cap, int kb, int nvalid,
+                                            int iw, int nw) {
+    constexpr int D = 256 / (int)sizeof(T), KPC = 16 / (int)sizeof(T);   // elements per 16 bytes
+    constexpr int RB = 32 * (int)sizeof(T), CPR = RB / 16, RPI = 1024 / RB;
+    const int lane = threadIdx.x & 63;
+    for (int j = iw; j < 16; j += nw) {
+        if (j < 8) {
+            const int key = 4 * j + (lane >> 4);
+            const int src = key < nvalid ? key : nvalid - 1;
+            const int c = (lane & 15) ^ kswz(key);
+            dma_b128(kc + (long long)(kb + src) * D + c * KPC, stage + j * 1024);
+        } else {
+            const int jj = j - 8;
+            const int d = jj * RPI + lane / CPR, p = lane % CPR;
+            const int c = sizeof(T) == 2 ? (p ^ ((d >> 2) & 3)) : p;
+            dma_b128(vc + (long long)d * cap + kb + c * KPC, stage + ATT_V_OFF + jj * 1024);
         }
     }
 }
 
-// Context keys [kb, kb+32) of one (b,h): K rows clamped to the last real key
-// (their scores are masked); V is read whole (kb + 32 <= cap) and masked at use.
-template <typename T>
-__device__ __forceinline__ void fetch_ctx(Frag64 (&kf)[2], VFrag<T> (&vf)[WaveAttn<T>::DT], const T* kc, const T* vc,
-                                          int cap, int kb, int nvalid) {
-    constexpr int D = WaveAttn<T>::D, DT = WaveAttn<T>::DT, PER = Elem<T>::PER16;
-    const int lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        int key = subblock_key(t, r);
-        key = key < nvalid ? key : (nvalid - 1);
-        load_frag64(kf[t], kc + (long long)(kb + key) * D + g * PER);
-    }
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-        vfrag_load<T>(vf[dt], vc + (long long)(dt * 16 + r) * cap + kb + g * 8);
-}
-
-// LDS of a workgroup: query fragments [16 * qtiles rows][256 B], block keys
-// [32][256 B], block V^T [D][32 keys]; the wave merge later reuses the space.
-__host__ __device__ inline size_t attn_q_lds_bytes(int qtiles) { return (size_t)qtiles * 16 * 256; }
-static inline size_t attn_slot_floats(int elem_bytes) {
-    const int DT = 256 / elem_bytes / 16;
-    return (size_t)4 * DT * 64 * 4 + 2 * 4 * 4 * 64;
-}
-static inline size_t attn_lds_bytes_host(int elem_bytes, int qtiles, int kg) {
-    const size_t prologue = attn_q_lds_bytes(qtiles) + 32 * 256 + (size_t)(256 / elem_bytes) * 32 * elem_bytes;
-    const size_t slot = kg >= 2 ? attn_slot_floats(elem_bytes) * sizeof(float) : 0;
-    return prologue > slot ? prologue : slot;
+// LDS of a workgroup: two stages per key group (chunk 0 builds the block's keys
+// and values in the first stage); afterwards the key-group merge reuses the
+// space with one slot (O^T, m, l of a wave) per sending wave.
+constexpr int ATT_MAX_TILES = 8;    // query tiles per workgroup
+constexpr int ATT_MAX_WAVES = 8;
+static inline size_t attn_slot_bytes(int elem_bytes) { return (size_t)(256 / elem_bytes / 16) * 4 * 64 * 4 + 2 * 64 * 4; }
+static inline size_t attn_lds_bytes_host(int elem_bytes, int qtw, int kg) {
+    const size_t stages = (size_t)kg * 2 * ATT_STAGE_BYTES;
+    const size_t merge = (size_t)qtw * (kg / 2) * attn_slot_bytes(elem_bytes);
+    return stages > merge ? stages : merge;
 }
 
 template <typename T>
-__global__ __launch_bounds__(ATT_THREADS) void attn_partial_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(64 * ATT_MAX_WAVES) void attn_partial_kernel(const AttnArgs a) {
     constexpr int D = WaveAttn<T>::D, DT = WaveAttn<T>::DT, PER = Elem<T>::PER16;
     extern __shared__ __align__(16) unsigned char smem[];
-    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int c = blockIdx.x, h = blockIdx.y / a.nqs, qs = blockIdx.y % a.nqs, b = blockIdx.z;
     int len = a.len[b];
     len = len < 0 ? 0 : (len > a.cap ? a.cap : len);
     const int nch = 1 + (len + a.chunk - 1) / a.chunk;
     if (c >= nch) return;
 
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, g = lane >> 4, r = lane & 15;
-    const int qgi = wv / a.kg, kgi = wv % a.kg;
-    const bool active_wave = wv < a.qg * a.kg;
     const int G = a.gamma;
     const int rows = a.group * G;
-    const int nqt_all = (rows + 15) >> 4;
-    const int qt0 = qgi * 4;
-    const int nqt = active_wave ? max(0, min(4, nqt_all - qt0)) : 0;
-    unsigned char* qlds = smem;
-    unsigned char* klds = qlds + attn_q_lds_bytes(nqt_all);
-    T* vlds = reinterpret_cast<T*>(klds + 32 * 256);   // [D][32]
+    const int qt = qs * a.qtw + wv / a.kg;          // this wave's query tile
+    const int kgi = wv % a.kg;
+    const bool active = qt * 16 < rows;
 
-    // ---- prologue: query fragments, normalised and rotated once per workgroup
-    for (int qt = wv; qt < nqt_all; qt += 4) {
+    WaveAttn<T> w;
+    w.m = -INFINITY;
+    w.l = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) w.o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    const T* kc = reinterpret_cast<const T*>(a.kcache) + ((long long)b * a.n_kv + h) * (long long)a.cap * D;
+    const T* vc = reinterpret_cast<const T*>(a.vcache) + ((long long)b * a.n_kv + h) * (long long)D * a.cap;
+    // this wave's context keys [k_lo, k_hi); empty for chunk 0 (the block).  Every
+    // wave runs n_iter sub-block steps (the count of key group 0) for the barriers.
+    const int per_wave = a.chunk / a.kg;
+    const int c0 = (c - 1) * a.chunk;
+    const int k_lo = c == 0 ? 0 : c0 + kgi * per_wave;
+    const int k_hi = c == 0 ? 0 : min(k_lo + per_wave, len);
+    const int n_iter = c == 0 ? 0 : (min(per_wave, len - c0) + 31) / 32;
+    const int tl = __builtin_amdgcn_readfirstlane(wv / a.kg);   // tile within the workgroup (wave-uniform)
+    const int kgi_u = __builtin_amdgcn_readfirstlane(kgi);
+    unsigned char* kgbuf = smem + kgi_u * 2 * ATT_STAGE_BYTES;
+    const uint32_t kgbuf_lds = lds_offset(smem) + (uint32_t)kgi_u * (2 * ATT_STAGE_BYTES);
+
+    // first context sub-block in flight while the queries are built
+    if (k_lo < k_hi) stage_issue<T>(kgbuf_lds, kc, vc, a.cap, k_lo, min(32, k_hi - k_lo), tl, a.qtw);
+
+    if (active) {
         const int R = qt * 16 + r;
         const bool valid = R < rows;
         const int hq = valid ? R / G : 0, j = valid ? R % G : 0;
@@ -353,14 +368,14 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_partial_kernel(const AttnArg
         load_row_raw<T>(x, a.qkv + (long long)(b * G + j) * a.qkv_ld + (h * a.group + hq) * D, valid);
         int pos = len + j;
         pos = pos < a.rope_rows ? pos : a.rope_rows - 1;
-        Frag64 f;
-        norm_rope_frag<T>(f, x, reinterpret_cast<const T*>(a.q_norm), a.eps, a.rope_cos + (long long)pos * (D / 2),
-                          a.rope_sin + (long long)pos * (D / 2));
-        if (!valid) zero_frag64(f);
-        store_frag_lds(qlds, R, f);
+        norm_rope_frag<T>(w.qf, x, reinterpret_cast<const T*>(a.q_norm), a.eps,
+                          a.rope_cos + (long long)pos * (D / 2), a.rope_sin + (long long)pos * (D / 2));
+        if (!valid) zero_frag64(w.qf);
     }
+
     if (c == 0) {
-        // the block's own keys (waves 0,1: keys 0..31, k RMSNorm + RoPE) and values (rounded)
+        // the block's own keys (waves 0,1: keys 0..31, k RMSNorm + RoPE) and values
+        // (rounded) into stage 0 of key group 0
         if (wv < 2) {
             const int key = wv * 16 + r;
             const bool valid = key < G;
@@ -372,153 +387,110 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_partial_kernel(const AttnArg
             norm_rope_frag<T>(f, x, reinterpret_cast<const T*>(a.k_norm), a.eps,
                               a.rope_cos + (long long)pos * (D / 2), a.rope_sin + (long long)pos * (D / 2));
             if (!valid) zero_frag64(f);
-            store_frag_lds(klds, key, f);
+            store_frag_lds(smem, key, f);
         }
-        // V^T of the block: all float4 loads of a thread are independent (one latency)
-        constexpr int NV4 = 32 * D / 4;
-        static_assert(NV4 % ATT_THREADS == 0, "block V tile split");
-        float4 vv[NV4 / ATT_THREADS];
+        // V^T of the block by the first 256 threads (every workgroup has >= 4 waves);
+        // all float4 loads of a thread are independent (one latency)
+        constexpr int NV4 = 32 * D / 4, KPC = 16 / (int)sizeof(T);
+        static_assert(NV4 % 256 == 0, "block V tile split");
+        if (threadIdx.x < 256) {
+            float4 vv[NV4 / 256];
 #pragma unroll
-        for (int it = 0; it < NV4 / ATT_THREADS; ++it) {
-            const int e4 = it * ATT_THREADS + threadIdx.x;
-            const int key = e4 / (D / 4), d4 = e4 % (D / 4);
-            vv[it] = key < G ? *reinterpret_cast<const float4*>(a.qkv + (long long)(b * G + key) * a.qkv_ld +
-                                                                (a.n_q + a.n_kv + h) * D + d4 * 4)
-                             : make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int it = 0; it < NV4 / 256; ++it) {
+                const int e4 = it * 256 + threadIdx.x;
+                const int key = e4 / (D / 4), d = (e4 % (D / 4)) * 4;
+                vv[it] = key < G ? *reinterpret_cast<const float4*>(a.qkv + (long long)(b * G + key) * a.qkv_ld +
+                                                                    (a.n_q + a.n_kv + h) * D + d)
+                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+#pragma unroll
+            for (int it = 0; it < NV4 / 256; ++it) {
+                const int e4 = it * 256 + threadIdx.x;
+                const int key = e4 / (D / 4), d = (e4 % (D / 4)) * 4;
+                const float vals[4] = {vv[it].x, vv[it].y, vv[it].z, vv[it].w};
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    *reinterpret_cast<T*>(smem + ATT_V_OFF + v_lds_off<T>(d + u, key / KPC) +
+                                          (key % KPC) * (int)sizeof(T)) = Elem<T>::from_f(vals[u]);
+            }
         }
-#pragma unroll
-        for (int it = 0; it < NV4 / ATT_THREADS; ++it) {
-            const int e4 = it * ATT_THREADS + threadIdx.x;
-            const int key = e4 / (D / 4), d = (e4 % (D / 4)) * 4;
-            vlds[(d + 0) * 32 + key] = Elem<T>::from_f(vv[it].x);
-            vlds[(d + 1) * 32 + key] = Elem<T>::from_f(vv[it].y);
-            vlds[(d + 2) * 32 + key] = Elem<T>::from_f(vv[it].z);
-            vlds[(d + 3) * 32 + key] = Elem<T>::from_f(vv[it].w);
-        }
-    }
-    __syncthreads();
-
-    WaveAttn<T> w;
-#pragma unroll
-    for (int qi = 0; qi < 4; ++qi) {
-        w.m[qi] = -INFINITY;
-        w.l[qi] = 0.f;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) w.o[qi][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
-
-    if (c == 0) {
-        if (nqt > 0 && kgi == 0) {
+        __syncthreads();
+        if (active && kgi == 0) {
             Frag64 kf[2];
             VFrag<T> vf[DT];
 #pragma unroll
-            for (int t = 0; t < 2; ++t) load_frag_lds(kf[t], klds, subblock_key(t, r));
+            for (int t = 0; t < 2; ++t) load_frag_lds(kf[t], smem, subblock_key(t, r));
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) vfrag_load<T>(vf[dt], vlds + (dt * 16 + r) * 32 + g * 8);
-            attn_subblock<T>(w, qlds, qt0, nqt, G, a.scale_log2, kf, vf);
+            for (int dt = 0; dt < DT; ++dt) vfrag_lds(vf[dt], smem + ATT_V_OFF, dt * 16 + r);
+            attn_subblock<T>(w, G, a.scale_log2, kf, vf);
         }
-    } else if (nqt > 0) {
-        const int per_wave = a.chunk / a.kg;
-        const int k_lo = (c - 1) * a.chunk + kgi * per_wave;
-        const int k_hi = min(k_lo + per_wave, len);
-        const T* kc = reinterpret_cast<const T*>(a.kcache) + ((long long)b * a.n_kv + h) * (long long)a.cap * D;
-        const T* vc = reinterpret_cast<const T*>(a.vcache) + ((long long)b * a.n_kv + h) * (long long)D * a.cap;
-        // two register buffers: sub-block kb+32 loads while kb is computed
-        Frag64 kfa[2], kfb[2];
-        VFrag<T> vfa[DT], vfb[DT];
-        if (k_lo < k_hi) fetch_ctx<T>(kfa, vfa, kc, vc, a.cap, k_lo, min(32, k_hi - k_lo));
-        for (int kb = k_lo; kb < k_hi; kb += 64) {
-            const int kb1 = kb + 32, kb2 = kb + 64;
-            if (kb1 < k_hi) fetch_ctx<T>(kfb, vfb, kc, vc, a.cap, kb1, min(32, k_hi - kb1));
-            attn_subblock<T>(w, qlds, qt0, nqt, min(32, k_hi - kb), a.scale_log2, kfa, vfa);
-            if (kb1 >= k_hi) break;
-            if (kb2 < k_hi) fetch_ctx<T>(kfa, vfa, kc, vc, a.cap, kb2, min(32, k_hi - kb2));
-            attn_subblock<T>(w, qlds, qt0, nqt, min(32, k_hi - kb1), a.scale_log2, kfb, vfb);
+    }
+    for (int it = 0; it < n_iter; ++it) {
+        const int kb = k_lo + 32 * it;
+        vm_wait<0>();       // this wave's loads of the current stage have landed
+        __syncthreads();    // ... and every wave's; the other stage is free again
+        if (kb + 32 < k_hi)
+            stage_issue<T>(kgbuf_lds + ((it + 1) & 1) * ATT_STAGE_BYTES, kc, vc, a.cap, kb + 32,
+                           min(32, k_hi - kb - 32), tl, a.qtw);
+        if (active && kb < k_hi) {
+            const unsigned char* st = kgbuf + (it & 1) * ATT_STAGE_BYTES;
+            Frag64 kf[2];
+            VFrag<T> vf[DT];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) load_frag_lds(kf[t], st, subblock_key(t, r));
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) vfrag_lds(vf[dt], st + ATT_V_OFF, dt * 16 + r);
+            attn_subblock<T>(w, min(32, k_hi - kb), a.scale_log2, kf, vf);
         }
     }
 
-    // ---- per-element (C-layout) statistics: l summed over the 4 lane groups
-    float mq[4][4], lq[4][4];
-#pragma unroll
-    for (int qi = 0; qi < 4; ++qi) {
-        float lt = w.l[qi];
-        lt += __shfl_xor(lt, 16, WAVE);
-        lt += __shfl_xor(lt, 32, WAVE);
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            mq[qi][v] = __shfl(w.m[qi], g * 4 + v, WAVE);
-            lq[qi][v] = __shfl(lt, g * 4 + v, WAVE);
-        }
-    }
+    // ---- l of query r summed over the 4 lane groups
+    float lt = w.l;
+    lt += __shfl_xor(lt, 16, WAVE);
+    lt += __shfl_xor(lt, 32, WAVE);
+    float mt = w.m;
 
-    // ---- merge the key-group waves of each query group through one LDS slot
-    // (pairwise rounds; the exchanges of a round run one after another)
-    __syncthreads();   // the prologue tiles are dead: the slot reuses their space
-    float* s = reinterpret_cast<float*>(smem);
-    float* sm = s + 4 * DT * 64 * 4;
+    // ---- merge the KG waves of each tile (all tiles at once; pairwise rounds)
+    const size_t slot_bytes = (size_t)DT * 4 * 64 * 4 + 2 * 64 * 4;
     for (int span = a.kg >> 1; span >= 1; span >>= 1) {
-        for (int x = 0; x < a.qg * span; ++x) {
-            const int xq = x / span, xp = x % span;
-            const bool sender = active_wave && qgi == xq && kgi == span + xp;
-            const bool receiver = active_wave && qgi == xq && kgi == xp;
-            if (sender) {
+        __syncthreads();   // previous users of the LDS space are done
+        if (kgi >= span && kgi < 2 * span) {
+            float* sl = reinterpret_cast<float*>(smem + (tl * span + (kgi - span)) * slot_bytes);
 #pragma unroll
-                for (int qi = 0; qi < 4; ++qi)
+            for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-                    for (int dt = 0; dt < DT; ++dt)
+                for (int v = 0; v < 4; ++v) sl[(dt * 4 + v) * 64 + lane] = w.o[dt][v];
+            sl[DT * 4 * 64 + lane] = mt;
+            sl[DT * 4 * 64 + 64 + lane] = lt;
+        }
+        __syncthreads();
+        if (kgi < span) {
+            const float* sl = reinterpret_cast<const float*>(smem + (tl * span + kgi) * slot_bytes);
+            const float m2 = sl[DT * 4 * 64 + lane];
+            const float l2 = sl[DT * 4 * 64 + 64 + lane];
+            const float mm = fmaxf(mt, m2);
+            const float f1 = (mm == -INFINITY) ? 0.f : exp2f(mt - mm);
+            const float f2 = (mm == -INFINITY) ? 0.f : exp2f(m2 - mm);
 #pragma unroll
-                        for (int v = 0; v < 4; ++v) s[((qi * DT + dt) * 4 + v) * 64 + lane] = w.o[qi][dt][v];
+            for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-                for (int qi = 0; qi < 4; ++qi)
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        sm[(qi * 4 + v) * 64 + lane] = mq[qi][v];
-                        sm[(16 + qi * 4 + v) * 64 + lane] = lq[qi][v];
-                    }
-            }
-            __syncthreads();
-            if (receiver) {
-#pragma unroll
-                for (int qi = 0; qi < 4; ++qi)
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const float m2 = sm[(qi * 4 + v) * 64 + lane];
-                        const float l2 = sm[(16 + qi * 4 + v) * 64 + lane];
-                        const float m1 = mq[qi][v];
-                        const float mm = fmaxf(m1, m2);
-                        const float f1 = (mm == -INFINITY) ? 0.f : exp2f(m1 - mm);
-                        const float f2 = (mm == -INFINITY) ? 0.f : exp2f(m2 - mm);
-#pragma unroll
-                        for (int dt = 0; dt < DT; ++dt)
-                            w.o[qi][dt][v] = w.o[qi][dt][v] * f1 + s[((qi * DT + dt) * 4 + v) * 64 + lane] * f2;
-                        mq[qi][v] = mm;
-                        lq[qi][v] = lq[qi][v] * f1 + l2 * f2;
-                    }
-            }
-            __syncthreads();
+                for (int v = 0; v < 4; ++v) w.o[dt][v] = w.o[dt][v] * f1 + sl[(dt * 4 + v) * 64 + lane] * f2;
+            mt = mm;
+            lt = lt * f1 + l2 * f2;
         }
     }
 
-    // ---- key-group 0 of every query group writes the chunk's partial
-    if (active_wave && kgi == 0 && nqt > 0) {
-        const long long base = (((long long)b * a.n_kv + h) * a.nch_max + c) * a.rpad;
-        float* op = a.opart + base * D;
-        float* mp = a.mlpart + base * 2;
+    // ---- key-group 0 of every tile writes the chunk's partial for its 16 rows
+    if (active && kgi == 0) {
+        const int R = qt * 16 + r;
+        if (R < rows) {
+            const long long row = (((long long)b * a.n_kv + h) * a.nch_max + c) * a.rpad + R;
+            float* op = a.opart + row * D;
 #pragma unroll
-        for (int qi = 0; qi < 4; ++qi)
-            if (qi < nqt)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int R = (qt0 + qi) * 16 + g * 4 + v;
-                    if (R < rows) {
-#pragma unroll
-                        for (int dt = 0; dt < DT; ++dt) op[(long long)R * D + dt * 16 + r] = w.o[qi][dt][v];
-                        if (r == 0) {
-                            mp[R * 2 + 0] = mq[qi][v];
-                            mp[R * 2 + 1] = lq[qi][v];
-                        }
-                    }
-                }
+            for (int dt = 0; dt < DT; ++dt)
+                *reinterpret_cast<float4*>(op + dt * 16 + g * 4) = make_float4(w.o[dt][0], w.o[dt][1], w.o[dt][2], w.o[dt][3]);
+            if (g == 0) *reinterpret_cast<float2*>(a.mlpart + row * 2) = make_float2(mt, lt);
+        }
     }
 }
 

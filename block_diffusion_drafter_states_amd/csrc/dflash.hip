@@ -67,6 +67,7 @@ int make_shape(const dflash_config* c, Shape& s) {
     if (s.H % s.step || s.I % s.step || (s.nq * s.D) % s.step || ((long long)s.F * s.H) % s.step)
         return DFLASH_EUNSUPPORTED;
     if (s.H % 128 || (s.nq * s.D) % 128 || (s.nkv * s.D) % 128 || s.I % 64) return DFLASH_EUNSUPPORTED;
+    if (cdiv(s.H, 16) > NORM_MAX_PARTIALS) return DFLASH_EUNSUPPORTED;   // per-tile sums of squares of a row
     s.group = s.nq / s.nkv;
     if (s.group * s.gmax > 256) return DFLASH_EUNSUPPORTED;
     s.rpad = cdiv(s.group * s.gmax, 16) * 16;
@@ -86,146 +87,160 @@ int make_shape(const dflash_config* c, Shape& s) {
 }
 
 struct GemmPlan {
-    int ns, ks, kw, n_tiles, mt, mgroups, layers, ntw, epi, amode;
-    bool prenorm;   // RMSNorm applied by rmsnorm_rows_kernel first (A_NORM request with several M-tiles)
+    int ns, ks, kw, n_tiles, mt, mgroups, layers, ntw, epi;
     size_t lds;
 };
 
 // Geometry of one projection.  wrows = weight rows (EPI_SWIGLU: rows of each of
 // gate/up).  Every workgroup owns complete output columns (no cross-workgroup
-// reduction); its waves split K (ks) and rows (ns).  Choices follow a sweep on
-// MI355X: A_PLAIN streams best with 4 waves splitting K and a 4-deep ring,
-// A_NORM (more A registers, 2-deep ring) with 2 or 1 waves along K; one
-// workgroup's LDS rings must fit the 160 KB of a CU.
-GemmPlan plan_gemm(const Shape& s, int epi, int amode, int wrows, int K, int M, int layers) {
+// reduction); its waves split K (ks) and rows (ns).  The A operand is always a
+// storage-type matrix (RMSNorm is applied by rmsnorm_rows_kernel first).
+// Choices follow a sweep on MI355X at 16 rows: 16-column tiles (ntw 1) with 8
+// waves along K for the 4096-row projections so that every CU streams, 32-column
+// tiles with 4 waves for wider ones, 4 waves per 16 gate + 16 up rows for
+// SwiGLU, two waves per 32 vocabulary rows for the LM head (weights read from
+// HBM, not from the last-level cache); one workgroup's LDS ring must fit the
+// 160 KB of a CU.
+GemmPlan plan_gemm(const Shape& s, int epi, int wrows, int K, int M, int layers) {
     GemmPlan p;
     p.epi = epi;
     p.layers = layers;
-    p.ntw = GEMM_NT;
     p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
     p.mgroups = cdiv(M, 16 * p.mt);
-    // normalising on load keeps fp32 rows of every M-tile in registers; beyond one
-    // M-tile the rows are normalised once up front and streamed as plain A
-    p.prenorm = amode == A_NORM && p.mt > 1;
-    if (p.prenorm) amode = A_PLAIN;
-    p.amode = amode;
-    const int ring = gemm_ring_depth(amode, p.mt, p.ntw);
+    p.ns = 1;
+    p.ntw = 2;
     int ks;
     if (epi == EPI_KV_INJECT) {
-        p.ns = s.D / (GEMM_NT * 16);            // one head per workgroup
-        p.n_tiles = 2 * s.nkv;
+        p.ns = s.D / (p.ntw * 16);              // one head per workgroup
         ks = 1;
     } else if (epi == EPI_ARGMAX) {
-        p.ns = 1;
-        p.n_tiles = cdiv(wrows, p.ns * p.ntw * 16);
-        ks = 1;
-    } else if (epi == EPI_SWIGLU) {
-        p.ns = 1;
-        p.n_tiles = cdiv(wrows, p.ns * 16);         // 16 output columns (gate + up tiles) per wave group
         ks = 2;
+    } else if (epi == EPI_SWIGLU) {
+        ks = 4;
     } else {
-        p.ns = 1;
-        p.n_tiles = cdiv(wrows, p.ns * p.ntw * 16);
-        ks = amode == A_PLAIN ? 4 : 2;
+        p.ntw = wrows / 32 >= 192 ? 2 : 1;
+        ks = p.ntw == 1 ? 8 : 4;
     }
+    if (epi == EPI_KV_INJECT) p.n_tiles = 2 * s.nkv;
+    else if (epi == EPI_SWIGLU) p.n_tiles = cdiv(wrows, 16);   // 16 gate + 16 up rows per workgroup
+    else p.n_tiles = cdiv(wrows, p.ns * p.ntw * 16);
+    const int ring = gemm_ring_depth(p.mt, p.ntw);
     while (ks > 1 && K / s.step < 2 * ks) ks /= 2;        // at least two k-steps per wave
     while (ks > 1 && gemm_lds_bytes_host(p.ns, ks, p.mt, p.ntw, ring) > GEMM_MAX_LDS) ks /= 2;
-    while (p.ns > 1 && gemm_lds_bytes_host(p.ns, ks, p.mt, p.ntw, ring) > GEMM_MAX_LDS) {
-        p.ns /= 2;
-        p.n_tiles *= 2;
-    }
     p.ks = ks;
     p.kw = cdiv(cdiv(K, ks), s.step) * s.step;
     p.lds = gemm_lds_bytes_host(p.ns, p.ks, p.mt, p.ntw, ring);
     return p;
 }
 
+// Attention launch shape: a workgroup takes up to ATT_MAX_TILES query tiles of
+// one (b, h, chunk), with kg waves per tile splitting the chunk's keys, and at
+// most ATT_MAX_WAVES (>= 4) waves in all.
 struct AttnPlan {
-    int qg, kg;
+    int qtw, kg, nqs;
 };
 
 AttnPlan plan_attn(const Shape& s, int gamma) {
     AttnPlan a;
     const int qt = cdiv(s.group * gamma, 16);
-    a.qg = cdiv(qt, 4);
-    a.kg = a.qg == 1 ? 4 : (a.qg == 2 ? 2 : 1);
+    a.qtw = std::min(qt, ATT_MAX_TILES);
+    a.kg = a.qtw <= 2 ? 4 : (a.qtw <= 4 ? 2 : 1);
+    a.nqs = cdiv(qt, a.qtw);
     return a;
 }
 
-// Workspace carving.  Everything is per-call scratch: no state survives a call.
+struct InjectPlans {
+    GemmPlan fuse, kv;
+};
+
+InjectPlans inject_plans(const Shape& s, int batch, int rows) {
+    const int M = batch * rows;
+    return {plan_gemm(s, EPI_STORE, s.H, s.F * s.H, M, 1), plan_gemm(s, EPI_KV_INJECT, 2 * s.nkv * s.D, s.H, M, s.L)};
+}
+
+struct DraftPlans {
+    GemmPlan qkv, o, gateup, down, lm;
+};
+
+DraftPlans draft_plans(const Shape& s, int M) {
+    return {plan_gemm(s, EPI_STORE, (s.nq + 2 * s.nkv) * s.D, s.H, M, 1), plan_gemm(s, EPI_STORE, s.H, s.nq * s.D, M, 1),
+            plan_gemm(s, EPI_SWIGLU, s.I, s.H, M, 1), plan_gemm(s, EPI_STORE, s.H, s.I, M, 1),
+            plan_gemm(s, EPI_ARGMAX, s.V, s.H, M, 1)};
+}
+
+// Workspace carving, sized from the same plans that the launches use.  Everything
+// is per-call scratch: no state survives a call.
 struct Layout {
     // draft
     size_t x, ssq_x, qkv, opart, mlpart, obuf, hbuf, amax, nbuf, draft_end;
+    int ssq_x_tiles, amax_tiles;
     // inject
     size_t c, ssq_c, cnorm, inject_end;
+    int ssq_c_tiles;
 };
-
-int lm_tiles(const Shape& s) { return cdiv(s.V, 8 * GEMM_NT * 16); }
 
 Layout make_layout(const Shape& s, int batch, int rows) {
     Layout l;
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
     const size_t M = (size_t)batch * s.gmax;
-    const int ntH = s.H / (GEMM_NT * 16);
+    const DraftPlans dp = draft_plans(s, (int)M);
+    l.ssq_x_tiles = std::max(1, std::max(dp.o.n_tiles, dp.down.n_tiles));
+    l.amax_tiles = dp.lm.n_tiles;
     l.x = take(M * s.H * 4);
-    l.ssq_x = take((size_t)ntH * M * 4);
+    l.ssq_x = take((size_t)l.ssq_x_tiles * M * 4);
     l.qkv = take(M * (size_t)(s.nq + 2 * s.nkv) * s.D * 4);
     l.opart = take((size_t)batch * s.nkv * s.nch_max * s.rpad * s.D * 4);
     l.mlpart = take((size_t)batch * s.nkv * s.nch_max * s.rpad * 2 * 4);
     l.obuf = take(M * s.nq * s.D * s.esize);
     l.hbuf = take(M * s.I * s.esize);
-    l.amax = take((size_t)lm_tiles(s) * M * 8);
-    l.nbuf = take(M > 16 ? M * s.H * s.esize : 0);            // normalised rows (batch > 1)
+    l.amax = take((size_t)l.amax_tiles * M * 8);
+    l.nbuf = take(M * s.H * s.esize);                         // RMSNorm-ed rows (GEMM A operand)
     l.draft_end = off;
     l.c = l.ssq_c = l.cnorm = 0;
+    l.ssq_c_tiles = 0;
     if (rows > 0) {
         const size_t Mi = (size_t)batch * rows;
+        l.ssq_c_tiles = inject_plans(s, batch, rows).fuse.n_tiles;
         l.c = take(Mi * s.H * 4);
-        l.ssq_c = take((size_t)ntH * Mi * 4);
-        l.cnorm = take(Mi > 16 ? (size_t)s.L * Mi * s.H * s.esize : 0);   // per-layer normalised rows
+        l.ssq_c = take((size_t)l.ssq_c_tiles * Mi * 4);
+        l.cnorm = take((size_t)s.L * Mi * s.H * s.esize);     // per-layer RMSNorm-ed rows
     }
     l.inject_end = off;
     return l;
 }
 
-template <typename T, int EPI, int AMODE, int MT>
+template <typename T, int EPI, int MT, int NTW>
 int launch_gemm(const GemmArgs& a, const GemmPlan& p, hipStream_t st, Tracer& tr, const char* name) {
-    constexpr int P = gemm_ring_depth(AMODE, MT, GEMM_NT);
+    constexpr int P = gemm_ring_depth(MT, NTW);
     dim3 grid(p.n_tiles, p.mgroups, p.layers);
     tr.begin(name);
-    hipLaunchKernelGGL((gemm_kernel<T, EPI, AMODE, MT, P>), grid, dim3(64 * p.ns * p.ks), p.lds, st, a);
+    hipLaunchKernelGGL((gemm_kernel<T, EPI, MT, NTW, P>), grid, dim3(64 * p.ns * p.ks), p.lds, st, a);
     const bool ok = hipGetLastError() == hipSuccess;
     tr.end();
     return ok ? DFLASH_OK : DFLASH_ELAUNCH;
 }
 
-template <typename T, int EPI, int AMODE>
+template <typename T, int EPI, int NTW>
 int launch_gemm_mt(const GemmArgs& a, const GemmPlan& p, hipStream_t st, Tracer& tr, const char* name) {
-    if constexpr (AMODE == A_NORM) {
-        return p.mt == 1 ? launch_gemm<T, EPI, A_NORM, 1>(a, p, st, tr, name) : DFLASH_EINVAL;
-    } else {
-        switch (p.mt) {
-            case 1: return launch_gemm<T, EPI, AMODE, 1>(a, p, st, tr, name);
-            case 2: return launch_gemm<T, EPI, AMODE, 2>(a, p, st, tr, name);
-            case 4: return launch_gemm<T, EPI, AMODE, 4>(a, p, st, tr, name);
-        }
-        return DFLASH_EINVAL;
+    switch (p.mt) {
+        case 1: return launch_gemm<T, EPI, 1, NTW>(a, p, st, tr, name);
+        case 2: return launch_gemm<T, EPI, 2, NTW>(a, p, st, tr, name);
+        case 4: return launch_gemm<T, EPI, 4, NTW>(a, p, st, tr, name);
     }
+    return DFLASH_EINVAL;
 }
 
 template <typename T>
 int gemm_dispatch(const GemmArgs& a, const GemmPlan& p, hipStream_t st, Tracer& tr, const char* name) {
-    if (p.epi == EPI_STORE && p.amode == A_PLAIN) return launch_gemm_mt<T, EPI_STORE, A_PLAIN>(a, p, st, tr, name);
-    if (p.epi == EPI_SWIGLU && p.amode == A_PLAIN) return launch_gemm_mt<T, EPI_SWIGLU, A_PLAIN>(a, p, st, tr, name);
-    if (p.epi == EPI_ARGMAX && p.amode == A_PLAIN) return launch_gemm_mt<T, EPI_ARGMAX, A_PLAIN>(a, p, st, tr, name);
-    if (p.epi == EPI_KV_INJECT && p.amode == A_PLAIN)
-        return launch_gemm_mt<T, EPI_KV_INJECT, A_PLAIN>(a, p, st, tr, name);
-    if (p.epi == EPI_STORE && p.amode == A_NORM) return launch_gemm_mt<T, EPI_STORE, A_NORM>(a, p, st, tr, name);
-    if (p.epi == EPI_SWIGLU && p.amode == A_NORM) return launch_gemm_mt<T, EPI_SWIGLU, A_NORM>(a, p, st, tr, name);
-    if (p.epi == EPI_ARGMAX && p.amode == A_NORM) return launch_gemm_mt<T, EPI_ARGMAX, A_NORM>(a, p, st, tr, name);
-    if (p.epi == EPI_KV_INJECT && p.amode == A_NORM)
-        return launch_gemm_mt<T, EPI_KV_INJECT, A_NORM>(a, p, st, tr, name);
+    switch (p.epi) {
+        case EPI_STORE:
+            return p.ntw == 1 ? launch_gemm_mt<T, EPI_STORE, 1>(a, p, st, tr, name)
+                              : launch_gemm_mt<T, EPI_STORE, 2>(a, p, st, tr, name);
+        case EPI_SWIGLU: return launch_gemm_mt<T, EPI_SWIGLU, 2>(a, p, st, tr, name);
+        case EPI_ARGMAX: return launch_gemm_mt<T, EPI_ARGMAX, 2>(a, p, st, tr, name);
+        case EPI_KV_INJECT: return launch_gemm_mt<T, EPI_KV_INJECT, 2>(a, p, st, tr, name);
+    }
     return DFLASH_EINVAL;
 }
 
@@ -259,42 +274,11 @@ bool weights_ok(const Shape& s, const dflash_weights* w) {
     return true;
 }
 
-struct InjectPlans {
-    GemmPlan fuse, kv;
-};
-
-InjectPlans inject_plans(const Shape& s, int batch, int rows) {
-    const int M = batch * rows;
-    return {plan_gemm(s, EPI_STORE, A_PLAIN, s.H, s.F * s.H, M, 1),
-            plan_gemm(s, EPI_KV_INJECT, A_NORM, 2 * s.nkv * s.D, s.H, M, s.L)};
-}
-
-struct DraftPlans {
-    GemmPlan qkv, o, gateup, down, lm;
-};
-
-DraftPlans draft_plans(const Shape& s, int M) {
-    return {plan_gemm(s, EPI_STORE, A_NORM, (s.nq + 2 * s.nkv) * s.D, s.H, M, 1),
-            plan_gemm(s, EPI_STORE, A_PLAIN, s.H, s.nq * s.D, M, 1),
-            plan_gemm(s, EPI_SWIGLU, A_NORM, s.I, s.H, M, 1),
-            plan_gemm(s, EPI_STORE, A_PLAIN, s.H, s.I, M, 1),
-            plan_gemm(s, EPI_ARGMAX, A_NORM, s.V, s.H, M, 1)};
-}
-
-// A operand = RMSNorm(x; w): normalised on load (one M-tile), or normalised once
-// into nbuf by rmsnorm_rows_kernel and then streamed as plain A.
+// A operand = RMSNorm(x; w) in the storage type: rows normalised into nbuf by
+// rmsnorm_rows_kernel (rstd from the producers' per-tile sums of squares).
 template <typename T>
-int set_norm_a(GemmArgs& a, const GemmPlan& p, const Shape& s, const float* x, int M, const float* ssq, int n_ssq,
-               const void* w, void* nbuf, hipStream_t st, Tracer& tr) {
-    if (!p.prenorm) {
-        a.a = x;
-        a.lda = s.H;
-        a.ssq = ssq;
-        a.n_ssq = n_ssq;
-        a.ssq_ld = M;
-        a.layer[0].norm_w = w;
-        return DFLASH_OK;
-    }
+int set_norm_a(GemmArgs& a, const Shape& s, const float* x, int M, const float* ssq, int n_ssq, const void* w,
+               void* nbuf, hipStream_t st, Tracer& tr) {
     NormWeights nw{};
     nw.w[0] = w;
     tr.begin("rmsnorm");
@@ -330,23 +314,18 @@ int run_inject(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int
         if ((rc = gemm_dispatch<T>(a, pl.fuse, st, tr, "fuse"))) return rc;
     }
     {   // stage 2: every layer's RMSNorm -> W_k | W_v -> k-norm + RoPE -> cache
+        if (pl.fuse.n_tiles > lay.ssq_c_tiles) return DFLASH_EUNSUPPORTED;
         GemmArgs a = gemm_base(s, pl.kv, M, s.H);
-        a.a = c;
+        NormWeights nw{};   // one normalised copy of c per layer (each layer has its own scale)
+        for (int l = 0; l < s.L; ++l) nw.w[l] = w->layers[l].in_norm;
+        T* cn = reinterpret_cast<T*>(wsb + lay.cnorm);
+        tr.begin("rmsnorm");
+        hipLaunchKernelGGL((rmsnorm_rows_kernel<T>), dim3(M, cdiv(s.H, 1024), s.L), dim3(256), 0, st, c, s.H, ssq_c,
+                           pl.fuse.n_tiles, M, nw, s.H, s.eps, cn, s.H, (long long)M * s.H);
+        tr.end();
+        if (hipGetLastError() != hipSuccess) return DFLASH_ELAUNCH;
+        for (int l = 0; l < s.L; ++l) a.layer[l].a = cn + (size_t)l * M * s.H;
         a.lda = s.H;
-        a.ssq = ssq_c;
-        a.n_ssq = pl.fuse.n_tiles;
-        a.ssq_ld = M;
-        if (pl.kv.prenorm) {   // one normalised copy of c per layer (each layer has its own scale)
-            NormWeights nw{};
-            for (int l = 0; l < s.L; ++l) nw.w[l] = w->layers[l].in_norm;
-            T* cn = reinterpret_cast<T*>(wsb + lay.cnorm);
-            tr.begin("rmsnorm");
-            hipLaunchKernelGGL((rmsnorm_rows_kernel<T>), dim3(M, cdiv(s.H, 1024), s.L), dim3(256), 0, st, c, s.H,
-                               ssq_c, pl.fuse.n_tiles, M, nw, s.H, s.eps, cn, s.H, (long long)M * s.H);
-            tr.end();
-            if (hipGetLastError() != hipSuccess) return DFLASH_ELAUNCH;
-            for (int l = 0; l < s.L; ++l) a.layer[l].a = cn + (size_t)l * M * s.H;
-        }
         a.N = 2 * s.nkv * s.D;
         a.seg_end[0] = s.nkv * s.D;
         a.seg_end[1] = a.seg_end[2] = 2 * s.nkv * s.D;
@@ -355,7 +334,6 @@ int run_inject(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int
             const dflash_layer_weights& lw = w->layers[l];
             a.layer[l].w[0] = lw.wk;
             a.layer[l].w[1] = lw.wv;
-            a.layer[l].norm_w = lw.in_norm;
             a.layer[l].head_norm = lw.k_norm;
             a.layer[l].kcache = static_cast<T*>(kv->k) + l * layer_elems;
             a.layer[l].vcache = static_cast<T*>(kv->v) + l * layer_elems;
@@ -383,6 +361,8 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
     char* wsb = static_cast<char*>(ws);
     const int M = batch * gamma;
     const DraftPlans pl = draft_plans(s, M);
+    if (pl.lm.n_tiles > lay.amax_tiles || std::max(pl.o.n_tiles, pl.down.n_tiles) > lay.ssq_x_tiles)
+        return DFLASH_EUNSUPPORTED;   // the workspace was carved for other plans
     float* x = reinterpret_cast<float*>(wsb + lay.x);
     float* ssq_x = reinterpret_cast<float*>(wsb + lay.ssq_x);
     float* qkv = reinterpret_cast<float*>(wsb + lay.qkv);
@@ -403,14 +383,14 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
     int n_ssq = 1;
 
     const AttnPlan ap = plan_attn(s, gamma);
-    const size_t attn_lds = attn_lds_bytes_host(s.esize, cdiv(s.group * gamma, 16), ap.kg);
+    const size_t attn_lds = attn_lds_bytes_host(s.esize, ap.qtw, ap.kg);
     const size_t layer_elems = (size_t)s.Bmax * s.nkv * s.cap * s.D;
 
     for (int l = 0; l < s.L; ++l) {
         const dflash_layer_weights& lw = w->layers[l];
         {   // raw q | k | v of the block (three weight tensors, one launch)
             GemmArgs a = gemm_base(s, pl.qkv, M, s.H);
-            if ((rc = set_norm_a<T>(a, pl.qkv, s, x, M, ssq_x, n_ssq, lw.in_norm, nbuf, st, tr))) return rc;
+            if ((rc = set_norm_a<T>(a, s, x, M, ssq_x, n_ssq, lw.in_norm, nbuf, st, tr))) return rc;
             a.N = qkv_ld;
             a.seg_end[0] = s.nq * s.D;
             a.seg_end[1] = (s.nq + s.nkv) * s.D;
@@ -446,11 +426,12 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
             a.chunk = s.chunk;
             a.gamma = gamma;
             a.group = s.group;
-            a.qg = ap.qg;
+            a.qtw = ap.qtw;
             a.kg = ap.kg;
+            a.nqs = ap.nqs;
             a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)s.D));
             tr.begin("attention");
-            hipLaunchKernelGGL((attn_partial_kernel<T>), dim3(s.nch_max, s.nkv, batch), dim3(ATT_THREADS), attn_lds,
+            hipLaunchKernelGGL((attn_partial_kernel<T>), dim3(s.nch_max, s.nkv * ap.nqs, batch), dim3(64 * ap.qtw * ap.kg), attn_lds,
                                st, a);
             tr.end();
             if (hipGetLastError() != hipSuccess) return DFLASH_ELAUNCH;
@@ -489,7 +470,7 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
         }
         {   // h = silu(W_gate a2) * (W_up a2)
             GemmArgs a = gemm_base(s, pl.gateup, M, s.H);
-            if ((rc = set_norm_a<T>(a, pl.gateup, s, x, M, ssq_x, n_ssq, lw.post_norm, nbuf, st, tr))) return rc;
+            if ((rc = set_norm_a<T>(a, s, x, M, ssq_x, n_ssq, lw.post_norm, nbuf, st, tr))) return rc;
             a.N = s.I;
             a.seg_end[0] = a.seg_end[1] = a.seg_end[2] = s.I;
             a.layer[0].w[0] = lw.w_gate;
@@ -524,7 +505,7 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
     }
     {   // final norm -> LM head -> per-tile argmax
         GemmArgs a = gemm_base(s, pl.lm, M, s.H);
-        if ((rc = set_norm_a<T>(a, pl.lm, s, x, M, ssq_x, n_ssq, w->final_norm, nbuf, st, tr))) return rc;
+        if ((rc = set_norm_a<T>(a, s, x, M, ssq_x, n_ssq, w->final_norm, nbuf, st, tr))) return rc;
         a.N = s.V;
         a.seg_end[0] = a.seg_end[1] = a.seg_end[2] = s.V;
         a.layer[0].w[0] = w->lm_head;

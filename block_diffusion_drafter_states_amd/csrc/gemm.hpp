@@ -6,7 +6,8 @@
 //
 // Geometry.  A workgroup owns WCOLS = NS * NTW * 16 complete weight rows
 // (output columns) and is made of NS x KS wavefronts: NS groups of waves own
-// different rows, the KS waves of a group split the K range.  No workgroup
+// different rows (NTW MFMA n-tiles of 16 rows per wave), the KS waves of a
+// group split the K range.  No workgroup
 // ever waits for another one: the KS partial sums are reduced through LDS in
 // a fixed order (deterministic) and the workgroup runs the fused epilogue.
 //
@@ -16,28 +17,22 @@
 // passing through registers.  Inside a 16-row x 256-byte ring tile, the
 // 16-byte chunk c of row rho sits at position c ^ rho, so the MFMA fragment
 // reads (lane r <- row r) hit 16 distinct bank groups.  The few activation
-// rows (L2-resident) are loaded into registers in the same ring slot; explicit
-// vmcnt waits (loads complete in issue order) make a slot's LDS data visible.
-//
-// A operand: A_PLAIN reads storage-type rows; A_NORM reads fp32 rows x and
-// applies RMSNorm on load, rho(x * rstd * w), with rstd from the per-tile sums
-// of squares that the producing kernel wrote (summed in a fixed order).
+// rows (storage type, already normalised where the model normalises them;
+// L2-resident) are loaded into registers in the same ring slot; explicit vmcnt
+// waits (loads complete in issue order) make a slot's LDS data visible.
 #pragma once
 
 #include "common.hpp"
 
 namespace dflash {
 
-enum { A_PLAIN = 0, A_NORM = 1 };
 enum { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_ARGMAX = 2, EPI_KV_INJECT = 3 };
 
 constexpr int MAX_LAYERS = 16;
-constexpr int GEMM_NT = 2;   // MFMA n-tiles (16 weight rows each) per wave
 
 struct GemmLayer {
     const void* a;          // nullable: this layer's A operand (overrides GemmArgs::a)
     const void* w[3];       // weight segments: rows [seg_end[i-1], seg_end[i]) come from w[i]
-    const void* norm_w;     // A_NORM scale [K]
     const void* head_norm;  // EPI_KV_INJECT: per-head k RMSNorm scale [D]
     void* kcache;           // EPI_KV_INJECT: this layer's K cache [Bmax][n_kv][cap][D]
     void* vcache;           // EPI_KV_INJECT: this layer's V cache [Bmax][n_kv][D][cap]
@@ -45,12 +40,9 @@ struct GemmLayer {
 
 struct GemmArgs {
     // ---- A operand
-    const void* a;          // T [M][lda] (A_PLAIN) or float [M][lda] (A_NORM)
+    const void* a;          // T [M][lda]
     long long lda;
-    const float* ssq;       // A_NORM: [n_ssq][ssq_ld] partial sums of squares per row
-    int n_ssq;
-    int ssq_ld;
-    float eps;
+    float eps;              // EPI_KV_INJECT: k RMSNorm epsilon
     int M;
     int K;
     // ---- W operand and geometry
@@ -81,57 +73,12 @@ struct GemmArgs {
     unsigned* status;
 };
 
-template <typename T, int AMODE>
-struct ASlot;   // raw A data of one k-step for one M-tile
-
-template <typename T>
-struct ASlot<T, A_PLAIN> {
-    Frag64 f;
-};
-
-template <typename T>
-struct ASlot<T, A_NORM> {
-    u32x4_t x[Elem<T>::PER16];   // fp32 bits: piece i holds PER16 values in PER16/4 vectors
-};
-
-template <typename T>
-__device__ __forceinline__ void pack_norm(Frag64& out, const u32x4_t* x, const Frag64& w, float rs);
-
-template <>
-__device__ __forceinline__ void pack_norm<bf16_t>(Frag64& out, const u32x4_t* x, const Frag64& w, float rs) {
-    // piece i: 8 values x[2i], x[2i+1]; scale w.q[i] = 8 bf16
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const u32x4_t wq = w.q[i], a = x[2 * i], b = x[2 * i + 1];
-        const uint32_t xv[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-        u32x4_t o;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float w0 = __uint_as_float(wq[j] << 16), w1 = __uint_as_float(wq[j] & 0xFFFF0000u);
-            o[j] = (uint32_t)f32_to_bf16(__uint_as_float(xv[2 * j]) * rs * w0) |
-                   ((uint32_t)f32_to_bf16(__uint_as_float(xv[2 * j + 1]) * rs * w1) << 16);
-        }
-        out.q[i] = o;
-    }
-}
-
-template <>
-__device__ __forceinline__ void pack_norm<float>(Frag64& out, const u32x4_t* x, const Frag64& w, float rs) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        u32x4_t o;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) o[j] = __float_as_uint(__uint_as_float(x[i][j]) * rs * __uint_as_float(w.q[i][j]));
-        out.q[i] = o;
-    }
-}
-
 // Ring depth (k-steps in flight): the weights live in LDS; the registers of a
 // slot hold only the A fragments (~160 VGPRs budget), and the loads of P-1
 // steps must fit the 6-bit vmcnt.
-__host__ __device__ constexpr int gemm_ring_depth(int amode, int mt, int ntw) {
-    const int slot = amode == A_PLAIN ? mt * 16 : mt * 32 + 16;
-    const int lps = ntw * 4 + (amode == A_PLAIN ? mt * 4 : mt * 8 + 4);   // bf16 count (the larger one)
+__host__ __device__ constexpr int gemm_ring_depth(int mt, int ntw) {
+    const int slot = mt * 16;
+    const int lps = ntw * 4 + mt * 4;
     int p = 160 / slot;
     p = p > 4 ? 4 : (p < 1 ? 1 : p);
     while (p > 1 && (p - 1) * lps > 63) --p;
@@ -149,28 +96,12 @@ template <typename T, int EPI>
 __device__ void gemm_epilogue(const GemmArgs& p, const GemmLayer& L, int tile, int m0, int mrows, int wcols,
                               const float* Ct);
 
-// s_waitcnt vmcnt(n) with lgkmcnt/expcnt left unconstrained (gfx9 encoding:
-// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] in [15:14]).
-template <int N>
-__device__ __forceinline__ void vmcnt_imm() {
-    static_assert(N >= 0 && N <= 63, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
-}
-
-// Wait until at most `later` ring steps (of LPS loads each) are still in flight.
-template <int LPS, int P>
-__device__ __forceinline__ void vmcnt_wait(int later) {
-    if (later <= 0) vmcnt_imm<0>();
-    else if (P > 1 && later == 1) vmcnt_imm<(P > 1 ? LPS : 0)>();
-    else if (P > 2 && later == 2) vmcnt_imm<(P > 2 ? 2 * LPS : 0)>();
-    else vmcnt_imm<(P > 3 ? 3 * LPS : 0)>();
-}
-
 // --------------------------------------------------------------------------------------------
-template <typename T, int EPI, int AMODE, int MT, int P>
+template <typename T, int EPI, int MT, int NTW, int P>
 __global__ __launch_bounds__(512) void gemm_kernel(const GemmArgs p) {
     constexpr int STEP = Elem<T>::STEP;
-    constexpr int NTW = GEMM_NT;   // weight frags per slot (EPI_SWIGLU: one gate tile + one up tile)
+    // NTW = weight tiles per ring slot (EPI_SWIGLU: one gate tile + one up tile)
+    static_assert(EPI != EPI_SWIGLU || NTW == 2, "SwiGLU pairs one gate and one up tile");
     extern __shared__ __align__(16) unsigned char smem[];
 
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, g = lane >> 4, r = lane & 15;
@@ -187,9 +118,8 @@ __global__ __launch_bounds__(512) void gemm_kernel(const GemmArgs p) {
 
     // ---- weight rows of this wave: ring loads fetch rows 4*i + (lane>>4) of each n-tile
     // vector-memory instructions per ring step, all issued by this loop in a fixed order:
-    // 4 direct-to-LDS loads per weight tile, then the A fragments (4 per M-tile; A_NORM:
-    // PER16 fp32 vectors per M-tile plus 4 for the norm scale)
-    constexpr int LPS = NTW * 4 + (AMODE == A_PLAIN ? MT * 4 : MT * Elem<T>::PER16 + 4);
+    // 4 direct-to-LDS loads per weight tile, then 4 per M-tile for the A fragments
+    constexpr int LPS = NTW * 4 + MT * 4;
     static_assert((P - 1) * LPS <= 63, "vmcnt range");
     const int lq = lane >> 4, lc = lane & 15;
     const char* wsrc[NTW][4];
@@ -219,54 +149,20 @@ __global__ __launch_bounds__(512) void gemm_kernel(const GemmArgs p) {
     const uint32_t ring_lds = lds_offset(smem) + (uint32_t)wv_u * (P * NTW * 4096);
     const char* ring = reinterpret_cast<const char*>(smem) + (size_t)wv_u * P * NTW * 4096;
 
-    // ---- rstd of the workgroup's rows, computed once: thread t sums partial tiles
-    // t/R, t/R + nthreads/R, ... of row t%R, then the per-row sums are added in
-    // chunk order (deterministic).
-    __shared__ float red_sh[512];
-    __shared__ float rstd_sh[64];
-    if constexpr (AMODE == A_NORM) {
-        constexpr int R = 16 * MT;
-        const int nthr = blockDim.x;
-        const int row = threadIdx.x % R, chunk = threadIdx.x / R, nchunk = nthr / R;
-        const int m = m0 + row;
-        float part = 0.f;
-        if (m < p.M)
-            for (int t = chunk; t < p.n_ssq; t += nchunk) part += p.ssq[(long long)t * p.ssq_ld + m];
-        red_sh[chunk * R + row] = part;
-        __syncthreads();
-        if (threadIdx.x < R) {
-            float sum = 0.f;
-            for (int c = 0; c < nchunk; ++c) sum += red_sh[c * R + threadIdx.x];
-            rstd_sh[threadIdx.x] = 1.0f / sqrtf(sum / (float)K + p.eps);
-        }
-        __syncthreads();
-    }
-
     // ---- A row pointers (one row per lane and M-tile)
     const char* arow[MT];
-    float rstd[MT];
     bool avalid[MT];
-    const char* nw = nullptr;
     const void* abase = L.a ? L.a : p.a;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
         const int m = m0 + mt * 16 + r;
         avalid[mt] = m < p.M;
         const int mm = avalid[mt] ? m : 0;   // padding rows read row 0; their MFMA input is zeroed
-        if (AMODE == A_PLAIN) {
-            arow[mt] = reinterpret_cast<const char*>(reinterpret_cast<const T*>(abase) + (long long)mm * p.lda + k0 +
-                                                     g * Elem<T>::PER16);
-        } else {
-            arow[mt] = reinterpret_cast<const char*>(reinterpret_cast<const float*>(abase) + (long long)mm * p.lda + k0 +
-                                                     g * Elem<T>::PER16);
-            rstd[mt] = rstd_sh[mt * 16 + r];
-        }
+        arow[mt] = reinterpret_cast<const char*>(reinterpret_cast<const T*>(abase) + (long long)mm * p.lda + k0 +
+                                                 g * Elem<T>::PER16);
     }
-    if (AMODE == A_NORM)
-        nw = reinterpret_cast<const char*>(reinterpret_cast<const T*>(L.norm_w) + k0 + g * Elem<T>::PER16);
 
-    ASlot<T, AMODE> areg[P][MT];
-    Frag64 nreg[P];
+    Frag64 areg[P][MT];
     auto issue = [&](int q, int step) {
 #pragma unroll
         for (int t = 0; t < NTW; ++t)
@@ -275,24 +171,9 @@ __global__ __launch_bounds__(512) void gemm_kernel(const GemmArgs p) {
                 dma_b128(wsrc[t][i] + (size_t)step * 256, ring_lds + (uint32_t)((q * NTW + t) * 4096 + i * 1024));
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-            if constexpr (AMODE == A_PLAIN) {
-                const char* a = arow[mt] + (size_t)step * 256;
+            const char* a = arow[mt] + (size_t)step * 256;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) vload_b128(areg[q][mt].f.q[i], a + i * 64);
-            } else {
-                // piece i of the lane: PER16 floats at i*STEP/4 elements (PER16/4 vectors)
-                constexpr int F4 = Elem<T>::PER16 / 4;
-                const char* xs = arow[mt] + (size_t)step * STEP * 4;
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int h = 0; h < F4; ++h) vload_b128(areg[q][mt].x[i * F4 + h], xs + (i * (STEP / 4) + h * 4) * 4);
-            }
-        }
-        if constexpr (AMODE == A_NORM) {
-            const char* wp = nw + (size_t)step * 256;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) vload_b128(nreg[q].q[i], wp + i * 64);
+            for (int i = 0; i < 4; ++i) vload_b128(areg[q][mt].q[i], a + i * 64);
         }
     };
     // all loads of ring slot q are complete once at most `later` later steps are outstanding
@@ -302,14 +183,7 @@ __global__ __launch_bounds__(512) void gemm_kernel(const GemmArgs p) {
         else if (P > 2 && later == 2) vm_wait<(P > 2 ? 2 * LPS : 0)>();
         else vm_wait<(P > 3 ? 3 * LPS : 0)>();
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            if constexpr (AMODE == A_PLAIN) tie(areg[q][mt].f);
-            else {
-#pragma unroll
-                for (int i = 0; i < Elem<T>::PER16; ++i) tie(areg[q][mt].x[i]);
-            }
-        }
-        if constexpr (AMODE == A_NORM) tie(nreg[q]);
+        for (int mt = 0; mt < MT; ++mt) tie(areg[q][mt]);
     };
 
 #pragma unroll
@@ -338,9 +212,7 @@ __global__ __launch_bounds__(512) void gemm_kernel(const GemmArgs p) {
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
                     if (mt * 16 < mrows) {
-                        Frag64 af;
-                        if constexpr (AMODE == A_PLAIN) af = areg[q][mt].f;
-                        else pack_norm<T>(af, areg[q][mt].x, nreg[q], rstd[mt]);
+                        Frag64 af = areg[q][mt];
                         if (!avalid[mt]) zero_frag64(af);
 #pragma unroll
                         for (int t = 0; t < NTW; ++t) mfma_kstep<T>(acc[mt][t], af, bf[t]);

@@ -62,31 +62,42 @@ __global__ __launch_bounds__(64) void verify_kernel(int batch, int gamma, const 
 // out[z][m][k] = rho(x[m][k] * rstd_m * w_z[k]); rstd_m from the per-tile sums of
 // squares of row m.  blockIdx.x = row, blockIdx.y = 1024-column chunk,
 // blockIdx.z = weight set (one per layer when the same rows feed every layer).
+// Every load of a thread is issued before the first reduction (one memory
+// latency); the partial sums are added in a fixed order (deterministic).
 struct NormWeights {
     const void* w[16];
 };
+
+constexpr int NORM_MAX_PARTIALS = 512;
 
 template <typename T>
 __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const float* __restrict__ x, int ldx,
                                                            const float* __restrict__ ssq, int n_ssq, int ssq_ld,
                                                            const NormWeights wz, int K, float eps,
                                                            T* __restrict__ out, int ldo, long long out_z) {
-    __shared__ float rs_sh;
+    __shared__ float red[4];
     const int m = blockIdx.x;
-    if (threadIdx.x < 64) {
-        float s = 0.f;
-        for (int t = threadIdx.x; t < n_ssq; t += 64) s += ssq[(long long)t * ssq_ld + m];
-        s = wave_sum(s);
-        if (threadIdx.x == 0) rs_sh = 1.0f / sqrtf(s / (float)K + eps);
-    }
-    __syncthreads();
-    const float rs = rs_sh;
+    const int k = blockIdx.y * 1024 + threadIdx.x * 4;   // K % 4 == 0
+    const bool has = k < K;
     const T* w = reinterpret_cast<const T*>(wz.w[blockIdx.z]);
-    T* o = out + (long long)blockIdx.z * out_z + (long long)m * ldo;
-    const float* xr = x + (long long)m * ldx;
-    const int kend = min(K, (int)(blockIdx.y + 1) * 1024);
-    for (int k = blockIdx.y * 1024 + threadIdx.x; k < kend; k += 256)
-        o[k] = Elem<T>::from_f(xr[k] * rs * Elem<T>::to_f(w[k]));
+    const float4 xv = has ? *reinterpret_cast<const float4*>(x + (long long)m * ldx + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+    float wv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) wv[u] = has ? Elem<T>::to_f(w[k + u]) : 0.f;
+    const int t0 = threadIdx.x, t1 = threadIdx.x + 256;
+    const float s0 = t0 < n_ssq ? ssq[(long long)t0 * ssq_ld + m] : 0.f;
+    const float s1 = t1 < n_ssq ? ssq[(long long)t1 * ssq_ld + m] : 0.f;
+    float s = wave_sum(s0 + s1);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+    __syncthreads();
+    const float rs = 1.0f / sqrtf(((red[0] + red[1]) + (red[2] + red[3])) / (float)K + eps);
+    if (has) {
+        T* o = out + (long long)blockIdx.z * out_z + (long long)m * ldo + k;
+        o[0] = Elem<T>::from_f(xv.x * rs * wv[0]);
+        o[1] = Elem<T>::from_f(xv.y * rs * wv[1]);
+        o[2] = Elem<T>::from_f(xv.z * rs * wv[2]);
+        o[3] = Elem<T>::from_f(xv.w * rs * wv[3]);
+    }
 }
 
 __global__ __launch_bounds__(256) void copy_f32_kernel(const float* __restrict__ src, float* __restrict__ dst,
