@@ -96,7 +96,8 @@ struct GemmPlan {
 // reduction); its waves split K (ks) and rows (ns).  The A operand is always a
 // storage-type matrix (RMSNorm is applied by rmsnorm_rows_kernel first).
 // Choices follow a sweep on MI355X at 16 rows: 16-column tiles (ntw 1) with 8
-// waves along K for the 4096-row projections so that every CU streams, 32-column
+// waves along K (4 when there are >= 512 workgroups) for the 2048- and
+// 4096-row projections so that every CU streams, 32-column
 // tiles with 4 waves for wider ones, 4 waves per 16 gate + 16 up rows for
 // SwiGLU, two waves per 32 vocabulary rows for the LM head (weights read from
 // HBM, not from the last-level cache); one workgroup's LDS ring must fit the
@@ -110,19 +111,15 @@ GemmPlan plan_gemm(const Shape& s, int epi, int wrows, int K, int M, int layers)
     p.ns = 1;
     p.ntw = 2;
     int ks;
-    if (epi == EPI_KV_INJECT) {
-        p.ns = s.D / (p.ntw * 16);              // one head per workgroup
-        ks = 1;
-    } else if (epi == EPI_ARGMAX) {
+    if (epi == EPI_ARGMAX) {
         ks = 2;
     } else if (epi == EPI_SWIGLU) {
         ks = 4;
     } else {
         p.ntw = wrows / 32 >= 192 ? 2 : 1;
-        ks = p.ntw == 1 ? 8 : 4;
+        ks = p.ntw == 2 ? 4 : (cdiv(wrows, 16) * layers >= 512 ? 4 : 8);
     }
-    if (epi == EPI_KV_INJECT) p.n_tiles = 2 * s.nkv;
-    else if (epi == EPI_SWIGLU) p.n_tiles = cdiv(wrows, 16);   // 16 gate + 16 up rows per workgroup
+    if (epi == EPI_SWIGLU) p.n_tiles = cdiv(wrows, 16);   // 16 gate + 16 up rows per workgroup
     else p.n_tiles = cdiv(wrows, p.ns * p.ntw * 16);
     const int ring = gemm_ring_depth(p.mt, p.ntw);
     while (ks > 1 && K / s.step < 2 * ks) ks /= 2;        // at least two k-steps per wave
@@ -155,7 +152,7 @@ struct InjectPlans {
 
 InjectPlans inject_plans(const Shape& s, int batch, int rows) {
     const int M = batch * rows;
-    return {plan_gemm(s, EPI_STORE, s.H, s.F * s.H, M, 1), plan_gemm(s, EPI_KV_INJECT, 2 * s.nkv * s.D, s.H, M, s.L)};
+    return {plan_gemm(s, EPI_STORE, s.H, s.F * s.H, M, 1), plan_gemm(s, EPI_STORE, 2 * s.nkv * s.D, s.H, M, s.L)};
 }
 
 struct DraftPlans {
@@ -175,7 +172,7 @@ struct Layout {
     size_t x, ssq_x, qkv, opart, mlpart, obuf, hbuf, amax, nbuf, draft_end;
     int ssq_x_tiles, amax_tiles;
     // inject
-    size_t c, ssq_c, cnorm, inject_end;
+    size_t c, ssq_c, cnorm, kvraw, inject_end;
     int ssq_c_tiles;
 };
 
@@ -197,7 +194,7 @@ Layout make_layout(const Shape& s, int batch, int rows) {
     l.amax = take((size_t)l.amax_tiles * M * 8);
     l.nbuf = take(M * s.H * s.esize);                         // RMSNorm-ed rows (GEMM A operand)
     l.draft_end = off;
-    l.c = l.ssq_c = l.cnorm = 0;
+    l.c = l.ssq_c = l.cnorm = l.kvraw = 0;
     l.ssq_c_tiles = 0;
     if (rows > 0) {
         const size_t Mi = (size_t)batch * rows;
@@ -205,6 +202,7 @@ Layout make_layout(const Shape& s, int batch, int rows) {
         l.c = take(Mi * s.H * 4);
         l.ssq_c = take((size_t)l.ssq_c_tiles * Mi * 4);
         l.cnorm = take((size_t)s.L * Mi * s.H * s.esize);     // per-layer RMSNorm-ed rows
+        l.kvraw = take((size_t)s.L * Mi * 2 * s.nkv * s.D * 4); // per-layer k | v projections
     }
     l.inject_end = off;
     return l;
@@ -239,7 +237,6 @@ int gemm_dispatch(const GemmArgs& a, const GemmPlan& p, hipStream_t st, Tracer& 
                               : launch_gemm_mt<T, EPI_STORE, 2>(a, p, st, tr, name);
         case EPI_SWIGLU: return launch_gemm_mt<T, EPI_SWIGLU, 2>(a, p, st, tr, name);
         case EPI_ARGMAX: return launch_gemm_mt<T, EPI_ARGMAX, 2>(a, p, st, tr, name);
-        case EPI_KV_INJECT: return launch_gemm_mt<T, EPI_KV_INJECT, 2>(a, p, st, tr, name);
     }
     return DFLASH_EINVAL;
 }
@@ -249,15 +246,11 @@ GemmArgs gemm_base(const Shape& s, const GemmPlan& p, int M, int K) {
     std::memset(&a, 0, sizeof(a));
     a.M = M;
     a.K = K;
-    a.eps = s.eps;
     a.ns = p.ns;
     a.ks = p.ks;
     a.kw = p.kw;
     a.n_tiles = p.n_tiles;
     a.n_layers = p.layers;
-    a.n_kv = s.nkv;
-    a.head_dim = s.D;
-    a.cap = s.cap;
     return a;
 }
 
@@ -298,6 +291,7 @@ int run_inject(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int
     const int M = batch * rows;
     float* c = reinterpret_cast<float*>(wsb + lay.c);
     float* ssq_c = reinterpret_cast<float*>(wsb + lay.ssq_c);
+    float* kvraw = reinterpret_cast<float*>(wsb + lay.kvraw);
     int rc;
     {   // stage 1: c = W_fuse . concat(feat)
         GemmArgs a = gemm_base(s, pl.fuse, M, s.F * s.H);
@@ -313,7 +307,7 @@ int run_inject(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int
         a.ssq_out_ld = M;
         if ((rc = gemm_dispatch<T>(a, pl.fuse, st, tr, "fuse"))) return rc;
     }
-    {   // stage 2: every layer's RMSNorm -> W_k | W_v -> k-norm + RoPE -> cache
+    {   // stage 2: every layer's RMSNorm -> W_k | W_v (one launch for all layers)
         if (pl.fuse.n_tiles > lay.ssq_c_tiles) return DFLASH_EUNSUPPORTED;
         GemmArgs a = gemm_base(s, pl.kv, M, s.H);
         NormWeights nw{};   // one normalised copy of c per layer (each layer has its own scale)
@@ -324,28 +318,43 @@ int run_inject(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int
                            pl.fuse.n_tiles, M, nw, s.H, s.eps, cn, s.H, (long long)M * s.H);
         tr.end();
         if (hipGetLastError() != hipSuccess) return DFLASH_ELAUNCH;
-        for (int l = 0; l < s.L; ++l) a.layer[l].a = cn + (size_t)l * M * s.H;
+        const int ld = 2 * s.nkv * s.D;
         a.lda = s.H;
-        a.N = 2 * s.nkv * s.D;
+        a.N = ld;
         a.seg_end[0] = s.nkv * s.D;
-        a.seg_end[1] = a.seg_end[2] = 2 * s.nkv * s.D;
-        const size_t layer_elems = (size_t)s.Bmax * s.nkv * s.cap * s.D;
+        a.seg_end[1] = a.seg_end[2] = ld;
+        a.ldo = ld;
         for (int l = 0; l < s.L; ++l) {
-            const dflash_layer_weights& lw = w->layers[l];
-            a.layer[l].w[0] = lw.wk;
-            a.layer[l].w[1] = lw.wv;
-            a.layer[l].head_norm = lw.k_norm;
-            a.layer[l].kcache = static_cast<T*>(kv->k) + l * layer_elems;
-            a.layer[l].vcache = static_cast<T*>(kv->v) + l * layer_elems;
+            a.layer[l].a = cn + (size_t)l * M * s.H;
+            a.layer[l].w[0] = w->layers[l].wk;
+            a.layer[l].w[1] = w->layers[l].wv;
+            a.layer[l].out = kvraw + (size_t)l * M * ld;
         }
-        a.gamma = rows;
+        if ((rc = gemm_dispatch<T>(a, pl.kv, st, tr, "inject_kv"))) return rc;
+    }
+    {   // stage 3: k-norm + RoPE -> K cache, v -> transposed V cache
+        KvFinishArgs a;
+        std::memset(&a, 0, sizeof(a));
+        a.kv = kvraw;
+        a.layer_stride = (long long)M * 2 * s.nkv * s.D;
+        a.rows_stride = rows;
+        a.n_kv = s.nkv;
+        a.head_dim = s.D;
+        a.cap = s.cap;
+        a.rope_rows = w->rope_rows;
+        a.cache_layer = (long long)s.Bmax * s.nkv * s.cap * s.D;
+        a.kcache = kv->k;
+        a.vcache = kv->v;
+        for (int l = 0; l < s.L; ++l) a.k_norm[l] = w->layers[l].k_norm;
+        a.eps = s.eps;
         a.len = kv->len;
         a.n_new = n_new;
         a.rope_cos = w->rope_cos;
         a.rope_sin = w->rope_sin;
-        a.rope_rows = w->rope_rows;
-        a.status = kv->status;
-        if ((rc = gemm_dispatch<T>(a, pl.kv, st, tr, "inject_kv"))) return rc;
+        tr.begin("kv_finish");
+        hipLaunchKernelGGL((kv_finish_kernel<T>), dim3(2 * s.nkv, s.L, batch), dim3(256), 0, st, a);
+        tr.end();
+        if (hipGetLastError() != hipSuccess) return DFLASH_ELAUNCH;
     }
     tr.begin("inject_finish");
     hipLaunchKernelGGL(inject_finish_kernel, dim3(1), dim3(64), 0, st, batch, rows, s.cap, w->rope_rows, kv->len,

@@ -1,7 +1,7 @@
 // Weight-streaming GEMM for few rows (up to 16*MT rows per workgroup): out = A . W^T.
 //
-// Used for every projection of the drafter (W_fuse, W_k|W_v injection,
-// W_q|W_k|W_v, W_o, W_gate|W_up, W_down, LM head).  At batch 1 the weights are
+// Used for every projection of the drafter (W_fuse, W_k|W_v of every layer for
+// injection, W_q|W_k|W_v, W_o, W_gate|W_up, W_down, LM head).  At batch 1 the weights are
 // the whole HBM traffic and each weight byte is read exactly once.
 //
 // Geometry.  A workgroup owns WCOLS = NS * NTW * 16 complete weight rows
@@ -26,23 +26,20 @@
 
 namespace dflash {
 
-enum { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_ARGMAX = 2, EPI_KV_INJECT = 3 };
+enum { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_ARGMAX = 2 };
 
 constexpr int MAX_LAYERS = 16;
 
 struct GemmLayer {
     const void* a;          // nullable: this layer's A operand (overrides GemmArgs::a)
     const void* w[3];       // weight segments: rows [seg_end[i-1], seg_end[i]) come from w[i]
-    const void* head_norm;  // EPI_KV_INJECT: per-head k RMSNorm scale [D]
-    void* kcache;           // EPI_KV_INJECT: this layer's K cache [Bmax][n_kv][cap][D]
-    void* vcache;           // EPI_KV_INJECT: this layer's V cache [Bmax][n_kv][D][cap]
+    float* out;             // nullable, EPI_STORE: this layer's output (overrides GemmArgs::out)
 };
 
 struct GemmArgs {
     // ---- A operand
     const void* a;          // T [M][lda]
     long long lda;
-    float eps;              // EPI_KV_INJECT: k RMSNorm epsilon
     int M;
     int K;
     // ---- W operand and geometry
@@ -51,7 +48,7 @@ struct GemmArgs {
     int ns, ks;             // wave groups along N, waves along K
     int kw;                 // K per wave (multiple of the k-step)
     int n_tiles;            // workgroups along N
-    int n_layers;           // grid z (EPI_KV_INJECT: layers), else 1
+    int n_layers;           // grid z: independent problems (one per layer), each with its own GemmLayer
     GemmLayer layer[MAX_LAYERS];
     // ---- epilogue
     float* out;             // EPI_STORE: fp32 [M][ldo] (+= when residual)
@@ -62,15 +59,7 @@ struct GemmArgs {
     void* out_t;            // EPI_SWIGLU: T [M][ldo]
     unsigned long long* amax;   // EPI_ARGMAX: [n_tiles][M] packed (value, index) maxima
     float* dbg_logits;      // EPI_ARGMAX: nullable [B][gamma-1][N]
-    int gamma;              // rows per sequence in A (block size; rows_stride for injection)
-    // EPI_KV_INJECT
-    int n_kv, head_dim, cap;
-    const int* len;
-    const int* n_new;
-    const float* rope_cos;
-    const float* rope_sin;
-    int rope_rows;
-    unsigned* status;
+    int gamma;              // EPI_ARGMAX: rows per sequence in A (block size)
 };
 
 // Ring depth (k-steps in flight): the weights live in LDS; the registers of a
@@ -259,25 +248,6 @@ __global__ __launch_bounds__(512) void gemm_kernel(const GemmArgs p) {
 // --------------------------------------------------------------------------------------------
 // Epilogues: one wavefront per output row (rows strided over the waves).
 
-template <typename T>
-__device__ __forceinline__ void head_norm_rope_store(const float* src, int D, const T* wnorm, float eps,
-                                                     const float* cosr, const float* sinr, T* dst) {
-    // lane i < D/2 owns the rotate-half pair (i, i + D/2)
-    const int lane = threadIdx.x & 63;
-    const int half = D >> 1;
-    float x1 = 0.f, x2 = 0.f;
-    if (lane < half) { x1 = src[lane]; x2 = src[lane + half]; }
-    const float ss = wave_sum(x1 * x1 + x2 * x2);
-    const float rs = 1.0f / sqrtf(ss / (float)D + eps);
-    if (lane < half) {
-        const float y1 = x1 * rs * Elem<T>::to_f(wnorm[lane]);
-        const float y2 = x2 * rs * Elem<T>::to_f(wnorm[lane + half]);
-        const float c = cosr[lane], s = sinr[lane];
-        dst[lane] = Elem<T>::from_f(y1 * c - y2 * s);
-        dst[lane + half] = Elem<T>::from_f(y2 * c + y1 * s);
-    }
-}
-
 template <typename T, int EPI>
 __device__ void gemm_epilogue(const GemmArgs& p, const GemmLayer& L, int tile, int m0, int mrows, int wcols,
                               const float* Ct) {
@@ -286,6 +256,7 @@ __device__ void gemm_epilogue(const GemmArgs& p, const GemmLayer& L, int tile, i
 
     if (EPI == EPI_STORE) {
         const int n0 = tile * wcols;
+        float* out = L.out ? L.out : p.out;
         for (int row = wv; row < mrows; row += nwaves) {
             const int m = m0 + row;
             float ss = 0.f;
@@ -293,7 +264,7 @@ __device__ void gemm_epilogue(const GemmArgs& p, const GemmLayer& L, int tile, i
                 const int n = n0 + c;
                 if (n < p.N) {
                     float v = Ct[row * wcols + c];
-                    float* o = p.out + (long long)m * p.ldo + n;
+                    float* o = out + (long long)m * p.ldo + n;
                     if (p.residual) v += *o;
                     *o = v;
                     ss += v * v;
@@ -339,42 +310,6 @@ __device__ void gemm_epilogue(const GemmArgs& p, const GemmLayer& L, int tile, i
             }
             if (lane == 0) p.amax[(long long)tile * p.M + m] = best;
         }
-    } else if (EPI == EPI_KV_INJECT) {
-        // the tile is one head (wcols == D): tiles [0, n_kv) are k heads, [n_kv, 2 n_kv) v heads
-        const int D = p.head_dim;
-        const int RS = p.gamma;
-        const int cap = p.cap;
-        const bool is_k = tile < p.n_kv;
-        const int h = is_k ? tile : tile - p.n_kv;
-        for (int row = wv; row < mrows; row += nwaves) {
-            const int m = m0 + row;
-            const int b = m / RS, i = m % RS;
-            const int len = p.len[b], nn = p.n_new[b];
-            if (nn < 0 || nn > RS || len < 0) continue;                       // flagged by inject_finish
-            if (i >= nn || len + nn > cap || len + nn > p.rope_rows) continue;  // flagged by inject_finish
-            const int pos = len + i;
-            const float* src = Ct + row * wcols;
-            if (is_k) {
-                T* dst = reinterpret_cast<T*>(L.kcache) + (((long long)b * p.n_kv + h) * cap + pos) * D;
-                head_norm_rope_store<T>(src, D, reinterpret_cast<const T*>(L.head_norm), p.eps,
-                                        p.rope_cos + (long long)pos * (D / 2), p.rope_sin + (long long)pos * (D / 2),
-                                        dst);
-            } else {
-                T* dst = reinterpret_cast<T*>(L.vcache) + ((long long)b * p.n_kv + h) * D * (long long)cap + pos;
-                for (int d = lane; d < D; d += 64) dst[(long long)d * cap] = Elem<T>::from_f(src[d]);
-            }
-        }
-    }
-}
-
-// Advance len[b] by n_new[b] after every layer's rows are written (one thread per sequence).
-__global__ __launch_bounds__(64) void inject_finish_kernel(int batch, int rows_stride, int cap, int rope_rows,
-                                                           int* len, const int* n_new, unsigned* status) {
-    for (int b = threadIdx.x; b < batch; b += 64) {
-        const int l = len[b], nn = n_new[b];
-        if (nn < 0 || nn > rows_stride || l < 0) { atomicOr(status, STATUS_BAD_COUNT); continue; }
-        if (l + nn > cap || l + nn > rope_rows) { atomicOr(status, STATUS_KV_OVERFLOW); continue; }
-        len[b] = l + nn;
     }
 }
 

@@ -100,6 +100,89 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const float* __restri
     }
 }
 
+// Per-head RMSNorm then rotate-half RoPE of one row of D values, rounded into
+// dst; one wavefront, lane i < D/2 owns the pair (i, i + D/2).
+template <typename T>
+__device__ __forceinline__ void head_norm_rope_store(const float* src, int D, const T* wnorm, float eps,
+                                                     const float* cosr, const float* sinr, T* dst) {
+    const int lane = threadIdx.x & 63;
+    const int half = D >> 1;
+    float x1 = 0.f, x2 = 0.f;
+    if (lane < half) { x1 = src[lane]; x2 = src[lane + half]; }
+    const float ss = wave_sum(x1 * x1 + x2 * x2);
+    const float rs = 1.0f / sqrtf(ss / (float)D + eps);
+    if (lane < half) {
+        const float y1 = x1 * rs * Elem<T>::to_f(wnorm[lane]);
+        const float y2 = x2 * rs * Elem<T>::to_f(wnorm[lane + half]);
+        const float c = cosr[lane], s = sinr[lane];
+        dst[lane] = Elem<T>::from_f(y1 * c - y2 * s);
+        dst[lane + half] = Elem<T>::from_f(y2 * c + y1 * s);
+    }
+}
+
+// Injected rows -> cache.  kv holds the fp32 projections [L][Mi][2 * n_kv * D]
+// (k heads, then v heads) of row m = b * rows_stride + i.  Row i < n_new[b] of
+// sequence b lands at position len[b] + i: k heads get the layer's k RMSNorm and
+// RoPE (K cache [L][Bmax][n_kv][cap][D]), v heads are rounded into the
+// transposed V cache [L][Bmax][n_kv][D][cap].  Invalid counts or overflow write
+// nothing (inject_finish_kernel flags them).  blockIdx = (head of 2 n_kv,
+// layer, sequence); 256 threads.
+struct KvFinishArgs {
+    const float* kv;
+    long long layer_stride;     // Mi * 2 * n_kv * D
+    int rows_stride, n_kv, head_dim, cap, rope_rows;
+    long long cache_layer;      // Bmax * n_kv * cap * D
+    void* kcache;
+    void* vcache;
+    const void* k_norm[16];     // per layer [D]
+    float eps;
+    const int* len;
+    const int* n_new;
+    const float* rope_cos;
+    const float* rope_sin;
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void kv_finish_kernel(const KvFinishArgs a) {
+    const int hh = blockIdx.x, l = blockIdx.y, b = blockIdx.z;
+    const int D = a.head_dim, RS = a.rows_stride, cap = a.cap;
+    const int len = a.len[b], nn = a.n_new[b];
+    if (nn < 0 || nn > RS || len < 0) return;
+    if (len + nn > cap || len + nn > a.rope_rows) return;
+    const bool is_k = hh < a.n_kv;
+    const int h = is_k ? hh : hh - a.n_kv;
+    const int ld = 2 * a.n_kv * D;
+    const float* src = a.kv + l * a.layer_stride + (long long)b * RS * ld + (long long)hh * D;
+    if (is_k) {
+        T* kc = reinterpret_cast<T*>(a.kcache) + l * a.cache_layer + ((long long)b * a.n_kv + h) * cap * (long long)D;
+        const int wv = threadIdx.x >> 6;
+        for (int i = wv; i < nn; i += 4) {
+            const int pos = len + i;
+            head_norm_rope_store<T>(src + (long long)i * ld, D, reinterpret_cast<const T*>(a.k_norm[l]), a.eps,
+                                    a.rope_cos + (long long)pos * (D / 2), a.rope_sin + (long long)pos * (D / 2),
+                                    kc + (long long)pos * D);
+        }
+    } else {
+        // V^T rows: consecutive threads write consecutive positions of one d
+        T* vc = reinterpret_cast<T*>(a.vcache) + l * a.cache_layer + ((long long)b * a.n_kv + h) * (long long)D * cap;
+        for (int e = threadIdx.x; e < D * nn; e += 256) {
+            const int d = e / nn, i = e % nn;
+            vc[(long long)d * cap + len + i] = Elem<T>::from_f(src[(long long)i * ld + d]);
+        }
+    }
+}
+
+// Advance len[b] by n_new[b] after every layer's rows are written (one thread per sequence).
+__global__ __launch_bounds__(64) void inject_finish_kernel(int batch, int rows_stride, int cap, int rope_rows,
+                                                           int* len, const int* n_new, unsigned* status) {
+    for (int b = threadIdx.x; b < batch; b += 64) {
+        const int l = len[b], nn = n_new[b];
+        if (nn < 0 || nn > rows_stride || l < 0) { atomicOr(status, STATUS_BAD_COUNT); continue; }
+        if (l + nn > cap || l + nn > rope_rows) { atomicOr(status, STATUS_KV_OVERFLOW); continue; }
+        len[b] = l + nn;
+    }
+}
+
 __global__ __launch_bounds__(256) void copy_f32_kernel(const float* __restrict__ src, float* __restrict__ dst,
                                                        long long n) {
     for (long long i = blockIdx.x * 256ll + threadIdx.x; i < n; i += (long long)gridDim.x * 256) dst[i] = src[i];
