@@ -22,6 +22,7 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import hashlib
 import json
 import os
 import statistics
@@ -63,6 +64,39 @@ class Hip:
 
     def destroy(self, e):
         self.h.hipEventDestroy(e)
+
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_PROFILE = os.path.join(HERE, "profiles", "lm_head_argmax_qwen3_8b_b1_traffic.md")
+
+
+def kernel_fingerprint() -> str:
+    """SHA-256 prefix of the sources that decide what the LM-head kernel reads:
+    csrc/common.hpp, csrc/gemm.hpp and the plan_gemm function of csrc/dflash.hip."""
+    csrc = os.path.join(HERE, "block_diffusion_drafter_states_amd", "csrc")
+    h = hashlib.sha256()
+    for f in ("common.hpp", "gemm.hpp"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    with open(os.path.join(csrc, "dflash.hip")) as fh:
+        src = fh.read()
+    i = src.index("GemmPlan plan_gemm(")
+    h.update(src[i:src.index("\n}\n", i)].encode())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload_is_profiled: bool):
+    """HBM bytes per LM-head launch from the committed rocprofv3 counter summary,
+    or None when the workload differs or the kernel sources changed since."""
+    if not workload_is_profiled or not os.path.exists(TRAFFIC_PROFILE):
+        return None
+    with open(TRAFFIC_PROFILE) as fh:
+        for line in fh:
+            if line.startswith("traffic-record:"):
+                rec = json.loads(line.split(":", 1)[1])
+                if rec.get("source_fingerprint") == kernel_fingerprint():
+                    return int(rec["bytes_per_launch"])
+    return None
 
 
 def algorithmic_bytes(cfg, B, C_mean, tau_mean):
@@ -128,6 +162,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--trace-cycles", type=int, default=20)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only copy MIB MiB device-to-device 5 times (a plain copy kernel of known size, "
+                         "to calibrate rocprofv3 FETCH_SIZE / WRITE_SIZE) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -146,6 +183,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy probe: 5 x {n} bytes read and written")
+        return
     dfl.lib()
 
     cfg = synth.get_config(args.config)
@@ -277,7 +323,7 @@ def main():
     kern_us = {nm: round(1000.0 * sum(v) / NT, 2) for nm, v in kern.items()}     # per cycle (all launches)
     lm = kern["lm_head_argmax"]
     lm_avg_ms = sum(lm) / len(lm)
-    lm_bytes = cfg.vocab * cfg.hidden * cfg.elem_bytes + B * gamma * cfg.hidden * 4
+    lm_bytes = cfg.vocab * cfg.hidden * cfg.elem_bytes + B * gamma * cfg.hidden * cfg.elem_bytes   # W_lm + normalised rows
     lm_gbs = lm_bytes / (lm_avg_ms * 1e-3) / 1e9
     log(f"lm_head_argmax {lm_avg_ms * 1000:.1f} us -> {lm_gbs:.0f} GB/s; per-cycle kernel us {kern_us}")
 
@@ -307,7 +353,10 @@ def main():
         "hbm_roofline_frac": round(bytes_cycle * cps / (HBM_PEAK_GBS * 1e9), 4),
         "roofline": {"bound": "hbm", "kernel": "lm_head_argmax", "achieved": round(lm_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(lm_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None, "avg_launch_us": round(lm_avg_ms * 1000, 2)},
+                     "traffic": measured_traffic(cfg.name == "qwen3_8b_drafter" and B == 1),
+                     "traffic_unit": "bytes/launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                     "algorithmic_bytes_per_launch": lm_bytes,
+                     "avg_launch_us": round(lm_avg_ms * 1000, 2)},
         "kernels_us_per_cycle": kern_us,
     }
     if not args.no_cpu_baseline:

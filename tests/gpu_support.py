@@ -2,6 +2,7 @@
 path (through the C ABI) and to the CPU oracle; results are compared here."""
 from __future__ import annotations
 
+import json
 import sys
 
 import numpy as np
@@ -110,3 +111,44 @@ def check_draft(cfg, got, ref, gap_min=1e-2):
     mism = int(((d != dr) & sure).sum())
     return {"hidden_rel": ex, "logits_rel": ez, "draft_checked": int(sure.sum()), "draft_mismatch": mism,
             "logit_maxabs": float(np.abs(z - zr).max())}
+
+
+def run_cycle_case(cfg, batch, lengths, gammas, cap, seed_tag):
+    """Prefill-inject `lengths`, then for each gamma: draft, compare, inject a few rows."""
+    log(f"case {cfg.name} batch={batch} lengths={list(lengths)} gammas={gammas} cap={cap}")
+    max_rows = max(max(lengths), max(gammas))
+    P = Pair(cfg, batch, cap, max_rows)
+    rows = max(lengths)
+    feat = gen.features(cfg, batch, rows, tag=f"{seed_tag}.prefill")
+    log(f"  inject prefill rows={rows}")
+    P.inject(feat, lengths)
+    P.torch.cuda.synchronize()
+    assert P.status() == 0
+    assert list(P.cache.len.cpu().numpy()[:batch]) == list(lengths)
+    k = decode(P.cache.read_k())
+    v = decode(P.cache.read_v())
+    ek, ev = rel_err(k, P.okv.k), rel_err(v, P.okv.v)
+    log(f"  kv rel err k={ek:.3e} v={ev:.3e}")
+    assert ek < tol(cfg) and ev < tol(cfg)
+    results = []
+    for ci, gamma in enumerate(gammas):
+        anchors = gen.tokens(cfg, f"{seed_tag}.anchor.{ci}", (batch,))
+        log(f"  draft cycle {ci} gamma={gamma}")
+        got = P.draft(anchors, gamma)
+        ref = P.oracle_draft(anchors, gamma)
+        m = check_draft(cfg, got, ref)
+        log(f"  {json.dumps(m)}")
+        assert m["hidden_rel"] < tol(cfg)
+        assert m["logits_rel"] < tol(cfg)
+        assert m["draft_mismatch"] == 0
+        assert m["draft_checked"] > 0
+        results.append(m)
+        # next cycle: inject a planted number of accepted rows
+        n_new = (gen.planted_accept(cfg, (batch,), gamma, tag=f"{seed_tag}.k.{ci}") + 1).astype(np.int32)
+        nf = gen.features(cfg, batch, gamma, tag=f"{seed_tag}.feat.{ci}")
+        log(f"  inject n_new={list(n_new)}")
+        P.inject(nf, n_new)
+        P.torch.cuda.synchronize()
+        assert P.status() == 0
+        assert list(P.cache.len.cpu().numpy()[:batch]) == list(P.okv.len)
+    return P, results

@@ -13,7 +13,7 @@ from synth import gen
 import oracle
 from oracle import dflash as O
 
-from gpu_support import Pair, log, rel_err, decode, tol, check_draft
+from gpu_support import Pair, log, rel_err, decode, tol, check_draft, run_cycle_case
 
 pytestmark = pytest.mark.gpu
 
@@ -22,62 +22,21 @@ C1 = synth.get_config("C1")
 # a ragged attention chunk, g = 2 and head_dim 128
 MINI = synth.Config("mini_bf16", "bf16", hidden=512, n_q=4, n_kv=2, head_dim=128, inter=1024,
                     n_layers=2, n_feat=2, vocab=1000, gamma=16, ctx=300, batch=2, index=77)
-# GQA group 8 (128 query rows per kv head at gamma 16 -> two query groups per workgroup)
+# GQA group 8 (128 query rows per kv head at gamma 16: eight query tiles in one workgroup)
 G8 = synth.Config("g8_bf16", "bf16", hidden=512, n_q=8, n_kv=1, head_dim=128, inter=512,
                   n_layers=1, n_feat=2, vocab=512, gamma=16, ctx=700, batch=1, index=78)
 
 
-def _run_cycle_case(cfg, batch, lengths, gammas, cap, seed_tag):
-    """Prefill-inject `lengths`, then for each gamma: draft, compare, inject a few rows."""
-    log(f"case {cfg.name} batch={batch} lengths={list(lengths)} gammas={gammas} cap={cap}")
-    max_rows = max(max(lengths), max(gammas))
-    P = Pair(cfg, batch, cap, max_rows)
-    rows = max(lengths)
-    feat = gen.features(cfg, batch, rows, tag=f"{seed_tag}.prefill")
-    log(f"  inject prefill rows={rows}")
-    P.inject(feat, lengths)
-    P.torch.cuda.synchronize()
-    assert P.status() == 0
-    assert list(P.cache.len.cpu().numpy()[:batch]) == list(lengths)
-    k = decode(P.cache.read_k())
-    v = decode(P.cache.read_v())
-    ek, ev = rel_err(k, P.okv.k), rel_err(v, P.okv.v)
-    log(f"  kv rel err k={ek:.3e} v={ev:.3e}")
-    assert ek < tol(cfg) and ev < tol(cfg)
-    results = []
-    for ci, gamma in enumerate(gammas):
-        anchors = gen.tokens(cfg, f"{seed_tag}.anchor.{ci}", (batch,))
-        log(f"  draft cycle {ci} gamma={gamma}")
-        got = P.draft(anchors, gamma)
-        ref = P.oracle_draft(anchors, gamma)
-        m = check_draft(cfg, got, ref)
-        log(f"  {json.dumps(m)}")
-        assert m["hidden_rel"] < tol(cfg)
-        assert m["logits_rel"] < tol(cfg)
-        assert m["draft_mismatch"] == 0
-        assert m["draft_checked"] > 0
-        results.append(m)
-        # next cycle: inject a planted number of accepted rows
-        n_new = (gen.planted_accept(cfg, (batch,), gamma, tag=f"{seed_tag}.k.{ci}") + 1).astype(np.int32)
-        nf = gen.features(cfg, batch, gamma, tag=f"{seed_tag}.feat.{ci}")
-        log(f"  inject n_new={list(n_new)}")
-        P.inject(nf, n_new)
-        P.torch.cuda.synchronize()
-        assert P.status() == 0
-        assert list(P.cache.len.cpu().numpy()[:batch]) == list(P.okv.len)
-    return P, results
-
-
 def test_c1_fp32_cycles():
-    _run_cycle_case(C1, 1, [C1.ctx], [8, 8, 4, 2], gen.kv_capacity(C1, 64), "c1")
+    run_cycle_case(C1, 1, [C1.ctx], [8, 8, 4, 2], gen.kv_capacity(C1, 64), "c1")
 
 
 def test_mini_bf16_ragged_batch_and_empty_context():
-    _run_cycle_case(MINI, 2, [300, 0], [16, 9, 2], gen.kv_capacity(MINI, 64), "mini")
+    run_cycle_case(MINI, 2, [300, 0], [16, 9, 2], gen.kv_capacity(MINI, 64), "mini")
 
 
 def test_group8_two_query_groups():
-    _run_cycle_case(G8, 1, [700], [16, 8], gen.kv_capacity(G8, 64), "g8")
+    run_cycle_case(G8, 1, [700], [16, 8], gen.kv_capacity(G8, 64), "g8")
 
 
 def test_draft_is_deterministic():
