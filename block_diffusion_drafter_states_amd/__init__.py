@@ -147,14 +147,27 @@ class Workspace:
         self.nbytes = workspace_bytes(model, batch, max_rows_per_seq)
         if self.nbytes == 0:
             raise DFlashError(_abi.DFLASH_EUNSUPPORTED, "dflash_workspace_bytes")
-        # zero-filled once: the library keeps self-resetting counters in it
-        self.buf = torch.zeros(self.nbytes, dtype=torch.uint8, device=model.device)
+        # scratch: every call writes what it reads, nothing survives a call
+        self.buf = torch.empty(self.nbytes, dtype=torch.uint8, device=model.device)
 
     def ptr(self) -> int:
         return self.buf.data_ptr()
 
 
 # ----------------------------------------------------------------------------- entry points
+
+def _need(t, name: str, dtype, shape: Sequence[Optional[int]]) -> None:
+    """The C ABI takes raw pointers: check what it cannot (device, dtype, layout, shape)."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name}: expected a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous tensor")
+    if t.dim() != len(shape) or any(s is not None and s != n for s, n in zip(shape, t.shape)):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+
 
 def workspace_bytes(model: Model, batch: int, max_rows_per_seq: int) -> int:
     return int(lib().dflash_workspace_bytes(ctypes.byref(model.c), batch, max_rows_per_seq))
@@ -163,8 +176,15 @@ def workspace_bytes(model: Model, batch: int, max_rows_per_seq: int) -> int:
 def inject_kv(model: Model, cache: Cache, feat, n_new, ws: Workspace, batch: Optional[int] = None,
               stream=None) -> None:
     """feat: device tensor [batch][rows][F][H] (storage dtype); n_new: device int32 [batch]."""
+    torch = _torch()
     batch = feat.shape[0] if batch is None else batch
     rows = feat.shape[1]
+    _need(feat, "feat", model.storage_dtype, (None, rows, model.cfg.n_feat, model.cfg.hidden))
+    if batch > feat.shape[0]:
+        raise ValueError(f"feat holds {feat.shape[0]} sequences, batch is {batch}")
+    _need(n_new, "n_new", torch.int32, (None,))
+    if n_new.shape[0] < batch:
+        raise ValueError(f"n_new holds {n_new.shape[0]} entries, batch is {batch}")
     check(lib().dflash_inject_kv(ctypes.byref(model.c), ctypes.byref(model.w), ctypes.byref(cache.s), batch,
                                  feat.data_ptr(), rows, n_new.data_ptr(), ws.ptr(), ws.nbytes,
                                  _stream_ptr(stream)), "dflash_inject_kv")
@@ -173,7 +193,14 @@ def inject_kv(model: Model, cache: Cache, feat, n_new, ws: Workspace, batch: Opt
 def draft_block(model: Model, cache: Cache, gamma: int, anchor, draft, ws: Workspace, dbg_hidden=None,
                 dbg_logits=None, stream=None) -> None:
     """anchor: device int32 [batch]; draft: device int32 [batch][gamma-1] (output)."""
+    torch = _torch()
     batch = anchor.shape[0]
+    _need(anchor, "anchor", torch.int32, (batch,))
+    _need(draft, "draft", torch.int32, (batch, gamma - 1))
+    if dbg_hidden is not None:
+        _need(dbg_hidden, "dbg_hidden", torch.float32, (batch, gamma, model.cfg.hidden))
+    if dbg_logits is not None:
+        _need(dbg_logits, "dbg_logits", torch.float32, (batch, gamma - 1, model.cfg.vocab))
     check(lib().dflash_draft_block(ctypes.byref(model.c), ctypes.byref(model.w), ctypes.byref(cache.s), batch,
                                    gamma, anchor.data_ptr(), draft.data_ptr(),
                                    None if dbg_hidden is None else dbg_hidden.data_ptr(),
@@ -183,7 +210,13 @@ def draft_block(model: Model, cache: Cache, gamma: int, anchor, draft, ws: Works
 
 def verify(draft, target, accept_len, committed, next_anchor, stream=None) -> None:
     """draft int32 [B][gamma-1], target int32 [B][gamma] -> accept_len [B], committed [B][gamma], next_anchor [B]."""
+    torch = _torch()
+    _need(target, "target", torch.int32, (None, None))
     B, gamma = target.shape
+    _need(draft, "draft", torch.int32, (B, gamma - 1))
+    _need(accept_len, "accept_len", torch.int32, (B,))
+    _need(committed, "committed", torch.int32, (B, gamma))
+    _need(next_anchor, "next_anchor", torch.int32, (B,))
     check(lib().dflash_verify(B, gamma, draft.data_ptr(), target.data_ptr(), accept_len.data_ptr(),
                               committed.data_ptr(), next_anchor.data_ptr(), _stream_ptr(stream)), "dflash_verify")
 

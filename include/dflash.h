@@ -126,8 +126,8 @@ typedef struct {
 
 /* Bytes of workspace needed by dflash_inject_kv / dflash_draft_block for up to
  * `batch` sequences and up to `max_rows_per_seq` injected rows per sequence per
- * call.  The workspace must be zero-filled once before its first use (it holds
- * self-resetting counters); every call leaves those counters at zero again.
+ * call.  The workspace is scratch: every call writes whatever it later reads
+ * from it, so it needs no initialisation and keeps nothing between calls.
  * Calls that share a workspace must be ordered (e.g. on one stream).
  * Returns 0 for an invalid or unsupported configuration. */
 size_t dflash_workspace_bytes(const dflash_config *cfg, int32_t batch, int32_t max_rows_per_seq);

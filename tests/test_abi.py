@@ -181,3 +181,21 @@ def test_traced_variants_validate_like_the_plain_calls():
                                      ws_need, None, ctypes.byref(good)) == DFLASH_EINVAL
     assert L.dflash_draft_block_traced(ctypes.byref(c), ctypes.byref(w), ctypes.byref(kv), 1, 1, FAKE, FAKE,
                                        None, None, FAKE, ws_need, None, ctypes.byref(good)) == DFLASH_EINVAL
+
+
+def test_binding_checks_tensor_arguments_before_calling_the_library():
+    # the binding passes raw pointers, so it must reject what the C side cannot see
+    import types
+    import torch
+    import block_diffusion_drafter_states_amd as dfl
+    cfg = synth.get_config("C1")
+    model = types.SimpleNamespace(cfg=cfg, storage_dtype=torch.float32)
+    cpu_feat = torch.zeros((1, 4, cfg.n_feat, cfg.hidden), dtype=torch.float32)
+    cpu_i32 = torch.zeros(1, dtype=torch.int32)
+    with pytest.raises(TypeError, match="device tensor"):
+        dfl.inject_kv(model, None, cpu_feat, cpu_i32, None)
+    with pytest.raises(TypeError, match="device tensor"):
+        dfl.draft_block(model, None, 8, cpu_i32, torch.zeros((1, 7), dtype=torch.int32), None)
+    with pytest.raises(TypeError, match="device tensor"):
+        dfl.verify(torch.zeros((1, 7), dtype=torch.int32), torch.zeros((1, 8), dtype=torch.int32),
+                   cpu_i32, torch.zeros((1, 8), dtype=torch.int32), cpu_i32)

@@ -1,0 +1,109 @@
+"""GPU parity on launch shapes the small cases do not reach: several 64-row GEMM
+groups with ragged context lengths (serving concurrency), GQA group 8 at a
+32k-token context with a block size that changes per cycle (long chain-of-thought
+drafting), and the Qwen3-8B-shaped drafter at full size in the launch
+configuration the benchmark times.  Same bars as the other parity tests."""
+import json
+
+import numpy as np
+import pytest
+
+import synth
+from synth import gen
+import oracle
+
+from gpu_support import Pair, log, rel_err, decode, tol, check_draft, run_cycle_case
+
+pytestmark = pytest.mark.gpu
+
+# batch 5 x gamma 16 = 80 block rows: one full and one ragged 64-row group; contexts 0..300
+MB = synth.Config("mb_bf16", "bf16", hidden=512, n_q=4, n_kv=2, head_dim=128, inter=1024,
+                  n_layers=2, n_feat=2, vocab=1000, gamma=16, ctx=300, batch=5, index=79)
+# 32 q / 4 kv heads (128 query rows per kv head at gamma 16), 32768-token context
+LC = synth.Config("longctx_g8_bf16", "bf16", hidden=512, n_q=32, n_kv=4, head_dim=128, inter=1024,
+                  n_layers=2, n_feat=2, vocab=1000, gamma=16, ctx=32768, batch=2, gammas=(16, 8), index=80)
+
+
+def test_batch_of_five_ragged_row_groups():
+    run_cycle_case(MB, 5, [0, 1, 300, 63, 257], [16, 2, 9], gen.kv_capacity(MB, 64), "mb")
+
+
+def _draft_inject_cycles(P, gammas, tag):
+    cfg, B = P.cfg, P.batch
+    for ci, gamma in enumerate(gammas):
+        anchors = gen.tokens(cfg, f"{tag}.anchor.{ci}", (B,))
+        log(f"  draft cycle {ci} gamma={gamma} len={list(P.okv.len)}")
+        got = P.draft(anchors, gamma)
+        ref = P.oracle_draft(anchors, gamma)
+        m = check_draft(cfg, got, ref)
+        log(f"  {json.dumps(m)}")
+        assert m["hidden_rel"] < tol(cfg) and m["logits_rel"] < tol(cfg)
+        assert m["draft_mismatch"] == 0 and m["draft_checked"] > 0
+        n_new = (gen.planted_accept(cfg, (B,), gamma, tag=f"{tag}.k.{ci}") + 1).astype(np.int32)
+        nf = gen.features(cfg, B, gamma, tag=f"{tag}.feat.{ci}")
+        log(f"  inject n_new={list(n_new)}")
+        P.inject(nf, n_new)
+        P.torch.cuda.synchronize()
+        assert P.status() == 0
+        assert list(P.cache.len.cpu().numpy()[:B]) == list(P.okv.len)
+
+
+def test_long_context_group8_dynamic_block():
+    cfg = LC
+    cap = gen.kv_capacity(cfg, 64)
+    log(f"case {cfg.name} lengths=[32768, 20001] cap={cap}")
+    P = Pair(cfg, 2, cap, 16)
+    P.set_context([32768, 20001], tag="lc")
+    _draft_inject_cycles(P, [16, 8, 16], "lc")
+    # the rows injected after the long context sit at positions 32768.. and 20001..
+    k = decode(P.cache.read_k())
+    v = decode(P.cache.read_v())
+    lens = P.okv.len
+    for b, c0 in enumerate([32768, 20001]):
+        ek = rel_err(k[:, b, :, c0:lens[b]], P.okv.k[:, b, :, c0:lens[b]])
+        ev = rel_err(v[:, b, :, c0:lens[b]], P.okv.v[:, b, :, c0:lens[b]])
+        log(f"  seq {b} injected rows {c0}..{lens[b]} k={ek:.3e} v={ev:.3e}")
+        assert ek < tol(cfg) and ev < tol(cfg)
+
+
+def test_qwen3_8b_shape_full_size():
+    """Headline shape at full size (H 4096, I 12288, V 151936, 5 layers, context 4096,
+    batch 1, gamma 16), with the capacity and launch plans of the benchmark."""
+    import torch
+    import block_diffusion_drafter_states_amd as dfl
+    cfg = synth.get_config("C3")
+    cap = (cfg.ctx + 2 * cfg.gamma_max + 63) // 64 * 64        # as in the benchmark
+    log(f"case {cfg.name} full size, cap={cap}")
+    P = Pair(cfg, 1, cap, cfg.gamma)
+    P.set_context([cfg.ctx], tag="full")
+    # one cycle's injection: tau = 6 rows at positions 4096..4101 of every layer and kv head
+    n_new = np.array([6], dtype=np.int32)
+    feat = gen.features(cfg, 1, cfg.gamma, tag="full.feat")
+    P.inject(feat, n_new)
+    torch.cuda.synchronize()
+    assert P.status() == 0 and int(P.cache.len.item()) == cfg.ctx + 6
+    k = decode(P.cache.read_k())[:, 0, :, cfg.ctx:cfg.ctx + 6]
+    v = decode(P.cache.read_v())[:, 0, :, cfg.ctx:cfg.ctx + 6]
+    ek = rel_err(k, P.okv.k[:, 0, :, cfg.ctx:cfg.ctx + 6])
+    ev = rel_err(v, P.okv.v[:, 0, :, cfg.ctx:cfg.ctx + 6])
+    log(f"  injected rows k={ek:.3e} v={ev:.3e}")
+    assert ek < tol(cfg) and ev < tol(cfg)
+    # the draft pass over [4102 context rows ; 16 block rows]
+    anchors = gen.tokens(cfg, "full.anchor", (1,))
+    got = P.draft(anchors, cfg.gamma)
+    ref = P.oracle_draft(anchors, cfg.gamma)
+    m = check_draft(cfg, got, ref)
+    log(f"  {json.dumps(m)}")
+    assert m["hidden_rel"] < tol(cfg) and m["logits_rel"] < tol(cfg)
+    assert m["draft_mismatch"] == 0 and m["draft_checked"] > 0
+    # verify against a planted target, exactly as the benchmark plants it
+    d = got[0]
+    kpl = np.array([4])
+    y = gen.planted_targets(cfg, d, kpl, tag="full.y")
+    acc = torch.zeros(1, dtype=torch.int32, device="cuda")
+    com = torch.zeros((1, cfg.gamma), dtype=torch.int32, device="cuda")
+    nxt = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dfl.verify(torch.as_tensor(d, device="cuda"), torch.as_tensor(y, device="cuda"), acc, com, nxt)
+    torch.cuda.synchronize()
+    tau, c, n = oracle.verify(d[0], y[0])
+    assert acc.item() == tau == 5 and com[0].tolist() == list(c) and nxt.item() == n
