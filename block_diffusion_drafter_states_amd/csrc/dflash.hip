@@ -231,6 +231,7 @@ int launch_gemm_mt(const GemmArgs& a, const GemmPlan& p, hipStream_t st, Tracer&
 
 template <typename T>
 int gemm_dispatch(const GemmArgs& a, const GemmPlan& p, hipStream_t st, Tracer& tr, const char* name) {
+    if (p.epi == EPI_STORE && (p.ns != 1 || 64 % (p.ntw * 16))) return DFLASH_EINVAL;   // store epilogue layout
     switch (p.epi) {
         case EPI_STORE:
             return p.ntw == 1 ? launch_gemm_mt<T, EPI_STORE, 1>(a, p, st, tr, name)

@@ -151,6 +151,27 @@ __global__ __launch_bounds__(512) void gemm_kernel(const GemmArgs p) {
                                                  g * Elem<T>::PER16);
     }
 
+    // EPI_STORE with a residual, one M-tile: the old output values do not depend
+    // on this kernel, so they are read now and the epilogue does not wait for a
+    // second memory latency (ns == 1: at most 4 * NTW elements per thread).
+    constexpr bool RES_EARLY = EPI == EPI_STORE && MT == 1;
+    constexpr int RPT = RES_EARLY ? 4 * NTW : 1;
+    const int wcols = p.ns * NTW * 16;
+    float* const outp = L.out ? L.out : p.out;
+    float resid[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) resid[i] = 0.f;
+    if constexpr (RES_EARLY) {
+        if (p.residual) {
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) {
+                const int e = threadIdx.x + i * blockDim.x;
+                const int row = e / wcols, n = tile * wcols + e % wcols;
+                if (e < mrows * wcols && n < p.N) resid[i] = outp[(long long)(m0 + row) * p.ldo + n];
+            }
+        }
+    }
+
     Frag64 areg[P][MT];
     auto issue = [&](int q, int step) {
 #pragma unroll
@@ -218,7 +239,6 @@ __global__ __launch_bounds__(512) void gemm_kernel(const GemmArgs p) {
 
     // ---- reduce the KS partial sums (fixed order) into Ct[mrows][wcols]
     float* slot = reinterpret_cast<float*>(smem);
-    const int wcols = p.ns * NTW * 16;
     float* Ct = slot + (size_t)p.ns * p.ks * MT * NTW * 4 * 64;
     {
         float* mine = slot + (size_t)wv * MT * NTW * 4 * 64;
@@ -231,7 +251,8 @@ __global__ __launch_bounds__(512) void gemm_kernel(const GemmArgs p) {
     }
     __syncthreads();
     const int nthreads = blockDim.x;
-    for (int e = threadIdx.x; e < mrows * wcols; e += nthreads) {
+    // sum of the KS partials of output element e (row-major over [mrows][wcols]), fixed order
+    auto ksum = [&](int e) {
         const int row = e / wcols, c = e % wcols;
         const int mt = row >> 4, gg = (row & 15) >> 2, v = row & 3;
         const int gi = c / (NTW * 16), t = (c % (NTW * 16)) >> 4, rr = c & 15;
@@ -239,14 +260,43 @@ __global__ __launch_bounds__(512) void gemm_kernel(const GemmArgs p) {
         float s = 0.f;
         for (int k = 0; k < p.ks; ++k)
             s += slot[((size_t)(gi * p.ks + k) * MT * NTW * 4 * 64) + ((mt * NTW + t) * 4 + v) * 64 + ln];
-        Ct[e] = s;
+        return s;
+    };
+    if constexpr (EPI == EPI_STORE) {
+        // element-parallel store (+ residual); a row's wcols elements sit in wcols
+        // consecutive lanes of one wave (wcols divides 64), so its sum of squares is
+        // reduced with xor shuffles in a fixed order
+        auto store = [&](int e, float res) {
+            const int row = e / wcols, n = tile * wcols + e % wcols;
+            float v = 0.f;
+            if (e < mrows * wcols && n < p.N) {
+                float* o = outp + (long long)(m0 + row) * p.ldo + n;
+                v = ksum(e);
+                if (p.residual) v += RES_EARLY ? res : *o;
+                *o = v;
+            }
+            float ss = v * v;
+            for (int w = 1; w < wcols; w <<= 1) ss += __shfl_xor(ss, w, WAVE);
+            if (p.ssq_out && e < mrows * wcols && e % wcols == 0)
+                p.ssq_out[(long long)tile * p.ssq_out_ld + m0 + row] = ss;
+        };
+        if constexpr (RES_EARLY) {
+#pragma unroll
+            for (int i = 0; i < RPT; ++i)
+                if (i * nthreads < 16 * MT * wcols) store(threadIdx.x + i * nthreads, resid[i]);
+        } else {
+            for (int e0 = 0; e0 < 16 * MT * wcols; e0 += nthreads) store(e0 + threadIdx.x, 0.f);
+        }
+        return;
     }
+    for (int e = threadIdx.x; e < mrows * wcols; e += nthreads) Ct[e] = ksum(e);
     __syncthreads();
     gemm_epilogue<T, EPI>(p, L, tile, m0, mrows, wcols, Ct);
 }
 
 // --------------------------------------------------------------------------------------------
-// Epilogues: one wavefront per output row (rows strided over the waves).
+// SwiGLU and argmax epilogues: one wavefront per output row (rows strided over the waves).
+// (The store epilogue is element-parallel, in the kernel.)
 
 template <typename T, int EPI>
 __device__ void gemm_epilogue(const GemmArgs& p, const GemmLayer& L, int tile, int m0, int mrows, int wcols,
@@ -254,26 +304,7 @@ __device__ void gemm_epilogue(const GemmArgs& p, const GemmLayer& L, int tile, i
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int nwaves = blockDim.x >> 6;
 
-    if (EPI == EPI_STORE) {
-        const int n0 = tile * wcols;
-        float* out = L.out ? L.out : p.out;
-        for (int row = wv; row < mrows; row += nwaves) {
-            const int m = m0 + row;
-            float ss = 0.f;
-            for (int c = lane; c < wcols; c += 64) {
-                const int n = n0 + c;
-                if (n < p.N) {
-                    float v = Ct[row * wcols + c];
-                    float* o = out + (long long)m * p.ldo + n;
-                    if (p.residual) v += *o;
-                    *o = v;
-                    ss += v * v;
-                }
-            }
-            ss = wave_sum(ss);
-            if (lane == 0 && p.ssq_out) p.ssq_out[(long long)tile * p.ssq_out_ld + m] = ss;
-        }
-    } else if (EPI == EPI_SWIGLU) {
+    if (EPI == EPI_SWIGLU) {
         // Ct column c = gi*32 + t*16 + rr: t = 0 gate, t = 1 up (same output column gi*16 + rr)
         const int ocols = wcols / 2;
         const int n0 = tile * ocols;
