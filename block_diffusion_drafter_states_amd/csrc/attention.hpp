@@ -10,9 +10,10 @@
 // up to 8 query tiles of 16 rows; it has KG waves per query tile, which split
 // the chunk's keys.  A wave owns one query tile:
 //  * it builds the tile's q fragments itself (per-head RMSNorm + RoPE);
-//  * the waves of a key group stream their keys through LDS in sub-blocks of
-//    32 (direct-to-LDS loads of whole 1 KB spans, double-buffered, each byte
-//    fetched once per workgroup) and every wave computes from LDS:
+//  * the waves of a key group stream their keys through an LDS ring of 32-key
+//    sub-blocks (direct-to-LDS loads of whole 1 KB spans, each byte fetched
+//    once per workgroup; the ring holds a whole 256-key chunk, so the chunk is
+//    requested at once) and every wave computes from LDS:
 //      S^T = K . Q^T    (A = key rows, B = queries)
 //    with the key rows permuted so that every lane ends up holding 8
 //    consecutive keys of one query - exactly the B-operand layout of
@@ -20,7 +21,7 @@
 //    whose result leaves every lane with output columns of the same query as its
 //    scores, so the online-softmax rescaling needs no data exchange;
 //  * online softmax in base 2 (log2(e)/sqrt(D) folded into the scale); for
-//    bf16 the PV product takes P as a hi + lo pair of bf16 values.
+//    bf16 the PV product takes P rounded to bf16.
 // Chunk 0's workgroup first builds the block's keys (k RMSNorm + RoPE) and
 // values (rounded, transposed) in LDS.  The KG waves of a tile merge through
 // LDS (all tiles at once); the workgroup writes (m, l, O) per chunk and
@@ -47,7 +48,7 @@ struct AttnArgs {
     float* mlpart;          // [B][n_kv][nch_max][rpad][2]  (m in log2 units, l)
     int n_q, n_kv, cap, rpad, nch_max, chunk;   // chunk = CH context keys per chunk
     int gamma, group;       // rows = group * gamma
-    int qtw, kg, nqs;       // query tiles per workgroup, waves per tile, workgroups per (b,h,chunk)
+    int nqs;                // workgroups per (b, h, chunk): query tiles split in groups of QTW
     float scale_log2;       // log2(e) / sqrt(D)
 };
 
@@ -84,20 +85,16 @@ __device__ __forceinline__ void vfrag_mask(VFrag<float>& v, int valid) {
     }
 }
 
-// P of one lane (8 consecutive keys of one query) as the MFMA A operand.
+// P of one lane (8 consecutive keys of one query) as the MFMA B operand: bf16
+// (the rounding of P is the one deviation the precision contract allows in the
+// attention product; V is bf16-exact already), or fp32 for fp32 storage.
 template <typename T> struct PFrag;
-// bf16: P = hi + lo with both parts bf16 (|P - hi - lo| <= 2^-17 |P|), so the
-// bf16 MFMA does not add the rounding of P to the result; V is bf16-exact.
-template <> struct PFrag<bf16_t> { u32x4_t hi, lo; };
+template <> struct PFrag<bf16_t> { u32x4_t q; };
 template <> struct PFrag<float> { float p[8]; };
 
 __device__ __forceinline__ void make_pfrag(PFrag<bf16_t>& f, const float (&p)[8]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const uint32_t h = pack2_bf16(p[2 * j], p[2 * j + 1]);
-        f.hi[j] = h;
-        f.lo[j] = pack2_bf16(p[2 * j] - __uint_as_float(h << 16), p[2 * j + 1] - __uint_as_float(h & 0xFFFF0000u));
-    }
+    for (int j = 0; j < 4; ++j) f.q[j] = pack2_bf16(p[2 * j], p[2 * j + 1]);
 }
 
 __device__ __forceinline__ void make_pfrag(PFrag<float>& f, const float (&p)[8]) {
@@ -107,8 +104,7 @@ __device__ __forceinline__ void make_pfrag(PFrag<float>& f, const float (&p)[8])
 
 // acc[d][q] += V^T(16 d, 8 keys of this lane group) . P^T(8 keys, q)
 __device__ __forceinline__ void pv_mfma(f32x4_t& acc, const PFrag<bf16_t>& p, const VFrag<bf16_t>& v) {
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(v.q), as_bf16x8(p.hi), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(v.q), as_bf16x8(p.lo), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(v.q), as_bf16x8(p.q), acc, 0, 0, 0);
 }
 
 __device__ __forceinline__ void pv_mfma(f32x4_t& acc, const PFrag<float>& p, const VFrag<float>& v) {
@@ -121,28 +117,63 @@ __device__ __forceinline__ void pv_mfma(f32x4_t& acc, const PFrag<float>& p, con
 // elements d = 4*PER*i + PER*g + j (j < PER, PER = 16 bytes / element size).
 // Rotate-half RoPE pairs d with d + D/2, i.e. piece i with piece i + 2 of the
 // same lane; the four lanes of a row (g = 0..3) are 16 lanes apart.
+//
+// RowIn holds what one lane needs to build its pieces of a normalised, rotated
+// row: the raw fp32 values, the norm scale and the cos/sin of its position.  The
+// loads are issued together as opaque loads (row_in_issue) and waited for
+// explicitly, so that they can be in flight together with the K/V stream.
 template <typename T>
-__device__ __forceinline__ void load_row_raw(float (&x)[4][Elem<T>::PER16], const float* row, bool valid) {
-    constexpr int PER = Elem<T>::PER16;
+struct RowIn {
+    static constexpr int PER = Elem<T>::PER16, F4 = PER / 4;
+    static constexpr int LOADS = 4 * F4 + 4 + 4 * F4;
+    u32x4_t x[4 * F4];               // piece i, vector h -> x[i * F4 + h]
+    Frag64 w;                        // norm scale
+    u32x4_t c[2 * F4], s[2 * F4];    // cos / sin for pieces 0, 1 (paired with 2, 3)
+};
+
+template <typename T>
+__device__ __forceinline__ void row_in_issue(RowIn<T>& in, const float* row, const T* wn, const float* cosr,
+                                             const float* sinr) {
+    constexpr int PER = RowIn<T>::PER, F4 = RowIn<T>::F4;
     const int g = (threadIdx.x & 63) >> 4;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int h = 0; h < PER / 4; ++h) {
-            const float4 v = valid ? *reinterpret_cast<const float4*>(row + i * 4 * PER + g * PER + h * 4)
-                                   : make_float4(0.f, 0.f, 0.f, 0.f);
-            x[i][h * 4 + 0] = v.x; x[i][h * 4 + 1] = v.y; x[i][h * 4 + 2] = v.z; x[i][h * 4 + 3] = v.w;
+        for (int h = 0; h < F4; ++h) vload_b128(in.x[i * F4 + h], row + i * 4 * PER + g * PER + h * 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vload_b128(in.w.q[i], wn + i * 4 * PER + g * PER);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int h = 0; h < F4; ++h) {
+            vload_b128(in.c[i * F4 + h], cosr + i * 4 * PER + g * PER + h * 4);
+            vload_b128(in.s[i * F4 + h], sinr + i * 4 * PER + g * PER + h * 4);
         }
+}
+
+template <typename T>
+__device__ __forceinline__ void row_in_tie(RowIn<T>& in) {
+#pragma unroll
+    for (int k = 0; k < 4 * RowIn<T>::F4; ++k) tie(in.x[k]);
+    tie(in.w);
+#pragma unroll
+    for (int k = 0; k < 2 * RowIn<T>::F4; ++k) {
+        tie(in.c[k]);
+        tie(in.s[k]);
+    }
 }
 
 // Per-head RMSNorm (over the D elements spread over the row's four lanes) then
 // rotate-half RoPE, rounded to the storage type, into an MFMA fragment.
 template <typename T>
-__device__ __forceinline__ void norm_rope_frag(Frag64& out, const float (&x)[4][Elem<T>::PER16], const T* wn,
-                                               float eps, const float* cosr, const float* sinr) {
-    constexpr int PER = Elem<T>::PER16;
+__device__ __forceinline__ void norm_rope_frag(Frag64& out, const RowIn<T>& in, float eps) {
+    constexpr int PER = RowIn<T>::PER, F4 = RowIn<T>::F4;
     constexpr int D = 16 * PER;
-    const int g = (threadIdx.x & 63) >> 4;
+    float x[4][PER];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < PER; ++j) x[i][j] = __uint_as_float(in.x[i * F4 + j / 4][j % 4]);
     float ss = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -151,32 +182,23 @@ __device__ __forceinline__ void norm_rope_frag(Frag64& out, const float (&x)[4][
     ss += __shfl_xor(ss, 16, WAVE);
     ss += __shfl_xor(ss, 32, WAVE);
     const float rs = 1.0f / sqrtf(ss / (float)D + eps);
-    Frag64 wf;
-    load_frag64(wf, wn + g * PER);
     float y[4][PER];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const T* wp = reinterpret_cast<const T*>(&wf.q[i]);
+        const T* wp = reinterpret_cast<const T*>(&in.w.q[i]);
 #pragma unroll
         for (int j = 0; j < PER; ++j) y[i][j] = x[i][j] * rs * Elem<T>::to_f(wp[j]);
     }
     float o[4][PER];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        float c[PER], sn[PER];
-#pragma unroll
-        for (int h = 0; h < PER / 4; ++h) {
-            const float4 c4 = *reinterpret_cast<const float4*>(cosr + i * 4 * PER + g * PER + h * 4);
-            const float4 s4 = *reinterpret_cast<const float4*>(sinr + i * 4 * PER + g * PER + h * 4);
-            c[h * 4 + 0] = c4.x; c[h * 4 + 1] = c4.y; c[h * 4 + 2] = c4.z; c[h * 4 + 3] = c4.w;
-            sn[h * 4 + 0] = s4.x; sn[h * 4 + 1] = s4.y; sn[h * 4 + 2] = s4.z; sn[h * 4 + 3] = s4.w;
-        }
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
-            o[i][j] = y[i][j] * c[j] - y[i + 2][j] * sn[j];
-            o[i + 2][j] = y[i + 2][j] * c[j] + y[i][j] * sn[j];
+            const float c = __uint_as_float(in.c[i * F4 + j / 4][j % 4]);
+            const float sn = __uint_as_float(in.s[i * F4 + j / 4][j % 4]);
+            o[i][j] = y[i][j] * c - y[i + 2][j] * sn;
+            o[i + 2][j] = y[i + 2][j] * c + y[i][j] * sn;
         }
-    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         if constexpr (sizeof(T) == 2) {
@@ -231,14 +253,18 @@ __device__ __forceinline__ void vfrag_lds(VFrag<float>& v, const unsigned char* 
 // so that lane group g of the result holds keys g*8 .. g*8+7.
 __device__ __forceinline__ int subblock_key(int t, int r) { return (r >> 2) * 8 + t * 4 + (r & 3); }
 
-// One 32-key sub-block of which the first `nvalid` keys are real.
-// One 32-key sub-block of which the first `nvalid` keys are real.
-template <typename T>
+// One 32-key sub-block.  MASKED: only the first `nvalid` (>= 1) keys are real
+// (the last sub-block of a sequence, and the block itself); their scores are
+// -inf and their V entries are cleared (stale cache rows may hold any bits).
+// Softmax in base 2 with the raw hardware exp2 (arguments are <= 0; results
+// below the fp32 normal range flush to 0).  O is rescaled only when the running
+// max of some query in the wave moved.
+template <typename T, bool MASKED>
 __device__ __forceinline__ void attn_subblock(WaveAttn<T>& w, int nvalid, float scale_log2, const Frag64 (&kf)[2],
                                               VFrag<T> (&vf)[WaveAttn<T>::DT]) {
     constexpr int DT = WaveAttn<T>::DT;
     const int g = (threadIdx.x & 63) >> 4;
-    if (nvalid < 32) {   // wave-uniform: only the last sub-block of a sequence
+    if constexpr (MASKED) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) vfrag_mask(vf[dt], nvalid - g * 8);
     }
@@ -255,45 +281,49 @@ __device__ __forceinline__ void attn_subblock(WaveAttn<T>& w, int nvalid, float 
     for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-            const float x = (g * 8 + t * 4 + v) < nvalid ? st[t][v] * scale_log2 : -INFINITY;
+            float x = st[t][v] * scale_log2;
+            if constexpr (MASKED) x = (g * 8 + t * 4 + v) < nvalid ? x : -INFINITY;
             s[t * 4 + v] = x;
             mx = fmaxf(mx, x);
         }
     mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
     mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
-    const float mnew = fmaxf(w.m, mx);
-    const bool dead = (mnew == -INFINITY);
-    const float alpha = dead ? 1.f : exp2f(w.m - mnew);
+    const float mnew = fmaxf(w.m, mx);            // finite: some key of the sub-block is real
+    const float alpha = __builtin_amdgcn_exp2f(w.m - mnew);
     float p[8];
     float psum = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        p[j] = dead ? 0.f : exp2f(s[j] - mnew);
+        p[j] = __builtin_amdgcn_exp2f(s[j] - mnew);
         psum += p[j];
     }
     w.l = w.l * alpha + psum;
+    if (__ballot(mnew != w.m)) {                  // wave-uniform
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) w.o[dt] *= alpha;
+    }
     w.m = mnew;
     PFrag<T> pf;
     make_pfrag(pf, p);
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-        w.o[dt] *= alpha;
-        pv_mfma(w.o[dt], pf, vf[dt]);
-    }
+    for (int dt = 0; dt < DT; ++dt) pv_mfma(w.o[dt], pf, vf[dt]);
 }
 
 // Direct-to-LDS loads of context keys [kb, kb+32) of one (b,h) into a stage:
 // 8 instructions of 1 KB for K (rows beyond the real keys repeat the last real
 // one; their scores are masked) and 8 for V^T (whole rows: kb + 32 <= cap; keys
 // beyond the real ones are cleared at use).  Instruction j goes to the wave
-// with j % nw == iw; the loop is wave-uniform.
-template <typename T>
+// iw = j % NW of the key group: every wave issues exactly 16 / NW of them.
+template <typename T, int NW>
 __device__ __forceinline__ void stage_issue(uint32_t stage, const T* kc, const T* vc, int cap, int kb, int nvalid,
-                                            int iw, int nw) {
+                                            int iw) {
     constexpr int D = 256 / (int)sizeof(T), KPC = 16 / (int)sizeof(T);   // elements per 16 bytes
     constexpr int RB = 32 * (int)sizeof(T), CPR = RB / 16, RPI = 1024 / RB;
     const int lane = threadIdx.x & 63;
-    for (int j = iw; j < 16; j += nw) {
+    static_assert(16 % NW == 0, "whole instructions per wave");
+#pragma unroll
+    for (int jj0 = 0; jj0 < 16 / NW; ++jj0) {
+        const int j = jj0 * NW + iw;
         if (j < 8) {
             const int key = 4 * j + (lane >> 4);
             const int src = key < nvalid ? key : nvalid - 1;
@@ -308,21 +338,47 @@ __device__ __forceinline__ void stage_issue(uint32_t stage, const T* kc, const T
     }
 }
 
-// LDS of a workgroup: two stages per key group (chunk 0 builds the block's keys
-// and values in the first stage); afterwards the key-group merge reuses the
-// space with one slot (O^T, m, l of a wave) per sending wave.
-constexpr int ATT_MAX_TILES = 8;    // query tiles per workgroup
+// Geometry, by the number QTW of query tiles per workgroup (1, 2, 4 or 8): KG
+// waves per tile split the chunk's keys (8 waves in all, 4 for QTW 1); every
+// key group owns a ring of ATT_RING / KG stages in LDS (128 KB in all), enough
+// for a whole 256-key chunk.  Chunk 0 builds the block's keys and values in the
+// first stage; afterwards the key-group merge reuses the space with one slot
+// (O^T, m, l of a wave) per sending wave.
+constexpr int ATT_MAX_TILES = 8;
 constexpr int ATT_MAX_WAVES = 8;
-static inline size_t attn_slot_bytes(int elem_bytes) { return (size_t)(256 / elem_bytes / 16) * 4 * 64 * 4 + 2 * 64 * 4; }
-static inline size_t attn_lds_bytes_host(int elem_bytes, int qtw, int kg) {
-    const size_t stages = (size_t)kg * 2 * ATT_STAGE_BYTES;
-    const size_t merge = (size_t)qtw * (kg / 2) * attn_slot_bytes(elem_bytes);
-    return stages > merge ? stages : merge;
+constexpr int ATT_RING = 8;                 // stages per workgroup
+template <int QTW> struct AttGeom {
+    static constexpr int KG = QTW >= 8 ? 1 : (QTW == 4 ? 2 : 4);
+    static constexpr int WAVES = QTW * KG;
+    static constexpr int R = ATT_RING / KG;     // ring stages per key group
+    static constexpr int NPW = 16 / QTW;        // loads per wave per stage
+    static_assert((R - 1) * NPW <= 63, "vmcnt range");
+};
+static inline size_t attn_lds_bytes_host() { return (size_t)ATT_RING * ATT_STAGE_BYTES; }
+
+// Wait until at most `later` (<= MAXL) stages of NPW loads each, issued after the
+// awaited loads, are still in flight.
+template <int NPW, int MAXL>
+__device__ __forceinline__ void wait_stage(int later) {
+    static_assert(MAXL * NPW <= 63, "vmcnt range");
+    switch (later) {
+        case 0: vm_wait<0>(); break;
+        case 1: vm_wait<(MAXL >= 1 ? NPW : 0)>(); break;
+        case 2: vm_wait<(MAXL >= 2 ? 2 * NPW : 0)>(); break;
+        case 3: vm_wait<(MAXL >= 3 ? 3 * NPW : 0)>(); break;
+        case 4: vm_wait<(MAXL >= 4 ? 4 * NPW : 0)>(); break;
+        case 5: vm_wait<(MAXL >= 5 ? 5 * NPW : 0)>(); break;
+        case 6: vm_wait<(MAXL >= 6 ? 6 * NPW : 0)>(); break;
+        case 7: vm_wait<(MAXL >= 7 ? 7 * NPW : 0)>(); break;
+        default: vm_wait<(MAXL >= 8 ? 8 * NPW : 0)>(); break;
+    }
 }
 
-template <typename T>
+template <typename T, int QTW>
 __global__ __launch_bounds__(64 * ATT_MAX_WAVES) void attn_partial_kernel(const AttnArgs a) {
     constexpr int D = WaveAttn<T>::D, DT = WaveAttn<T>::DT, PER = Elem<T>::PER16;
+    using Geo = AttGeom<QTW>;
+    constexpr int KG = Geo::KG, R = Geo::R, NPW = Geo::NPW;
     extern __shared__ __align__(16) unsigned char smem[];
     const int c = blockIdx.x, h = blockIdx.y / a.nqs, qs = blockIdx.y % a.nqs, b = blockIdx.z;
     int len = a.len[b];
@@ -333,8 +389,8 @@ __global__ __launch_bounds__(64 * ATT_MAX_WAVES) void attn_partial_kernel(const 
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, g = lane >> 4, r = lane & 15;
     const int G = a.gamma;
     const int rows = a.group * G;
-    const int qt = qs * a.qtw + wv / a.kg;          // this wave's query tile
-    const int kgi = wv % a.kg;
+    const int qt = qs * QTW + wv / KG;              // this wave's query tile
+    const int kgi = wv % KG;
     const bool active = qt * 16 < rows;
 
     WaveAttn<T> w;
@@ -347,30 +403,43 @@ __global__ __launch_bounds__(64 * ATT_MAX_WAVES) void attn_partial_kernel(const 
     const T* vc = reinterpret_cast<const T*>(a.vcache) + ((long long)b * a.n_kv + h) * (long long)D * a.cap;
     // this wave's context keys [k_lo, k_hi); empty for chunk 0 (the block).  Every
     // wave runs n_iter sub-block steps (the count of key group 0) for the barriers.
-    const int per_wave = a.chunk / a.kg;
+    const int per_wave = a.chunk / KG;
     const int c0 = (c - 1) * a.chunk;
     const int k_lo = c == 0 ? 0 : c0 + kgi * per_wave;
     const int k_hi = c == 0 ? 0 : min(k_lo + per_wave, len);
     const int n_iter = c == 0 ? 0 : (min(per_wave, len - c0) + 31) / 32;
-    const int tl = __builtin_amdgcn_readfirstlane(wv / a.kg);   // tile within the workgroup (wave-uniform)
+    const int tl = __builtin_amdgcn_readfirstlane(wv / KG);     // tile within the workgroup (wave-uniform)
     const int kgi_u = __builtin_amdgcn_readfirstlane(kgi);
-    unsigned char* kgbuf = smem + kgi_u * 2 * ATT_STAGE_BYTES;
-    const uint32_t kgbuf_lds = lds_offset(smem) + (uint32_t)kgi_u * (2 * ATT_STAGE_BYTES);
+    unsigned char* kgbuf = smem + kgi_u * R * ATT_STAGE_BYTES;
+    const uint32_t kgbuf_lds = lds_offset(smem) + (uint32_t)kgi_u * (R * ATT_STAGE_BYTES);
 
-    // first context sub-block in flight while the queries are built
-    if (k_lo < k_hi) stage_issue<T>(kgbuf_lds, kc, vc, a.cap, k_lo, min(32, k_hi - k_lo), tl, a.qtw);
-
+    // the tile's query inputs first, then the first R sub-blocks of K/V (the whole
+    // chunk at 256 keys): the queries are built while the K/V stream is in flight
+    const int Rq = qt * 16 + r;
+    const bool qvalid = Rq < rows;
+    RowIn<T> qin;
     if (active) {
-        const int R = qt * 16 + r;
-        const bool valid = R < rows;
-        const int hq = valid ? R / G : 0, j = valid ? R % G : 0;
-        float x[4][PER];
-        load_row_raw<T>(x, a.qkv + (long long)(b * G + j) * a.qkv_ld + (h * a.group + hq) * D, valid);
+        const int hq = qvalid ? Rq / G : 0, j = qvalid ? Rq % G : 0;
         int pos = len + j;
         pos = pos < a.rope_rows ? pos : a.rope_rows - 1;
-        norm_rope_frag<T>(w.qf, x, reinterpret_cast<const T*>(a.q_norm), a.eps,
-                          a.rope_cos + (long long)pos * (D / 2), a.rope_sin + (long long)pos * (D / 2));
-        if (!valid) zero_frag64(w.qf);
+        row_in_issue<T>(qin, a.qkv + (long long)(b * G + j) * a.qkv_ld + (h * a.group + hq) * D,
+                        reinterpret_cast<const T*>(a.q_norm), a.rope_cos + (long long)pos * (D / 2),
+                        a.rope_sin + (long long)pos * (D / 2));
+    }
+    int n_issued = 0;
+#pragma unroll
+    for (int st = 0; st < R; ++st) {
+        const int kb = k_lo + 32 * st;
+        if (kb < k_hi) {
+            stage_issue<T, QTW>(kgbuf_lds + st * ATT_STAGE_BYTES, kc, vc, a.cap, kb, min(32, k_hi - kb), tl);
+            ++n_issued;
+        }
+    }
+    if (active) {
+        wait_stage<NPW, R>(n_issued);      // the query loads came first
+        row_in_tie(qin);
+        norm_rope_frag<T>(w.qf, qin, a.eps);
+        if (!qvalid) zero_frag64(w.qf);
     }
 
     if (c == 0) {
@@ -379,13 +448,16 @@ __global__ __launch_bounds__(64 * ATT_MAX_WAVES) void attn_partial_kernel(const 
         if (wv < 2) {
             const int key = wv * 16 + r;
             const bool valid = key < G;
-            float x[4][PER];
-            load_row_raw<T>(x, a.qkv + (long long)(b * G + (valid ? key : 0)) * a.qkv_ld + (a.n_q + h) * D, valid);
             int pos = len + (valid ? key : 0);
             pos = pos < a.rope_rows ? pos : a.rope_rows - 1;
+            RowIn<T> kin;
+            row_in_issue<T>(kin, a.qkv + (long long)(b * G + (valid ? key : 0)) * a.qkv_ld + (a.n_q + h) * D,
+                            reinterpret_cast<const T*>(a.k_norm), a.rope_cos + (long long)pos * (D / 2),
+                            a.rope_sin + (long long)pos * (D / 2));
+            vm_wait<0>();
+            row_in_tie(kin);
             Frag64 f;
-            norm_rope_frag<T>(f, x, reinterpret_cast<const T*>(a.k_norm), a.eps,
-                              a.rope_cos + (long long)pos * (D / 2), a.rope_sin + (long long)pos * (D / 2));
+            norm_rope_frag<T>(f, kin, a.eps);
             if (!valid) zero_frag64(f);
             store_frag_lds(smem, key, f);
         }
@@ -422,25 +494,33 @@ __global__ __launch_bounds__(64 * ATT_MAX_WAVES) void attn_partial_kernel(const 
             for (int t = 0; t < 2; ++t) load_frag_lds(kf[t], smem, subblock_key(t, r));
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) vfrag_lds(vf[dt], smem + ATT_V_OFF, dt * 16 + r);
-            attn_subblock<T>(w, G, a.scale_log2, kf, vf);
+            attn_subblock<T, true>(w, G, a.scale_log2, kf, vf);
         }
     }
     for (int it = 0; it < n_iter; ++it) {
         const int kb = k_lo + 32 * it;
-        vm_wait<0>();       // this wave's loads of the current stage have landed
-        __syncthreads();    // ... and every wave's; the other stage is free again
-        if (kb + 32 < k_hi)
-            stage_issue<T>(kgbuf_lds + ((it + 1) & 1) * ATT_STAGE_BYTES, kc, vc, a.cap, kb + 32,
-                           min(32, k_hi - kb - 32), tl, a.qtw);
+        // this wave's loads of stage `it` have landed (loads complete in issue order;
+        // the stages issued after it by this wave may still be in flight) ...
+        const int later_kb_end = min(k_hi, k_lo + 32 * min(n_iter, it + R));
+        wait_stage<NPW, R - 1>(max(0, (later_kb_end - kb - 1) / 32));
+        __syncthreads();    // ... and every wave's
         if (active && kb < k_hi) {
-            const unsigned char* st = kgbuf + (it & 1) * ATT_STAGE_BYTES;
+            const unsigned char* st = kgbuf + (it % R) * ATT_STAGE_BYTES;
             Frag64 kf[2];
             VFrag<T> vf[DT];
 #pragma unroll
             for (int t = 0; t < 2; ++t) load_frag_lds(kf[t], st, subblock_key(t, r));
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) vfrag_lds(vf[dt], st + ATT_V_OFF, dt * 16 + r);
-            attn_subblock<T>(w, min(32, k_hi - kb), a.scale_log2, kf, vf);
+            const int nvalid = __builtin_amdgcn_readfirstlane(min(32, k_hi - kb));
+            if (nvalid < 32) attn_subblock<T, true>(w, nvalid, a.scale_log2, kf, vf);
+            else attn_subblock<T, false>(w, 32, a.scale_log2, kf, vf);
+        }
+        if (it + R < n_iter) {          // refill this stage once every wave has read it
+            __syncthreads();
+            const int kbn = kb + 32 * R;
+            if (kbn < k_hi)
+                stage_issue<T, QTW>(kgbuf_lds + (it % R) * ATT_STAGE_BYTES, kc, vc, a.cap, kbn, min(32, k_hi - kbn), tl);
         }
     }
 
@@ -452,7 +532,7 @@ __global__ __launch_bounds__(64 * ATT_MAX_WAVES) void attn_partial_kernel(const 
 
     // ---- merge the KG waves of each tile (all tiles at once; pairwise rounds)
     const size_t slot_bytes = (size_t)DT * 4 * 64 * 4 + 2 * 64 * 4;
-    for (int span = a.kg >> 1; span >= 1; span >>= 1) {
+    for (int span = KG >> 1; span >= 1; span >>= 1) {
         __syncthreads();   // previous users of the LDS space are done
         if (kgi >= span && kgi < 2 * span) {
             float* sl = reinterpret_cast<float*>(smem + (tl * span + (kgi - span)) * slot_bytes);

@@ -68,6 +68,7 @@ int make_shape(const dflash_config* c, Shape& s) {
         return DFLASH_EUNSUPPORTED;
     if (s.H % 128 || (s.nq * s.D) % 128 || (s.nkv * s.D) % 128 || s.I % 64) return DFLASH_EUNSUPPORTED;
     if (cdiv(s.H, 16) > NORM_MAX_PARTIALS) return DFLASH_EUNSUPPORTED;   // per-tile sums of squares of a row
+    if (s.H > EMBED_MAX_HIDDEN) return DFLASH_EUNSUPPORTED;
     s.group = s.nq / s.nkv;
     if (s.group * s.gmax > 256) return DFLASH_EUNSUPPORTED;
     s.rpad = cdiv(s.group * s.gmax, 16) * 16;
@@ -130,20 +131,33 @@ GemmPlan plan_gemm(const Shape& s, int epi, int wrows, int K, int M, int layers)
     return p;
 }
 
-// Attention launch shape: a workgroup takes up to ATT_MAX_TILES query tiles of
-// one (b, h, chunk), with kg waves per tile splitting the chunk's keys, and at
-// most ATT_MAX_WAVES (>= 4) waves in all.
+// Attention launch shape: a workgroup takes QTW query tiles (the next power of
+// two >= the tiles of one (b, h), at most ATT_MAX_TILES) of one (b, h, chunk).
 struct AttnPlan {
-    int qtw, kg, nqs;
+    int qtw, nqs;
 };
 
 AttnPlan plan_attn(const Shape& s, int gamma) {
     AttnPlan a;
     const int qt = cdiv(s.group * gamma, 16);
-    a.qtw = std::min(qt, ATT_MAX_TILES);
-    a.kg = a.qtw <= 2 ? 4 : (a.qtw <= 4 ? 2 : 1);
+    a.qtw = 1;
+    while (a.qtw < qt && a.qtw < ATT_MAX_TILES) a.qtw *= 2;
     a.nqs = cdiv(qt, a.qtw);
     return a;
+}
+
+template <typename T>
+int launch_attention(const AttnArgs& a, const AttnPlan& ap, int nch_max, int nkv, int batch, hipStream_t st) {
+    const dim3 grid(nch_max, nkv * ap.nqs, batch);
+    const size_t lds = attn_lds_bytes_host();
+    switch (ap.qtw) {
+        case 1: hipLaunchKernelGGL((attn_partial_kernel<T, 1>), grid, dim3(64 * AttGeom<1>::WAVES), lds, st, a); break;
+        case 2: hipLaunchKernelGGL((attn_partial_kernel<T, 2>), grid, dim3(64 * AttGeom<2>::WAVES), lds, st, a); break;
+        case 4: hipLaunchKernelGGL((attn_partial_kernel<T, 4>), grid, dim3(64 * AttGeom<4>::WAVES), lds, st, a); break;
+        case 8: hipLaunchKernelGGL((attn_partial_kernel<T, 8>), grid, dim3(64 * AttGeom<8>::WAVES), lds, st, a); break;
+        default: return DFLASH_EINVAL;
+    }
+    return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_ELAUNCH;
 }
 
 struct InjectPlans {
@@ -172,7 +186,7 @@ struct Layout {
     size_t x, ssq_x, qkv, opart, mlpart, obuf, hbuf, amax, nbuf, draft_end;
     int ssq_x_tiles, amax_tiles;
     // inject
-    size_t c, ssq_c, cnorm, kvraw, inject_end;
+    size_t c, ssq_c, cnorm, kvraw, lensnap, inject_end;
     int ssq_c_tiles;
 };
 
@@ -194,7 +208,7 @@ Layout make_layout(const Shape& s, int batch, int rows) {
     l.amax = take((size_t)l.amax_tiles * M * 8);
     l.nbuf = take(M * s.H * s.esize);                         // RMSNorm-ed rows (GEMM A operand)
     l.draft_end = off;
-    l.c = l.ssq_c = l.cnorm = l.kvraw = 0;
+    l.c = l.ssq_c = l.cnorm = l.kvraw = l.lensnap = 0;
     l.ssq_c_tiles = 0;
     if (rows > 0) {
         const size_t Mi = (size_t)batch * rows;
@@ -203,6 +217,7 @@ Layout make_layout(const Shape& s, int batch, int rows) {
         l.ssq_c = take((size_t)l.ssq_c_tiles * Mi * 4);
         l.cnorm = take((size_t)s.L * Mi * s.H * s.esize);     // per-layer RMSNorm-ed rows
         l.kvraw = take((size_t)s.L * Mi * 2 * s.nkv * s.D * 4); // per-layer k | v projections
+        l.lensnap = take((size_t)batch * 4);                     // len before this injection
     }
     l.inject_end = off;
     return l;
@@ -277,7 +292,7 @@ int set_norm_a(GemmArgs& a, const Shape& s, const float* x, int M, const float* 
     nw.w[0] = w;
     tr.begin("rmsnorm");
     hipLaunchKernelGGL((rmsnorm_rows_kernel<T>), dim3(M, cdiv(s.H, 1024), 1), dim3(256), 0, st, x, s.H, ssq, n_ssq, M,
-                       nw, s.H, s.eps, static_cast<T*>(nbuf), s.H, 0LL);
+                       nw, s.H, s.eps, static_cast<T*>(nbuf), s.H, 0LL, nullptr, nullptr, 0);
     tr.end();
     a.a = nbuf;
     a.lda = s.H;
@@ -293,6 +308,7 @@ int run_inject(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int
     float* c = reinterpret_cast<float*>(wsb + lay.c);
     float* ssq_c = reinterpret_cast<float*>(wsb + lay.ssq_c);
     float* kvraw = reinterpret_cast<float*>(wsb + lay.kvraw);
+    int* lensnap = reinterpret_cast<int*>(wsb + lay.lensnap);
     int rc;
     {   // stage 1: c = W_fuse . concat(feat)
         GemmArgs a = gemm_base(s, pl.fuse, M, s.F * s.H);
@@ -316,7 +332,7 @@ int run_inject(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int
         T* cn = reinterpret_cast<T*>(wsb + lay.cnorm);
         tr.begin("rmsnorm");
         hipLaunchKernelGGL((rmsnorm_rows_kernel<T>), dim3(M, cdiv(s.H, 1024), s.L), dim3(256), 0, st, c, s.H, ssq_c,
-                           pl.fuse.n_tiles, M, nw, s.H, s.eps, cn, s.H, (long long)M * s.H);
+                           pl.fuse.n_tiles, M, nw, s.H, s.eps, cn, s.H, (long long)M * s.H, kv->len, lensnap, batch);
         tr.end();
         if (hipGetLastError() != hipSuccess) return DFLASH_ELAUNCH;
         const int ld = 2 * s.nkv * s.D;
@@ -348,20 +364,18 @@ int run_inject(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int
         a.vcache = kv->v;
         for (int l = 0; l < s.L; ++l) a.k_norm[l] = w->layers[l].k_norm;
         a.eps = s.eps;
+        a.len_snap = lensnap;
         a.len = kv->len;
         a.n_new = n_new;
         a.rope_cos = w->rope_cos;
         a.rope_sin = w->rope_sin;
+        a.status = kv->status;
         tr.begin("kv_finish");
         hipLaunchKernelGGL((kv_finish_kernel<T>), dim3(2 * s.nkv, s.L, batch), dim3(256), 0, st, a);
         tr.end();
         if (hipGetLastError() != hipSuccess) return DFLASH_ELAUNCH;
     }
-    tr.begin("inject_finish");
-    hipLaunchKernelGGL(inject_finish_kernel, dim3(1), dim3(64), 0, st, batch, rows, s.cap, w->rope_rows, kv->len,
-                       n_new, kv->status);
-    tr.end();
-    return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_ELAUNCH;
+    return DFLASH_OK;
 }
 
 template <typename T>
@@ -385,22 +399,27 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
     const int qkv_ld = (s.nq + 2 * s.nkv) * s.D;
     int rc;
 
-    tr.begin("embed");
-    hipLaunchKernelGGL((embed_block_kernel<T>), dim3(M), dim3(256), 0, st, static_cast<const T*>(w->embed), anchor,
-                       s.mask, s.V, gamma, s.H, x, ssq_x, kv->status);
+    tr.begin("embed_norm");
+    hipLaunchKernelGGL((embed_norm_kernel<T>), dim3(M), dim3(256), 0, st, static_cast<const T*>(w->embed), anchor,
+                       s.mask, s.V, gamma, s.H, static_cast<const T*>(w->layers[0].in_norm), s.eps, x,
+                       static_cast<T*>(nbuf), kv->status);
     tr.end();
     if (hipGetLastError() != hipSuccess) return DFLASH_ELAUNCH;
-    int n_ssq = 1;
+    int n_ssq = 0;      // per-tile partial sums of squares of x (written by o / down)
 
     const AttnPlan ap = plan_attn(s, gamma);
-    const size_t attn_lds = attn_lds_bytes_host(s.esize, ap.qtw, ap.kg);
     const size_t layer_elems = (size_t)s.Bmax * s.nkv * s.cap * s.D;
 
     for (int l = 0; l < s.L; ++l) {
         const dflash_layer_weights& lw = w->layers[l];
         {   // raw q | k | v of the block (three weight tensors, one launch)
             GemmArgs a = gemm_base(s, pl.qkv, M, s.H);
-            if ((rc = set_norm_a<T>(a, s, x, M, ssq_x, n_ssq, lw.in_norm, nbuf, st, tr))) return rc;
+            if (l == 0) {       // the embedding kernel normalised the rows already
+                a.a = nbuf;
+                a.lda = s.H;
+            } else if ((rc = set_norm_a<T>(a, s, x, M, ssq_x, n_ssq, lw.in_norm, nbuf, st, tr))) {
+                return rc;
+            }
             a.N = qkv_ld;
             a.seg_end[0] = s.nq * s.D;
             a.seg_end[1] = (s.nq + s.nkv) * s.D;
@@ -436,15 +455,12 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
             a.chunk = s.chunk;
             a.gamma = gamma;
             a.group = s.group;
-            a.qtw = ap.qtw;
-            a.kg = ap.kg;
             a.nqs = ap.nqs;
             a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)s.D));
             tr.begin("attention");
-            hipLaunchKernelGGL((attn_partial_kernel<T>), dim3(s.nch_max, s.nkv * ap.nqs, batch), dim3(64 * ap.qtw * ap.kg), attn_lds,
-                               st, a);
+            rc = launch_attention<T>(a, ap, s.nch_max, s.nkv, batch, st);
             tr.end();
-            if (hipGetLastError() != hipSuccess) return DFLASH_ELAUNCH;
+            if (rc) return rc;
             MergeArgs mgr;
             mgr.opart = opart;
             mgr.mlpart = mlpart;

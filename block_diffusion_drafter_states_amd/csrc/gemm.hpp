@@ -344,17 +344,25 @@ __device__ void gemm_epilogue(const GemmArgs& p, const GemmLayer& L, int tile, i
     }
 }
 
-// draft[b][j-1] = argmax over the vocabulary tiles of row b*gamma + j (one workgroup per draft row).
+// draft[b][j-1] = argmax over the vocabulary tiles of row m = b*gamma + j (one
+// workgroup per draft row; amax is [n_tiles][M], tiles written contiguously by
+// the LM-head epilogue; the 8 loads of a thread per round are independent).
 __global__ __launch_bounds__(256) void argmax_finish_kernel(const unsigned long long* __restrict__ amax, int n_tiles,
                                                             int M, int gamma, int* __restrict__ draft) {
     __shared__ unsigned long long red[4];
     const int i = blockIdx.x;                      // b*(gamma-1) + (j-1)
     const int b = i / (gamma - 1), j = i % (gamma - 1) + 1;
-    const int m = b * gamma + j;
+    const unsigned long long* col = amax + (b * gamma + j);
     unsigned long long best = 0ull;
-    for (int t = threadIdx.x; t < n_tiles; t += 256) {
-        const unsigned long long v = amax[(long long)t * M + m];
-        best = v > best ? v : best;
+    for (int t0 = 0; t0 < n_tiles; t0 += 8 * 256) {
+        unsigned long long v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int t = t0 + u * 256 + threadIdx.x;
+            v[u] = t < n_tiles ? col[(long long)t * M] : 0ull;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) best = v[u] > best ? v[u] : best;
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {

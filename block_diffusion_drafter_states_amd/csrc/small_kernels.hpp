@@ -5,13 +5,20 @@
 
 namespace dflash {
 
-// x[b*gamma + j][:] = E[id] with id = anchor[b] (j == 0) or the mask id; also the
-// row's sum of squares (one partial tile) for the first layer's RMSNorm.
+// x[b*gamma + j][:] = E[id] with id = anchor[b] (j == 0) or the mask id, and the
+// first layer's input RMSNorm of that row, rho(x * rstd * w), into xn (one
+// workgroup owns the whole row, so its sum of squares needs no partial tiles).
+// Token ids outside [0, vocab) set STATUS_BAD_TOKEN and read row 0.
+constexpr int EMBED_MAX_HIDDEN = 8192;
+
 template <typename T>
-__global__ __launch_bounds__(256) void embed_block_kernel(const T* __restrict__ embed, const int* __restrict__ anchor,
-                                                          int mask_id, int vocab, int gamma, int H,
-                                                          float* __restrict__ x, float* __restrict__ ssq,
-                                                          unsigned* status) {
+__global__ __launch_bounds__(256) void embed_norm_kernel(const T* __restrict__ embed, const int* __restrict__ anchor,
+                                                         int mask_id, int vocab, int gamma, int H,
+                                                         const T* __restrict__ w_norm, float eps,
+                                                         float* __restrict__ x, T* __restrict__ xn,
+                                                         unsigned* status) {
+    constexpr int EPC = 16 / (int)sizeof(T);                    // elements per 16-byte chunk
+    constexpr int MAXC = EMBED_MAX_HIDDEN / EPC / 256;           // chunks per thread
     __shared__ float red[4];
     const int m = blockIdx.x;
     const int b = m / gamma, j = m % gamma;
@@ -21,17 +28,47 @@ __global__ __launch_bounds__(256) void embed_block_kernel(const T* __restrict__ 
         id = 0;
     }
     const T* e = embed + (long long)id * H;
-    float* xr = x + (long long)m * H;
-    float s = 0.f;
-    for (int k = threadIdx.x; k < H; k += 256) {
-        const float v = Elem<T>::to_f(e[k]);
-        xr[k] = v;
-        s += v * v;
+    u32x4_t ev[MAXC], wv[MAXC];
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+        const int k = (c * 256 + threadIdx.x) * EPC;
+        if (k < H) {
+            ev[c] = *reinterpret_cast<const u32x4_t*>(e + k);
+            wv[c] = *reinterpret_cast<const u32x4_t*>(w_norm + k);
+        }
     }
-    s = wave_sum(s);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+    float ss = 0.f;
+    float xv[MAXC][EPC];
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+        const int k = (c * 256 + threadIdx.x) * EPC;
+        if (k < H) {
+            const T* ep = reinterpret_cast<const T*>(&ev[c]);
+#pragma unroll
+            for (int u = 0; u < EPC; ++u) {
+                xv[c][u] = Elem<T>::to_f(ep[u]);
+                ss += xv[c][u] * xv[c][u];
+            }
+            float* xr = x + (long long)m * H + k;
+#pragma unroll
+            for (int u = 0; u < EPC; u += 4)
+                *reinterpret_cast<float4*>(xr + u) = make_float4(xv[c][u], xv[c][u + 1], xv[c][u + 2], xv[c][u + 3]);
+        }
+    }
+    ss = wave_sum(ss);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
     __syncthreads();
-    if (threadIdx.x == 0) ssq[m] = (red[0] + red[1]) + (red[2] + red[3]);
+    const float rs = 1.0f / sqrtf(((red[0] + red[1]) + (red[2] + red[3])) / (float)H + eps);
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+        const int k = (c * 256 + threadIdx.x) * EPC;
+        if (k < H) {
+            const T* wp = reinterpret_cast<const T*>(&wv[c]);
+            T* o = xn + (long long)m * H + k;
+#pragma unroll
+            for (int u = 0; u < EPC; ++u) o[u] = Elem<T>::from_f(xv[c][u] * rs * Elem<T>::to_f(wp[u]));
+        }
+    }
 }
 
 // One wavefront per sequence: k = leading matches of draft[j] == target[j].
@@ -70,12 +107,19 @@ struct NormWeights {
 
 constexpr int NORM_MAX_PARTIALS = 512;
 
+// When len_snap is given, block 0 also copies len[0 .. n_len) there (the K/V
+// cache writes that follow read positions from the copy while len itself is
+// advanced).
 template <typename T>
 __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const float* __restrict__ x, int ldx,
                                                            const float* __restrict__ ssq, int n_ssq, int ssq_ld,
                                                            const NormWeights wz, int K, float eps,
-                                                           T* __restrict__ out, int ldo, long long out_z) {
+                                                           T* __restrict__ out, int ldo, long long out_z,
+                                                           const int* __restrict__ len, int* __restrict__ len_snap,
+                                                           int n_len) {
     __shared__ float red[4];
+    if (len_snap && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0)
+        for (int b = threadIdx.x; b < n_len; b += 256) len_snap[b] = len[b];
     const int m = blockIdx.x;
     const int k = blockIdx.y * 1024 + threadIdx.x * 4;   // K % 4 == 0
     const bool has = k < K;
@@ -124,9 +168,11 @@ __device__ __forceinline__ void head_norm_rope_store(const float* src, int D, co
 // (k heads, then v heads) of row m = b * rows_stride + i.  Row i < n_new[b] of
 // sequence b lands at position len[b] + i: k heads get the layer's k RMSNorm and
 // RoPE (K cache [L][Bmax][n_kv][cap][D]), v heads are rounded into the
-// transposed V cache [L][Bmax][n_kv][D][cap].  Invalid counts or overflow write
-// nothing (inject_finish_kernel flags them).  blockIdx = (head of 2 n_kv,
-// layer, sequence); 256 threads.
+// transposed V cache [L][Bmax][n_kv][D][cap].  Positions come from len_snap, a
+// copy of len taken before this kernel; workgroup (0, 0, b) then advances
+// len[b] += n_new[b], or sets STATUS_BAD_COUNT / STATUS_KV_OVERFLOW and writes
+// nothing for that sequence.  blockIdx = (head of 2 n_kv, layer, sequence);
+// 256 threads.
 struct KvFinishArgs {
     const float* kv;
     long long layer_stride;     // Mi * 2 * n_kv * D
@@ -136,19 +182,27 @@ struct KvFinishArgs {
     void* vcache;
     const void* k_norm[16];     // per layer [D]
     float eps;
-    const int* len;
+    const int* len_snap;
+    int* len;
     const int* n_new;
     const float* rope_cos;
     const float* rope_sin;
+    unsigned* status;
 };
 
 template <typename T>
 __global__ __launch_bounds__(256) void kv_finish_kernel(const KvFinishArgs a) {
     const int hh = blockIdx.x, l = blockIdx.y, b = blockIdx.z;
     const int D = a.head_dim, RS = a.rows_stride, cap = a.cap;
-    const int len = a.len[b], nn = a.n_new[b];
-    if (nn < 0 || nn > RS || len < 0) return;
-    if (len + nn > cap || len + nn > a.rope_rows) return;
+    const int len = a.len_snap[b], nn = a.n_new[b];
+    const bool bad_count = nn < 0 || nn > RS || len < 0;
+    const bool overflow = !bad_count && (len + nn > cap || len + nn > a.rope_rows);
+    if (hh == 0 && l == 0 && threadIdx.x == 0) {
+        if (bad_count) atomicOr(a.status, STATUS_BAD_COUNT);
+        else if (overflow) atomicOr(a.status, STATUS_KV_OVERFLOW);
+        else a.len[b] = len + nn;
+    }
+    if (bad_count || overflow) return;
     const bool is_k = hh < a.n_kv;
     const int h = is_k ? hh : hh - a.n_kv;
     const int ld = 2 * a.n_kv * D;
@@ -169,17 +223,6 @@ __global__ __launch_bounds__(256) void kv_finish_kernel(const KvFinishArgs a) {
             const int d = e / nn, i = e % nn;
             vc[(long long)d * cap + len + i] = Elem<T>::from_f(src[(long long)i * ld + d]);
         }
-    }
-}
-
-// Advance len[b] by n_new[b] after every layer's rows are written (one thread per sequence).
-__global__ __launch_bounds__(64) void inject_finish_kernel(int batch, int rows_stride, int cap, int rope_rows,
-                                                           int* len, const int* n_new, unsigned* status) {
-    for (int b = threadIdx.x; b < batch; b += 64) {
-        const int l = len[b], nn = n_new[b];
-        if (nn < 0 || nn > rows_stride || l < 0) { atomicOr(status, STATUS_BAD_COUNT); continue; }
-        if (l + nn > cap || l + nn > rope_rows) { atomicOr(status, STATUS_KV_OVERFLOW); continue; }
-        len[b] = l + nn;
     }
 }
 
