@@ -100,17 +100,35 @@ class Pair:
 
 
 def check_draft(cfg, got, ref, gap_min=1e-2):
-    """Compare (draft, hidden, logits) of GPU vs oracle; returns a dict of metrics."""
+    """Compare (draft, hidden, logits) of GPU vs oracle; returns a dict of metrics.
+
+    The argmax is taken on the GPU in fp32 over the logits it also returns, so the
+    drafted ids must be exactly the argmax (lowest index on ties) of those returned
+    logits.  Against the fp64 oracle the ids are unique only where the oracle's top-2
+    gap exceeds twice the largest logit error: no rounding within that error can then
+    flip the choice, so there the ids must match.  Elsewhere several ids are correct,
+    and the one chosen must be within that error of the oracle's maximum."""
     d, x, z = got
     dr, xr, zr = ref
     assert np.isfinite(x).all() and np.isfinite(z).all()
     ex = rel_err(x, xr)
     ez = rel_err(z, zr)
+    err = float(np.abs(z - zr).max())
     gap = top2_gap(zr)
-    sure = gap >= gap_min
+    sure = gap > max(gap_min, 2.0 * err)
     mism = int(((d != dr) & sure).sum())
+    self_mism = int((d != np.argmax(z, axis=-1)).sum())
+    picked = np.take_along_axis(zr, d[..., None].astype(np.int64), axis=-1)[..., 0]
+    not_near = int((picked < zr.max(axis=-1) - 2.0 * err).sum())
     return {"hidden_rel": ex, "logits_rel": ez, "draft_checked": int(sure.sum()), "draft_mismatch": mism,
-            "logit_maxabs": float(np.abs(z - zr).max())}
+            "argmax_self_mismatch": self_mism, "not_near_optimal": not_near, "logit_maxabs": err}
+
+
+def assert_draft(cfg, m) -> None:
+    assert m["hidden_rel"] < tol(cfg) and m["logits_rel"] < tol(cfg)
+    assert m["argmax_self_mismatch"] == 0
+    assert m["draft_mismatch"] == 0 and m["not_near_optimal"] == 0
+    assert m["draft_checked"] > 0
 
 
 def run_cycle_case(cfg, batch, lengths, gammas, cap, seed_tag):
@@ -138,10 +156,7 @@ def run_cycle_case(cfg, batch, lengths, gammas, cap, seed_tag):
         ref = P.oracle_draft(anchors, gamma)
         m = check_draft(cfg, got, ref)
         log(f"  {json.dumps(m)}")
-        assert m["hidden_rel"] < tol(cfg)
-        assert m["logits_rel"] < tol(cfg)
-        assert m["draft_mismatch"] == 0
-        assert m["draft_checked"] > 0
+        assert_draft(cfg, m)
         results.append(m)
         # next cycle: inject a planted number of accepted rows
         n_new = (gen.planted_accept(cfg, (batch,), gamma, tag=f"{seed_tag}.k.{ci}") + 1).astype(np.int32)

@@ -199,3 +199,33 @@ def test_binding_checks_tensor_arguments_before_calling_the_library():
     with pytest.raises(TypeError, match="device tensor"):
         dfl.verify(torch.zeros((1, 7), dtype=torch.int32), torch.zeros((1, 8), dtype=torch.int32),
                    cpu_i32, torch.zeros((1, 8), dtype=torch.int32), cpu_i32)
+
+
+def test_draft_check_flags_wrong_ids():
+    """The GPU draft check itself: exact ids where the top-2 gap exceeds twice the
+    logit error, self-consistent argmax, near-optimal choice elsewhere; mistakes are
+    planted in the reference-side arrays on the CPU."""
+    import numpy as np
+    import gpu_support as G
+    cfg = type("C", (), {"dtype": "bf16"})()
+    rng = np.random.default_rng(5)
+    zr = rng.standard_normal((3, 7, 50))
+    z = zr + 1e-3 * rng.standard_normal(zr.shape)
+    d = np.argmax(z, axis=-1)
+    x = rng.standard_normal((3, 8, 4))
+    good = G.check_draft(cfg, (d, x, z), (np.argmax(zr, -1), x, zr))
+    G.assert_draft(cfg, good)
+    bad_d = d.copy()
+    bad_d[1, 2] = np.argmin(z[1, 2])
+    m = G.check_draft(cfg, (bad_d, x, z), (np.argmax(zr, -1), x, zr))
+    assert m["argmax_self_mismatch"] == 1 and m["not_near_optimal"] == 1
+    with pytest.raises(AssertionError):
+        G.assert_draft(cfg, m)
+    # ids that are the argmax of the returned logits, but one logit is far off the
+    # reference: the margin widens so no id is sure, and the logit bound fails
+    z2 = z.copy()
+    z2[0, 0, np.argmin(zr[0, 0])] = zr[0, 0].max() + 5.0
+    m = G.check_draft(cfg, (np.argmax(z2, -1), x, z2), (np.argmax(zr, -1), x, zr))
+    assert m["argmax_self_mismatch"] == 0 and m["logits_rel"] > G.tol(cfg)
+    with pytest.raises(AssertionError):
+        G.assert_draft(cfg, m)

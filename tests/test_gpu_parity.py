@@ -13,7 +13,7 @@ from synth import gen
 import oracle
 from oracle import dflash as O
 
-from gpu_support import Pair, log, rel_err, decode, tol, check_draft, run_cycle_case
+from gpu_support import Pair, log, rel_err, decode, tol, check_draft, assert_draft, run_cycle_case
 
 pytestmark = pytest.mark.gpu
 
@@ -62,7 +62,7 @@ def test_draft_against_synthetic_context_cache():
     ref = P.oracle_draft(anchors, 16)
     m = check_draft(cfg, got, ref)
     log(f"  {json.dumps(m)}")
-    assert m["hidden_rel"] < tol(cfg) and m["logits_rel"] < tol(cfg) and m["draft_mismatch"] == 0
+    assert_draft(cfg, m)
 
 
 def test_verify_matches_oracle_bit_exact():
