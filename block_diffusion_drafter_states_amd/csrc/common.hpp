@@ -113,6 +113,14 @@ __device__ __forceinline__ void vload_b128(u32x4_t& d, const void* g) {
     asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(d) : "v"(g) : "memory");
 }
 
+__device__ __forceinline__ void vload_b32(uint32_t& d, const void* g) {
+    asm volatile("global_load_dword %0, %1, off" : "=v"(d) : "v"(g) : "memory");
+}
+
+__device__ __forceinline__ void vload_u16(uint32_t& d, const void* g) {
+    asm volatile("global_load_ushort %0, %1, off" : "=v"(d) : "v"(g) : "memory");
+}
+
 template <int N>
 __device__ __forceinline__ void vm_wait() {
     static_assert(N >= 0 && N <= 63, "vmcnt range");
@@ -120,6 +128,7 @@ __device__ __forceinline__ void vm_wait() {
 }
 
 __device__ __forceinline__ void tie(u32x4_t& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void tie(uint32_t& x) { asm volatile("" : "+v"(x)); }
 __device__ __forceinline__ void tie(Frag64& f) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) tie(f.q[i]);

@@ -183,7 +183,7 @@ DraftPlans draft_plans(const Shape& s, int M) {
 // is per-call scratch: no state survives a call.
 struct Layout {
     // draft
-    size_t x, ssq_x, qkv, opart, mlpart, obuf, hbuf, amax, nbuf, draft_end;
+    size_t x, ssq_x, qkv, opart, mlpart, obuf, hbuf, amax, fin_best, fin_count, nbuf, draft_end;
     int ssq_x_tiles, amax_tiles;
     // inject
     size_t c, ssq_c, cnorm, kvraw, lensnap, inject_end;
@@ -206,6 +206,8 @@ Layout make_layout(const Shape& s, int batch, int rows) {
     l.obuf = take(M * s.nq * s.D * s.esize);
     l.hbuf = take(M * s.I * s.esize);
     l.amax = take((size_t)l.amax_tiles * M * 8);
+    l.fin_best = take(M * 8);                                 // per draft row: running argmax, slices done
+    l.fin_count = take(M * 4);
     l.nbuf = take(M * s.H * s.esize);                         // RMSNorm-ed rows (GEMM A operand)
     l.draft_end = off;
     l.c = l.ssq_c = l.cnorm = l.kvraw = l.lensnap = 0;
@@ -247,6 +249,8 @@ int launch_gemm_mt(const GemmArgs& a, const GemmPlan& p, hipStream_t st, Tracer&
 template <typename T>
 int gemm_dispatch(const GemmArgs& a, const GemmPlan& p, hipStream_t st, Tracer& tr, const char* name) {
     if (p.epi == EPI_STORE && (p.ns != 1 || 64 % (p.ntw * 16))) return DFLASH_EINVAL;   // store epilogue layout
+    for (int k = 0; k < 2; ++k)     // a 16-row weight tile never straddles two segments
+        if (a.seg_end[k] < a.N && a.seg_end[k] % 16) return DFLASH_EINVAL;
     switch (p.epi) {
         case EPI_STORE:
             return p.ntw == 1 ? launch_gemm_mt<T, EPI_STORE, 1>(a, p, st, tr, name)
@@ -396,13 +400,16 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
     void* hbuf = wsb + lay.hbuf;
     unsigned long long* amax = reinterpret_cast<unsigned long long*>(wsb + lay.amax);
     void* nbuf = wsb + lay.nbuf;
+    unsigned long long* fin_best = reinterpret_cast<unsigned long long*>(wsb + lay.fin_best);
+    int* fin_count = reinterpret_cast<int*>(wsb + lay.fin_count);
+    const int n_draft = batch * (gamma - 1);
     const int qkv_ld = (s.nq + 2 * s.nkv) * s.D;
     int rc;
 
     tr.begin("embed_norm");
     hipLaunchKernelGGL((embed_norm_kernel<T>), dim3(M), dim3(256), 0, st, static_cast<const T*>(w->embed), anchor,
                        s.mask, s.V, gamma, s.H, static_cast<const T*>(w->layers[0].in_norm), s.eps, x,
-                       static_cast<T*>(nbuf), kv->status);
+                       static_cast<T*>(nbuf), kv->status, fin_best, fin_count, n_draft);
     tr.end();
     if (hipGetLastError() != hipSuccess) return DFLASH_ELAUNCH;
     int n_ssq = 0;      // per-tile partial sums of squares of x (written by o / down)
@@ -541,8 +548,8 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
         if ((rc = gemm_dispatch<T>(a, pl.lm, st, tr, "lm_head_argmax"))) return rc;
     }
     tr.begin("argmax_finish");
-    hipLaunchKernelGGL(argmax_finish_kernel, dim3(batch * (gamma - 1)), dim3(256), 0, st, amax, pl.lm.n_tiles, M,
-                       gamma, draft);
+    hipLaunchKernelGGL(argmax_finish_kernel, dim3(ARGMAX_SLICES, n_draft), dim3(256), 0, st, amax, pl.lm.n_tiles, M,
+                       gamma, fin_best, fin_count, draft);
     tr.end();
     return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_ELAUNCH;
 }

@@ -111,29 +111,35 @@ __global__ __launch_bounds__(512) void gemm_kernel(const GemmArgs p) {
     constexpr int LPS = NTW * 4 + MT * 4;
     static_assert((P - 1) * LPS <= 63, "vmcnt range");
     const int lq = lane >> 4, lc = lane & 15;
+    // The segment of a 16-row tile is wave-uniform (segment boundaries are
+    // multiples of 16 rows), so the base pointer is picked in scalar registers and
+    // no lane waits for a load before the first weight request.
+    const int ns_u = __builtin_amdgcn_readfirstlane(ns_i);
     const char* wsrc[NTW][4];
 #pragma unroll
-    for (int t = 0; t < NTW; ++t)
+    for (int t = 0; t < NTW; ++t) {
+        const T* base;
+        int r0, rows;                                    // first row of the tile in its segment; segment rows
+        if (EPI == EPI_SWIGLU) {
+            r0 = tile * (p.ns * 16) + ns_u * 16;
+            base = reinterpret_cast<const T*>(L.w[t]);    // t = 0 gate, t = 1 up
+            rows = p.N;
+        } else {
+            const int n0 = min(tile * (p.ns * NTW * 16) + ns_u * (NTW * 16) + t * 16, p.N - 1);
+            const int sg = n0 < p.seg_end[0] ? 0 : (n0 < p.seg_end[1] ? 1 : 2);
+            const int lo = sg == 0 ? 0 : (sg == 1 ? p.seg_end[0] : p.seg_end[1]);
+            base = reinterpret_cast<const T*>(sg == 0 ? L.w[0] : (sg == 1 ? L.w[1] : L.w[2]));
+            r0 = n0 - lo;
+            rows = (sg == 0 ? p.seg_end[0] : (sg == 1 ? p.seg_end[1] : p.seg_end[2])) - lo;
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int rho = i * 4 + lq;                  // row within the 16-row tile
-            const T* base;
-            int row, rows;
-            if (EPI == EPI_SWIGLU) {
-                row = tile * (p.ns * 16) + ns_i * 16 + rho;
-                base = reinterpret_cast<const T*>(L.w[t]);    // t = 0 gate, t = 1 up
-                rows = p.N;
-            } else {
-                const int n = min(tile * (p.ns * NTW * 16) + ns_i * (NTW * 16) + t * 16 + rho, p.N - 1);
-                const int sg = n < p.seg_end[0] ? 0 : (n < p.seg_end[1] ? 1 : 2);
-                const int lo = sg == 0 ? 0 : p.seg_end[sg - 1];
-                base = reinterpret_cast<const T*>(L.w[sg]);
-                row = n - lo;
-                rows = p.seg_end[sg] - lo;
-            }
-            row = min(row, rows - 1);   // ragged last tile: re-read a valid row; its result is discarded
+            // ragged last tile: re-read a valid row; its result is discarded
+            const int row = min(r0 + rho, rows - 1);
             wsrc[t][i] = reinterpret_cast<const char*>(base + (long long)row * K + k0) + ((lc ^ rho) * 16);
         }
+    }
     const int wv_u = __builtin_amdgcn_readfirstlane(wv);
     const uint32_t ring_lds = lds_offset(smem) + (uint32_t)wv_u * (P * NTW * 4096);
     const char* ring = reinterpret_cast<const char*>(smem) + (size_t)wv_u * P * NTW * 4096;
@@ -152,22 +158,25 @@ __global__ __launch_bounds__(512) void gemm_kernel(const GemmArgs p) {
     }
 
     // EPI_STORE with a residual, one M-tile: the old output values do not depend
-    // on this kernel, so they are read now and the epilogue does not wait for a
-    // second memory latency (ns == 1: at most 4 * NTW elements per thread).
+    // on this kernel, so they are requested now, ahead of the weight stream (ns ==
+    // 1: at most 4 * NTW elements per thread), and read after the stream's last
+    // wait: the epilogue does not wait for a second memory latency.  Issued before
+    // every ring load, they complete first, so the ring's waits stay valid.
     constexpr bool RES_EARLY = EPI == EPI_STORE && MT == 1;
     constexpr int RPT = RES_EARLY ? 4 * NTW : 1;
     const int wcols = p.ns * NTW * 16;
     float* const outp = L.out ? L.out : p.out;
-    float resid[RPT];
+    uint32_t resid_u[RPT];
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) resid[i] = 0.f;
+    for (int i = 0; i < RPT; ++i) resid_u[i] = 0u;
     if constexpr (RES_EARLY) {
         if (p.residual) {
 #pragma unroll
             for (int i = 0; i < RPT; ++i) {
                 const int e = threadIdx.x + i * blockDim.x;
                 const int row = e / wcols, n = tile * wcols + e % wcols;
-                if (e < mrows * wcols && n < p.N) resid[i] = outp[(long long)(m0 + row) * p.ldo + n];
+                const bool ok = e < mrows * wcols && n < p.N;     // else: a valid address, value unused
+                vload_b32(resid_u[i], outp + (ok ? (long long)(m0 + row) * p.ldo + n : 0));
             }
         }
     }
@@ -236,6 +245,12 @@ __global__ __launch_bounds__(512) void gemm_kernel(const GemmArgs p) {
     }
     vm_wait<0>();
     __syncthreads();   // every wave is done with its ring: the LDS is reused below
+    float resid[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        tie(resid_u[i]);
+        resid[i] = __uint_as_float(resid_u[i]);
+    }
 
     // ---- reduce the KS partial sums (fixed order) into Ct[mrows][wcols]
     float* slot = reinterpret_cast<float*>(smem);
@@ -344,37 +359,55 @@ __device__ void gemm_epilogue(const GemmArgs& p, const GemmLayer& L, int tile, i
     }
 }
 
-// draft[b][j-1] = argmax over the vocabulary tiles of row m = b*gamma + j (one
-// workgroup per draft row; amax is [n_tiles][M], tiles written contiguously by
-// the LM-head epilogue; the 8 loads of a thread per round are independent).
+// draft[b][j-1] = argmax over the vocabulary tiles of row m = b*gamma + j.
+// Workgroup (s, i) takes slice s of the tiles of draft row i (amax is [n_tiles][M],
+// so a row's maxima sit M * 8 bytes apart; ARGMAX_SLICES workgroups per row spread
+// those reads over many CUs), folds its maximum into best[i] with a 64-bit atomic
+// max (order-independent, so the result is deterministic) and counts itself in
+// count[i]; the last of the row's workgroups reads best[i] back with an atomic and
+// writes the index.  best and count start at zero (the embedding kernel of the
+// same call clears them).
+constexpr int ARGMAX_SLICES = 16;
+
 __global__ __launch_bounds__(256) void argmax_finish_kernel(const unsigned long long* __restrict__ amax, int n_tiles,
-                                                            int M, int gamma, int* __restrict__ draft) {
+                                                            int M, int gamma, unsigned long long* best, int* count,
+                                                            int* __restrict__ draft) {
     __shared__ unsigned long long red[4];
-    const int i = blockIdx.x;                      // b*(gamma-1) + (j-1)
+    const int s = blockIdx.x, i = blockIdx.y;      // slice, b*(gamma-1) + (j-1)
     const int b = i / (gamma - 1), j = i % (gamma - 1) + 1;
     const unsigned long long* col = amax + (b * gamma + j);
-    unsigned long long best = 0ull;
-    for (int t0 = 0; t0 < n_tiles; t0 += 8 * 256) {
-        unsigned long long v[8];
+    const int per = (n_tiles + ARGMAX_SLICES - 1) / ARGMAX_SLICES;
+    const int t0 = s * per, t1 = min(n_tiles, t0 + per);
+    unsigned long long v[4];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int t = t0 + u * 256 + threadIdx.x;
-            v[u] = t < n_tiles ? col[(long long)t * M] : 0ull;
+    for (int u = 0; u < 4; ++u) v[u] = 0ull;
+    for (int tb = t0; tb < t1; tb += 4 * 256) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int t = tb + u * 256 + threadIdx.x;
+            const unsigned long long x = t < t1 ? col[(long long)t * M] : 0ull;
+            v[u] = x > v[u] ? x : v[u];
         }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) best = v[u] > best ? v[u] : best;
     }
+    unsigned long long mx = v[0];
+#pragma unroll
+    for (int u = 1; u < 4; ++u) mx = v[u] > mx ? v[u] : mx;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
-        const unsigned long long other = __shfl_xor(best, o, WAVE);
-        best = other > best ? other : best;
+        const unsigned long long other = __shfl_xor(mx, o, WAVE);
+        mx = other > mx ? other : mx;
     }
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = best;
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
     __syncthreads();
     if (threadIdx.x == 0) {
-        unsigned long long v = red[0];
-        for (int k = 1; k < 4; ++k) v = red[k] > v ? red[k] : v;
-        draft[i] = (int)unpack_argmax_index(v);
+        unsigned long long w = red[0];
+        for (int k = 1; k < 4; ++k) w = red[k] > w ? red[k] : w;
+        atomicMax(best + i, w);
+        __threadfence();
+        if (atomicAdd(count + i, 1) == ARGMAX_SLICES - 1) {
+            __threadfence();
+            draft[i] = (int)unpack_argmax_index(atomicMax(best + i, 0ull));
+        }
     }
 }
 
