@@ -163,6 +163,30 @@ __device__ __forceinline__ void row_in_tie(RowIn<T>& in) {
     }
 }
 
+// The same inputs read from rows staged in LDS (raw fp32 row, norm weight, cos and
+// sin rows), with the lane layout of row_in_issue.
+template <typename T>
+__device__ __forceinline__ void row_in_lds(RowIn<T>& in, const unsigned char* row, const unsigned char* wn,
+                                           const unsigned char* cosr, const unsigned char* sinr) {
+    constexpr int PER = RowIn<T>::PER, F4 = RowIn<T>::F4;
+    const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int h = 0; h < F4; ++h)
+            in.x[i * F4 + h] = *reinterpret_cast<const u32x4_t*>(row + (i * 4 * PER + g * PER + h * 4) * 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        in.w.q[i] = *reinterpret_cast<const u32x4_t*>(wn + (i * 4 * PER + g * PER) * (int)sizeof(T));
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int h = 0; h < F4; ++h) {
+            in.c[i * F4 + h] = *reinterpret_cast<const u32x4_t*>(cosr + (i * 4 * PER + g * PER + h * 4) * 4);
+            in.s[i * F4 + h] = *reinterpret_cast<const u32x4_t*>(sinr + (i * 4 * PER + g * PER + h * 4) * 4);
+        }
+}
+
 // Per-head RMSNorm (over the D elements spread over the row's four lanes) then
 // rotate-half RoPE, rounded to the storage type, into an MFMA fragment.
 template <typename T>
@@ -225,6 +249,13 @@ template <> __device__ __forceinline__ int v_lds_off<float>(int d, int c) { retu
 
 constexpr int ATT_STAGE_BYTES = 16384;   // K (32 x 256 B) then V^T (8 KB)
 constexpr int ATT_V_OFF = 8192;
+// chunk 0 only (it streams no context): raw inputs of the block's keys and values
+// staged behind stage 0
+constexpr int ATT_RAW_K = 16384;         // 16 fp32 rows of D (at most 512 B each)
+constexpr int ATT_RAW_V = 24576;
+constexpr int ATT_RAW_COS = 32768;       // 16 rows of D / 2 fp32 (at most 256 B each)
+constexpr int ATT_RAW_SIN = 36864;
+constexpr int ATT_RAW_KN = 40960;        // k-norm weight (1 KB slot)
 
 __device__ __forceinline__ void store_frag_lds(unsigned char* kt, int key, const Frag64& f) {
     const int g = (threadIdx.x & 63) >> 4;
@@ -413,8 +444,11 @@ __global__ __launch_bounds__(64 * ATT_MAX_WAVES) void attn_partial_kernel(const 
     unsigned char* kgbuf = smem + kgi_u * R * ATT_STAGE_BYTES;
     const uint32_t kgbuf_lds = lds_offset(smem) + (uint32_t)kgi_u * (R * ATT_STAGE_BYTES);
 
-    // the tile's query inputs first, then the first R sub-blocks of K/V (the whole
-    // chunk at 256 keys): the queries are built while the K/V stream is in flight
+    // The tile's query inputs first; then, in chunk 0, the block's own raw key and
+    // value rows, their RoPE rows and the k-norm weight straight into free LDS,
+    // else the first R sub-blocks of K/V (the whole chunk at 256 keys): all a
+    // workgroup reads before its first sub-block is in flight at once, and one wait
+    // covers it.
     const int Rq = qt * 16 + r;
     const bool qvalid = Rq < rows;
     RowIn<T> qin;
@@ -426,6 +460,41 @@ __global__ __launch_bounds__(64 * ATT_MAX_WAVES) void attn_partial_kernel(const 
                         reinterpret_cast<const T*>(a.q_norm), a.rope_cos + (long long)pos * (D / 2),
                         a.rope_sin + (long long)pos * (D / 2));
     }
+    if (c == 0) {
+        // direct-to-LDS loads of 1 KB, round-robin over the waves: raw k rows, raw
+        // v rows (fp32, D * 4 bytes each), cos and sin rows of the block positions
+        // (D * 2 bytes each), the k-norm weight.  Rows beyond the block repeat row 0;
+        // their keys are cleared below.
+        constexpr int KRB = D * 4, KLPR = KRB / 16, KRPI = 64 / KLPR, KNI = 16 / KRPI;
+        constexpr int CRB = D * 2, CLPR = CRB / 16, CRPI = 64 / CLPR, CNI = 16 / CRPI;
+        constexpr int NI = 2 * KNI + 2 * CNI + 1;
+        const int nw = blockDim.x >> 6;
+        const int wv_u = __builtin_amdgcn_readfirstlane(wv);
+        const uint32_t base = lds_offset(smem);
+        for (int ins = wv_u; ins < NI; ins += nw) {
+            const void* src;
+            uint32_t dst;
+            if (ins < 2 * KNI) {
+                const int jj = ins % KNI, key = KRPI * jj + lane / KLPR;
+                const int kk = key < G ? key : 0;
+                const int col = ins < KNI ? (a.n_q + h) * D : (a.n_q + a.n_kv + h) * D;
+                src = a.qkv + (long long)(b * G + kk) * a.qkv_ld + col + (lane % KLPR) * 4;
+                dst = base + (ins < KNI ? ATT_RAW_K : ATT_RAW_V) + jj * 1024;
+            } else if (ins < 2 * KNI + 2 * CNI) {
+                const int ic = ins - 2 * KNI;
+                const int jj = ic % CNI, key = CRPI * jj + lane / CLPR;
+                int pos = len + (key < G ? key : 0);
+                pos = pos < a.rope_rows ? pos : a.rope_rows - 1;
+                src = (ic < CNI ? a.rope_cos : a.rope_sin) + (long long)pos * (D / 2) + (lane % CLPR) * 4;
+                dst = base + (ic < CNI ? ATT_RAW_COS : ATT_RAW_SIN) + jj * 1024;
+            } else {
+                constexpr int WCH = D * (int)sizeof(T) / 16;      // 16-byte pieces of the weight
+                src = reinterpret_cast<const unsigned char*>(a.k_norm) + (lane % WCH) * 16;
+                dst = base + ATT_RAW_KN;
+            }
+            dma_b128(src, dst);
+        }
+    }
     int n_issued = 0;
 #pragma unroll
     for (int st = 0; st < R; ++st) {
@@ -435,51 +504,39 @@ __global__ __launch_bounds__(64 * ATT_MAX_WAVES) void attn_partial_kernel(const 
             ++n_issued;
         }
     }
-    if (active) {
-        wait_stage<NPW, R>(n_issued);      // the query loads came first
-        row_in_tie(qin);
-        norm_rope_frag<T>(w.qf, qin, a.eps);
-        if (!qvalid) zero_frag64(w.qf);
-    }
-
     if (c == 0) {
-        // the block's own keys (waves 0,1: keys 0..31, k RMSNorm + RoPE) and values
-        // (rounded) into stage 0 of key group 0
-        if (wv < 2) {
-            const int key = wv * 16 + r;
-            const bool valid = key < G;
-            int pos = len + (valid ? key : 0);
-            pos = pos < a.rope_rows ? pos : a.rope_rows - 1;
-            RowIn<T> kin;
-            row_in_issue<T>(kin, a.qkv + (long long)(b * G + (valid ? key : 0)) * a.qkv_ld + (a.n_q + h) * D,
-                            reinterpret_cast<const T*>(a.k_norm), a.rope_cos + (long long)pos * (D / 2),
-                            a.rope_sin + (long long)pos * (D / 2));
-            vm_wait<0>();
-            row_in_tie(kin);
-            Frag64 f;
-            norm_rope_frag<T>(f, kin, a.eps);
-            if (!valid) zero_frag64(f);
-            store_frag_lds(smem, key, f);
+        vm_wait<0>();                       // one latency for every input of chunk 0
+        __syncthreads();                    // ... of every wave
+        if (active) {
+            row_in_tie(qin);
+            norm_rope_frag<T>(w.qf, qin, a.eps);
+            if (!qvalid) zero_frag64(w.qf);
         }
-        // V^T of the block by the first 256 threads (every workgroup has >= 4 waves);
-        // all float4 loads of a thread are independent (one latency)
+        // the block's keys (wave 0: keys 0..15, k RMSNorm + RoPE; wave 1: keys 16..31,
+        // never real since a block has at most 16 tokens) and values (rounded) into
+        // stage 0 of key group 0
+        if (wv < 2) {
+            Frag64 f;
+            zero_frag64(f);
+            if (wv == 0) {
+                RowIn<T> kin;
+                row_in_lds<T>(kin, smem + ATT_RAW_K + r * (D * 4), smem + ATT_RAW_KN,
+                              smem + ATT_RAW_COS + r * (D * 2), smem + ATT_RAW_SIN + r * (D * 2));
+                norm_rope_frag<T>(f, kin, a.eps);
+                if (r >= G) zero_frag64(f);
+            }
+            store_frag_lds(smem, wv * 16 + r, f);
+        }
         constexpr int NV4 = 32 * D / 4, KPC = 16 / (int)sizeof(T);
         static_assert(NV4 % 256 == 0, "block V tile split");
         if (threadIdx.x < 256) {
-            float4 vv[NV4 / 256];
 #pragma unroll
             for (int it = 0; it < NV4 / 256; ++it) {
                 const int e4 = it * 256 + threadIdx.x;
                 const int key = e4 / (D / 4), d = (e4 % (D / 4)) * 4;
-                vv[it] = key < G ? *reinterpret_cast<const float4*>(a.qkv + (long long)(b * G + key) * a.qkv_ld +
-                                                                    (a.n_q + a.n_kv + h) * D + d)
-                                 : make_float4(0.f, 0.f, 0.f, 0.f);
-            }
-#pragma unroll
-            for (int it = 0; it < NV4 / 256; ++it) {
-                const int e4 = it * 256 + threadIdx.x;
-                const int key = e4 / (D / 4), d = (e4 % (D / 4)) * 4;
-                const float vals[4] = {vv[it].x, vv[it].y, vv[it].z, vv[it].w};
+                const float4 vv = key < G ? *reinterpret_cast<const float4*>(smem + ATT_RAW_V + key * (D * 4) + d * 4)
+                                          : make_float4(0.f, 0.f, 0.f, 0.f);
+                const float vals[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
                     *reinterpret_cast<T*>(smem + ATT_V_OFF + v_lds_off<T>(d + u, key / KPC) +
@@ -496,6 +553,11 @@ __global__ __launch_bounds__(64 * ATT_MAX_WAVES) void attn_partial_kernel(const 
             for (int dt = 0; dt < DT; ++dt) vfrag_lds(vf[dt], smem + ATT_V_OFF, dt * 16 + r);
             attn_subblock<T, true>(w, G, a.scale_log2, kf, vf);
         }
+    } else if (active) {
+        wait_stage<NPW, R>(n_issued);      // the query loads came first
+        row_in_tie(qin);
+        norm_rope_frag<T>(w.qf, qin, a.eps);
+        if (!qvalid) zero_frag64(w.qf);
     }
     for (int it = 0; it < n_iter; ++it) {
         const int kb = k_lo + 32 * it;
