@@ -99,6 +99,24 @@ def measured_traffic(workload_is_profiled: bool):
     return None
 
 
+SHAPES = {"tiny_f32": "tiny fp32 drafter", "qwen3_4b_drafter": "Qwen3-4B-shaped drafter (tied LM head)",
+          "qwen3_8b_drafter": "Qwen3-8B-shaped drafter", "llama31_8b_drafter_b32": "LLaMA-3.1-8B-shaped drafter",
+          "coder30b_drafter_longctx": "Qwen3-Coder-30B-drafter-shaped (GQA 8)"}
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}     # dense, MI355X published
+
+
+def gemm_flops(cfg, B, gamma, tau_mean):
+    """Multiply-add flops of the cycle's projections (2 per MAC): injection of tau rows per
+    sequence, the drafter's projections over the B * gamma block rows, the LM head over all of
+    them (the kernel computes the anchor row too)."""
+    H, F, D, L = cfg.hidden, cfg.n_feat, cfg.head_dim, cfg.n_layers
+    rows_inj, rows_blk = B * tau_mean, B * gamma
+    inj = rows_inj * (F * H * H + L * 2 * cfg.n_kv * D * H)
+    blk = rows_blk * L * ((cfg.n_q + 2 * cfg.n_kv) * D * H + cfg.n_q * D * H + 3 * cfg.inter * H)
+    lm = rows_blk * cfg.vocab * H
+    return 2.0 * (inj + blk + lm)
+
+
 def algorithmic_bytes(cfg, B, C_mean, tau_mean):
     """Bytes one cycle must move: each weight once (W_k/W_v once for injection and
     drafting together), the context K/V once, feature rows read, new K/V written."""
@@ -151,6 +169,45 @@ def cpu_oracle_baseline(cfg, W, K, V, lengths, feats, anchors, plant_k, gamma, b
                       f"batch {B}, fp64 numpy oracle, {el:.1f}s"}
 
 
+GEMM_LAUNCHES = ("fuse", "inject_kv", "qkv_proj", "o_proj", "gate_up", "down_proj", "lm_head_argmax")
+
+
+def prefill(args, dfl, cfg, gen, torch):
+    """Injection of a whole prompt's feature rows (C3: 4096 positions) into an empty cache:
+    the fusion and every layer's W_k | W_v over all rows, an MFMA-bound contraction."""
+    B, rows = 1, cfg.ctx
+    cap = (rows + 2 * cfg.gamma_max + 63) // 64 * 64
+    W = gen.weights(cfg)
+    model = dfl.Model(cfg, W, device="cuda", max_batch=B, kv_capacity=cap)
+    cache = dfl.Cache(model)
+    ws = dfl.Workspace(model, B, rows)
+    feat = dfl.to_device(gen.features(cfg, B, rows, tag="bench.prefill"), "cuda")
+    n_new = torch.full((B,), rows, dtype=torch.int32, device="cuda")
+    times = []
+    for r in range(args.warmup + args.steps):
+        cache.len.zero_()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dfl.inject_kv(model, cache, feat, n_new, ws)
+        e1.record()
+        torch.cuda.synchronize()
+        if r >= args.warmup:
+            times.append(e0.elapsed_time(e1))
+    assert int(cache.status.item()) == 0 and int(cache.len[0].item()) == rows
+    ms = statistics.median(times)
+    H, F, D, L = cfg.hidden, cfg.n_feat, cfg.head_dim, cfg.n_layers
+    flops = 2.0 * rows * (F * H * H + L * 2 * cfg.n_kv * D * H)
+    peak = MFMA_PEAK_TFLOPS[cfg.dtype]
+    tflops = flops / (ms * 1e-3) / 1e12
+    print(json.dumps({"metric": "prefill injection time", "value": round(ms * 1000, 1), "unit": "us",
+                      "higher_is_better": False, "steps": args.steps, "warmup": args.warmup, "dtype": cfg.dtype,
+                      "config": {"workload": f"{cfg.name}: {SHAPES.get(cfg.name, cfg.name)}, "
+                                             f"{rows} feature rows into an empty cache", "rows": rows},
+                      "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": peak, "unit": "TFLOP/s",
+                                   "frac": round(tflops / peak, 4), "gflop": round(flops / 1e9, 1)}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -162,6 +219,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--trace-cycles", type=int, default=20)
+    ap.add_argument("--prefill", action="store_true",
+                    help="time the injection of a whole context's feature rows instead of the cycle")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device 5 times (a plain copy kernel of known size, "
                          "to calibrate rocprofv3 FETCH_SIZE / WRITE_SIZE) and exit")
@@ -195,6 +254,9 @@ def main():
     dfl.lib()
 
     cfg = synth.get_config(args.config)
+    if args.prefill:
+        prefill(args, dfl, cfg, gen, torch)
+        return
     B = args.batch
     cfg = cfg.with_(batch=B)
     gamma = cfg.gamma
@@ -342,7 +404,7 @@ def main():
         "dtype": cfg.dtype,
         "data": "synthetic (seeded random-init drafter weights, N(0,1) target features and context K/V, "
                 "planted target tokens)",
-        "config": {"workload": f"{cfg.name}: Qwen3-8B-shaped drafter, batch {B}, gamma {gamma}, "
+        "config": {"workload": f"{cfg.name}: {SHAPES.get(cfg.name, cfg.name)}, batch {B}, gamma {gamma}, "
                                f"context {int(lengths.mean())}",
                    "batch": B, "gamma": gamma, "context": int(lengths.mean()), "hidden": cfg.hidden,
                    "layers": cfg.n_layers, "vocab": cfg.vocab, "parallelism": "single GPU"},
@@ -359,6 +421,16 @@ def main():
                      "avg_launch_us": round(lm_avg_ms * 1000, 2)},
         "kernels_us_per_cycle": kern_us,
     }
+    if B > 1:
+        # contraction throughput (the dense-MFMA regime of large batches): the cycle's GEMM flops
+        # over the whole cycle and over the projection launches alone
+        gf = gemm_flops(cfg, B, gamma, tau_mean)
+        gemm_us = sum(v for k, v in kern_us.items() if k in GEMM_LAUNCHES)
+        peak = MFMA_PEAK_TFLOPS[cfg.dtype]
+        result["mfma"] = {"gemm_gflop_per_cycle": round(gf / 1e9, 1), "peak_tflops": peak,
+                          "frac_whole_cycle": round(gf * cps / 1e12 / peak, 4),
+                          "frac_gemm_launches": round(gf / (gemm_us * 1e-6) / 1e12 / peak, 4),
+                          "gemm_us_per_cycle": round(gemm_us, 1)}
     if not args.no_cpu_baseline:
         Kh, Vh = gen.context_kv(cfg, lengths, cap, tag="bench.ctx")
         result["cpu_baseline"] = cpu_oracle_baseline(cfg, W, Kh, Vh, lengths, feats_host, anchor0, plant_k, gamma,

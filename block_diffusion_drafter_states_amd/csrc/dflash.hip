@@ -9,6 +9,7 @@
 #include "../../include/dflash.h"
 #include "attention.hpp"
 #include "gemm.hpp"
+#include "gemm_tiled.hpp"
 #include "small_kernels.hpp"
 
 using namespace dflash;
@@ -89,8 +90,11 @@ int make_shape(const dflash_config* c, Shape& s) {
 
 struct GemmPlan {
     int ns, ks, kw, n_tiles, mt, mgroups, layers, ntw, epi;
+    bool tiled;     // gemm_tiled_kernel (many rows) instead of the weight-streaming kernel
     size_t lds;
 };
+
+constexpr int TILED_MIN_ROWS = 128;   // from this many rows on, A is reused from LDS across 128 weight rows
 
 // Geometry of one projection.  wrows = weight rows (EPI_SWIGLU: rows of each of
 // gate/up).  Every workgroup owns complete output columns (no cross-workgroup
@@ -107,6 +111,18 @@ GemmPlan plan_gemm(const Shape& s, int epi, int wrows, int K, int M, int layers)
     GemmPlan p;
     p.epi = epi;
     p.layers = layers;
+    p.tiled = M >= TILED_MIN_ROWS;
+    if (p.tiled) {
+        p.ns = 1;
+        p.ks = 4;
+        p.kw = K;
+        p.mt = 8;
+        p.ntw = 0;
+        p.mgroups = cdiv(M, TG_BM);
+        p.n_tiles = cdiv(wrows, tg_cols(epi));
+        p.lds = TG_LDS;
+        return p;
+    }
     p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
     p.mgroups = cdiv(M, 16 * p.mt);
     p.ns = 1;
@@ -195,7 +211,9 @@ Layout make_layout(const Shape& s, int batch, int rows) {
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
     const size_t M = (size_t)batch * s.gmax;
-    const DraftPlans dp = draft_plans(s, (int)M);
+    // tile counts from the weight-streaming plans, which have the most tiles (the tiled
+    // plans of a call with many rows use fewer), so any call's plans fit
+    const DraftPlans dp = draft_plans(s, std::min((int)M, TILED_MIN_ROWS - 1));
     l.ssq_x_tiles = std::max(1, std::max(dp.o.n_tiles, dp.down.n_tiles));
     l.amax_tiles = dp.lm.n_tiles;
     l.x = take(M * s.H * 4);
@@ -214,7 +232,7 @@ Layout make_layout(const Shape& s, int batch, int rows) {
     l.ssq_c_tiles = 0;
     if (rows > 0) {
         const size_t Mi = (size_t)batch * rows;
-        l.ssq_c_tiles = inject_plans(s, batch, rows).fuse.n_tiles;
+        l.ssq_c_tiles = plan_gemm(s, EPI_STORE, s.H, s.F * s.H, std::min((int)Mi, TILED_MIN_ROWS - 1), 1).n_tiles;
         l.c = take(Mi * s.H * 4);
         l.ssq_c = take((size_t)l.ssq_c_tiles * Mi * 4);
         l.cnorm = take((size_t)s.L * Mi * s.H * s.esize);     // per-layer RMSNorm-ed rows
@@ -246,8 +264,28 @@ int launch_gemm_mt(const GemmArgs& a, const GemmPlan& p, hipStream_t st, Tracer&
     return DFLASH_EINVAL;
 }
 
+template <typename T, int EPI>
+int launch_gemm_tiled(const GemmArgs& a, const GemmPlan& p, hipStream_t st, Tracer& tr, const char* name) {
+    dim3 grid(cdiv(p.n_tiles, 8) * 8, p.mgroups, p.layers);   // the kernel maps blocks XCD-aware
+    tr.begin(name);
+    hipLaunchKernelGGL((gemm_tiled_kernel<T, EPI>), grid, dim3(TG_THREADS), p.lds, st, a);
+    const bool ok = hipGetLastError() == hipSuccess;
+    tr.end();
+    return ok ? DFLASH_OK : DFLASH_ELAUNCH;
+}
+
 template <typename T>
 int gemm_dispatch(const GemmArgs& a, const GemmPlan& p, hipStream_t st, Tracer& tr, const char* name) {
+    if (p.tiled) {
+        for (int k = 0; k < 2; ++k)     // a 16-row weight tile never straddles two segments
+            if (a.seg_end[k] < a.N && a.seg_end[k] % 16) return DFLASH_EINVAL;
+        switch (p.epi) {
+            case EPI_STORE: return launch_gemm_tiled<T, EPI_STORE>(a, p, st, tr, name);
+            case EPI_SWIGLU: return launch_gemm_tiled<T, EPI_SWIGLU>(a, p, st, tr, name);
+            case EPI_ARGMAX: return launch_gemm_tiled<T, EPI_ARGMAX>(a, p, st, tr, name);
+        }
+        return DFLASH_EINVAL;
+    }
     if (p.epi == EPI_STORE && (p.ns != 1 || 64 % (p.ntw * 16))) return DFLASH_EINVAL;   // store epilogue layout
     for (int k = 0; k < 2; ++k)     // a 16-row weight tile never straddles two segments
         if (a.seg_end[k] < a.N && a.seg_end[k] % 16) return DFLASH_EINVAL;

@@ -1,0 +1,216 @@
+// Tiled GEMM for many rows (M >= 128: batch x block rows at larger batches, a whole
+// prompt's injection): out = A . W^T with the same epilogues as the weight-streaming
+// GEMM (store + residual + per-tile sums of squares, SwiGLU, argmax).
+//
+// At these sizes the product is a dense contraction: each workgroup computes a 128 x 128
+// block (128 rows of A against 128 weight rows; SwiGLU: 64 gate + 64 up rows of the
+// same 64 output columns), its four waves arranged 2 x 2, each wave 64 x 64 (4 x 4 MFMA
+// tiles of 16 x 16).  Both operands go HBM -> LDS with direct-to-LDS loads, one k-step
+// (256 bytes of every row) per stage, two stages: 64 KB of A + W per stage, 128 KB in
+// all.  Inside a 16-row x 256-byte tile the 16-byte chunk c of row rho sits at c ^ rho,
+// so the fragment reads of 16 lanes (one row each) hit 16 different bank groups.
+//
+// The M-blocks of one weight block are dispatched on the same XCD (workgroup w runs on
+// XCD w % 8), one after the other, so the weight block comes from HBM once and from
+// that XCD's L2 for the other M-blocks.
+#pragma once
+
+#include "common.hpp"
+#include "gemm.hpp"
+
+namespace dflash {
+
+constexpr int TG_BM = 128, TG_BN = 128;                  // rows of A / of W per workgroup
+constexpr int TG_STAGE = (TG_BM + TG_BN) * 256;          // bytes per k-step stage
+constexpr int TG_LDS = 2 * TG_STAGE;                     // 128 KB
+constexpr int TG_THREADS = 256;
+
+// LDS fragment of 16 rows (one per lane r) x one k-step, lane group g: 4 x 16 bytes
+__device__ __forceinline__ void tg_frag(Frag64& f, const unsigned char* tile, int r, int g) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.q[i] = *reinterpret_cast<const u32x4_t*>(tile + r * 256 + (((i * 4 + g) ^ r) << 4));
+}
+
+// Output columns per workgroup (SwiGLU: 64 outputs from 64 gate + 64 up rows).
+__host__ __device__ constexpr int tg_cols(int epi) { return epi == EPI_SWIGLU ? 64 : TG_BN; }
+
+template <typename T, int EPI>
+__global__ __launch_bounds__(TG_THREADS) void gemm_tiled_kernel(const GemmArgs p) {
+    constexpr int STEP = Elem<T>::STEP;
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, g = lane >> 4, r = lane & 15;
+    const int wm = wv >> 1, wn = wv & 1;
+
+    // ---- workgroup -> (weight block, M-block): the M-blocks of a weight block share an XCD
+    const int mgroups = gridDim.y;
+    const int wlin = blockIdx.x + blockIdx.y * gridDim.x;
+    const int xcd = wlin & 7, wslot = wlin >> 3;
+    const int tile = (wslot / mgroups) * 8 + xcd;           // gridDim.x = n_tiles rounded up to 8
+    const int m0 = (wslot % mgroups) * TG_BM;
+    if (tile >= p.n_tiles) return;                          // whole workgroup, before any barrier
+    const int layer = blockIdx.z;
+    const GemmLayer& L = p.layer[layer];
+    const int K = p.K;
+    const int nsteps = K / STEP;
+
+    // ---- load plan: 64 direct-to-LDS instructions per stage (32 for the 8 A tiles, 32 for
+    // the 8 W tiles), instruction j by wave j % 4; each fetches 4 rows x 256 bytes
+    const int lq = lane >> 4, lc = lane & 15;
+    const void* abase = L.a ? L.a : p.a;
+    const char* src[16];
+    uint32_t dst[16];
+    const uint32_t lds0 = lds_offset(smem);
+    const int wv_u = __builtin_amdgcn_readfirstlane(wv);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+        const int j = u * 4 + wv_u;                 // 0..63, wave-uniform
+        const int t = j >> 2, i = j & 3;            // tile 0..15 (0..7 A, 8..15 W), rows 4i..4i+3
+        const int rho = i * 4 + lq;
+        const T* rowp;
+        if (t < 8) {
+            int m = m0 + t * 16 + rho;
+            m = m < p.M ? m : p.M - 1;              // rows past M: re-read a valid row, result discarded
+            rowp = reinterpret_cast<const T*>(abase) + (long long)m * p.lda;
+        } else {
+            const int nt = t - 8;
+            const T* base;
+            int row, rows;
+            if (EPI == EPI_SWIGLU) {                // n-tile 2c: gate tile c, 2c + 1: up tile c
+                row = tile * 64 + (nt >> 1) * 16 + rho;
+                base = reinterpret_cast<const T*>((nt & 1) ? L.w[1] : L.w[0]);
+                rows = p.N;
+            } else {                                // segment of a 16-row tile: wave-uniform
+                const int n0 = min(tile * TG_BN + nt * 16, p.N - 1);
+                const int sg = n0 < p.seg_end[0] ? 0 : (n0 < p.seg_end[1] ? 1 : 2);
+                const int lo = sg == 0 ? 0 : (sg == 1 ? p.seg_end[0] : p.seg_end[1]);
+                base = reinterpret_cast<const T*>(sg == 0 ? L.w[0] : (sg == 1 ? L.w[1] : L.w[2]));
+                row = n0 - lo + rho;
+                rows = (sg == 0 ? p.seg_end[0] : (sg == 1 ? p.seg_end[1] : p.seg_end[2])) - lo;
+            }
+            row = min(row, rows - 1);
+            rowp = base + (long long)row * K;
+        }
+        src[u] = reinterpret_cast<const char*>(rowp) + ((lc ^ rho) * 16);
+        dst[u] = (uint32_t)(t * 4096 + i * 1024);
+    }
+    auto issue = [&](int stage, int step) {
+#pragma unroll
+        for (int u = 0; u < 16; ++u) dma_b128(src[u] + (size_t)step * 256, lds0 + stage * TG_STAGE + dst[u]);
+    };
+
+    f32x4_t acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    issue(0, 0);
+    if (nsteps > 1) issue(1, 1);
+    for (int s = 0; s < nsteps; ++s) {
+        // this wave's loads of stage s have landed (at most one later stage is in flight) ...
+        if (s + 1 < nsteps) vm_wait<16>();
+        else vm_wait<0>();
+        __syncthreads();    // ... and every wave's
+        const unsigned char* st = smem + (s & 1) * TG_STAGE;
+        Frag64 af[4], bf[4];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) tg_frag(af[a], st + (wm * 4 + a) * 4096, r, g);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) tg_frag(bf[b], st + (8 + wn * 4 + b) * 4096, r, g);
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) mfma_kstep<T>(acc[a][b], af[a], bf[b]);
+        __syncthreads();    // every wave has read the stage before it is refilled
+        if (s + 2 < nsteps) issue(s & 1, s + 2);
+    }
+
+    // ---- epilogues.  Lane (g, r) of tile (a, b) holds C[m][n] for
+    // m = m0 + wm*64 + a*16 + 4g + v, n-tile column wn*64 + b*16 + r of the workgroup.
+    float* red = reinterpret_cast<float*>(smem);            // the stages are no longer read
+    if constexpr (EPI == EPI_STORE) {
+        float* const outp = L.out ? L.out : p.out;
+        const int ncol0 = tile * TG_BN + wn * 64;
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int mr = wm * 64 + a * 16 + 4 * g + v;    // row within the workgroup
+                const int m = m0 + mr;
+                float ss = 0.f;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const int n = ncol0 + b * 16 + r;
+                    float x = acc[a][b][v];
+                    if (m < p.M && n < p.N) {
+                        float* o = outp + (long long)m * p.ldo + n;
+                        if (p.residual) x += *o;
+                        *o = x;
+                    } else {
+                        x = 0.f;
+                    }
+                    ss += x * x;
+                }
+                // sum over the 16 lanes of the row (fixed order), then over the two wn waves
+                ss += __shfl_xor(ss, 1, WAVE);
+                ss += __shfl_xor(ss, 2, WAVE);
+                ss += __shfl_xor(ss, 4, WAVE);
+                ss += __shfl_xor(ss, 8, WAVE);
+                if (r == 0) red[wn * TG_BM + mr] = ss;
+            }
+        __syncthreads();
+        if (p.ssq_out && threadIdx.x < TG_BM && m0 + (int)threadIdx.x < p.M)
+            p.ssq_out[(long long)tile * p.ssq_out_ld + m0 + threadIdx.x] = red[threadIdx.x] + red[TG_BM + threadIdx.x];
+    } else if constexpr (EPI == EPI_SWIGLU) {
+        // tiles b = 0, 2: gate of output tiles 0, 1 of this wave; b = 1, 3: up
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int m = m0 + wm * 64 + a * 16 + 4 * g + v;
+                    const int n = tile * 64 + wn * 32 + c * 16 + r;
+                    if (m < p.M && n < p.N) {
+                        const float gt = acc[a][2 * c][v], up = acc[a][2 * c + 1][v];
+                        const float h = gt / (1.0f + __expf(-gt)) * up;
+                        reinterpret_cast<T*>(p.out_t)[(long long)m * p.ldo + n] = Elem<T>::from_f(h);
+                    }
+                }
+    } else {    // EPI_ARGMAX
+        unsigned long long* redu = reinterpret_cast<unsigned long long*>(smem);
+        const int G = p.gamma;
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int mr = wm * 64 + a * 16 + 4 * g + v;
+                const int m = m0 + mr;
+                unsigned long long best = 0ull;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const int n = tile * TG_BN + wn * 64 + b * 16 + r;
+                    if (m < p.M && n < p.N) {
+                        const float x = acc[a][b][v];
+                        const unsigned long long key = pack_argmax(x, (uint32_t)n);
+                        best = key > best ? key : best;
+                        const int bb = m / G, jj = m % G;
+                        if (p.dbg_logits && jj > 0) p.dbg_logits[((long long)bb * (G - 1) + (jj - 1)) * p.N + n] = x;
+                    }
+                }
+#pragma unroll
+                for (int o = 1; o < 16; o <<= 1) {
+                    const unsigned long long other = __shfl_xor(best, o, WAVE);
+                    best = other > best ? other : best;
+                }
+                if (r == 0) redu[wn * TG_BM + mr] = best;
+            }
+        __syncthreads();
+        if (threadIdx.x < TG_BM && m0 + (int)threadIdx.x < p.M) {
+            const unsigned long long x0 = redu[threadIdx.x], x1 = redu[TG_BM + threadIdx.x];
+            p.amax[(long long)tile * p.M + m0 + threadIdx.x] = x0 > x1 ? x0 : x1;
+        }
+    }
+}
+
+}  // namespace dflash
