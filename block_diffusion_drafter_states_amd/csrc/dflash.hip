@@ -91,6 +91,7 @@ int make_shape(const dflash_config* c, Shape& s) {
 struct GemmPlan {
     int ns, ks, kw, n_tiles, mt, mgroups, layers, ntw, epi;
     bool tiled;     // gemm_tiled_kernel (many rows) instead of the weight-streaming kernel
+    int bn;         // tiled: weight rows per workgroup (128, or 64 when that leaves CUs idle)
     size_t lds;
 };
 
@@ -109,6 +110,7 @@ constexpr int TILED_MIN_ROWS = 128;   // from this many rows on, A is reused fro
 // 160 KB of a CU.
 GemmPlan plan_gemm(const Shape& s, int epi, int wrows, int K, int M, int layers) {
     GemmPlan p;
+    p.bn = 0;
     p.epi = epi;
     p.layers = layers;
     p.tiled = M >= TILED_MIN_ROWS;
@@ -119,8 +121,12 @@ GemmPlan plan_gemm(const Shape& s, int epi, int wrows, int K, int M, int layers)
         p.mt = 8;
         p.ntw = 0;
         p.mgroups = cdiv(M, TG_BM);
-        p.n_tiles = cdiv(wrows, tg_cols(epi));
-        p.lds = TG_LDS;
+        p.bn = 128;
+        // 64-wide blocks when 128-wide ones would leave half the CUs idle (measured at 512 rows:
+        // down 4096 x 14336 138 -> 90 us; q|k|v 6144 x 4096, 192 blocks, 47 -> 58 us the other way)
+        if (epi != EPI_SWIGLU && cdiv(wrows, 128) * p.mgroups * layers <= 128) p.bn = 64;
+        p.n_tiles = cdiv(wrows, tg_cols(epi, p.bn));
+        p.lds = tg_lds_bytes(p.bn);
         return p;
     }
     p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
@@ -264,11 +270,11 @@ int launch_gemm_mt(const GemmArgs& a, const GemmPlan& p, hipStream_t st, Tracer&
     return DFLASH_EINVAL;
 }
 
-template <typename T, int EPI>
+template <typename T, int EPI, int BN>
 int launch_gemm_tiled(const GemmArgs& a, const GemmPlan& p, hipStream_t st, Tracer& tr, const char* name) {
     dim3 grid(cdiv(p.n_tiles, 8) * 8, p.mgroups, p.layers);   // the kernel maps blocks XCD-aware
     tr.begin(name);
-    hipLaunchKernelGGL((gemm_tiled_kernel<T, EPI>), grid, dim3(TG_THREADS), p.lds, st, a);
+    hipLaunchKernelGGL((gemm_tiled_kernel<T, EPI, BN>), grid, dim3(TG_THREADS), p.lds, st, a);
     const bool ok = hipGetLastError() == hipSuccess;
     tr.end();
     return ok ? DFLASH_OK : DFLASH_ELAUNCH;
@@ -279,10 +285,15 @@ int gemm_dispatch(const GemmArgs& a, const GemmPlan& p, hipStream_t st, Tracer& 
     if (p.tiled) {
         for (int k = 0; k < 2; ++k)     // a 16-row weight tile never straddles two segments
             if (a.seg_end[k] < a.N && a.seg_end[k] % 16) return DFLASH_EINVAL;
+        const bool wide = p.bn == 128;
         switch (p.epi) {
-            case EPI_STORE: return launch_gemm_tiled<T, EPI_STORE>(a, p, st, tr, name);
-            case EPI_SWIGLU: return launch_gemm_tiled<T, EPI_SWIGLU>(a, p, st, tr, name);
-            case EPI_ARGMAX: return launch_gemm_tiled<T, EPI_ARGMAX>(a, p, st, tr, name);
+            case EPI_STORE:
+                return wide ? launch_gemm_tiled<T, EPI_STORE, 128>(a, p, st, tr, name)
+                            : launch_gemm_tiled<T, EPI_STORE, 64>(a, p, st, tr, name);
+            case EPI_SWIGLU: return wide ? launch_gemm_tiled<T, EPI_SWIGLU, 128>(a, p, st, tr, name) : DFLASH_EINVAL;
+            case EPI_ARGMAX:
+                return wide ? launch_gemm_tiled<T, EPI_ARGMAX, 128>(a, p, st, tr, name)
+                            : launch_gemm_tiled<T, EPI_ARGMAX, 64>(a, p, st, tr, name);
         }
         return DFLASH_EINVAL;
     }
@@ -586,8 +597,8 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
         if ((rc = gemm_dispatch<T>(a, pl.lm, st, tr, "lm_head_argmax"))) return rc;
     }
     tr.begin("argmax_finish");
-    hipLaunchKernelGGL(argmax_finish_kernel, dim3(ARGMAX_SLICES, n_draft), dim3(256), 0, st, amax, pl.lm.n_tiles, M,
-                       gamma, fin_best, fin_count, draft);
+    hipLaunchKernelGGL(argmax_finish_kernel, dim3(ARGMAX_SLICES, cdiv(M, 64)), dim3(256), 0, st, amax, pl.lm.n_tiles,
+                       M, gamma, fin_best, fin_count, draft);
     tr.end();
     return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_ELAUNCH;
 }

@@ -360,49 +360,47 @@ __device__ void gemm_epilogue(const GemmArgs& p, const GemmLayer& L, int tile, i
 }
 
 // draft[b][j-1] = argmax over the vocabulary tiles of row m = b*gamma + j.
-// Workgroup (s, i) takes slice s of the tiles of draft row i (amax is [n_tiles][M],
-// so a row's maxima sit M * 8 bytes apart; ARGMAX_SLICES workgroups per row spread
-// those reads over many CUs), folds its maximum into best[i] with a 64-bit atomic
-// max (order-independent, so the result is deterministic) and counts itself in
-// count[i]; the last of the row's workgroups reads best[i] back with an atomic and
-// writes the index.  best and count start at zero (the embedding kernel of the
-// same call clears them).
+// amax is [n_tiles][M].  Workgroup (s, rb) takes slice s of the tiles for the 64 rows
+// rb*64 .. rb*64+63: wave w reads tiles s0 + w, s0 + w + 4, ..., one row per lane, so
+// every read is 64 consecutive maxima.  Per draft row i it folds its maximum into
+// best[i] with a 64-bit atomic max (order-independent, so the result is deterministic)
+// and counts itself in count[i]; the last of the row's ARGMAX_SLICES workgroups reads
+// best[i] back with an atomic and writes the index.  best and count start at zero (the
+// embedding kernel of the same call clears them).
 constexpr int ARGMAX_SLICES = 16;
 
 __global__ __launch_bounds__(256) void argmax_finish_kernel(const unsigned long long* __restrict__ amax, int n_tiles,
                                                             int M, int gamma, unsigned long long* best, int* count,
                                                             int* __restrict__ draft) {
-    __shared__ unsigned long long red[4];
-    const int s = blockIdx.x, i = blockIdx.y;      // slice, b*(gamma-1) + (j-1)
-    const int b = i / (gamma - 1), j = i % (gamma - 1) + 1;
-    const unsigned long long* col = amax + (b * gamma + j);
+    __shared__ unsigned long long red[4][64];
+    const int s = blockIdx.x;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int m = blockIdx.y * 64 + lane;
     const int per = (n_tiles + ARGMAX_SLICES - 1) / ARGMAX_SLICES;
     const int t0 = s * per, t1 = min(n_tiles, t0 + per);
     unsigned long long v[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) v[u] = 0ull;
-    for (int tb = t0; tb < t1; tb += 4 * 256) {
+    if (m < M) {
+        for (int tb = t0 + w; tb < t1; tb += 16) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int t = tb + u * 256 + threadIdx.x;
-            const unsigned long long x = t < t1 ? col[(long long)t * M] : 0ull;
-            v[u] = x > v[u] ? x : v[u];
+            for (int u = 0; u < 4; ++u) {
+                const int t = tb + 4 * u;
+                const unsigned long long x = t < t1 ? amax[(long long)t * M + m] : 0ull;
+                v[u] = x > v[u] ? x : v[u];
+            }
         }
     }
     unsigned long long mx = v[0];
 #pragma unroll
     for (int u = 1; u < 4; ++u) mx = v[u] > mx ? v[u] : mx;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        const unsigned long long other = __shfl_xor(mx, o, WAVE);
-        mx = other > mx ? other : mx;
-    }
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+    red[w][lane] = mx;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        unsigned long long w = red[0];
-        for (int k = 1; k < 4; ++k) w = red[k] > w ? red[k] : w;
-        atomicMax(best + i, w);
+    if (threadIdx.x < 64 && m < M && m % gamma != 0) {
+        unsigned long long x = red[0][lane];
+        for (int k = 1; k < 4; ++k) x = red[k][lane] > x ? red[k][lane] : x;
+        const int i = (m / gamma) * (gamma - 1) + (m % gamma - 1);
+        atomicMax(best + i, x);
         __threadfence();
         if (atomicAdd(count + i, 1) == ARGMAX_SLICES - 1) {
             __threadfence();

@@ -2,12 +2,12 @@
 // prompt's injection): out = A . W^T with the same epilogues as the weight-streaming
 // GEMM (store + residual + per-tile sums of squares, SwiGLU, argmax).
 //
-// At these sizes the product is a dense contraction: each workgroup computes a 128 x 128
-// block (128 rows of A against 128 weight rows; SwiGLU: 64 gate + 64 up rows of the
-// same 64 output columns), its four waves arranged 2 x 2, each wave 64 x 64 (4 x 4 MFMA
-// tiles of 16 x 16).  Both operands go HBM -> LDS with direct-to-LDS loads, one k-step
-// (256 bytes of every row) per stage, two stages: 64 KB of A + W per stage, 128 KB in
-// all.  Inside a 16-row x 256-byte tile the 16-byte chunk c of row rho sits at c ^ rho,
+// At these sizes the product is a dense contraction: each workgroup computes a 128 x BN
+// block (128 rows of A against BN = 128 or 64 weight rows; SwiGLU: 64 gate + 64 up rows
+// of the same 64 output columns), its four waves arranged 2 x 2, each wave 64 x BN/2
+// (4 x BN/32 MFMA tiles of 16 x 16).  Both operands go HBM -> LDS with direct-to-LDS
+// loads, one k-step (256 bytes of every row) per stage, two stages: at BN = 128, 64 KB of
+// A + W per stage, 128 KB in all.  Inside a 16-row x 256-byte tile the 16-byte chunk c of row rho sits at c ^ rho,
 // so the fragment reads of 16 lanes (one row each) hit 16 different bank groups.
 //
 // The M-blocks of one weight block are dispatched on the same XCD (workgroup w runs on
@@ -20,10 +20,11 @@
 
 namespace dflash {
 
-constexpr int TG_BM = 128, TG_BN = 128;                  // rows of A / of W per workgroup
-constexpr int TG_STAGE = (TG_BM + TG_BN) * 256;          // bytes per k-step stage
-constexpr int TG_LDS = 2 * TG_STAGE;                     // 128 KB
+constexpr int TG_BM = 128;                               // rows of A per workgroup
 constexpr int TG_THREADS = 256;
+// bytes per k-step stage and of the two stages, for BN weight rows per workgroup
+__host__ __device__ constexpr int tg_stage_bytes(int bn) { return (TG_BM + bn) * 256; }
+__host__ __device__ constexpr int tg_lds_bytes(int bn) { return 2 * tg_stage_bytes(bn); }
 
 // LDS fragment of 16 rows (one per lane r) x one k-step, lane group g: 4 x 16 bytes
 __device__ __forceinline__ void tg_frag(Frag64& f, const unsigned char* tile, int r, int g) {
@@ -32,11 +33,19 @@ __device__ __forceinline__ void tg_frag(Frag64& f, const unsigned char* tile, in
 }
 
 // Output columns per workgroup (SwiGLU: 64 outputs from 64 gate + 64 up rows).
-__host__ __device__ constexpr int tg_cols(int epi) { return epi == EPI_SWIGLU ? 64 : TG_BN; }
+__host__ __device__ constexpr int tg_cols(int epi, int bn) { return epi == EPI_SWIGLU ? bn / 2 : bn; }
 
-template <typename T, int EPI>
+// BN = 128 or 64 weight rows per workgroup (64: twice the workgroups for narrow weights;
+// SwiGLU always 128).  Wave (wm, wn) computes A rows wm*64 .. +63 against W rows
+// wn*BN/2 .. +BN/2-1: 4 x WN MFMA tiles.
+template <typename T, int EPI, int BN>
 __global__ __launch_bounds__(TG_THREADS) void gemm_tiled_kernel(const GemmArgs p) {
+    static_assert(BN == 128 || (BN == 64 && EPI != EPI_SWIGLU), "tile width");
     constexpr int STEP = Elem<T>::STEP;
+    constexpr int WN = BN / 32;                             // n-tiles per wave
+    constexpr int NI = 32 + BN / 4;                         // direct-to-LDS instructions per stage
+    constexpr int NIW = NI / 4;                             // ... per wave
+    constexpr int STAGE = tg_stage_bytes(BN);
     extern __shared__ __align__(16) unsigned char smem[];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, g = lane >> 4, r = lane & 15;
     const int wm = wv >> 1, wn = wv & 1;
@@ -53,18 +62,18 @@ __global__ __launch_bounds__(TG_THREADS) void gemm_tiled_kernel(const GemmArgs p
     const int K = p.K;
     const int nsteps = K / STEP;
 
-    // ---- load plan: 64 direct-to-LDS instructions per stage (32 for the 8 A tiles, 32 for
-    // the 8 W tiles), instruction j by wave j % 4; each fetches 4 rows x 256 bytes
+    // ---- load plan: NI direct-to-LDS instructions per stage (32 for the 8 A tiles, BN / 4
+    // for the BN / 16 W tiles), instruction j by wave j % 4; each fetches 4 rows x 256 bytes
     const int lq = lane >> 4, lc = lane & 15;
     const void* abase = L.a ? L.a : p.a;
-    const char* src[16];
-    uint32_t dst[16];
+    const char* src[NIW];
+    uint32_t dst[NIW];
     const uint32_t lds0 = lds_offset(smem);
     const int wv_u = __builtin_amdgcn_readfirstlane(wv);
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-        const int j = u * 4 + wv_u;                 // 0..63, wave-uniform
-        const int t = j >> 2, i = j & 3;            // tile 0..15 (0..7 A, 8..15 W), rows 4i..4i+3
+    for (int u = 0; u < NIW; ++u) {
+        const int j = u * 4 + wv_u;                 // 0..NI-1, wave-uniform
+        const int t = j >> 2, i = j & 3;            // tile (0..7 A, 8.. W), rows 4i..4i+3
         const int rho = i * 4 + lq;
         const T* rowp;
         if (t < 8) {
@@ -80,7 +89,7 @@ __global__ __launch_bounds__(TG_THREADS) void gemm_tiled_kernel(const GemmArgs p
                 base = reinterpret_cast<const T*>((nt & 1) ? L.w[1] : L.w[0]);
                 rows = p.N;
             } else {                                // segment of a 16-row tile: wave-uniform
-                const int n0 = min(tile * TG_BN + nt * 16, p.N - 1);
+                const int n0 = min(tile * BN + nt * 16, p.N - 1);
                 const int sg = n0 < p.seg_end[0] ? 0 : (n0 < p.seg_end[1] ? 1 : 2);
                 const int lo = sg == 0 ? 0 : (sg == 1 ? p.seg_end[0] : p.seg_end[1]);
                 base = reinterpret_cast<const T*>(sg == 0 ? L.w[0] : (sg == 1 ? L.w[1] : L.w[2]));
@@ -95,42 +104,42 @@ __global__ __launch_bounds__(TG_THREADS) void gemm_tiled_kernel(const GemmArgs p
     }
     auto issue = [&](int stage, int step) {
 #pragma unroll
-        for (int u = 0; u < 16; ++u) dma_b128(src[u] + (size_t)step * 256, lds0 + stage * TG_STAGE + dst[u]);
+        for (int u = 0; u < NIW; ++u) dma_b128(src[u] + (size_t)step * 256, lds0 + stage * STAGE + dst[u]);
     };
 
-    f32x4_t acc[4][4];
+    f32x4_t acc[4][WN];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int b = 0; b < WN; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     issue(0, 0);
     if (nsteps > 1) issue(1, 1);
     for (int s = 0; s < nsteps; ++s) {
         // this wave's loads of stage s have landed (at most one later stage is in flight) ...
-        if (s + 1 < nsteps) vm_wait<16>();
+        if (s + 1 < nsteps) vm_wait<NIW>();
         else vm_wait<0>();
         __syncthreads();    // ... and every wave's
-        const unsigned char* st = smem + (s & 1) * TG_STAGE;
-        Frag64 af[4], bf[4];
+        const unsigned char* st = smem + (s & 1) * STAGE;
+        Frag64 af[4], bf[WN];
 #pragma unroll
         for (int a = 0; a < 4; ++a) tg_frag(af[a], st + (wm * 4 + a) * 4096, r, g);
 #pragma unroll
-        for (int b = 0; b < 4; ++b) tg_frag(bf[b], st + (8 + wn * 4 + b) * 4096, r, g);
+        for (int b = 0; b < WN; ++b) tg_frag(bf[b], st + (8 + wn * WN + b) * 4096, r, g);
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
-            for (int b = 0; b < 4; ++b) mfma_kstep<T>(acc[a][b], af[a], bf[b]);
+            for (int b = 0; b < WN; ++b) mfma_kstep<T>(acc[a][b], af[a], bf[b]);
         __syncthreads();    // every wave has read the stage before it is refilled
         if (s + 2 < nsteps) issue(s & 1, s + 2);
     }
 
     // ---- epilogues.  Lane (g, r) of tile (a, b) holds C[m][n] for
-    // m = m0 + wm*64 + a*16 + 4g + v, n-tile column wn*64 + b*16 + r of the workgroup.
+    // m = m0 + wm*64 + a*16 + 4g + v, column wn*BN/2 + b*16 + r of the workgroup.
     float* red = reinterpret_cast<float*>(smem);            // the stages are no longer read
     if constexpr (EPI == EPI_STORE) {
         float* const outp = L.out ? L.out : p.out;
-        const int ncol0 = tile * TG_BN + wn * 64;
+        const int ncol0 = tile * BN + wn * (BN / 2);
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -139,7 +148,7 @@ __global__ __launch_bounds__(TG_THREADS) void gemm_tiled_kernel(const GemmArgs p
                 const int m = m0 + mr;
                 float ss = 0.f;
 #pragma unroll
-                for (int b = 0; b < 4; ++b) {
+                for (int b = 0; b < WN; ++b) {
                     const int n = ncol0 + b * 16 + r;
                     float x = acc[a][b][v];
                     if (m < p.M && n < p.N) {
@@ -188,8 +197,8 @@ __global__ __launch_bounds__(TG_THREADS) void gemm_tiled_kernel(const GemmArgs p
                 const int m = m0 + mr;
                 unsigned long long best = 0ull;
 #pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const int n = tile * TG_BN + wn * 64 + b * 16 + r;
+                for (int b = 0; b < WN; ++b) {
+                    const int n = tile * BN + wn * (BN / 2) + b * 16 + r;
                     if (m < p.M && n < p.N) {
                         const float x = acc[a][b][v];
                         const unsigned long long key = pack_argmax(x, (uint32_t)n);
