@@ -92,6 +92,7 @@ struct GemmPlan {
     int ns, ks, kw, n_tiles, mt, mgroups, layers, ntw, epi;
     bool tiled;     // gemm_tiled_kernel (many rows) instead of the weight-streaming kernel
     int bn;         // tiled: weight rows per workgroup (128, or 64 when that leaves CUs idle)
+    int kb;         // tiled: bytes of every row per LDS stage (256; 128 for launches with many workgroups)
     size_t lds;
 };
 
@@ -111,6 +112,7 @@ constexpr int TILED_MIN_ROWS = 128;   // from this many rows on, A is reused fro
 GemmPlan plan_gemm(const Shape& s, int epi, int wrows, int K, int M, int layers) {
     GemmPlan p;
     p.bn = 0;
+    p.kb = 0;
     p.epi = epi;
     p.layers = layers;
     p.tiled = M >= TILED_MIN_ROWS;
@@ -126,7 +128,11 @@ GemmPlan plan_gemm(const Shape& s, int epi, int wrows, int K, int M, int layers)
         // down 4096 x 14336 138 -> 90 us; q|k|v 6144 x 4096, 192 blocks, 47 -> 58 us the other way)
         if (epi != EPI_SWIGLU && cdiv(wrows, 128) * p.mgroups * layers <= 128) p.bn = 64;
         p.n_tiles = cdiv(wrows, tg_cols(epi, p.bn));
-        p.lds = tg_lds_bytes(p.bn);
+        // 128-byte stages (64 KB at BN 128: several workgroups per CU) pay off from ~2
+        // workgroups per CU on (measured at 512 rows: LM head 857 -> 636 us, gate|up
+        // 182 -> 143 us; with 256 workgroups they pack onto fewer CUs and lose)
+        p.kb = (long long)p.n_tiles * p.mgroups * layers >= 512 ? 128 : 256;
+        p.lds = tg_lds_bytes(p.bn, p.kb);
         return p;
     }
     p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
@@ -274,7 +280,8 @@ template <typename T, int EPI, int BN>
 int launch_gemm_tiled(const GemmArgs& a, const GemmPlan& p, hipStream_t st, Tracer& tr, const char* name) {
     dim3 grid(cdiv(p.n_tiles, 8) * 8, p.mgroups, p.layers);   // the kernel maps blocks XCD-aware
     tr.begin(name);
-    hipLaunchKernelGGL((gemm_tiled_kernel<T, EPI, BN>), grid, dim3(TG_THREADS), p.lds, st, a);
+    if (p.kb == 128) hipLaunchKernelGGL((gemm_tiled_kernel<T, EPI, BN, 128>), grid, dim3(TG_THREADS), p.lds, st, a);
+    else hipLaunchKernelGGL((gemm_tiled_kernel<T, EPI, BN, 256>), grid, dim3(TG_THREADS), p.lds, st, a);
     const bool ok = hipGetLastError() == hipSuccess;
     tr.end();
     return ok ? DFLASH_OK : DFLASH_ELAUNCH;
@@ -597,8 +604,10 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
         if ((rc = gemm_dispatch<T>(a, pl.lm, st, tr, "lm_head_argmax"))) return rc;
     }
     tr.begin("argmax_finish");
-    hipLaunchKernelGGL(argmax_finish_kernel, dim3(ARGMAX_SLICES, cdiv(M, 64)), dim3(256), 0, st, amax, pl.lm.n_tiles,
-                       M, gamma, fin_best, fin_count, draft);
+    const int row_blocks = cdiv(M, 64);
+    const int n_slices = std::max(1, std::min(pl.lm.n_tiles, 256 / row_blocks));
+    hipLaunchKernelGGL(argmax_finish_kernel, dim3(n_slices, row_blocks), dim3(256), 0, st, amax, pl.lm.n_tiles,
+                       n_slices, M, gamma, fin_best, fin_count, draft);
     tr.end();
     return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_ELAUNCH;
 }

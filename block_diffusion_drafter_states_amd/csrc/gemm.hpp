@@ -360,23 +360,22 @@ __device__ void gemm_epilogue(const GemmArgs& p, const GemmLayer& L, int tile, i
 }
 
 // draft[b][j-1] = argmax over the vocabulary tiles of row m = b*gamma + j.
-// amax is [n_tiles][M].  Workgroup (s, rb) takes slice s of the tiles for the 64 rows
-// rb*64 .. rb*64+63: wave w reads tiles s0 + w, s0 + w + 4, ..., one row per lane, so
-// every read is 64 consecutive maxima.  Per draft row i it folds its maximum into
-// best[i] with a 64-bit atomic max (order-independent, so the result is deterministic)
-// and counts itself in count[i]; the last of the row's ARGMAX_SLICES workgroups reads
-// best[i] back with an atomic and writes the index.  best and count start at zero (the
-// embedding kernel of the same call clears them).
-constexpr int ARGMAX_SLICES = 16;
-
+// amax is [n_tiles][M].  Workgroup (s, rb) takes slice s of n_slices of the tiles for
+// the 64 rows rb*64 .. rb*64+63: wave w reads tiles s0 + w, s0 + w + 4, ..., one row per
+// lane, so every read is 64 consecutive maxima (the host picks n_slices for about 256
+// workgroups, so a wave reads only a few tiles).  Per draft row i it folds its maximum
+// into best[i] with a 64-bit atomic max (order-independent, so the result is
+// deterministic) and counts itself in count[i]; the last of the row's n_slices
+// workgroups reads best[i] back with an atomic and writes the index.  best and count
+// start at zero (the embedding kernel of the same call clears them).
 __global__ __launch_bounds__(256) void argmax_finish_kernel(const unsigned long long* __restrict__ amax, int n_tiles,
-                                                            int M, int gamma, unsigned long long* best, int* count,
-                                                            int* __restrict__ draft) {
+                                                            int n_slices, int M, int gamma, unsigned long long* best,
+                                                            int* count, int* __restrict__ draft) {
     __shared__ unsigned long long red[4][64];
     const int s = blockIdx.x;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int m = blockIdx.y * 64 + lane;
-    const int per = (n_tiles + ARGMAX_SLICES - 1) / ARGMAX_SLICES;
+    const int per = (n_tiles + n_slices - 1) / n_slices;
     const int t0 = s * per, t1 = min(n_tiles, t0 + per);
     unsigned long long v[4];
 #pragma unroll
@@ -402,7 +401,7 @@ __global__ __launch_bounds__(256) void argmax_finish_kernel(const unsigned long 
         const int i = (m / gamma) * (gamma - 1) + (m % gamma - 1);
         atomicMax(best + i, x);
         __threadfence();
-        if (atomicAdd(count + i, 1) == ARGMAX_SLICES - 1) {
+        if (atomicAdd(count + i, 1) == n_slices - 1) {
             __threadfence();
             draft[i] = (int)unpack_argmax_index(atomicMax(best + i, 0ull));
         }

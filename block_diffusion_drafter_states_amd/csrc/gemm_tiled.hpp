@@ -6,9 +6,12 @@
 // block (128 rows of A against BN = 128 or 64 weight rows; SwiGLU: 64 gate + 64 up rows
 // of the same 64 output columns), its four waves arranged 2 x 2, each wave 64 x BN/2
 // (4 x BN/32 MFMA tiles of 16 x 16).  Both operands go HBM -> LDS with direct-to-LDS
-// loads, one k-step (256 bytes of every row) per stage, two stages: at BN = 128, 64 KB of
-// A + W per stage, 128 KB in all.  Inside a 16-row x 256-byte tile the 16-byte chunk c of row rho sits at c ^ rho,
-// so the fragment reads of 16 lanes (one row each) hit 16 different bank groups.
+// loads, KB bytes of every row per stage, two stages.  KB = 256 (128 KB of LDS at
+// BN = 128: one workgroup per CU) for launches with few workgroups, KB = 128 (64 KB:
+// several workgroups per CU hide each other's barriers and load latency) for launches
+// with many.  Inside a 16-row tile the 16-byte chunk c of row rho sits at c ^ swz(rho)
+// (rho for 256-byte rows, (rho >> 1) & 7 for 128-byte rows), so the fragment reads of
+// 16 lanes (one row each) hit 16 different bank groups.
 //
 // The M-blocks of one weight block are dispatched on the same XCD (workgroup w runs on
 // XCD w % 8), one after the other, so the weight block comes from HBM once and from
@@ -22,14 +25,34 @@ namespace dflash {
 
 constexpr int TG_BM = 128;                               // rows of A per workgroup
 constexpr int TG_THREADS = 256;
-// bytes per k-step stage and of the two stages, for BN weight rows per workgroup
-__host__ __device__ constexpr int tg_stage_bytes(int bn) { return (TG_BM + bn) * 256; }
-__host__ __device__ constexpr int tg_lds_bytes(int bn) { return 2 * tg_stage_bytes(bn); }
+// bytes per stage and of the two stages, for BN weight rows and KB bytes per row
+__host__ __device__ constexpr int tg_stage_bytes(int bn, int kb) { return (TG_BM + bn) * kb; }
+__host__ __device__ constexpr int tg_lds_bytes(int bn, int kb) { return 2 * tg_stage_bytes(bn, kb); }
 
-// LDS fragment of 16 rows (one per lane r) x one k-step, lane group g: 4 x 16 bytes
-__device__ __forceinline__ void tg_frag(Frag64& f, const unsigned char* tile, int r, int g) {
+template <int KB> __device__ __forceinline__ int tg_swz(int rho) { return KB == 256 ? rho : ((rho >> 1) & 7); }
+
+// LDS fragment of 16 rows (one per lane r) x KB bytes, lane group g: KB / 64 pieces of 16 bytes
+template <int KB>
+__device__ __forceinline__ void tg_frag(u32x4_t (&f)[KB / 64], const unsigned char* tile, int r, int g) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) f.q[i] = *reinterpret_cast<const u32x4_t*>(tile + r * 256 + (((i * 4 + g) ^ r) << 4));
+    for (int i = 0; i < KB / 64; ++i)
+        f[i] = *reinterpret_cast<const u32x4_t*>(tile + r * KB + (((i * 4 + g) ^ tg_swz<KB>(r)) << 4));
+}
+
+// acc += A . B^T over the KB bytes of a stage (lane pieces of 8 bf16 or 4 fp32 elements)
+template <typename T, int CH>
+__device__ __forceinline__ void tg_mfma(f32x4_t& acc, const u32x4_t (&a)[CH], const u32x4_t (&b)[CH]) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+        if constexpr (sizeof(T) == 2) {
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[i]), as_bf16x8(b[i]), acc, 0, 0, 0);
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[i][c]), __uint_as_float(b[i][c]), acc, 0,
+                                                          0, 0);
+        }
+    }
 }
 
 // Output columns per workgroup (SwiGLU: 64 outputs from 64 gate + 64 up rows).
@@ -38,14 +61,20 @@ __host__ __device__ constexpr int tg_cols(int epi, int bn) { return epi == EPI_S
 // BN = 128 or 64 weight rows per workgroup (64: twice the workgroups for narrow weights;
 // SwiGLU always 128).  Wave (wm, wn) computes A rows wm*64 .. +63 against W rows
 // wn*BN/2 .. +BN/2-1: 4 x WN MFMA tiles.
-template <typename T, int EPI, int BN>
+template <typename T, int EPI, int BN, int KB>
 __global__ __launch_bounds__(TG_THREADS) void gemm_tiled_kernel(const GemmArgs p) {
     static_assert(BN == 128 || (BN == 64 && EPI != EPI_SWIGLU), "tile width");
-    constexpr int STEP = Elem<T>::STEP;
+    static_assert(KB == 256 || KB == 128, "stage row bytes");
+    constexpr int STEP = Elem<T>::STEP * KB / 256;          // elements of a row per stage
     constexpr int WN = BN / 32;                             // n-tiles per wave
-    constexpr int NI = 32 + BN / 4;                         // direct-to-LDS instructions per stage
+    constexpr int LPR = KB / 16;                            // lanes per row in a 1 KB instruction
+    constexpr int RPI = 64 / LPR;                           // rows per instruction
+    constexpr int IPT = 16 / RPI;                           // instructions per 16-row tile
+    constexpr int TILEB = 16 * KB;                          // bytes of a 16-row tile
+    constexpr int CH = KB / 64;                             // 16-byte pieces per lane and tile
+    constexpr int NI = (TG_BM + BN) / 16 * IPT;             // direct-to-LDS instructions per stage
     constexpr int NIW = NI / 4;                             // ... per wave
-    constexpr int STAGE = tg_stage_bytes(BN);
+    constexpr int STAGE = tg_stage_bytes(BN, KB);
     extern __shared__ __align__(16) unsigned char smem[];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, g = lane >> 4, r = lane & 15;
     const int wm = wv >> 1, wn = wv & 1;
@@ -62,9 +91,9 @@ __global__ __launch_bounds__(TG_THREADS) void gemm_tiled_kernel(const GemmArgs p
     const int K = p.K;
     const int nsteps = K / STEP;
 
-    // ---- load plan: NI direct-to-LDS instructions per stage (32 for the 8 A tiles, BN / 4
-    // for the BN / 16 W tiles), instruction j by wave j % 4; each fetches 4 rows x 256 bytes
-    const int lq = lane >> 4, lc = lane & 15;
+    // ---- load plan: NI direct-to-LDS instructions per stage (8 A tiles, BN / 16 W tiles,
+    // IPT per tile), instruction j by wave j % 4; each fetches RPI rows x KB bytes
+    const int lq = lane / LPR, lc = lane % LPR;
     const void* abase = L.a ? L.a : p.a;
     const char* src[NIW];
     uint32_t dst[NIW];
@@ -73,8 +102,8 @@ __global__ __launch_bounds__(TG_THREADS) void gemm_tiled_kernel(const GemmArgs p
 #pragma unroll
     for (int u = 0; u < NIW; ++u) {
         const int j = u * 4 + wv_u;                 // 0..NI-1, wave-uniform
-        const int t = j >> 2, i = j & 3;            // tile (0..7 A, 8.. W), rows 4i..4i+3
-        const int rho = i * 4 + lq;
+        const int t = j / IPT, i = j % IPT;         // tile (0..7 A, 8.. W), rows RPI*i ..
+        const int rho = i * RPI + lq;
         const T* rowp;
         if (t < 8) {
             int m = m0 + t * 16 + rho;
@@ -99,12 +128,12 @@ __global__ __launch_bounds__(TG_THREADS) void gemm_tiled_kernel(const GemmArgs p
             row = min(row, rows - 1);
             rowp = base + (long long)row * K;
         }
-        src[u] = reinterpret_cast<const char*>(rowp) + ((lc ^ rho) * 16);
-        dst[u] = (uint32_t)(t * 4096 + i * 1024);
+        src[u] = reinterpret_cast<const char*>(rowp) + ((lc ^ tg_swz<KB>(rho)) * 16);
+        dst[u] = (uint32_t)(t * TILEB + i * 1024);
     }
     auto issue = [&](int stage, int step) {
 #pragma unroll
-        for (int u = 0; u < NIW; ++u) dma_b128(src[u] + (size_t)step * 256, lds0 + stage * STAGE + dst[u]);
+        for (int u = 0; u < NIW; ++u) dma_b128(src[u] + (size_t)step * KB, lds0 + stage * STAGE + dst[u]);
     };
 
     f32x4_t acc[4][WN];
@@ -121,15 +150,15 @@ __global__ __launch_bounds__(TG_THREADS) void gemm_tiled_kernel(const GemmArgs p
         else vm_wait<0>();
         __syncthreads();    // ... and every wave's
         const unsigned char* st = smem + (s & 1) * STAGE;
-        Frag64 af[4], bf[WN];
+        u32x4_t af[4][CH], bf[WN][CH];
 #pragma unroll
-        for (int a = 0; a < 4; ++a) tg_frag(af[a], st + (wm * 4 + a) * 4096, r, g);
+        for (int a = 0; a < 4; ++a) tg_frag<KB>(af[a], st + (wm * 4 + a) * TILEB, r, g);
 #pragma unroll
-        for (int b = 0; b < WN; ++b) tg_frag(bf[b], st + (8 + wn * WN + b) * 4096, r, g);
+        for (int b = 0; b < WN; ++b) tg_frag<KB>(bf[b], st + (8 + wn * WN + b) * TILEB, r, g);
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
-            for (int b = 0; b < WN; ++b) mfma_kstep<T>(acc[a][b], af[a], bf[b]);
+            for (int b = 0; b < WN; ++b) tg_mfma<T, CH>(acc[a][b], af[a], bf[b]);
         __syncthreads();    // every wave has read the stage before it is refilled
         if (s + 2 < nsteps) issue(s & 1, s + 2);
     }

@@ -140,3 +140,25 @@ def test_coder30b_drafter_shape_32k_context_dynamic_block():
     # 32768-token context, block size alternating 16 / 8
     cfg = synth.get_config("C5")
     _full_size_cycles(cfg, [cfg.ctx] * cfg.batch, [16, 8], "c5full")
+
+
+def test_qwen3_8b_shape_prefill_injection():
+    """A whole prompt's feature rows at once: 2048 rows through W_fuse (4096 x 20480) and
+    every layer's W_k | W_v, the many-row GEMM path (128 x 128 blocks, 512 of them for the
+    fusion, 128-byte LDS stages); the written K and V rows against the oracle."""
+    import torch
+    cfg = synth.get_config("C3")
+    rows = 2048
+    cap = (rows + 2 * cfg.gamma_max + 63) // 64 * 64
+    log(f"case {cfg.name} prefill injection of {rows} rows, cap={cap}")
+    P = Pair(cfg, 1, cap, rows)
+    feat = gen.features(cfg, 1, rows, tag="prefill.feat")
+    P.inject(feat, np.array([rows], dtype=np.int32))
+    torch.cuda.synchronize()
+    assert P.status() == 0 and int(P.cache.len.item()) == rows
+    k = decode(P.cache.read_k())[:, 0, :, :rows]
+    v = decode(P.cache.read_v())[:, 0, :, :rows]
+    ek = rel_err(k, P.okv.k[:, 0, :, :rows])
+    ev = rel_err(v, P.okv.v[:, 0, :, :rows])
+    log(f"  injected rows k={ek:.3e} v={ev:.3e}")
+    assert ek < tol(cfg) and ev < tol(cfg)
