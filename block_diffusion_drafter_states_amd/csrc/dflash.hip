@@ -431,7 +431,9 @@ int run_inject(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int
         a.rope_sin = w->rope_sin;
         a.status = kv->status;
         tr.begin("kv_finish");
-        hipLaunchKernelGGL((kv_finish_kernel<T>), dim3(2 * s.nkv, s.L, batch), dim3(256), 0, st, a);
+        const int rb_n = cdiv(rows, KV_ROWS);
+        if ((long long)batch * rb_n > 65535) return DFLASH_EUNSUPPORTED;
+        hipLaunchKernelGGL((kv_finish_kernel<T>), dim3(2 * s.nkv, s.L, batch * rb_n), dim3(256), 0, st, a, rb_n);
         tr.end();
         if (hipGetLastError() != hipSuccess) return DFLASH_ELAUNCH;
     }

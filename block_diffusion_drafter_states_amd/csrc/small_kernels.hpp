@@ -196,28 +196,37 @@ struct KvFinishArgs {
     unsigned* status;
 };
 
+// Grid (2 n_kv, L, batch * row blocks): workgroup (hh, l, b * rb_n + rb) writes rows
+// rb * KV_ROWS .. of sequence b for head hh (k heads first, then v heads) of layer l,
+// so a whole prompt's injection spreads over many workgroups.  Workgroup (0, 0, b * rb_n)
+// checks the counts and advances len[b]; every workgroup reads the position from the
+// snapshot taken before this injection.
+constexpr int KV_ROWS = 64;
+
 template <typename T>
-__global__ __launch_bounds__(256) void kv_finish_kernel(const KvFinishArgs a) {
-    const int hh = blockIdx.x, l = blockIdx.y, b = blockIdx.z;
+__global__ __launch_bounds__(256) void kv_finish_kernel(const KvFinishArgs a, int rb_n) {
+    const int hh = blockIdx.x, l = blockIdx.y, b = blockIdx.z / rb_n, rb = blockIdx.z % rb_n;
     const int D = a.head_dim, RS = a.rows_stride, cap = a.cap;
     const int len = a.len_snap[b], nn = a.n_new[b];
     const bool bad_count = nn < 0 || nn > RS || len < 0;
     const bool overflow = !bad_count && (len + nn > cap || len + nn > a.rope_rows);
-    if (hh == 0 && l == 0 && threadIdx.x == 0) {
+    if (hh == 0 && l == 0 && rb == 0 && threadIdx.x == 0) {
         if (bad_count) atomicOr(a.status, STATUS_BAD_COUNT);
         else if (overflow) atomicOr(a.status, STATUS_KV_OVERFLOW);
         else a.len[b] = len + nn;
     }
     if (bad_count || overflow) return;
+    const int i0 = rb * KV_ROWS, nr = min(KV_ROWS, nn - i0);
+    if (nr <= 0) return;
     const bool is_k = hh < a.n_kv;
     const int h = is_k ? hh : hh - a.n_kv;
     const int ld = 2 * a.n_kv * D;
-    const float* src = a.kv + l * a.layer_stride + (long long)b * RS * ld + (long long)hh * D;
+    const float* src = a.kv + l * a.layer_stride + ((long long)b * RS + i0) * ld + (long long)hh * D;
     if (is_k) {
         T* kc = reinterpret_cast<T*>(a.kcache) + l * a.cache_layer + ((long long)b * a.n_kv + h) * cap * (long long)D;
         const int wv = threadIdx.x >> 6;
-        for (int i = wv; i < nn; i += 4) {
-            const int pos = len + i;
+        for (int i = wv; i < nr; i += 4) {
+            const int pos = len + i0 + i;
             head_norm_rope_store<T>(src + (long long)i * ld, D, reinterpret_cast<const T*>(a.k_norm[l]), a.eps,
                                     a.rope_cos + (long long)pos * (D / 2), a.rope_sin + (long long)pos * (D / 2),
                                     kc + (long long)pos * D);
@@ -225,9 +234,9 @@ __global__ __launch_bounds__(256) void kv_finish_kernel(const KvFinishArgs a) {
     } else {
         // V^T rows: consecutive threads write consecutive positions of one d
         T* vc = reinterpret_cast<T*>(a.vcache) + l * a.cache_layer + ((long long)b * a.n_kv + h) * (long long)D * cap;
-        for (int e = threadIdx.x; e < D * nn; e += 256) {
-            const int d = e / nn, i = e % nn;
-            vc[(long long)d * cap + len + i] = Elem<T>::from_f(src[(long long)i * ld + d]);
+        for (int e = threadIdx.x; e < D * nr; e += 256) {
+            const int d = e / nr, i = e % nr;
+            vc[(long long)d * cap + len + i0 + i] = Elem<T>::from_f(src[(long long)i * ld + d]);
         }
     }
 }
