@@ -74,7 +74,9 @@ class Model:
     """
 
     def __init__(self, cfg, W: Dict[str, object], device="cuda", max_batch: int = 1,
-                 kv_capacity: int = 64, gamma_max: Optional[int] = None):
+                 kv_capacity: int = 64, gamma_max: Optional[int] = None, share_from: Optional["Model"] = None):
+        """``share_from``: a model whose embedding and LM head tensors this one uses (a
+        verifying target and its drafter share them); ``W['w_fuse']`` may then be absent."""
         self.cfg = cfg
         self.device = device
         gmax = gamma_max if gamma_max is not None else cfg.gamma_max
@@ -84,8 +86,13 @@ class Model:
                                mask_token_id=cfg.mask_id, max_batch=max_batch, kv_capacity=kv_capacity,
                                rms_eps=cfg.eps, dtype=_abi.DFLASH_BF16 if cfg.dtype == "bf16" else _abi.DFLASH_F32)
         up = lambda a: to_device(a, device)
-        self.t = {"w_fuse": up(W["w_fuse"]), "embed": up(W["embed"]), "final_norm": up(W["final_norm"])}
-        self.t["lm_head"] = self.t["embed"] if W["lm_head"] is W["embed"] else up(W["lm_head"])
+        self.t = {"final_norm": up(W["final_norm"])}
+        self.t["w_fuse"] = up(W["w_fuse"]) if W.get("w_fuse") is not None else None
+        if share_from is not None:
+            self.t["embed"], self.t["lm_head"] = share_from.t["embed"], share_from.t["lm_head"]
+        else:
+            self.t["embed"] = up(W["embed"])
+            self.t["lm_head"] = self.t["embed"] if W["lm_head"] is W["embed"] else up(W["lm_head"])
         cos, sin = rope_table(cfg.head_dim, cfg.rope_theta, kv_capacity + gmax)
         self.t["rope_cos"] = _torch().from_numpy(cos).to(device)
         self.t["rope_sin"] = _torch().from_numpy(sin).to(device)
@@ -95,7 +102,8 @@ class Model:
             for f in LAYER_FIELDS:
                 setattr(arr[l], f, lw[f].data_ptr())
         self._layer_arr = arr
-        self.w = dflash_weights(w_fuse=self.t["w_fuse"].data_ptr(), embed=self.t["embed"].data_ptr(),
+        fuse_ptr = self.t["w_fuse"].data_ptr() if self.t["w_fuse"] is not None else None
+        self.w = dflash_weights(w_fuse=fuse_ptr, embed=self.t["embed"].data_ptr(),
                                 final_norm=self.t["final_norm"].data_ptr(), lm_head=self.t["lm_head"].data_ptr(),
                                 rope_cos=self.t["rope_cos"].data_ptr(), rope_sin=self.t["rope_sin"].data_ptr(),
                                 rope_rows=kv_capacity + gmax,
@@ -219,6 +227,37 @@ def verify(draft, target, accept_len, committed, next_anchor, stream=None) -> No
     _need(next_anchor, "next_anchor", torch.int32, (B,))
     check(lib().dflash_verify(B, gamma, draft.data_ptr(), target.data_ptr(), accept_len.data_ptr(),
                               committed.data_ptr(), next_anchor.data_ptr(), _stream_ptr(stream)), "dflash_verify")
+
+
+def target_forward(model: Model, cache: Cache, tokens, y, ws: Workspace, feat=None, taps: Sequence[int] = (),
+                   dbg_logits=None, stream=None) -> None:
+    """A verifying target's causal forward over tokens int32 [B][rows] at positions len..: writes
+    the rows' K/V, y int32 [B][rows] (argmax), feat storage [B][rows][len(taps)][H] (hidden states
+    after the 1-based decoder layers in taps), dbg_logits fp32 [B][rows][V]; len unchanged."""
+    torch = _torch()
+    _need(tokens, "tokens", torch.int32, (None, None))
+    B, rows = tokens.shape
+    _need(y, "y", torch.int32, (B, rows))
+    taps = [int(t) for t in taps]
+    if taps:
+        _need(feat, "feat", model.storage_dtype, (B, rows, len(taps), model.cfg.hidden))
+    if dbg_logits is not None:
+        _need(dbg_logits, "dbg_logits", torch.float32, (B, rows, model.cfg.vocab))
+    tap_arr = (ctypes.c_int32 * max(1, len(taps)))(*taps)
+    check(lib().dflash_target_forward(ctypes.byref(model.c), ctypes.byref(model.w), ctypes.byref(cache.s), B, rows,
+                                      tokens.data_ptr(), y.data_ptr(), None if not taps else feat.data_ptr(),
+                                      tap_arr if taps else None, len(taps),
+                                      None if dbg_logits is None else dbg_logits.data_ptr(), ws.ptr(), ws.nbytes,
+                                      _stream_ptr(stream)), "dflash_target_forward")
+
+
+def advance_len(model: Model, cache: Cache, n, batch: Optional[int] = None, stream=None) -> None:
+    """len[b] += n[b] (n device int32 [batch], e.g. verify's accept_len)."""
+    torch = _torch()
+    _need(n, "n", torch.int32, (None,))
+    batch = n.shape[0] if batch is None else batch
+    check(lib().dflash_advance_len(ctypes.byref(cache.s), batch, model.c.kv_capacity, n.data_ptr(),
+                                   _stream_ptr(stream)), "dflash_advance_len")
 
 
 def status_str(code: int) -> str:

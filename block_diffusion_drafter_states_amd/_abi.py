@@ -26,7 +26,8 @@ STATUS_BAD_TOKEN = 2
 STATUS_BAD_COUNT = 4
 
 EXPORTED = ("dflash_workspace_bytes", "dflash_inject_kv", "dflash_draft_block", "dflash_verify",
-            "dflash_inject_kv_traced", "dflash_draft_block_traced", "dflash_status_str")
+            "dflash_inject_kv_traced", "dflash_draft_block_traced", "dflash_target_forward", "dflash_advance_len",
+            "dflash_status_str")
 
 
 class dflash_config(ctypes.Structure):
@@ -88,6 +89,13 @@ def lib(path: str = LIB_PATH) -> ctypes.CDLL:
     L.dflash_inject_kv_traced.argtypes = L.dflash_inject_kv.argtypes + [P(dflash_trace)]
     L.dflash_draft_block_traced.restype = ctypes.c_int
     L.dflash_draft_block_traced.argtypes = L.dflash_draft_block.argtypes + [P(dflash_trace)]
+    L.dflash_target_forward.restype = ctypes.c_int
+    L.dflash_target_forward.argtypes = [P(dflash_config), P(dflash_weights), P(dflash_kv), ctypes.c_int32,
+                                        ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_size_t, ctypes.c_void_p]
+    L.dflash_advance_len.restype = ctypes.c_int
+    L.dflash_advance_len.argtypes = [P(dflash_kv), ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
     L.dflash_status_str.restype = ctypes.c_char_p
     L.dflash_status_str.argtypes = [ctypes.c_int]
     _LIB = L

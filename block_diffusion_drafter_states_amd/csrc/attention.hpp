@@ -50,6 +50,7 @@ struct AttnArgs {
     int gamma, group;       // rows = group * gamma
     int nqs;                // workgroups per (b, h, chunk): query tiles split in groups of QTW
     float scale_log2;       // log2(e) / sqrt(D)
+    int causal;             // block keys after a query's own position are masked (a verifying target)
 };
 
 // Per-wave attention state for one query tile.
@@ -285,14 +286,15 @@ __device__ __forceinline__ void vfrag_lds(VFrag<float>& v, const unsigned char* 
 __device__ __forceinline__ int subblock_key(int t, int r) { return (r >> 2) * 8 + t * 4 + (r & 3); }
 
 // One 32-key sub-block.  MASKED: only the first `nvalid` (>= 1) keys are real
-// (the last sub-block of a sequence, and the block itself); their scores are
-// -inf and their V entries are cleared (stale cache rows may hold any bits).
+// (the last sub-block of a sequence, and the block itself); their V entries are
+// cleared (stale cache rows may hold any bits), and scores of keys at or past
+// this lane's `klim` (<= nvalid, >= 1; = nvalid except for causal block rows) are -inf.
 // Softmax in base 2 with the raw hardware exp2 (arguments are <= 0; results
 // below the fp32 normal range flush to 0).  O is rescaled only when the running
 // max of some query in the wave moved.
 template <typename T, bool MASKED>
-__device__ __forceinline__ void attn_subblock(WaveAttn<T>& w, int nvalid, float scale_log2, const Frag64 (&kf)[2],
-                                              VFrag<T> (&vf)[WaveAttn<T>::DT]) {
+__device__ __forceinline__ void attn_subblock(WaveAttn<T>& w, int nvalid, int klim, float scale_log2,
+                                              const Frag64 (&kf)[2], VFrag<T> (&vf)[WaveAttn<T>::DT]) {
     constexpr int DT = WaveAttn<T>::DT;
     const int g = (threadIdx.x & 63) >> 4;
     if constexpr (MASKED) {
@@ -313,7 +315,7 @@ __device__ __forceinline__ void attn_subblock(WaveAttn<T>& w, int nvalid, float 
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             float x = st[t][v] * scale_log2;
-            if constexpr (MASKED) x = (g * 8 + t * 4 + v) < nvalid ? x : -INFINITY;
+            if constexpr (MASKED) x = (g * 8 + t * 4 + v) < klim ? x : -INFINITY;
             s[t * 4 + v] = x;
             mx = fmaxf(mx, x);
         }
@@ -551,7 +553,9 @@ __global__ __launch_bounds__(64 * ATT_MAX_WAVES) void attn_partial_kernel(const 
             for (int t = 0; t < 2; ++t) load_frag_lds(kf[t], smem, subblock_key(t, r));
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) vfrag_lds(vf[dt], smem + ATT_V_OFF, dt * 16 + r);
-            attn_subblock<T, true>(w, G, a.scale_log2, kf, vf);
+            // causal block rows: query row Rq is position Rq % G of the block and sees keys 0 .. Rq % G
+            const int klim = (a.causal && qvalid) ? Rq % G + 1 : G;
+            attn_subblock<T, true>(w, G, klim, a.scale_log2, kf, vf);
         }
     } else if (active) {
         wait_stage<NPW, R>(n_issued);      // the query loads came first
@@ -575,8 +579,8 @@ __global__ __launch_bounds__(64 * ATT_MAX_WAVES) void attn_partial_kernel(const 
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) vfrag_lds(vf[dt], st + ATT_V_OFF, dt * 16 + r);
             const int nvalid = __builtin_amdgcn_readfirstlane(min(32, k_hi - kb));
-            if (nvalid < 32) attn_subblock<T, true>(w, nvalid, a.scale_log2, kf, vf);
-            else attn_subblock<T, false>(w, 32, a.scale_log2, kf, vf);
+            if (nvalid < 32) attn_subblock<T, true>(w, nvalid, nvalid, a.scale_log2, kf, vf);
+            else attn_subblock<T, false>(w, 32, 32, a.scale_log2, kf, vf);
         }
         if (it + R < n_iter) {          // refill this stage once every wave has read it
             __syncthreads();

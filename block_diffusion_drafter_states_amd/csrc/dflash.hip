@@ -17,6 +17,7 @@ using namespace dflash;
 namespace {
 
 constexpr size_t ALIGN = 256;
+constexpr int TARGET_MAX_LAYERS = 128;   // a verifying target model; the drafter's injection needs L <= MAX_LAYERS
 constexpr size_t GEMM_MAX_LDS = 160 * 1024 - 4096;   // dynamic LDS per workgroup (static LDS needs the rest)
 
 inline size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
@@ -63,7 +64,7 @@ int make_shape(const dflash_config* c, Shape& s) {
     if (s.mask < 0 || s.mask >= s.V) return DFLASH_EINVAL;
     if (s.nq % s.nkv) return DFLASH_EUNSUPPORTED;
     if (s.D * s.esize != 256) return DFLASH_EUNSUPPORTED;
-    if (s.L > MAX_LAYERS) return DFLASH_EUNSUPPORTED;
+    if (s.L > TARGET_MAX_LAYERS) return DFLASH_EUNSUPPORTED;   // the injection needs L <= MAX_LAYERS
     if (s.cap % 64) return DFLASH_EUNSUPPORTED;
     if (s.H % s.step || s.I % s.step || (s.nq * s.D) % s.step || ((long long)s.F * s.H) % s.step)
         return DFLASH_EUNSUPPORTED;
@@ -330,9 +331,9 @@ GemmArgs gemm_base(const Shape& s, const GemmPlan& p, int M, int K) {
     return a;
 }
 
-bool weights_ok(const Shape& s, const dflash_weights* w) {
-    if (!w || !w->w_fuse || !w->embed || !w->final_norm || !w->lm_head || !w->rope_cos || !w->rope_sin ||
-        !w->layers)
+bool weights_ok(const Shape& s, const dflash_weights* w, bool need_fuse = true) {
+    if (!w || (need_fuse && !w->w_fuse) || !w->embed || !w->final_norm || !w->lm_head || !w->rope_cos ||
+        !w->rope_sin || !w->layers)
         return false;
     for (int l = 0; l < s.L; ++l) {
         const dflash_layer_weights& x = w->layers[l];
@@ -414,6 +415,9 @@ int run_inject(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int
         std::memset(&a, 0, sizeof(a));
         a.kv = kvraw;
         a.layer_stride = (long long)M * 2 * s.nkv * s.D;
+        a.row_ld = 2 * s.nkv * s.D;
+        a.layer0 = 0;
+        a.update_len = 1;
         a.rows_stride = rows;
         a.n_kv = s.nkv;
         a.head_dim = s.D;
@@ -440,10 +444,25 @@ int run_inject(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int
     return DFLASH_OK;
 }
 
+// What differs between the drafter's block pass and a verifying target's forward over the
+// same rows: the target reads its own tokens, masks later block positions (causal), keeps
+// the block's K/V in its cache, taps hidden states and takes the argmax of every row.
+struct PassMode {
+    const int* tokens;      // nullable: [batch][gamma] ids (else anchor + mask tokens)
+    int causal;
+    int write_kv;           // K / V^T rows of the block at len .. len + gamma - 1 (len unchanged)
+    const int* taps;        // [host] n_taps 1-based decoder layers; feat [batch][gamma][n_taps][H]
+    int n_taps;
+    void* feat;
+    int first_row;          // argmax rows: 1 (drafts) or 0 (every row)
+};
+
+constexpr PassMode DRAFT_PASS = {nullptr, 0, 0, nullptr, 0, nullptr, 1};
+
 template <typename T>
 int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int batch, int gamma,
               const int* anchor, int* draft, float* dbg_hidden, float* dbg_logits, void* ws, const Layout& lay,
-              hipStream_t st, Tracer& tr) {
+              hipStream_t st, Tracer& tr, const PassMode& md = DRAFT_PASS) {
     char* wsb = static_cast<char*>(ws);
     const int M = batch * gamma;
     const DraftPlans pl = draft_plans(s, M);
@@ -460,13 +479,13 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
     void* nbuf = wsb + lay.nbuf;
     unsigned long long* fin_best = reinterpret_cast<unsigned long long*>(wsb + lay.fin_best);
     int* fin_count = reinterpret_cast<int*>(wsb + lay.fin_count);
-    const int n_draft = batch * (gamma - 1);
+    const int n_draft = batch * (gamma - md.first_row);
     const int qkv_ld = (s.nq + 2 * s.nkv) * s.D;
     int rc;
 
     tr.begin("embed_norm");
     hipLaunchKernelGGL((embed_norm_kernel<T>), dim3(M), dim3(256), 0, st, static_cast<const T*>(w->embed), anchor,
-                       s.mask, s.V, gamma, s.H, static_cast<const T*>(w->layers[0].in_norm), s.eps, x,
+                       md.tokens, s.mask, s.V, gamma, s.H, static_cast<const T*>(w->layers[0].in_norm), s.eps, x,
                        static_cast<T*>(nbuf), kv->status, fin_best, fin_count, n_draft);
     tr.end();
     if (hipGetLastError() != hipSuccess) return DFLASH_ELAUNCH;
@@ -496,6 +515,36 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
             a.ldo = qkv_ld;
             if ((rc = gemm_dispatch<T>(a, pl.qkv, st, tr, "qkv_proj"))) return rc;
         }
+        if (md.write_kv) {  // the block's k (RMSNorm + RoPE) and v rows into this layer's cache
+            KvFinishArgs a;
+            std::memset(&a, 0, sizeof(a));
+            a.kv = qkv + (size_t)s.nq * s.D;
+            a.layer_stride = 0;
+            a.row_ld = qkv_ld;
+            a.rows_stride = gamma;
+            a.n_kv = s.nkv;
+            a.head_dim = s.D;
+            a.cap = s.cap;
+            a.rope_rows = w->rope_rows;
+            a.layer0 = l;
+            a.update_len = 0;
+            a.cache_layer = (long long)s.Bmax * s.nkv * s.cap * s.D;
+            a.kcache = kv->k;
+            a.vcache = kv->v;
+            a.k_norm[0] = lw.k_norm;
+            a.eps = s.eps;
+            a.len_snap = kv->len;
+            a.len = kv->len;
+            a.n_new = nullptr;
+            a.n_const = gamma;
+            a.rope_cos = w->rope_cos;
+            a.rope_sin = w->rope_sin;
+            a.status = kv->status;
+            tr.begin("kv_write");
+            hipLaunchKernelGGL((kv_finish_kernel<T>), dim3(2 * s.nkv, 1, batch), dim3(256), 0, st, a, 1);
+            tr.end();
+            if (hipGetLastError() != hipSuccess) return DFLASH_ELAUNCH;
+        }
         {   // attention over [context ; block]
             AttnArgs a;
             std::memset(&a, 0, sizeof(a));
@@ -521,6 +570,7 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
             a.gamma = gamma;
             a.group = s.group;
             a.nqs = ap.nqs;
+            a.causal = md.causal;
             a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)s.D));
             tr.begin("attention");
             rc = launch_attention<T>(a, ap, s.nch_max, s.nkv, batch, st);
@@ -585,6 +635,16 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
             if ((rc = gemm_dispatch<T>(a, pl.down, st, tr, "down_proj"))) return rc;
             n_ssq = pl.down.n_tiles;
         }
+        for (int f = 0; f < md.n_taps; ++f) {   // hidden state after decoder layer l + 1
+            if (md.taps[f] != l + 1) continue;
+            const long long n = (long long)M * s.H;
+            const unsigned blocks = (unsigned)std::min<long long>(2048, (n + 255) / 256);
+            tr.begin("tap");
+            hipLaunchKernelGGL((tap_kernel<T>), dim3(blocks), dim3(256), 0, st, x, n, s.H, md.n_taps, f,
+                               static_cast<T*>(md.feat));
+            tr.end();
+            if (hipGetLastError() != hipSuccess) return DFLASH_ELAUNCH;
+        }
     }
     if (dbg_hidden) {
         const long long n = (long long)M * s.H;
@@ -603,13 +663,14 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
         a.gamma = gamma;
         a.amax = amax;
         a.dbg_logits = dbg_logits;
+        a.dbg_first = md.first_row;
         if ((rc = gemm_dispatch<T>(a, pl.lm, st, tr, "lm_head_argmax"))) return rc;
     }
     tr.begin("argmax_finish");
     const int row_blocks = cdiv(M, 64);
     const int n_slices = std::max(1, std::min(pl.lm.n_tiles, 256 / row_blocks));
     hipLaunchKernelGGL(argmax_finish_kernel, dim3(n_slices, row_blocks), dim3(256), 0, st, amax, pl.lm.n_tiles,
-                       n_slices, M, gamma, fin_best, fin_count, draft);
+                       n_slices, M, gamma, md.first_row, fin_best, fin_count, draft);
     tr.end();
     return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_ELAUNCH;
 }
@@ -622,6 +683,7 @@ size_t dflash_workspace_bytes(const dflash_config* cfg, int32_t batch, int32_t m
     Shape s;
     if (make_shape(cfg, s) != DFLASH_OK) return 0;
     if (batch < 1 || batch > s.Bmax || max_rows_per_seq < 0) return 0;
+    if (max_rows_per_seq > 0 && s.L > MAX_LAYERS) return 0;   // injection: one launch serves every layer
     const Layout l = make_layout(s, batch, max_rows_per_seq);
     return l.inject_end;
 }
@@ -634,6 +696,7 @@ int dflash_inject_kv_traced(const dflash_config* cfg, const dflash_weights* w, c
     if (rc) return rc;
     if (!w || !kv || !feat || !n_new || !kv->k || !kv->v || !kv->len || !kv->status) return DFLASH_EINVAL;
     if (!weights_ok(s, w)) return DFLASH_EINVAL;
+    if (s.L > MAX_LAYERS) return DFLASH_EUNSUPPORTED;      // one launch serves every layer
     if (batch < 1 || batch > s.Bmax || rows_stride < 1) return DFLASH_EINVAL;
     if (w->rope_rows < s.cap + s.gmax) return DFLASH_EINVAL;
     if (trace && trace->capacity < 0) return DFLASH_EINVAL;
@@ -691,6 +754,38 @@ int dflash_verify(int32_t batch, int32_t gamma, const int32_t* draft, const int3
     if (!draft || !target || !accept_len || !committed || !next_anchor) return DFLASH_EINVAL;
     hipLaunchKernelGGL(verify_kernel, dim3(batch), dim3(64), 0, static_cast<hipStream_t>(stream), batch, gamma, draft,
                        target, accept_len, committed, next_anchor);
+    return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_ELAUNCH;
+}
+
+int dflash_target_forward(const dflash_config* cfg, const dflash_weights* w, const dflash_kv* kv, int32_t batch,
+                          int32_t rows, const int32_t* tokens, int32_t* y, void* feat, const int32_t* taps,
+                          int32_t n_taps, float* dbg_logits, void* workspace, size_t workspace_bytes, void* stream) {
+    Shape s;
+    int rc = make_shape(cfg, s);
+    if (rc) return rc;
+    if (!w || !kv || !tokens || !y || !kv->k || !kv->v || !kv->len || !kv->status) return DFLASH_EINVAL;
+    if (!weights_ok(s, w, false)) return DFLASH_EINVAL;
+    if (batch < 1 || batch > s.Bmax || rows < 1 || rows > s.gmax) return DFLASH_EINVAL;
+    if (n_taps < 0 || n_taps > MAX_LAYERS || (n_taps > 0 && (!taps || !feat))) return DFLASH_EINVAL;
+    for (int f = 0; f < n_taps; ++f)
+        if (taps[f] < 1 || taps[f] > s.L) return DFLASH_EINVAL;
+    if (w->rope_rows < s.cap + s.gmax) return DFLASH_EINVAL;
+    if (!workspace) return DFLASH_EWORKSPACE;
+    const Layout lay = make_layout(s, batch, 0);
+    if (workspace_bytes < lay.draft_end) return DFLASH_EWORKSPACE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    Tracer tr{nullptr, st};
+    const PassMode md = {tokens, 1, 1, taps, n_taps, feat, 0};
+    return s.bf16 ? run_draft<bf16_t>(s, w, kv, batch, rows, nullptr, y, nullptr, dbg_logits, workspace, lay, st, tr,
+                                      md)
+                  : run_draft<float>(s, w, kv, batch, rows, nullptr, y, nullptr, dbg_logits, workspace, lay, st, tr,
+                                     md);
+}
+
+int dflash_advance_len(const dflash_kv* kv, int32_t batch, int32_t kv_capacity, const int32_t* n, void* stream) {
+    if (!kv || !kv->len || !kv->status || !n || batch < 1 || kv_capacity < 1) return DFLASH_EINVAL;
+    hipLaunchKernelGGL(advance_len_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), kv->len, n, batch,
+                       kv_capacity, kv->status);
     return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_ELAUNCH;
 }
 

@@ -58,8 +58,9 @@ struct GemmArgs {
     int ssq_out_ld;
     void* out_t;            // EPI_SWIGLU: T [M][ldo]
     unsigned long long* amax;   // EPI_ARGMAX: [n_tiles][M] packed (value, index) maxima
-    float* dbg_logits;      // EPI_ARGMAX: nullable [B][gamma-1][N]
+    float* dbg_logits;      // EPI_ARGMAX: nullable [B][gamma-dbg_first][N] logits of rows j >= dbg_first
     int gamma;              // EPI_ARGMAX: rows per sequence in A (block size)
+    int dbg_first;
 };
 
 // Ring depth (k-steps in flight): the weights live in LDS; the registers of a
@@ -346,7 +347,8 @@ __device__ void gemm_epilogue(const GemmArgs& p, const GemmLayer& L, int tile, i
                     const float v = Ct[row * wcols + c];
                     const unsigned long long key = pack_argmax(v, (uint32_t)n);
                     best = key > best ? key : best;
-                    if (p.dbg_logits && jj > 0) p.dbg_logits[((long long)b * (G - 1) + (jj - 1)) * p.N + n] = v;
+                    if (p.dbg_logits && jj >= p.dbg_first)
+                        p.dbg_logits[((long long)b * (G - p.dbg_first) + (jj - p.dbg_first)) * p.N + n] = v;
                 }
             }
 #pragma unroll
@@ -359,7 +361,9 @@ __device__ void gemm_epilogue(const GemmArgs& p, const GemmLayer& L, int tile, i
     }
 }
 
-// draft[b][j-1] = argmax over the vocabulary tiles of row m = b*gamma + j.
+// out[b][j - first] = argmax over the vocabulary tiles of row m = b*gamma + j, for
+// j >= first (first = 1: the drafts, rows after the anchor; 0: every row, a target's
+// verification).
 // amax is [n_tiles][M].  Workgroup (s, rb) takes slice s of n_slices of the tiles for
 // the 64 rows rb*64 .. rb*64+63: wave w reads tiles s0 + w, s0 + w + 4, ..., one row per
 // lane, so every read is 64 consecutive maxima (the host picks n_slices for about 256
@@ -369,8 +373,9 @@ __device__ void gemm_epilogue(const GemmArgs& p, const GemmLayer& L, int tile, i
 // workgroups reads best[i] back with an atomic and writes the index.  best and count
 // start at zero (the embedding kernel of the same call clears them).
 __global__ __launch_bounds__(256) void argmax_finish_kernel(const unsigned long long* __restrict__ amax, int n_tiles,
-                                                            int n_slices, int M, int gamma, unsigned long long* best,
-                                                            int* count, int* __restrict__ draft) {
+                                                            int n_slices, int M, int gamma, int first,
+                                                            unsigned long long* best, int* count,
+                                                            int* __restrict__ draft) {
     __shared__ unsigned long long red[4][64];
     const int s = blockIdx.x;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -395,10 +400,10 @@ __global__ __launch_bounds__(256) void argmax_finish_kernel(const unsigned long 
     for (int u = 1; u < 4; ++u) mx = v[u] > mx ? v[u] : mx;
     red[w][lane] = mx;
     __syncthreads();
-    if (threadIdx.x < 64 && m < M && m % gamma != 0) {
+    if (threadIdx.x < 64 && m < M && m % gamma >= first) {
         unsigned long long x = red[0][lane];
         for (int k = 1; k < 4; ++k) x = red[k][lane] > x ? red[k][lane] : x;
-        const int i = (m / gamma) * (gamma - 1) + (m % gamma - 1);
+        const int i = (m / gamma) * (gamma - first) + (m % gamma - first);
         atomicMax(best + i, x);
         __threadfence();
         if (atomicAdd(count + i, 1) == n_slices - 1) {

@@ -233,7 +233,8 @@ __global__ __launch_bounds__(TG_THREADS) void gemm_tiled_kernel(const GemmArgs p
                         const unsigned long long key = pack_argmax(x, (uint32_t)n);
                         best = key > best ? key : best;
                         const int bb = m / G, jj = m % G;
-                        if (p.dbg_logits && jj > 0) p.dbg_logits[((long long)bb * (G - 1) + (jj - 1)) * p.N + n] = x;
+                        if (p.dbg_logits && jj >= p.dbg_first)
+                            p.dbg_logits[((long long)bb * (G - p.dbg_first) + (jj - p.dbg_first)) * p.N + n] = x;
                     }
                 }
 #pragma unroll

@@ -13,7 +13,8 @@ constexpr int EMBED_MAX_HIDDEN = 8192;
 
 template <typename T>
 __global__ __launch_bounds__(256) void embed_norm_kernel(const T* __restrict__ embed, const int* __restrict__ anchor,
-                                                         int mask_id, int vocab, int gamma, int H,
+                                                         const int* __restrict__ tokens, int mask_id, int vocab,
+                                                         int gamma, int H,
                                                          const T* __restrict__ w_norm, float eps,
                                                          float* __restrict__ x, T* __restrict__ xn,
                                                          unsigned* status, unsigned long long* __restrict__ fin_best,
@@ -28,7 +29,7 @@ __global__ __launch_bounds__(256) void embed_norm_kernel(const T* __restrict__ e
             fin_count[i] = 0;
         }
     const int b = m / gamma, j = m % gamma;
-    int id = (j == 0) ? anchor[b] : mask_id;
+    int id = tokens ? tokens[m] : ((j == 0) ? anchor[b] : mask_id);
     if (id < 0 || id >= vocab) {
         if (threadIdx.x == 0) atomicOr(status, STATUS_BAD_TOKEN);
         id = 0;
@@ -180,17 +181,21 @@ __device__ __forceinline__ void head_norm_rope_store(const float* src, int D, co
 // nothing for that sequence.  blockIdx = (head of 2 n_kv, layer, sequence);
 // 256 threads.
 struct KvFinishArgs {
-    const float* kv;
-    long long layer_stride;     // Mi * 2 * n_kv * D
+    const float* kv;            // [layers][rows][row_ld]; k heads then v heads at the row start
+    long long layer_stride;     // between layers of kv
+    int row_ld;                 // floats between rows of kv (2 * n_kv * D for injection)
     int rows_stride, n_kv, head_dim, cap, rope_rows;
+    int layer0;                 // cache layer of grid layer 0
+    int update_len;             // advance len by n_new (injection) or leave it (target block rows)
+    int n_const;
     long long cache_layer;      // Bmax * n_kv * cap * D
     void* kcache;
     void* vcache;
-    const void* k_norm[16];     // per layer [D]
+    const void* k_norm[16];     // per grid layer [D]
     float eps;
     const int* len_snap;
     int* len;
-    const int* n_new;
+    const int* n_new;           // nullable: then every sequence writes n_const rows
     const float* rope_cos;
     const float* rope_sin;
     unsigned* status;
@@ -205,29 +210,29 @@ constexpr int KV_ROWS = 64;
 
 template <typename T>
 __global__ __launch_bounds__(256) void kv_finish_kernel(const KvFinishArgs a, int rb_n) {
-    const int hh = blockIdx.x, l = blockIdx.y, b = blockIdx.z / rb_n, rb = blockIdx.z % rb_n;
+    const int hh = blockIdx.x, gl = blockIdx.y, l = a.layer0 + gl, b = blockIdx.z / rb_n, rb = blockIdx.z % rb_n;
     const int D = a.head_dim, RS = a.rows_stride, cap = a.cap;
-    const int len = a.len_snap[b], nn = a.n_new[b];
+    const int len = a.len_snap[b], nn = a.n_new ? a.n_new[b] : a.n_const;
     const bool bad_count = nn < 0 || nn > RS || len < 0;
     const bool overflow = !bad_count && (len + nn > cap || len + nn > a.rope_rows);
-    if (hh == 0 && l == 0 && rb == 0 && threadIdx.x == 0) {
+    if (hh == 0 && gl == 0 && rb == 0 && threadIdx.x == 0) {
         if (bad_count) atomicOr(a.status, STATUS_BAD_COUNT);
         else if (overflow) atomicOr(a.status, STATUS_KV_OVERFLOW);
-        else a.len[b] = len + nn;
+        else if (a.update_len) a.len[b] = len + nn;
     }
     if (bad_count || overflow) return;
     const int i0 = rb * KV_ROWS, nr = min(KV_ROWS, nn - i0);
     if (nr <= 0) return;
     const bool is_k = hh < a.n_kv;
     const int h = is_k ? hh : hh - a.n_kv;
-    const int ld = 2 * a.n_kv * D;
-    const float* src = a.kv + l * a.layer_stride + ((long long)b * RS + i0) * ld + (long long)hh * D;
+    const int ld = a.row_ld;
+    const float* src = a.kv + gl * a.layer_stride + ((long long)b * RS + i0) * ld + (long long)hh * D;
     if (is_k) {
         T* kc = reinterpret_cast<T*>(a.kcache) + l * a.cache_layer + ((long long)b * a.n_kv + h) * cap * (long long)D;
         const int wv = threadIdx.x >> 6;
         for (int i = wv; i < nr; i += 4) {
             const int pos = len + i0 + i;
-            head_norm_rope_store<T>(src + (long long)i * ld, D, reinterpret_cast<const T*>(a.k_norm[l]), a.eps,
+            head_norm_rope_store<T>(src + (long long)i * ld, D, reinterpret_cast<const T*>(a.k_norm[gl]), a.eps,
                                     a.rope_cos + (long long)pos * (D / 2), a.rope_sin + (long long)pos * (D / 2),
                                     kc + (long long)pos * D);
         }
@@ -238,6 +243,30 @@ __global__ __launch_bounds__(256) void kv_finish_kernel(const KvFinishArgs a, in
             const int d = e / nr, i = e % nr;
             vc[(long long)d * cap + len + i0 + i] = Elem<T>::from_f(src[(long long)i * ld + d]);
         }
+    }
+}
+
+// feat[b][j][f][:] = x[b * rows + j][:] in the storage type: the hidden state after a
+// tapped decoder layer, as the drafter's injection reads it ([B][rows][F][H]).
+template <typename T>
+__global__ __launch_bounds__(256) void tap_kernel(const float* __restrict__ x, long long n, int H, int F, int f,
+                                                  T* __restrict__ feat) {
+    for (long long e = blockIdx.x * 256ll + threadIdx.x; e < n; e += (long long)gridDim.x * 256) {
+        const long long m = e / H;
+        const int k = (int)(e % H);
+        feat[(m * F + f) * H + k] = Elem<T>::from_f(x[e]);
+    }
+}
+
+// len[b] += n[b] after a verification (n = accepted length) or a chunk of a prompt;
+// a count outside 0 .. cap - len sets a status bit and leaves len.
+__global__ __launch_bounds__(64) void advance_len_kernel(int* __restrict__ len, const int* __restrict__ n, int batch,
+                                                         int cap, unsigned* status) {
+    for (int b = threadIdx.x; b < batch; b += 64) {
+        const int l = len[b], k = n[b];
+        if (k < 0 || l < 0) atomicOr(status, STATUS_BAD_COUNT);
+        else if (l + k > cap) atomicOr(status, STATUS_KV_OVERFLOW);
+        else len[b] = l + k;
     }
 }
 

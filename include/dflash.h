@@ -13,6 +13,13 @@
  *   - dflash_verify:      greedy verification - the longest prefix of drafts
  *                         equal to the target's greedy tokens plus one bonus
  *                         token (sections 1, 4 and 5: lossless vs. greedy).
+ * Around the cycle, for a target model of the drafter's layer recipe:
+ *   - dflash_target_forward: the target's parallel check of a block (the
+ *                         verification forward of sections 1 and 2.2) with its
+ *                         greedy tokens and the tapped hidden states that the
+ *                         next dflash_inject_kv consumes (section 2.2, first
+ *                         bullet: evenly spread target layers);
+ *   - dflash_advance_len: len += accepted rows after verification.
  *
  * General rules
  *   - Pointers are device pointers unless marked [host].  The library never
@@ -197,6 +204,37 @@ int dflash_draft_block_traced(const dflash_config *cfg, const dflash_weights *w,
                               int32_t batch, int32_t gamma, const int32_t *anchor, int32_t *draft,
                               float *dbg_hidden, float *dbg_logits,
                               void *workspace, size_t workspace_bytes, void *stream, dflash_trace *trace);
+
+/* Target-side verification forward (summary sections 1 and 2.2): a causal
+ * model with the drafter's layer recipe (n_layers decoder layers, its own K/V
+ * cache in `kv`, same layouts; the embedding and LM head may be the pointers
+ * the drafter uses, which shares them with the target - section 2.3).  For each
+ * sequence b, the `rows` tokens tokens[b][*] at positions len[b] .. len[b] +
+ * rows - 1: writes their k (RMSNorm + RoPE) and v rows into every layer's cache
+ * at those positions, attends to [cached context (len[b] rows) ; the block's
+ * rows up to and including its own position], and returns
+ *   y     int32 [batch][rows]: argmax (ties -> lowest id) of the logits of
+ *         every row - the target's greedy token after each position;
+ *   feat  nullable, storage dtype [batch][rows][n_taps][H]: the residual stream
+ *         after decoder layer taps[f] (1-based), the layout dflash_inject_kv reads;
+ *   dbg_logits nullable fp32 [batch][rows][V].
+ * len is not changed: after dflash_verify, dflash_advance_len(kv, batch, cap,
+ * accept_len) keeps the accepted rows (later rows are overwritten next time);
+ * a prompt is processed in chunks of at most gamma_max rows, each followed by
+ * dflash_advance_len with n = rows.  w->w_fuse is not used (may be NULL).
+ * 1 <= rows <= gamma_max, 1 <= batch <= max_batch, 0 <= n_taps <= 16, taps
+ * [host] in 1 .. n_layers, n_layers <= 128.  Workspace: dflash_workspace_bytes
+ * (cfg, batch, 0).  Device errors (token id, len + rows > kv_capacity) set
+ * status bits as for the other calls. */
+int dflash_target_forward(const dflash_config *cfg, const dflash_weights *w, const dflash_kv *kv,
+                          int32_t batch, int32_t rows, const int32_t *tokens, int32_t *y, void *feat,
+                          const int32_t *taps, int32_t n_taps, float *dbg_logits,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+/* len[b] += n[b] for b < batch (n device int32 [batch], e.g. dflash_verify's
+ * accept_len); a count that is negative or would pass kv_capacity sets
+ * DFLASH_STATUS_BAD_COUNT / DFLASH_STATUS_KV_OVERFLOW and leaves len[b]. */
+int dflash_advance_len(const dflash_kv *kv, int32_t batch, int32_t kv_capacity, const int32_t *n, void *stream);
 
 /* Human-readable name of a dflash_status value (static string). */
 const char *dflash_status_str(int status);
