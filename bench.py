@@ -208,6 +208,78 @@ def prefill(args, dfl, cfg, gen, torch):
                                    "frac": round(tflops / peak, 4), "gflop": round(flops / 1e9, 1)}}), flush=True)
 
 
+def target_verify(args, dfl, cfg, gen, torch):
+    """The verifying target's forward over one block: a Qwen3-8B-shaped target (the drafter's
+    layer recipe, 36 layers, untied LM head) checks anchor + gamma-1 drafts at context C, keeping
+    the block's K/V rows, tapping 5 evenly spread layers' hidden states for the drafter and taking
+    every row's argmax.  HBM-bound at small batch: every weight once plus the context K/V."""
+    import numpy as np
+    B, gamma, C = args.batch, cfg.gamma, cfg.ctx
+    L = 36
+    tcfg = cfg.with_(n_layers=L, batch=B, index=cfg.index + 1000)
+    cap = (C + 2 * cfg.gamma_max + 63) // 64 * 64
+    t0 = time.time()
+    W = gen.weights(tcfg)
+    W["w_fuse"] = None
+    log(f"target weights generated {time.time() - t0:.1f}s")
+    model = dfl.Model(tcfg, W, device="cuda", max_batch=B, kv_capacity=cap)
+    del W
+    cache = dfl.Cache(model)
+    lengths = np.full(B, C, dtype=np.int32)
+    Kc, Vc = gen.context_kv(tcfg, lengths, C, tag="bench.target.ctx")
+    cache.set_context(Kc, Vc, lengths)
+    del Kc, Vc
+    ws = dfl.Workspace(model, B, 0)
+    taps = [int(round(t)) for t in np.linspace(1, L, cfg.n_feat)]
+    log(f"target uploaded {time.time() - t0:.1f}s; taps {taps}; workspace {ws.nbytes / 2**20:.1f} MiB")
+    NT = 8
+    toks = [torch.as_tensor(gen.tokens(tcfg, f"bench.target.tok.{i}", (B, gamma)).astype(np.int32), device="cuda")
+            for i in range(NT)]
+    y = torch.empty((B, gamma), dtype=torch.int32, device="cuda")
+    feat = torch.empty((B, gamma, len(taps), cfg.hidden), dtype=model.storage_dtype, device="cuda")
+    len_base = torch.as_tensor(lengths, device="cuda")
+
+    def step(i):
+        cache.len[:B].copy_(len_base)
+        dfl.target_forward(model, cache, toks[i % NT], y, ws, feat=feat, taps=taps)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    times = []
+    for r in range(args.reps):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(args.steps):
+            step(i)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / args.steps)
+    assert int(cache.status.item()) == 0
+    ms = statistics.median(times)
+    e = tcfg.elem_bytes
+    H, D = cfg.hidden, cfg.head_dim
+    w_bytes = L * ((cfg.n_q + 2 * cfg.n_kv) * D * H + cfg.n_q * D * H + 3 * cfg.inter * H) * e + cfg.vocab * H * e
+    kv_bytes = L * B * cfg.n_kv * C * D * 2 * e
+    io_bytes = B * gamma * (L * 2 * cfg.n_kv * D + len(taps) * H) * e
+    total = w_bytes + kv_bytes + io_bytes
+    gbs = total / (ms * 1e-3) / 1e9
+    log(f"target forward {ms * 1000:.1f} us ({gbs:.0f} GB/s of {total / 1e9:.2f} GB), reps "
+        f"{[round(t * 1000, 1) for t in times]}")
+    print(json.dumps({"metric": "target verification forward time", "value": round(ms * 1000, 1), "unit": "us",
+                      "higher_is_better": False, "steps": args.steps, "warmup": args.warmup, "dtype": cfg.dtype,
+                      "data": "synthetic (seeded random-init target weights and context K/V)",
+                      "config": {"workload": f"Qwen3-8B-shaped target ({L} layers, hidden {H}, GQA "
+                                             f"{cfg.n_q}/{cfg.n_kv}, vocab {cfg.vocab}), batch {B}, block of "
+                                             f"{gamma} rows at context {C}, {len(taps)} tapped layers {taps}",
+                                 "batch": B, "gamma": gamma, "context": C, "layers": L},
+                      "verified_rows_per_s": round(B * gamma / (ms * 1e-3), 1),
+                      "roofline": {"bound": "hbm", "kernel": "whole forward", "achieved": round(gbs, 1),
+                                   "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                   "algorithmic_bytes": int(total)}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -221,6 +293,8 @@ def main():
     ap.add_argument("--trace-cycles", type=int, default=20)
     ap.add_argument("--prefill", action="store_true",
                     help="time the injection of a whole context's feature rows instead of the cycle")
+    ap.add_argument("--target", action="store_true",
+                    help="time the verifying target's forward over one block (36-layer target of the config's shape)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device 5 times (a plain copy kernel of known size, "
                          "to calibrate rocprofv3 FETCH_SIZE / WRITE_SIZE) and exit")
@@ -256,6 +330,9 @@ def main():
     cfg = synth.get_config(args.config)
     if args.prefill:
         prefill(args, dfl, cfg, gen, torch)
+        return
+    if args.target:
+        target_verify(args, dfl, cfg, gen, torch)
         return
     B = args.batch
     cfg = cfg.with_(batch=B)
