@@ -23,7 +23,8 @@
 //  * online softmax in base 2 (log2(e)/sqrt(D) folded into the scale); for
 //    bf16 the PV product takes P rounded to bf16.
 // Chunk 0's workgroup first builds the block's keys (k RMSNorm + RoPE) and
-// values (rounded, transposed) in LDS.  The KG waves of a tile merge through
+// values (rounded, transposed) in LDS; for a verifying target it also copies
+// them into the cache at positions len .. len + gamma - 1 (len is not changed).  The KG waves of a tile merge through
 // LDS (all tiles at once); the workgroup writes (m, l, O) per chunk and
 // attn_merge combines the chunks with log-sum-exp weights in fixed chunk order.
 #pragma once
@@ -51,6 +52,9 @@ struct AttnArgs {
     int nqs;                // workgroups per (b, h, chunk): query tiles split in groups of QTW
     float scale_log2;       // log2(e) / sqrt(D)
     int causal;             // block keys after a query's own position are masked (a verifying target)
+    void* kwrite;           // nullable: this layer's K cache, where the block's keys are kept at len ..
+    void* vwrite;           // ... and its V^T cache (a verifying target); nothing is written when null
+    unsigned* status;       // sticky error bits (with kwrite: len < 0, len + gamma beyond the cache)
 };
 
 // Per-wave attention state for one query tile.
@@ -556,6 +560,31 @@ __global__ __launch_bounds__(64 * ATT_MAX_WAVES) void attn_partial_kernel(const 
             // causal block rows: query row Rq is position Rq % G of the block and sees keys 0 .. Rq % G
             const int klim = (a.causal && qvalid) ? Rq % G + 1 : G;
             attn_subblock<T, true>(w, G, klim, a.scale_log2, kf, vf);
+        }
+        if (a.kwrite != nullptr && qs == 0) {
+            // the block's keys and values as used above, into the cache (one workgroup per (b, h))
+            const int raw = a.len[b];
+            const bool bad = raw < 0;
+            const bool over = !bad && (raw + G > a.cap || raw + G > a.rope_rows);
+            if (h == 0 && threadIdx.x == 0) {
+                if (bad) atomicOr(a.status, STATUS_BAD_COUNT);
+                else if (over) atomicOr(a.status, STATUS_KV_OVERFLOW);
+            }
+            if (!bad && !over) {
+                constexpr int KPC = 16 / (int)sizeof(T), CPR = D / KPC;     // 16-byte chunks per key row
+                T* kw = reinterpret_cast<T*>(a.kwrite) + ((long long)b * a.n_kv + h) * (long long)a.cap * D;
+                T* vw = reinterpret_cast<T*>(a.vwrite) + ((long long)b * a.n_kv + h) * (long long)D * a.cap;
+                for (int e = threadIdx.x; e < G * CPR; e += blockDim.x) {
+                    const int key = e / CPR, cc = e % CPR;
+                    *reinterpret_cast<u32x4_t*>(kw + (long long)(raw + key) * D + cc * KPC) =
+                        *reinterpret_cast<const u32x4_t*>(smem + k_lds_off(key, cc));
+                }
+                for (int e = threadIdx.x; e < D * G; e += blockDim.x) {
+                    const int d = e / G, key = e % G;
+                    vw[(long long)d * a.cap + raw + key] = *reinterpret_cast<const T*>(
+                        smem + ATT_V_OFF + v_lds_off<T>(d, key / KPC) + (key % KPC) * (int)sizeof(T));
+                }
+            }
         }
     } else if (active) {
         wait_stage<NPW, R>(n_issued);      // the query loads came first

@@ -74,15 +74,12 @@ int make_shape(const dflash_config* c, Shape& s) {
     s.group = s.nq / s.nkv;
     if (s.group * s.gmax > 256) return DFLASH_EUNSUPPORTED;
     s.rpad = cdiv(s.group * s.gmax, 16) * 16;
-    // context keys per attention chunk: large enough that the per-chunk partial
-    // (rpad x D fp32) is <= 1/8 of the chunk's K+V bytes, small enough to give
-    // >= 512 workgroups when the cache is full
-    int ch = 16 * s.rpad / s.esize;
-    ch = std::max(256, std::min(2048, ch));
-    int p2 = 256;
-    while (p2 < ch) p2 <<= 1;
-    ch = p2;
-    while (ch > 256 && (long long)s.Bmax * s.nkv * cdiv(s.cap, ch) < 512) ch >>= 1;
+    // context keys per attention chunk: the largest power of two in 256 .. 2048 that
+    // still gives >= 1024 workgroups (four per CU) when the cache is full.  A workgroup
+    // streams its chunk through the LDS ring, so longer chunks amortise its start (query
+    // build, first loads) and its partial write; below four per CU the GPU idles.
+    int ch = 2048;
+    while (ch > 256 && (long long)s.Bmax * s.nkv * cdiv(s.cap, ch) < 1024) ch >>= 1;
     s.chunk = ch;
     s.nch_max = 1 + cdiv(s.cap, ch);
     if (s.nch_max > MERGE_MAX_CHUNKS) return DFLASH_EUNSUPPORTED;
@@ -515,36 +512,6 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
             a.ldo = qkv_ld;
             if ((rc = gemm_dispatch<T>(a, pl.qkv, st, tr, "qkv_proj"))) return rc;
         }
-        if (md.write_kv) {  // the block's k (RMSNorm + RoPE) and v rows into this layer's cache
-            KvFinishArgs a;
-            std::memset(&a, 0, sizeof(a));
-            a.kv = qkv + (size_t)s.nq * s.D;
-            a.layer_stride = 0;
-            a.row_ld = qkv_ld;
-            a.rows_stride = gamma;
-            a.n_kv = s.nkv;
-            a.head_dim = s.D;
-            a.cap = s.cap;
-            a.rope_rows = w->rope_rows;
-            a.layer0 = l;
-            a.update_len = 0;
-            a.cache_layer = (long long)s.Bmax * s.nkv * s.cap * s.D;
-            a.kcache = kv->k;
-            a.vcache = kv->v;
-            a.k_norm[0] = lw.k_norm;
-            a.eps = s.eps;
-            a.len_snap = kv->len;
-            a.len = kv->len;
-            a.n_new = nullptr;
-            a.n_const = gamma;
-            a.rope_cos = w->rope_cos;
-            a.rope_sin = w->rope_sin;
-            a.status = kv->status;
-            tr.begin("kv_write");
-            hipLaunchKernelGGL((kv_finish_kernel<T>), dim3(2 * s.nkv, 1, batch), dim3(256), 0, st, a, 1);
-            tr.end();
-            if (hipGetLastError() != hipSuccess) return DFLASH_ELAUNCH;
-        }
         {   // attention over [context ; block]
             AttnArgs a;
             std::memset(&a, 0, sizeof(a));
@@ -571,6 +538,11 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
             a.group = s.group;
             a.nqs = ap.nqs;
             a.causal = md.causal;
+            if (md.write_kv) {  // the block's keys and values are kept in this layer's cache
+                a.kwrite = static_cast<T*>(kv->k) + l * layer_elems;
+                a.vwrite = static_cast<T*>(kv->v) + l * layer_elems;
+            }
+            a.status = kv->status;
             a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)s.D));
             tr.begin("attention");
             rc = launch_attention<T>(a, ap, s.nch_max, s.nkv, batch, st);
