@@ -291,6 +291,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--trace-cycles", type=int, default=20)
+    ap.add_argument("--gamma", type=int, default=0, help="block size (default: the configuration's)")
+    ap.add_argument("--layers", type=int, default=0, help="draft layers (default: the configuration's)")
     ap.add_argument("--prefill", action="store_true",
                     help="time the injection of a whole context's feature rows instead of the cycle")
     ap.add_argument("--target", action="store_true",
@@ -328,6 +330,10 @@ def main():
     dfl.lib()
 
     cfg = synth.get_config(args.config)
+    if args.gamma:
+        cfg = cfg.with_(gamma=args.gamma, gammas=None)
+    if args.layers:
+        cfg = cfg.with_(n_layers=args.layers)
     if args.prefill:
         prefill(args, dfl, cfg, gen, torch)
         return
@@ -427,7 +433,7 @@ def main():
 
     # ---- per-launch timing with library-recorded events
     hip = Hip()
-    CAP = 64
+    CAP = 256
     names_arr = [(ctypes.c_char_p * CAP)(), (ctypes.c_char_p * CAP)()]
     probe = [_abi.dflash_trace(events=None, capacity=CAP, count=0,
                                names=ctypes.cast(names_arr[k], ctypes.POINTER(ctypes.c_char_p))) for k in range(2)]
@@ -481,8 +487,8 @@ def main():
         "dtype": cfg.dtype,
         "data": "synthetic (seeded random-init drafter weights, N(0,1) target features and context K/V, "
                 "planted target tokens)",
-        "config": {"workload": f"{cfg.name}: {SHAPES.get(cfg.name, cfg.name)}, batch {B}, gamma {gamma}, "
-                               f"context {int(lengths.mean())}",
+        "config": {"workload": f"{cfg.name}: {SHAPES.get(cfg.name, cfg.name)}, {cfg.n_layers} layers, batch {B}, "
+                               f"gamma {gamma}, context {int(lengths.mean())}",
                    "batch": B, "gamma": gamma, "context": int(lengths.mean()), "hidden": cfg.hidden,
                    "layers": cfg.n_layers, "vocab": cfg.vocab, "parallelism": "single GPU"},
         "draft_tokens_per_s": round(cps * B * (gamma - 1), 1),

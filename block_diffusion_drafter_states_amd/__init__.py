@@ -260,5 +260,22 @@ def advance_len(model: Model, cache: Cache, n, batch: Optional[int] = None, stre
                                    _stream_ptr(stream)), "dflash_advance_len")
 
 
+def choose_gamma(tau: Sequence[int], gamma_used: Sequence[int], cost_us: Sequence[float], gamma_min: int = 2,
+                 gamma_max: int = 16, prior_p: float = 0.8, prior_weight: float = 4.0) -> Tuple[int, float]:
+    """Block size for the next cycle from recent (accept length, block size) pairs and a table
+    cost_us[g] (g = 0..gamma_max, <= 0: not a candidate) of measured cycle times; returns
+    (gamma, estimated per-position acceptance).  Host-only (dflash_choose_gamma)."""
+    n = len(tau)
+    if len(gamma_used) != n or len(cost_us) < gamma_max + 1:
+        raise ValueError("tau / gamma_used lengths differ or cost_us is shorter than gamma_max + 1")
+    t = (ctypes.c_int32 * max(1, n))(*tau)
+    g = (ctypes.c_int32 * max(1, n))(*gamma_used)
+    c = (ctypes.c_float * len(cost_us))(*cost_us)
+    out_g, out_p = ctypes.c_int32(0), ctypes.c_double(0.0)
+    check(lib().dflash_choose_gamma(t, g, n, c, gamma_min, gamma_max, prior_p, prior_weight, ctypes.byref(out_g),
+                                    ctypes.byref(out_p)), "dflash_choose_gamma")
+    return int(out_g.value), float(out_p.value)
+
+
 def status_str(code: int) -> str:
     return lib().dflash_status_str(code).decode()

@@ -42,6 +42,8 @@ struct Tracer {
 };
 inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 
+constexpr int MAX_GAMMA = 16;     // block rows: one 16-row MFMA tile per (sequence, q head)
+
 struct Shape {
     int H, nq, nkv, D, I, L, F, V, gmax, mask, Bmax, cap, esize, step, group, rpad, chunk, nch_max;
     float eps;
@@ -60,7 +62,7 @@ int make_shape(const dflash_config* c, Shape& s) {
     if (s.H <= 0 || s.nq <= 0 || s.nkv <= 0 || s.D <= 0 || s.I <= 0 || s.L <= 0 || s.F <= 0 || s.V < 2 ||
         s.Bmax <= 0 || s.cap <= 0 || !(s.eps > 0.f) || !std::isfinite(s.eps))
         return DFLASH_EINVAL;
-    if (s.gmax < 2 || s.gmax > 16) return DFLASH_EINVAL;
+    if (s.gmax < 2 || s.gmax > MAX_GAMMA) return DFLASH_EINVAL;
     if (s.mask < 0 || s.mask >= s.V) return DFLASH_EINVAL;
     if (s.nq % s.nkv) return DFLASH_EUNSUPPORTED;
     if (s.D * s.esize != 256) return DFLASH_EUNSUPPORTED;
@@ -759,6 +761,44 @@ int dflash_advance_len(const dflash_kv* kv, int32_t batch, int32_t kv_capacity, 
     hipLaunchKernelGGL(advance_len_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), kv->len, n, batch,
                        kv_capacity, kv->status);
     return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_ELAUNCH;
+}
+
+int dflash_choose_gamma(const int32_t* tau, const int32_t* gamma_used, int32_t n, const float* cost_us,
+                        int32_t gamma_min, int32_t gamma_max, double prior_p, double prior_weight,
+                        int32_t* gamma_out, double* p_out) {
+    if (n < 0 || (n > 0 && (!tau || !gamma_used)) || !cost_us || !gamma_out) return DFLASH_EINVAL;
+    if (gamma_min < 2 || gamma_max > MAX_GAMMA || gamma_min > gamma_max) return DFLASH_EINVAL;
+    if (!(prior_p >= 0.0 && prior_p <= 1.0) || !(prior_weight >= 0.0)) return DFLASH_EINVAL;
+    // maximum-likelihood estimate of the per-position acceptance with pseudo-counts
+    double acc = 0.0, rej = 0.0;
+    for (int i = 0; i < n; ++i) {
+        if (gamma_used[i] < 2 || gamma_used[i] > MAX_GAMMA || tau[i] < 1 || tau[i] > gamma_used[i])
+            return DFLASH_EINVAL;
+        acc += tau[i] - 1;
+        if (tau[i] < gamma_used[i]) rej += 1.0;
+    }
+    const double den = acc + rej + prior_weight;
+    const double p = den > 0.0 ? (acc + prior_weight * prior_p) / den : prior_p;
+    // expected tokens per cycle over cycle time; E(g) summed term by term
+    int best = 0;
+    double best_rate = -1.0;
+    for (int g = gamma_min; g <= gamma_max; ++g) {
+        if (!(cost_us[g] > 0.0f)) continue;
+        double e = 0.0, pj = 1.0;
+        for (int j = 0; j < g; ++j) {
+            e += pj;
+            pj *= p;
+        }
+        const double rate = e / (double)cost_us[g];
+        if (rate > best_rate) {
+            best_rate = rate;
+            best = g;
+        }
+    }
+    if (best == 0) return DFLASH_EINVAL;
+    *gamma_out = best;
+    if (p_out) *p_out = p;
+    return DFLASH_OK;
 }
 
 const char* dflash_status_str(int status) {

@@ -58,6 +58,101 @@ __device__ __forceinline__ void tg_mfma(f32x4_t& acc, const u32x4_t (&a)[CH], co
 // Output columns per workgroup (SwiGLU: 64 outputs from 64 gate + 64 up rows).
 __host__ __device__ constexpr int tg_cols(int epi, int bn) { return epi == EPI_SWIGLU ? bn / 2 : bn; }
 
+// Epilogues of a workgroup's 128 x BN block (the stages are no longer read).  Lane (g, r)
+// of tile (a, b) holds C[m][n] for m = m0 + wm*64 + a*16 + 4g + v, column wn*BN/2 + b*16 + r
+// of the workgroup.
+template <typename T, int EPI, int BN>
+__device__ __forceinline__ void tg_epilogue(const GemmArgs& p, const GemmLayer& L, f32x4_t (&acc)[4][BN / 32],
+                                            int tile, int m0, int wm, int wn, unsigned char* smem) {
+    constexpr int WN = BN / 32;
+    const int lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
+    float* red = reinterpret_cast<float*>(smem);            // the stages are no longer read
+    if constexpr (EPI == EPI_STORE) {
+        float* const outp = L.out ? L.out : p.out;
+        const int ncol0 = tile * BN + wn * (BN / 2);
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int mr = wm * 64 + a * 16 + 4 * g + v;    // row within the workgroup
+                const int m = m0 + mr;
+                float ss = 0.f;
+#pragma unroll
+                for (int b = 0; b < WN; ++b) {
+                    const int n = ncol0 + b * 16 + r;
+                    float x = acc[a][b][v];
+                    if (m < p.M && n < p.N) {
+                        float* o = outp + (long long)m * p.ldo + n;
+                        if (p.residual) x += *o;
+                        *o = x;
+                    } else {
+                        x = 0.f;
+                    }
+                    ss += x * x;
+                }
+                // sum over the 16 lanes of the row (fixed order), then over the two wn waves
+                ss += __shfl_xor(ss, 1, WAVE);
+                ss += __shfl_xor(ss, 2, WAVE);
+                ss += __shfl_xor(ss, 4, WAVE);
+                ss += __shfl_xor(ss, 8, WAVE);
+                if (r == 0) red[wn * TG_BM + mr] = ss;
+            }
+        __syncthreads();
+        if (p.ssq_out && threadIdx.x < TG_BM && m0 + (int)threadIdx.x < p.M)
+            p.ssq_out[(long long)tile * p.ssq_out_ld + m0 + threadIdx.x] = red[threadIdx.x] + red[TG_BM + threadIdx.x];
+    } else if constexpr (EPI == EPI_SWIGLU) {
+        // tiles b = 0, 2: gate of output tiles 0, 1 of this wave; b = 1, 3: up
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int m = m0 + wm * 64 + a * 16 + 4 * g + v;
+                    const int n = tile * 64 + wn * 32 + c * 16 + r;
+                    if (m < p.M && n < p.N) {
+                        const float gt = acc[a][2 * c][v], up = acc[a][2 * c + 1][v];
+                        const float h = gt / (1.0f + __expf(-gt)) * up;
+                        reinterpret_cast<T*>(p.out_t)[(long long)m * p.ldo + n] = Elem<T>::from_f(h);
+                    }
+                }
+    } else {    // EPI_ARGMAX
+        unsigned long long* redu = reinterpret_cast<unsigned long long*>(smem);
+        const int G = p.gamma;
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int mr = wm * 64 + a * 16 + 4 * g + v;
+                const int m = m0 + mr;
+                unsigned long long best = 0ull;
+#pragma unroll
+                for (int b = 0; b < WN; ++b) {
+                    const int n = tile * BN + wn * (BN / 2) + b * 16 + r;
+                    if (m < p.M && n < p.N) {
+                        const float x = acc[a][b][v];
+                        const unsigned long long key = pack_argmax(x, (uint32_t)n);
+                        best = key > best ? key : best;
+                        const int bb = m / G, jj = m % G;
+                        if (p.dbg_logits && jj >= p.dbg_first)
+                            p.dbg_logits[((long long)bb * (G - p.dbg_first) + (jj - p.dbg_first)) * p.N + n] = x;
+                    }
+                }
+#pragma unroll
+                for (int o = 1; o < 16; o <<= 1) {
+                    const unsigned long long other = __shfl_xor(best, o, WAVE);
+                    best = other > best ? other : best;
+                }
+                if (r == 0) redu[wn * TG_BM + mr] = best;
+            }
+        __syncthreads();
+        if (threadIdx.x < TG_BM && m0 + (int)threadIdx.x < p.M) {
+            const unsigned long long x0 = redu[threadIdx.x], x1 = redu[TG_BM + threadIdx.x];
+            p.amax[(long long)tile * p.M + m0 + threadIdx.x] = x0 > x1 ? x0 : x1;
+        }
+    }
+}
+
 // BN = 128 or 64 weight rows per workgroup (64: twice the workgroups for narrow weights;
 // SwiGLU always 128).  Wave (wm, wn) computes A rows wm*64 .. +63 against W rows
 // wn*BN/2 .. +BN/2-1: 4 x WN MFMA tiles.
@@ -163,93 +258,8 @@ __global__ __launch_bounds__(TG_THREADS) void gemm_tiled_kernel(const GemmArgs p
         if (s + 2 < nsteps) issue(s & 1, s + 2);
     }
 
-    // ---- epilogues.  Lane (g, r) of tile (a, b) holds C[m][n] for
-    // m = m0 + wm*64 + a*16 + 4g + v, column wn*BN/2 + b*16 + r of the workgroup.
-    float* red = reinterpret_cast<float*>(smem);            // the stages are no longer read
-    if constexpr (EPI == EPI_STORE) {
-        float* const outp = L.out ? L.out : p.out;
-        const int ncol0 = tile * BN + wn * (BN / 2);
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int mr = wm * 64 + a * 16 + 4 * g + v;    // row within the workgroup
-                const int m = m0 + mr;
-                float ss = 0.f;
-#pragma unroll
-                for (int b = 0; b < WN; ++b) {
-                    const int n = ncol0 + b * 16 + r;
-                    float x = acc[a][b][v];
-                    if (m < p.M && n < p.N) {
-                        float* o = outp + (long long)m * p.ldo + n;
-                        if (p.residual) x += *o;
-                        *o = x;
-                    } else {
-                        x = 0.f;
-                    }
-                    ss += x * x;
-                }
-                // sum over the 16 lanes of the row (fixed order), then over the two wn waves
-                ss += __shfl_xor(ss, 1, WAVE);
-                ss += __shfl_xor(ss, 2, WAVE);
-                ss += __shfl_xor(ss, 4, WAVE);
-                ss += __shfl_xor(ss, 8, WAVE);
-                if (r == 0) red[wn * TG_BM + mr] = ss;
-            }
-        __syncthreads();
-        if (p.ssq_out && threadIdx.x < TG_BM && m0 + (int)threadIdx.x < p.M)
-            p.ssq_out[(long long)tile * p.ssq_out_ld + m0 + threadIdx.x] = red[threadIdx.x] + red[TG_BM + threadIdx.x];
-    } else if constexpr (EPI == EPI_SWIGLU) {
-        // tiles b = 0, 2: gate of output tiles 0, 1 of this wave; b = 1, 3: up
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int c = 0; c < 2; ++c)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int m = m0 + wm * 64 + a * 16 + 4 * g + v;
-                    const int n = tile * 64 + wn * 32 + c * 16 + r;
-                    if (m < p.M && n < p.N) {
-                        const float gt = acc[a][2 * c][v], up = acc[a][2 * c + 1][v];
-                        const float h = gt / (1.0f + __expf(-gt)) * up;
-                        reinterpret_cast<T*>(p.out_t)[(long long)m * p.ldo + n] = Elem<T>::from_f(h);
-                    }
-                }
-    } else {    // EPI_ARGMAX
-        unsigned long long* redu = reinterpret_cast<unsigned long long*>(smem);
-        const int G = p.gamma;
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int mr = wm * 64 + a * 16 + 4 * g + v;
-                const int m = m0 + mr;
-                unsigned long long best = 0ull;
-#pragma unroll
-                for (int b = 0; b < WN; ++b) {
-                    const int n = tile * BN + wn * (BN / 2) + b * 16 + r;
-                    if (m < p.M && n < p.N) {
-                        const float x = acc[a][b][v];
-                        const unsigned long long key = pack_argmax(x, (uint32_t)n);
-                        best = key > best ? key : best;
-                        const int bb = m / G, jj = m % G;
-                        if (p.dbg_logits && jj >= p.dbg_first)
-                            p.dbg_logits[((long long)bb * (G - p.dbg_first) + (jj - p.dbg_first)) * p.N + n] = x;
-                    }
-                }
-#pragma unroll
-                for (int o = 1; o < 16; o <<= 1) {
-                    const unsigned long long other = __shfl_xor(best, o, WAVE);
-                    best = other > best ? other : best;
-                }
-                if (r == 0) redu[wn * TG_BM + mr] = best;
-            }
-        __syncthreads();
-        if (threadIdx.x < TG_BM && m0 + (int)threadIdx.x < p.M) {
-            const unsigned long long x0 = redu[threadIdx.x], x1 = redu[TG_BM + threadIdx.x];
-            p.amax[(long long)tile * p.M + m0 + threadIdx.x] = x0 > x1 ? x0 : x1;
-        }
-    }
+    tg_epilogue<T, EPI, BN>(p, L, acc, tile, m0, wm, wn, smem);
 }
+
 
 }  // namespace dflash

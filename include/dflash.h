@@ -236,6 +236,27 @@ int dflash_target_forward(const dflash_config *cfg, const dflash_weights *w, con
  * DFLASH_STATUS_BAD_COUNT / DFLASH_STATUS_KV_OVERFLOW and leaves len[b]. */
 int dflash_advance_len(const dflash_kv *kv, int32_t batch, int32_t kv_capacity, const int32_t *n, void *stream);
 
+/* Block size for the next cycle (summary section 4, ablations: a drafter trained
+ * on 16-token blocks also drafts smaller ones at inference; picking the size per
+ * cycle is this library's policy, not the summary's).  Host-only: [host] arrays,
+ * no GPU work, usable while the previous cycle still runs.
+ * Model: every draft position is accepted with the same probability p once the
+ * ones before it were, so a cycle of block size g commits on average
+ * E(g) = 1 + p + ... + p^(g-1) tokens.  p is estimated from recent cycles by
+ * maximum likelihood with pseudo-counts: a cycle with accept length t and block
+ * size g contributes t-1 accepted positions and, if t < g, one rejected one;
+ *   p = (accepted + prior_weight * prior_p) / (accepted + rejected + prior_weight)
+ * (prior_p when the denominator is 0).  The choice maximises E(g) / cost_us[g]
+ * over gamma_min <= g <= gamma_max with cost_us[g] > 0 (ties: the smaller g).
+ *   tau, gamma_used  [host] int32 [n]: 1 <= tau[i] <= gamma_used[i] <= 16, n >= 0
+ *   cost_us          [host] float [gamma_max + 1]: time of one cycle at block size g
+ *   2 <= gamma_min <= gamma_max <= 16; 0 <= prior_p <= 1; prior_weight >= 0
+ *   gamma_out        [host] the choice; p_out [host, nullable] the estimate of p
+ * Returns DFLASH_EINVAL for arguments out of range or no candidate with a cost. */
+int dflash_choose_gamma(const int32_t *tau, const int32_t *gamma_used, int32_t n, const float *cost_us,
+                        int32_t gamma_min, int32_t gamma_max, double prior_p, double prior_weight,
+                        int32_t *gamma_out, double *p_out);
+
 /* Human-readable name of a dflash_status value (static string). */
 const char *dflash_status_str(int status);
 
