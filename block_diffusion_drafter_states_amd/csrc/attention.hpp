@@ -674,8 +674,9 @@ struct MergeArgs {
     const float* opart;
     const float* mlpart;
     const int* len;
-    void* out;              // T [B*gamma][n_q*D]
+    void* out;              // T [B*gamma][n_q*D], or in fragment order (out_frag)
     int n_kv, group, gamma, rpad, nch_max, chunk, cap, head_dim;
+    int out_frag;
 };
 
 constexpr int MERGE_MAX_CHUNKS = 1024;
@@ -731,9 +732,11 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(const MergeArgs a) {
             }
         }
     }
-    T* out = reinterpret_cast<T*>(a.out) + (long long)m * (gridDim.y * D) + (long long)hq_all * D + lane * DPL;
+    T* out = reinterpret_cast<T*>(a.out);
+    const int ncol = gridDim.y * D, col = hq_all * D + lane * DPL;
 #pragma unroll
-    for (int k = 0; k < DPL; ++k) out[k] = Elem<T>::from_f(num[k] / den);
+    for (int k = 0; k < DPL; ++k)
+        out[a.out_frag ? afrag_offset<T>(m, col + k, ncol) : (long long)m * ncol + col + k] = Elem<T>::from_f(num[k] / den);
 }
 
 }  // namespace dflash

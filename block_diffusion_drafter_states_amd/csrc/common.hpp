@@ -90,6 +90,21 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4_t& v) {
     return r;
 }
 
+// ---- A operand in fragment order ------------------------------------------------------------
+// The weight-streaming GEMM reads, per 16-row tile of A and 256-byte k-step, piece i of lane
+// (g, r) = row r, 16-byte chunk 4i + g of the step.  Rows laid out plainly put the 16 rows of one
+// load instruction 64 bytes apart in 16 cache lines; producers feeding that GEMM write A in
+// fragment order instead, where that instruction reads 1 KB of contiguous bytes:
+//   A[m][k] at element ((((m / 16) * (K / S) + k / S) * 4 + i) * 64 + g * 16 + m % 16) * E + k % E
+// with S elements per 256-byte step, E per 16 bytes and 4i + g = (k % S) / E.  A buffer holds
+// whole 16-row tiles; K must be a multiple of S.
+template <typename T>
+__host__ __device__ __forceinline__ long long afrag_offset(int m, int k, int K) {
+    constexpr int E = 16 / (int)sizeof(T), S = 256 / (int)sizeof(T);
+    const int kk = k % S, c = kk / E;
+    return ((((long long)(m >> 4) * (K / S) + k / S) * 4 + (c >> 2)) * 64 + (c & 3) * 16 + (m & 15)) * E + kk % E;
+}
+
 // ---- explicitly scheduled vector-memory operations (streaming loops) ----------------------
 // These are opaque to the compiler's wait-count pass: the caller issues them in a
 // fixed order and waits with vm_wait<N>() (loads complete in issue order), then

@@ -41,6 +41,7 @@ struct Tracer {
     }
 };
 inline int cdiv(int a, int b) { return (a + b - 1) / b; }
+inline int pad16(int m) { return cdiv(m, 16) * 16; }
 
 constexpr int MAX_GAMMA = 16;     // block rows: one 16-row MFMA tile per (sequence, q head)
 
@@ -233,12 +234,13 @@ Layout make_layout(const Shape& s, int batch, int rows) {
     l.qkv = take(M * (size_t)(s.nq + 2 * s.nkv) * s.D * 4);
     l.opart = take((size_t)batch * s.nkv * s.nch_max * s.rpad * s.D * 4);
     l.mlpart = take((size_t)batch * s.nkv * s.nch_max * s.rpad * 2 * 4);
-    l.obuf = take(M * s.nq * s.D * s.esize);
-    l.hbuf = take(M * s.I * s.esize);
+    const size_t Mp = pad16((int)M);                          // GEMM A operands: whole 16-row tiles
+    l.obuf = take(Mp * s.nq * s.D * s.esize);
+    l.hbuf = take(Mp * s.I * s.esize);
     l.amax = take((size_t)l.amax_tiles * M * 8);
     l.fin_best = take(M * 8);                                 // per draft row: running argmax, slices done
     l.fin_count = take(M * 4);
-    l.nbuf = take(M * s.H * s.esize);                         // RMSNorm-ed rows (GEMM A operand)
+    l.nbuf = take(Mp * s.H * s.esize);                        // RMSNorm-ed rows (GEMM A operand)
     l.draft_end = off;
     l.c = l.ssq_c = l.cnorm = l.kvraw = l.lensnap = 0;
     l.ssq_c_tiles = 0;
@@ -247,7 +249,7 @@ Layout make_layout(const Shape& s, int batch, int rows) {
         l.ssq_c_tiles = plan_gemm(s, EPI_STORE, s.H, s.F * s.H, std::min((int)Mi, TILED_MIN_ROWS - 1), 1).n_tiles;
         l.c = take(Mi * s.H * 4);
         l.ssq_c = take((size_t)l.ssq_c_tiles * Mi * 4);
-        l.cnorm = take((size_t)s.L * Mi * s.H * s.esize);     // per-layer RMSNorm-ed rows
+        l.cnorm = take((size_t)s.L * pad16((int)Mi) * s.H * s.esize);   // per-layer RMSNorm-ed rows
         l.kvraw = take((size_t)s.L * Mi * 2 * s.nkv * s.D * 4); // per-layer k | v projections
         l.lensnap = take((size_t)batch * 4);                     // len before this injection
     }
@@ -290,6 +292,7 @@ int launch_gemm_tiled(const GemmArgs& a, const GemmPlan& p, hipStream_t st, Trac
 template <typename T>
 int gemm_dispatch(const GemmArgs& a, const GemmPlan& p, hipStream_t st, Tracer& tr, const char* name) {
     if (p.tiled) {
+        if (a.a_frag || a.out_frag) return DFLASH_EINVAL;     // the tiled kernel reads and writes plain rows
         for (int k = 0; k < 2; ++k)     // a 16-row weight tile never straddles two segments
             if (a.seg_end[k] < a.N && a.seg_end[k] % 16) return DFLASH_EINVAL;
         const bool wide = p.bn == 128;
@@ -344,18 +347,20 @@ bool weights_ok(const Shape& s, const dflash_weights* w, bool need_fuse = true) 
 }
 
 // A operand = RMSNorm(x; w) in the storage type: rows normalised into nbuf by
-// rmsnorm_rows_kernel (rstd from the producers' per-tile sums of squares).
+// rmsnorm_rows_kernel (rstd from the producers' per-tile sums of squares), in fragment
+// order when the consumer is the weight-streaming GEMM (afrag).
 template <typename T>
 int set_norm_a(GemmArgs& a, const Shape& s, const float* x, int M, const float* ssq, int n_ssq, const void* w,
-               void* nbuf, hipStream_t st, Tracer& tr) {
+               void* nbuf, int afrag, hipStream_t st, Tracer& tr) {
     NormWeights nw{};
     nw.w[0] = w;
     tr.begin("rmsnorm");
     hipLaunchKernelGGL((rmsnorm_rows_kernel<T>), dim3(M, cdiv(s.H, 1024), 1), dim3(256), 0, st, x, s.H, ssq, n_ssq, M,
-                       nw, s.H, s.eps, static_cast<T*>(nbuf), s.H, 0LL, nullptr, nullptr, 0);
+                       nw, s.H, s.eps, static_cast<T*>(nbuf), s.H, 0LL, nullptr, nullptr, 0, afrag);
     tr.end();
     a.a = nbuf;
     a.lda = s.H;
+    a.a_frag = afrag;
     return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_ELAUNCH;
 }
 
@@ -390,9 +395,12 @@ int run_inject(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int
         NormWeights nw{};   // one normalised copy of c per layer (each layer has its own scale)
         for (int l = 0; l < s.L; ++l) nw.w[l] = w->layers[l].in_norm;
         T* cn = reinterpret_cast<T*>(wsb + lay.cnorm);
+        const int afrag = M < TILED_MIN_ROWS ? 1 : 0;       // fragment order for the weight-streaming GEMM
+        const size_t cn_layer = (size_t)pad16(M) * s.H;    // whole 16-row tiles per layer
         tr.begin("rmsnorm");
         hipLaunchKernelGGL((rmsnorm_rows_kernel<T>), dim3(M, cdiv(s.H, 1024), s.L), dim3(256), 0, st, c, s.H, ssq_c,
-                           pl.fuse.n_tiles, M, nw, s.H, s.eps, cn, s.H, (long long)M * s.H, kv->len, lensnap, batch);
+                           pl.fuse.n_tiles, M, nw, s.H, s.eps, cn, s.H, (long long)cn_layer, kv->len, lensnap, batch,
+                           afrag);
         tr.end();
         if (hipGetLastError() != hipSuccess) return DFLASH_ELAUNCH;
         const int ld = 2 * s.nkv * s.D;
@@ -401,8 +409,9 @@ int run_inject(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int
         a.seg_end[0] = s.nkv * s.D;
         a.seg_end[1] = a.seg_end[2] = ld;
         a.ldo = ld;
+        a.a_frag = afrag;
         for (int l = 0; l < s.L; ++l) {
-            a.layer[l].a = cn + (size_t)l * M * s.H;
+            a.layer[l].a = cn + (size_t)l * cn_layer;
             a.layer[l].w[0] = w->layers[l].wk;
             a.layer[l].w[1] = w->layers[l].wv;
             a.layer[l].out = kvraw + (size_t)l * M * ld;
@@ -479,13 +488,15 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
     unsigned long long* fin_best = reinterpret_cast<unsigned long long*>(wsb + lay.fin_best);
     int* fin_count = reinterpret_cast<int*>(wsb + lay.fin_count);
     const int n_draft = batch * (gamma - md.first_row);
+    // the weight-streaming GEMM (fewer than TILED_MIN_ROWS rows) reads A in fragment order
+    const int afrag = M < TILED_MIN_ROWS ? 1 : 0;
     const int qkv_ld = (s.nq + 2 * s.nkv) * s.D;
     int rc;
 
     tr.begin("embed_norm");
     hipLaunchKernelGGL((embed_norm_kernel<T>), dim3(M), dim3(256), 0, st, static_cast<const T*>(w->embed), anchor,
                        md.tokens, s.mask, s.V, gamma, s.H, static_cast<const T*>(w->layers[0].in_norm), s.eps, x,
-                       static_cast<T*>(nbuf), kv->status, fin_best, fin_count, n_draft);
+                       static_cast<T*>(nbuf), kv->status, fin_best, fin_count, n_draft, afrag);
     tr.end();
     if (hipGetLastError() != hipSuccess) return DFLASH_ELAUNCH;
     int n_ssq = 0;      // per-tile partial sums of squares of x (written by o / down)
@@ -500,7 +511,8 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
             if (l == 0) {       // the embedding kernel normalised the rows already
                 a.a = nbuf;
                 a.lda = s.H;
-            } else if ((rc = set_norm_a<T>(a, s, x, M, ssq_x, n_ssq, lw.in_norm, nbuf, st, tr))) {
+                a.a_frag = afrag;
+            } else if ((rc = set_norm_a<T>(a, s, x, M, ssq_x, n_ssq, lw.in_norm, nbuf, afrag, st, tr))) {
                 return rc;
             }
             a.N = qkv_ld;
@@ -563,6 +575,7 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
             mgr.chunk = s.chunk;
             mgr.cap = s.cap;
             mgr.head_dim = s.D;
+            mgr.out_frag = afrag;
             tr.begin("attn_merge");
             hipLaunchKernelGGL((attn_merge_kernel<T>), dim3(M, s.nq), dim3(64), 0, st, mgr);
             tr.end();
@@ -572,6 +585,7 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
             GemmArgs a = gemm_base(s, pl.o, M, s.nq * s.D);
             a.a = obuf;
             a.lda = s.nq * s.D;
+            a.a_frag = afrag;
             a.N = s.H;
             a.seg_end[0] = a.seg_end[1] = a.seg_end[2] = s.H;
             a.layer[0].w[0] = lw.wo;
@@ -585,19 +599,21 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
         }
         {   // h = silu(W_gate a2) * (W_up a2)
             GemmArgs a = gemm_base(s, pl.gateup, M, s.H);
-            if ((rc = set_norm_a<T>(a, s, x, M, ssq_x, n_ssq, lw.post_norm, nbuf, st, tr))) return rc;
+            if ((rc = set_norm_a<T>(a, s, x, M, ssq_x, n_ssq, lw.post_norm, nbuf, afrag, st, tr))) return rc;
             a.N = s.I;
             a.seg_end[0] = a.seg_end[1] = a.seg_end[2] = s.I;
             a.layer[0].w[0] = lw.w_gate;
             a.layer[0].w[1] = lw.w_up;
             a.out_t = hbuf;
             a.ldo = s.I;
+            a.out_frag = afrag;
             if ((rc = gemm_dispatch<T>(a, pl.gateup, st, tr, "gate_up"))) return rc;
         }
         {   // x += W_down h
             GemmArgs a = gemm_base(s, pl.down, M, s.I);
             a.a = hbuf;
             a.lda = s.I;
+            a.a_frag = afrag;
             a.N = s.H;
             a.seg_end[0] = a.seg_end[1] = a.seg_end[2] = s.H;
             a.layer[0].w[0] = lw.w_down;
@@ -630,7 +646,7 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
     }
     {   // final norm -> LM head -> per-tile argmax
         GemmArgs a = gemm_base(s, pl.lm, M, s.H);
-        if ((rc = set_norm_a<T>(a, s, x, M, ssq_x, n_ssq, w->final_norm, nbuf, st, tr))) return rc;
+        if ((rc = set_norm_a<T>(a, s, x, M, ssq_x, n_ssq, w->final_norm, nbuf, afrag, st, tr))) return rc;
         a.N = s.V;
         a.seg_end[0] = a.seg_end[1] = a.seg_end[2] = s.V;
         a.layer[0].w[0] = w->lm_head;

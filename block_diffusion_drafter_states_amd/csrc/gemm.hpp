@@ -38,8 +38,9 @@ struct GemmLayer {
 
 struct GemmArgs {
     // ---- A operand
-    const void* a;          // T [M][lda]
+    const void* a;          // T [M][lda], or in fragment order (a_frag, weight-streaming kernel only)
     long long lda;
+    int a_frag;             // A in fragment order (afrag_offset, K columns, whole 16-row tiles)
     int M;
     int K;
     // ---- W operand and geometry
@@ -56,7 +57,8 @@ struct GemmArgs {
     int residual;
     float* ssq_out;         // EPI_STORE: [n_tiles][ssq_out_ld] sums of squares of the new rows (nullable)
     int ssq_out_ld;
-    void* out_t;            // EPI_SWIGLU: T [M][ldo]
+    void* out_t;            // EPI_SWIGLU: T [M][ldo], or in fragment order with N columns (out_frag)
+    int out_frag;
     unsigned long long* amax;   // EPI_ARGMAX: [n_tiles][M] packed (value, index) maxima
     float* dbg_logits;      // EPI_ARGMAX: nullable [B][gamma-dbg_first][N] logits of rows j >= dbg_first
     int gamma;              // EPI_ARGMAX: rows per sequence in A (block size)
@@ -145,17 +147,25 @@ __global__ __launch_bounds__(512) void gemm_kernel(const GemmArgs p) {
     const uint32_t ring_lds = lds_offset(smem) + (uint32_t)wv_u * (P * NTW * 4096);
     const char* ring = reinterpret_cast<const char*>(smem) + (size_t)wv_u * P * NTW * 4096;
 
-    // ---- A row pointers (one row per lane and M-tile)
+    // ---- A row pointers (one row per lane and M-tile) and the byte strides of a k-step
+    // and of a piece: plain rows, or fragment order (one contiguous 1 KB per piece)
     const char* arow[MT];
     bool avalid[MT];
     const void* abase = L.a ? L.a : p.a;
+    const int a_step = p.a_frag ? 4096 : 256, a_piece = p.a_frag ? 1024 : 64;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
         const int m = m0 + mt * 16 + r;
         avalid[mt] = m < p.M;
-        const int mm = avalid[mt] ? m : 0;   // padding rows read row 0; their MFMA input is zeroed
-        arow[mt] = reinterpret_cast<const char*>(reinterpret_cast<const T*>(abase) + (long long)mm * p.lda + k0 +
-                                                 g * Elem<T>::PER16);
+        if (p.a_frag) {         // tiles past the last one re-read it; their MFMA input is zeroed
+            const int tl = min((m0 >> 4) + mt, (p.M - 1) >> 4);
+            arow[mt] = reinterpret_cast<const char*>(abase) +
+                       ((((long long)tl * (K / STEP) + k0 / STEP) * 4) * 64 + lane) * 16;
+        } else {
+            const int mm = avalid[mt] ? m : 0;   // padding rows read row 0; their MFMA input is zeroed
+            arow[mt] = reinterpret_cast<const char*>(reinterpret_cast<const T*>(abase) + (long long)mm * p.lda + k0 +
+                                                     g * Elem<T>::PER16);
+        }
     }
 
     // EPI_STORE with a residual, one M-tile: the old output values do not depend
@@ -191,9 +201,9 @@ __global__ __launch_bounds__(512) void gemm_kernel(const GemmArgs p) {
                 dma_b128(wsrc[t][i] + (size_t)step * 256, ring_lds + (uint32_t)((q * NTW + t) * 4096 + i * 1024));
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-            const char* a = arow[mt] + (size_t)step * 256;
+            const char* a = arow[mt] + (size_t)step * a_step;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) vload_b128(areg[q][mt].q[i], a + i * 64);
+            for (int i = 0; i < 4; ++i) vload_b128(areg[q][mt].q[i], a + i * a_piece);
         }
     };
     // all loads of ring slot q are complete once at most `later` later steps are outstanding
@@ -331,7 +341,9 @@ __device__ void gemm_epilogue(const GemmArgs& p, const GemmLayer& L, int tile, i
                 const float gt = Ct[row * wcols + cg];
                 const float up = Ct[row * wcols + cg + 16];
                 const float h = gt / (1.0f + __expf(-gt)) * up;
-                if (n0 + co < p.N) reinterpret_cast<T*>(p.out_t)[(long long)m * p.ldo + n0 + co] = Elem<T>::from_f(h);
+                if (n0 + co < p.N)
+                    reinterpret_cast<T*>(p.out_t)[p.out_frag ? afrag_offset<T>(m, n0 + co, p.N)
+                                                             : (long long)m * p.ldo + n0 + co] = Elem<T>::from_f(h);
             }
         }
     } else if (EPI == EPI_ARGMAX) {

@@ -18,7 +18,7 @@ __global__ __launch_bounds__(256) void embed_norm_kernel(const T* __restrict__ e
                                                          const T* __restrict__ w_norm, float eps,
                                                          float* __restrict__ x, T* __restrict__ xn,
                                                          unsigned* status, unsigned long long* __restrict__ fin_best,
-                                                         int* __restrict__ fin_count, int n_fin) {
+                                                         int* __restrict__ fin_count, int n_fin, int xn_frag) {
     constexpr int EPC = 16 / (int)sizeof(T);                    // elements per 16-byte chunk
     constexpr int MAXC = EMBED_MAX_HIDDEN / EPC / 256;           // chunks per thread
     __shared__ float red[4];
@@ -71,7 +71,7 @@ __global__ __launch_bounds__(256) void embed_norm_kernel(const T* __restrict__ e
         const int k = (c * 256 + threadIdx.x) * EPC;
         if (k < H) {
             const T* wp = reinterpret_cast<const T*>(&wv[c]);
-            T* o = xn + (long long)m * H + k;
+            T* o = xn + (xn_frag ? afrag_offset<T>(m, k, H) : (long long)m * H + k);   // one 16-byte chunk
 #pragma unroll
             for (int u = 0; u < EPC; ++u) o[u] = Elem<T>::from_f(xv[c][u] * rs * Elem<T>::to_f(wp[u]));
         }
@@ -123,7 +123,7 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const float* __restri
                                                            const NormWeights wz, int K, float eps,
                                                            T* __restrict__ out, int ldo, long long out_z,
                                                            const int* __restrict__ len, int* __restrict__ len_snap,
-                                                           int n_len) {
+                                                           int n_len, int out_frag) {
     __shared__ float red[4];
     if (len_snap && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0)
         for (int b = threadIdx.x; b < n_len; b += 256) len_snap[b] = len[b];
@@ -143,7 +143,8 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const float* __restri
     __syncthreads();
     const float rs = 1.0f / sqrtf(((red[0] + red[1]) + (red[2] + red[3])) / (float)K + eps);
     if (has) {
-        T* o = out + (long long)blockIdx.z * out_z + (long long)m * ldo + k;
+        // four consecutive columns stay contiguous in fragment order (k % 4 == 0)
+        T* o = out + (long long)blockIdx.z * out_z + (out_frag ? afrag_offset<T>(m, k, K) : (long long)m * ldo + k);
         o[0] = Elem<T>::from_f(xv.x * rs * wv[0]);
         o[1] = Elem<T>::from_f(xv.y * rs * wv[1]);
         o[2] = Elem<T>::from_f(xv.z * rs * wv[2]);
