@@ -375,23 +375,30 @@ __device__ __forceinline__ void stage_issue(uint32_t stage, const T* kc, const T
     }
 }
 
-// Geometry, by the number QTW of query tiles per workgroup (1, 2, 4 or 8): KG
-// waves per tile split the chunk's keys (8 waves in all, 4 for QTW 1); every
-// key group owns a ring of ATT_RING / KG stages in LDS (128 KB in all), enough
-// for a whole 256-key chunk.  Chunk 0 builds the block's keys and values in the
+// Geometry, by the number QTW of query tiles per workgroup (1, 2, 4 or 8) and the
+// ring size RING (stages of 16 KB per workgroup): KG waves per tile split the
+// chunk's keys (8 waves in all, 4 for QTW 1); every key group owns a ring of
+// RING / KG stages in LDS.  RING 8 (128 KB) holds a whole 256-key chunk, for
+// launches with fewer workgroups than CUs; RING 4 (64 KB) for launches with many
+// (measured 2-4% faster there).  Chunk 0 builds the block's keys and values in the
 // first stage; afterwards the key-group merge reuses the space with one slot
 // (O^T, m, l of a wave) per sending wave.
 constexpr int ATT_MAX_TILES = 8;
 constexpr int ATT_MAX_WAVES = 8;
-constexpr int ATT_RING = 8;                 // stages per workgroup
-template <int QTW> struct AttGeom {
+template <int QTW, int RING> struct AttGeom {
     static constexpr int KG = QTW >= 8 ? 1 : (QTW == 4 ? 2 : 4);
     static constexpr int WAVES = QTW * KG;
-    static constexpr int R = ATT_RING / KG;     // ring stages per key group
+    static constexpr int R = RING / KG;         // ring stages per key group
     static constexpr int NPW = 16 / QTW;        // loads per wave per stage
+    static_assert(R >= 1 && RING % KG == 0, "whole stages per key group");
     static_assert((R - 1) * NPW <= 63, "vmcnt range");
 };
-static inline size_t attn_lds_bytes_host() { return (size_t)ATT_RING * ATT_STAGE_BYTES; }
+// LDS of a workgroup: the ring, which also holds chunk 0's staged inputs (up to
+// ATT_RAW_KN + 1 KB) and the key-group merge slots (at most 4 of 8.5 KB)
+static inline size_t attn_lds_bytes_host(int ring) {
+    const size_t r = (size_t)ring * ATT_STAGE_BYTES;
+    return r > (size_t)ATT_RAW_KN + 1024 ? r : (size_t)ATT_RAW_KN + 1024;
+}
 
 // Wait until at most `later` (<= MAXL) stages of NPW loads each, issued after the
 // awaited loads, are still in flight.
@@ -411,10 +418,10 @@ __device__ __forceinline__ void wait_stage(int later) {
     }
 }
 
-template <typename T, int QTW>
+template <typename T, int QTW, int RING>
 __global__ __launch_bounds__(64 * ATT_MAX_WAVES) void attn_partial_kernel(const AttnArgs a) {
     constexpr int D = WaveAttn<T>::D, DT = WaveAttn<T>::DT, PER = Elem<T>::PER16;
-    using Geo = AttGeom<QTW>;
+    using Geo = AttGeom<QTW, RING>;
     constexpr int KG = Geo::KG, R = Geo::R, NPW = Geo::NPW;
     extern __shared__ __align__(16) unsigned char smem[];
     const int c = blockIdx.x, h = blockIdx.y / a.nqs, qs = blockIdx.y % a.nqs, b = blockIdx.z;
@@ -626,7 +633,8 @@ __global__ __launch_bounds__(64 * ATT_MAX_WAVES) void attn_partial_kernel(const 
     float mt = w.m;
 
     // ---- merge the KG waves of each tile (all tiles at once; pairwise rounds)
-    const size_t slot_bytes = (size_t)DT * 4 * 64 * 4 + 2 * 64 * 4;
+    constexpr int slot_bytes = DT * 4 * 64 * 4 + 2 * 64 * 4;
+    static_assert(QTW * (KG / 2) * slot_bytes <= ATT_RAW_KN + 1024, "merge slots fit the smallest LDS size");
     for (int span = KG >> 1; span >= 1; span >>= 1) {
         __syncthreads();   // previous users of the LDS space are done
         if (kgi >= span && kgi < 2 * span) {

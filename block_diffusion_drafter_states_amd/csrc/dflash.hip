@@ -98,6 +98,14 @@ struct GemmPlan {
 };
 
 constexpr int TILED_MIN_ROWS = 128;   // from this many rows on, A is reused from LDS across 128 weight rows
+// ... except where the tiled launch would have fewer than TILED_MIN_WGS workgroups
+// while the weight-streaming one (K split inside the workgroup, each weight read once
+// per 64-row group) fits one round of STREAM_ROUND_WGS (one per CU).  Measured on
+// MI355X at 128 rows: 2048-wide projections (32 tiled blocks against 256 streaming
+// workgroups) 40 -> 24 us for W_o and 49 -> 31 us for W_down; 2560-wide ones (40
+// blocks against 320 workgroups, two rounds) stay faster tiled (38 against 41 us).
+constexpr int TILED_MIN_WGS = 128;
+constexpr int STREAM_ROUND_WGS = 256;
 
 // Geometry of one projection.  wrows = weight rows (EPI_SWIGLU: rows of each of
 // gate/up).  Every workgroup owns complete output columns (no cross-workgroup
@@ -110,32 +118,13 @@ constexpr int TILED_MIN_ROWS = 128;   // from this many rows on, A is reused fro
 // SwiGLU, two waves per 32 vocabulary rows for the LM head (weights read from
 // HBM, not from the last-level cache); one workgroup's LDS ring must fit the
 // 160 KB of a CU.
-GemmPlan plan_gemm(const Shape& s, int epi, int wrows, int K, int M, int layers) {
+GemmPlan plan_streaming(const Shape& s, int epi, int wrows, int K, int M, int layers) {
     GemmPlan p;
     p.bn = 0;
     p.kb = 0;
     p.epi = epi;
     p.layers = layers;
-    p.tiled = M >= TILED_MIN_ROWS;
-    if (p.tiled) {
-        p.ns = 1;
-        p.ks = 4;
-        p.kw = K;
-        p.mt = 8;
-        p.ntw = 0;
-        p.mgroups = cdiv(M, TG_BM);
-        p.bn = 128;
-        // 64-wide blocks when 128-wide ones would leave half the CUs idle (measured at 512 rows:
-        // down 4096 x 14336 138 -> 90 us; q|k|v 6144 x 4096, 192 blocks, 47 -> 58 us the other way)
-        if (epi != EPI_SWIGLU && cdiv(wrows, 128) * p.mgroups * layers <= 128) p.bn = 64;
-        p.n_tiles = cdiv(wrows, tg_cols(epi, p.bn));
-        // 128-byte stages (64 KB at BN 128: several workgroups per CU) pay off from ~2
-        // workgroups per CU on (measured at 512 rows: LM head 857 -> 636 us, gate|up
-        // 182 -> 143 us; with 256 workgroups they pack onto fewer CUs and lose)
-        p.kb = (long long)p.n_tiles * p.mgroups * layers >= 512 ? 128 : 256;
-        p.lds = tg_lds_bytes(p.bn, p.kb);
-        return p;
-    }
+    p.tiled = false;
     p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
     p.mgroups = cdiv(M, 16 * p.mt);
     p.ns = 1;
@@ -160,30 +149,73 @@ GemmPlan plan_gemm(const Shape& s, int epi, int wrows, int K, int M, int layers)
     return p;
 }
 
+GemmPlan plan_gemm(const Shape& s, int epi, int wrows, int K, int M, int layers) {
+    const GemmPlan ps = plan_streaming(s, epi, wrows, K, M, layers);
+    if (M < TILED_MIN_ROWS) return ps;
+    GemmPlan p = ps;
+    p.tiled = true;
+    p.ns = 1;
+    p.ks = 4;
+    p.kw = K;
+    p.mt = 8;
+    p.ntw = 0;
+    p.mgroups = cdiv(M, TG_BM);
+    p.bn = 128;
+    // 64-wide blocks when 128-wide ones would leave half the CUs idle (measured at 512 rows:
+    // down 4096 x 14336 138 -> 90 us; q|k|v 6144 x 4096, 192 blocks, 47 -> 58 us the other way)
+    if (epi != EPI_SWIGLU && cdiv(wrows, 128) * p.mgroups * layers <= 128) p.bn = 64;
+    p.n_tiles = cdiv(wrows, tg_cols(epi, p.bn));
+    const long long tiled_wgs = (long long)p.n_tiles * p.mgroups * layers;
+    if (tiled_wgs < TILED_MIN_WGS && (long long)ps.n_tiles * ps.mgroups * layers <= STREAM_ROUND_WGS) return ps;
+    // 128-byte stages (64 KB at BN 128: several workgroups per CU) pay off from ~2
+    // workgroups per CU on (measured at 512 rows: LM head 857 -> 636 us, gate|up
+    // 182 -> 143 us; with 256 workgroups they pack onto fewer CUs and lose)
+    p.kb = tiled_wgs >= 512 ? 128 : 256;
+    p.lds = tg_lds_bytes(p.bn, p.kb);
+    return p;
+}
+
 // Attention launch shape: a workgroup takes QTW query tiles (the next power of
 // two >= the tiles of one (b, h), at most ATT_MAX_TILES) of one (b, h, chunk).
+// The ring is 8 stages unless the launch has at least ATT_SMALL_RING_WGS
+// workgroups, when 4-stage rings are used.
+constexpr long long ATT_SMALL_RING_WGS = 512;
+
 struct AttnPlan {
-    int qtw, nqs;
+    int qtw, nqs, ring;
 };
 
-AttnPlan plan_attn(const Shape& s, int gamma) {
+AttnPlan plan_attn(const Shape& s, int gamma, int batch) {
     AttnPlan a;
     const int qt = cdiv(s.group * gamma, 16);
     a.qtw = 1;
     while (a.qtw < qt && a.qtw < ATT_MAX_TILES) a.qtw *= 2;
     a.nqs = cdiv(qt, a.qtw);
+    a.ring = (long long)s.nch_max * s.nkv * a.nqs * batch >= ATT_SMALL_RING_WGS ? 4 : 8;
     return a;
+}
+
+template <typename T, int QTW, int RING>
+void launch_attention_k(const AttnArgs& a, dim3 grid, hipStream_t st) {
+    hipLaunchKernelGGL((attn_partial_kernel<T, QTW, RING>), grid, dim3(64 * AttGeom<QTW, RING>::WAVES),
+                       attn_lds_bytes_host(RING), st, a);
+}
+
+template <typename T, int QTW>
+void launch_attention_q(const AttnArgs& a, const AttnPlan& ap, dim3 grid, hipStream_t st) {
+    if (ap.ring == 4) launch_attention_k<T, QTW, 4>(a, grid, st);
+    else launch_attention_k<T, QTW, 8>(a, grid, st);
 }
 
 template <typename T>
 int launch_attention(const AttnArgs& a, const AttnPlan& ap, int nch_max, int nkv, int batch, hipStream_t st) {
     const dim3 grid(nch_max, nkv * ap.nqs, batch);
-    const size_t lds = attn_lds_bytes_host();
+    if (ap.ring != 4 && ap.ring != 8) return DFLASH_EINVAL;
     switch (ap.qtw) {
-        case 1: hipLaunchKernelGGL((attn_partial_kernel<T, 1>), grid, dim3(64 * AttGeom<1>::WAVES), lds, st, a); break;
-        case 2: hipLaunchKernelGGL((attn_partial_kernel<T, 2>), grid, dim3(64 * AttGeom<2>::WAVES), lds, st, a); break;
-        case 4: hipLaunchKernelGGL((attn_partial_kernel<T, 4>), grid, dim3(64 * AttGeom<4>::WAVES), lds, st, a); break;
-        case 8: hipLaunchKernelGGL((attn_partial_kernel<T, 8>), grid, dim3(64 * AttGeom<8>::WAVES), lds, st, a); break;
+        case 1: launch_attention_q<T, 1>(a, ap, grid, st); break;
+        case 2: launch_attention_q<T, 2>(a, ap, grid, st); break;
+        case 4: launch_attention_q<T, 4>(a, ap, grid, st); break;
+        case 8: launch_attention_q<T, 8>(a, ap, grid, st); break;
         default: return DFLASH_EINVAL;
     }
     return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_ELAUNCH;
@@ -501,7 +533,7 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
     if (hipGetLastError() != hipSuccess) return DFLASH_ELAUNCH;
     int n_ssq = 0;      // per-tile partial sums of squares of x (written by o / down)
 
-    const AttnPlan ap = plan_attn(s, gamma);
+    const AttnPlan ap = plan_attn(s, gamma, batch);
     const size_t layer_elems = (size_t)s.Bmax * s.nkv * s.cap * s.D;
 
     for (int l = 0; l < s.L; ++l) {

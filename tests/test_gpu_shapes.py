@@ -1,5 +1,6 @@
 """GPU parity on launch shapes the small cases do not reach: several 64-row GEMM
-groups with ragged context lengths (serving concurrency), GQA group 8 at a
+groups with ragged context lengths (serving concurrency), attention launches with
+enough workgroups for the small LDS rings, GQA group 8 at a
 32k-token context with a block size that changes per cycle (long chain-of-thought
 drafting), and the Qwen3-8B-shaped drafter at full size in the launch
 configuration the benchmark times.  Same bars as the other parity tests."""
@@ -22,10 +23,25 @@ MB = synth.Config("mb_bf16", "bf16", hidden=512, n_q=4, n_kv=2, head_dim=128, in
 # 32 q / 4 kv heads (128 query rows per kv head at gamma 16), 32768-token context
 LC = synth.Config("longctx_g8_bf16", "bf16", hidden=512, n_q=32, n_kv=4, head_dim=128, inter=1024,
                   n_layers=2, n_feat=2, vocab=1000, gamma=16, ctx=32768, batch=2, gammas=(16, 8), index=80)
+# 8 sequences x 4 kv heads (group 2) at contexts up to 4095: 576 attention workgroups, so
+# the 4-stage LDS rings (two workgroups per CU) with 2 query tiles (gamma 16) and 1
+# (gamma 8, 4) per workgroup
+MR = synth.Config("ring4_bf16", "bf16", hidden=512, n_q=8, n_kv=4, head_dim=128, inter=1024,
+                  n_layers=2, n_feat=2, vocab=1000, gamma=16, ctx=4095, batch=8, index=82)
+# 8 sequences x 16 kv heads (group 4) at contexts up to 8000: 1024-key attention chunks
+# (lengths on both sides of a chunk boundary) in 4-stage rings, with 4 query tiles per
+# workgroup at gamma 16, 3 at gamma 11 (the fourth tile is empty), 2 at gamma 6
+# (a partly filled tile) and 1 at gamma 3
+MT = synth.Config("long_chunks_bf16", "bf16", hidden=512, n_q=64, n_kv=16, head_dim=128, inter=1024,
+                  n_layers=1, n_feat=2, vocab=1000, gamma=16, ctx=8000, batch=8, index=83)
 
 
 def test_batch_of_five_ragged_row_groups():
     run_cycle_case(MB, 5, [0, 1, 300, 63, 257], [16, 2, 9], gen.kv_capacity(MB, 64), "mb")
+
+
+def test_many_attention_workgroups_small_rings():
+    run_cycle_case(MR, 8, [0, 1, 31, 257, 1000, 2047, 3000, 4095], [16, 8, 4], gen.kv_capacity(MR, 64), "mr")
 
 
 def _draft_inject_cycles(P, gammas, tag):
@@ -63,6 +79,16 @@ def test_long_context_group8_dynamic_block():
         ev = rel_err(v[:, b, :, c0:lens[b]], P.okv.v[:, b, :, c0:lens[b]])
         log(f"  seq {b} injected rows {c0}..{lens[b]} k={ek:.3e} v={ev:.3e}")
         assert ek < tol(cfg) and ev < tol(cfg)
+
+
+def test_long_chunks_ragged_tiles():
+    cfg = MT
+    cap = gen.kv_capacity(cfg, 64)
+    lengths = [8000, 1, 0, 1023, 1024, 1025, 5000, 7777]
+    log(f"case {cfg.name} lengths={lengths} cap={cap}")
+    P = Pair(cfg, 8, cap, 16)
+    P.set_context(lengths, tag="mt")
+    _draft_inject_cycles(P, [16, 11, 6, 3], "mt")
 
 
 def test_qwen3_8b_shape_full_size():
