@@ -24,6 +24,7 @@ import argparse
 import ctypes
 import hashlib
 import json
+import math
 import os
 import statistics
 import sys
@@ -208,6 +209,49 @@ def prefill(args, dfl, cfg, gen, torch):
                                    "frac": round(tflops / peak, 4), "gflop": round(flops / 1e9, 1)}}), flush=True)
 
 
+def block_loss_leg(args, dfl, cfg, gen, torch):
+    """The drafter's training objective over one batch of blocks (position-weighted block
+    cross-entropy): the drafting forward pass with a log-sum-exp LM-head epilogue instead of
+    the argmax, timed beside the drafting pass itself on the same inputs."""
+    B, gamma = args.batch, cfg.gamma
+    cfg = cfg.with_(batch=B)
+    lengths = gen.context_lengths(cfg)
+    cap = (int(lengths.max()) + 2 * cfg.gamma_max + 63) // 64 * 64
+    W = gen.weights(cfg)
+    model = dfl.Model(cfg, W, device="cuda", max_batch=B, kv_capacity=cap)
+    cache = dfl.Cache(model)
+    Kc, Vc = gen.context_kv(cfg, lengths, int(lengths.max()), tag="bench.ctx")
+    cache.set_context(Kc, Vc, lengths)
+    ws = dfl.Workspace(model, B, gamma)
+    anchor = torch.as_tensor(gen.tokens(cfg, "bench.loss.anchor", (B,)), device="cuda")
+    labels = torch.as_tensor(gen.tokens(cfg, "bench.loss.labels", (B, gamma - 1)), device="cuda")
+    loss = torch.zeros((1,), dtype=torch.float32, device="cuda")
+    draft = torch.zeros((B, gamma - 1), dtype=torch.int32, device="cuda")
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1000.0 / args.steps
+
+    us_loss = timed(lambda: dfl.block_loss(model, cache, gamma, anchor, labels, loss, ws))
+    us_draft = timed(lambda: dfl.draft_block(model, cache, gamma, anchor, draft, ws))
+    assert int(cache.status.item()) == 0 and math.isfinite(float(loss.item()))
+    print(json.dumps({"metric": "block loss evaluations/s", "value": round(1e6 / us_loss, 2), "unit": "blocks-batches/s",
+                      "higher_is_better": True, "steps": args.steps, "warmup": args.warmup, "dtype": cfg.dtype,
+                      "us_per_call": round(us_loss, 1), "draft_block_us_per_call": round(us_draft, 1),
+                      "loss": float(loss.item()),
+                      "config": {"workload": f"{cfg.name}: {SHAPES.get(cfg.name, cfg.name)}, batch {B}, gamma {gamma}, "
+                                             f"context {int(lengths.mean())}", "batch": B, "gamma": gamma}}),
+          flush=True)
+
+
 def target_verify(args, dfl, cfg, gen, torch):
     """The verifying target's forward over one block: a Qwen3-8B-shaped target (the drafter's
     layer recipe, 36 layers, untied LM head) checks anchor + gamma-1 drafts at context C, keeping
@@ -297,6 +341,8 @@ def main():
                     help="time the injection of a whole context's feature rows instead of the cycle")
     ap.add_argument("--target", action="store_true",
                     help="time the verifying target's forward over one block (36-layer target of the config's shape)")
+    ap.add_argument("--loss", action="store_true",
+                    help="time the drafter's position-weighted block cross-entropy beside the drafting pass")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device 5 times (a plain copy kernel of known size, "
                          "to calibrate rocprofv3 FETCH_SIZE / WRITE_SIZE) and exit")
@@ -339,6 +385,9 @@ def main():
         return
     if args.target:
         target_verify(args, dfl, cfg, gen, torch)
+        return
+    if args.loss:
+        block_loss_leg(args, dfl, cfg, gen, torch)
         return
     B = args.batch
     cfg = cfg.with_(batch=B)

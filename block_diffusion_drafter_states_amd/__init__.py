@@ -216,6 +216,26 @@ def draft_block(model: Model, cache: Cache, gamma: int, anchor, draft, ws: Works
                                    ws.ptr(), ws.nbytes, _stream_ptr(stream)), "dflash_draft_block")
 
 
+def block_loss(model: Model, cache: Cache, gamma: int, anchor, labels, loss, ws: Workspace, row_loss=None,
+               dbg_logits=None, stream=None) -> None:
+    """The drafter's weighted block cross-entropy: anchor int32 [B], labels int32 [B][gamma-1]
+    -> loss fp32 [1] (weights exp(-(j-1)/gamma) on mask row j), row_loss fp32 [B][gamma-1]."""
+    torch = _torch()
+    batch = anchor.shape[0]
+    _need(anchor, "anchor", torch.int32, (batch,))
+    _need(labels, "labels", torch.int32, (batch, gamma - 1))
+    _need(loss, "loss", torch.float32, (1,))
+    if row_loss is not None:
+        _need(row_loss, "row_loss", torch.float32, (batch, gamma - 1))
+    if dbg_logits is not None:
+        _need(dbg_logits, "dbg_logits", torch.float32, (batch, gamma - 1, model.cfg.vocab))
+    check(lib().dflash_block_loss(ctypes.byref(model.c), ctypes.byref(model.w), ctypes.byref(cache.s), batch,
+                                  gamma, anchor.data_ptr(), labels.data_ptr(), loss.data_ptr(),
+                                  None if row_loss is None else row_loss.data_ptr(),
+                                  None if dbg_logits is None else dbg_logits.data_ptr(),
+                                  ws.ptr(), ws.nbytes, _stream_ptr(stream)), "dflash_block_loss")
+
+
 def verify(draft, target, accept_len, committed, next_anchor, stream=None) -> None:
     """draft int32 [B][gamma-1], target int32 [B][gamma] -> accept_len [B], committed [B][gamma], next_anchor [B]."""
     torch = _torch()

@@ -44,6 +44,7 @@ inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 inline int pad16(int m) { return cdiv(m, 16) * 16; }
 
 constexpr int MAX_GAMMA = 16;     // block rows: one 16-row MFMA tile per (sequence, q head)
+constexpr int LSE_MAX_SLICES = 256; // block loss: slices of the LM-head tiles folded per row in stage 1
 
 struct Shape {
     int H, nq, nkv, D, I, L, F, V, gmax, mask, Bmax, cap, esize, step, group, rpad, chunk, nch_max;
@@ -130,7 +131,7 @@ GemmPlan plan_streaming(const Shape& s, int epi, int wrows, int K, int M, int la
     p.ns = 1;
     p.ntw = 2;
     int ks;
-    if (epi == EPI_ARGMAX) {
+    if (epi == EPI_ARGMAX || epi == EPI_LSE) {
         ks = 2;
     } else if (epi == EPI_SWIGLU) {
         ks = 4;
@@ -244,7 +245,7 @@ DraftPlans draft_plans(const Shape& s, int M) {
 // is per-call scratch: no state survives a call.
 struct Layout {
     // draft
-    size_t x, ssq_x, qkv, opart, mlpart, obuf, hbuf, amax, fin_best, fin_count, nbuf, draft_end;
+    size_t x, ssq_x, qkv, opart, mlpart, obuf, hbuf, amax, fin_best, fin_count, nbuf, lse_part, lab, draft_end;
     int ssq_x_tiles, amax_tiles;
     // inject
     size_t c, ssq_c, cnorm, kvraw, lensnap, inject_end;
@@ -273,6 +274,8 @@ Layout make_layout(const Shape& s, int batch, int rows) {
     l.fin_best = take(M * 8);                                 // per draft row: running argmax, slices done
     l.fin_count = take(M * 4);
     l.nbuf = take(Mp * s.H * s.esize);                        // RMSNorm-ed rows (GEMM A operand)
+    l.lse_part = take((size_t)LSE_MAX_SLICES * M * 8);        // block loss: per-slice (max, sum exp)
+    l.lab = take(M * 4);                                      // block loss: the label's logit per row
     l.draft_end = off;
     l.c = l.ssq_c = l.cnorm = l.kvraw = l.lensnap = 0;
     l.ssq_c_tiles = 0;
@@ -336,6 +339,9 @@ int gemm_dispatch(const GemmArgs& a, const GemmPlan& p, hipStream_t st, Tracer& 
             case EPI_ARGMAX:
                 return wide ? launch_gemm_tiled<T, EPI_ARGMAX, 128>(a, p, st, tr, name)
                             : launch_gemm_tiled<T, EPI_ARGMAX, 64>(a, p, st, tr, name);
+            case EPI_LSE:
+                return wide ? launch_gemm_tiled<T, EPI_LSE, 128>(a, p, st, tr, name)
+                            : launch_gemm_tiled<T, EPI_LSE, 64>(a, p, st, tr, name);
         }
         return DFLASH_EINVAL;
     }
@@ -348,6 +354,7 @@ int gemm_dispatch(const GemmArgs& a, const GemmPlan& p, hipStream_t st, Tracer& 
                               : launch_gemm_mt<T, EPI_STORE, 2>(a, p, st, tr, name);
         case EPI_SWIGLU: return launch_gemm_mt<T, EPI_SWIGLU, 2>(a, p, st, tr, name);
         case EPI_ARGMAX: return launch_gemm_mt<T, EPI_ARGMAX, 2>(a, p, st, tr, name);
+        case EPI_LSE: return launch_gemm_mt<T, EPI_LSE, 2>(a, p, st, tr, name);
     }
     return DFLASH_EINVAL;
 }
@@ -495,6 +502,9 @@ struct PassMode {
     int n_taps;
     void* feat;
     int first_row;          // argmax rows: 1 (drafts) or 0 (every row)
+    const int* labels;      // nullable: [batch][gamma-1] labels of the mask rows -> block loss instead of drafts
+    float* loss;            // with labels: [1] weighted mean cross-entropy
+    float* row_loss;        // with labels: nullable [batch][gamma-1] cross-entropy per mask row
 };
 
 constexpr PassMode DRAFT_PASS = {nullptr, 0, 0, nullptr, 0, nullptr, 1};
@@ -676,8 +686,11 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
         tr.end();
         if (hipGetLastError() != hipSuccess) return DFLASH_ELAUNCH;
     }
-    {   // final norm -> LM head -> per-tile argmax
-        GemmArgs a = gemm_base(s, pl.lm, M, s.H);
+    {   // final norm -> LM head -> per-tile argmax (or log-sum-exp and label logits)
+        const bool loss = md.labels != nullptr;
+        const GemmPlan plm = loss ? plan_gemm(s, EPI_LSE, s.V, s.H, M, 1) : pl.lm;
+        if (plm.n_tiles != pl.lm.n_tiles) return DFLASH_EUNSUPPORTED;   // same geometry as the argmax plan
+        GemmArgs a = gemm_base(s, plm, M, s.H);
         if ((rc = set_norm_a<T>(a, s, x, M, ssq_x, n_ssq, w->final_norm, nbuf, afrag, st, tr))) return rc;
         a.N = s.V;
         a.seg_end[0] = a.seg_end[1] = a.seg_end[2] = s.V;
@@ -686,10 +699,30 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
         a.amax = amax;
         a.dbg_logits = dbg_logits;
         a.dbg_first = md.first_row;
-        if ((rc = gemm_dispatch<T>(a, pl.lm, st, tr, "lm_head_argmax"))) return rc;
+        if (loss) {
+            a.lse = reinterpret_cast<float2*>(amax);     // the same [n_tiles][M] 8-byte slots
+            a.labels = md.labels;
+            a.lab_logit = reinterpret_cast<float*>(wsb + lay.lab);
+        }
+        if ((rc = gemm_dispatch<T>(a, plm, st, tr, loss ? "lm_head_lse" : "lm_head_argmax"))) return rc;
+    }
+    const int row_blocks = cdiv(M, 64);
+    if (md.labels) {
+        const int n_slices = std::max(1, std::min({pl.lm.n_tiles, 256 / row_blocks, LSE_MAX_SLICES}));
+        float2* part = reinterpret_cast<float2*>(wsb + lay.lse_part);
+        tr.begin("lse_slices");
+        hipLaunchKernelGGL(lse_slices_kernel, dim3(n_slices, row_blocks), dim3(256), 0, st,
+                           reinterpret_cast<const float2*>(amax), pl.lm.n_tiles, n_slices, M, part);
+        tr.end();
+        if (hipGetLastError() != hipSuccess) return DFLASH_ELAUNCH;
+        tr.begin("block_loss");
+        hipLaunchKernelGGL(block_loss_kernel, dim3(1), dim3(BLOCK_LOSS_THREADS), 0, st, part, n_slices, M, gamma,
+                           md.labels, reinterpret_cast<const float*>(wsb + lay.lab), s.V, md.loss, md.row_loss,
+                           kv->status);
+        tr.end();
+        return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_ELAUNCH;
     }
     tr.begin("argmax_finish");
-    const int row_blocks = cdiv(M, 64);
     const int n_slices = std::max(1, std::min(pl.lm.n_tiles, 256 / row_blocks));
     hipLaunchKernelGGL(argmax_finish_kernel, dim3(n_slices, row_blocks), dim3(256), 0, st, amax, pl.lm.n_tiles,
                        n_slices, M, gamma, md.first_row, fin_best, fin_count, draft);
@@ -768,6 +801,31 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, const 
                        void* workspace, size_t workspace_bytes, void* stream) {
     return dflash_draft_block_traced(cfg, w, kv, batch, gamma, anchor, draft, dbg_hidden, dbg_logits, workspace,
                                      workspace_bytes, stream, nullptr);
+}
+
+int dflash_block_loss(const dflash_config* cfg, const dflash_weights* w, const dflash_kv* kv, int32_t batch,
+                      int32_t gamma, const int32_t* anchor, const int32_t* labels, float* loss, float* row_loss,
+                      float* dbg_logits, void* workspace, size_t workspace_bytes, void* stream) {
+    Shape s;
+    int rc = make_shape(cfg, s);
+    if (rc) return rc;
+    if (!w || !kv || !anchor || !labels || !loss || !kv->k || !kv->v || !kv->len || !kv->status) return DFLASH_EINVAL;
+    if (!weights_ok(s, w, false)) return DFLASH_EINVAL;
+    if (batch < 1 || batch > s.Bmax || gamma < 2 || gamma > s.gmax) return DFLASH_EINVAL;
+    if (w->rope_rows < s.cap + s.gmax) return DFLASH_EINVAL;
+    if (!workspace) return DFLASH_EWORKSPACE;
+    const Layout lay = make_layout(s, batch, 0);
+    if (workspace_bytes < lay.draft_end) return DFLASH_EWORKSPACE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    Tracer tr{nullptr, st};
+    PassMode md = DRAFT_PASS;
+    md.labels = labels;
+    md.loss = loss;
+    md.row_loss = row_loss;
+    return s.bf16 ? run_draft<bf16_t>(s, w, kv, batch, gamma, anchor, nullptr, nullptr, dbg_logits, workspace, lay,
+                                      st, tr, md)
+                  : run_draft<float>(s, w, kv, batch, gamma, anchor, nullptr, nullptr, dbg_logits, workspace, lay,
+                                     st, tr, md);
 }
 
 int dflash_verify(int32_t batch, int32_t gamma, const int32_t* draft, const int32_t* target, int32_t* accept_len,

@@ -26,7 +26,7 @@
 
 namespace dflash {
 
-enum { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_ARGMAX = 2 };
+enum { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_ARGMAX = 2, EPI_LSE = 3 };
 
 constexpr int MAX_LAYERS = 16;
 
@@ -61,8 +61,11 @@ struct GemmArgs {
     int out_frag;
     unsigned long long* amax;   // EPI_ARGMAX: [n_tiles][M] packed (value, index) maxima
     float* dbg_logits;      // EPI_ARGMAX: nullable [B][gamma-dbg_first][N] logits of rows j >= dbg_first
-    int gamma;              // EPI_ARGMAX: rows per sequence in A (block size)
+    int gamma;              // EPI_ARGMAX / EPI_LSE: rows per sequence in A (block size)
     int dbg_first;
+    float2* lse;            // EPI_LSE: [n_tiles][M] per tile (max logit, sum of exp(logit - max))
+    const int* labels;      // EPI_LSE: [B][gamma-1] label ids of rows j >= 1
+    float* lab_logit;       // EPI_LSE: [M] logit of row m's label (written by the tile holding it)
 };
 
 // Ring depth (k-steps in flight): the weights live in LDS; the registers of a
@@ -321,8 +324,11 @@ __global__ __launch_bounds__(512) void gemm_kernel(const GemmArgs p) {
 }
 
 // --------------------------------------------------------------------------------------------
-// SwiGLU and argmax epilogues: one wavefront per output row (rows strided over the waves).
+// SwiGLU, argmax and log-sum-exp epilogues: one wavefront per output row (rows strided
+// over the waves).
 // (The store epilogue is element-parallel, in the kernel.)
+
+__device__ __forceinline__ int nthreads_epi(int threads, int lpr) { return threads / lpr; }
 
 template <typename T, int EPI>
 __device__ void gemm_epilogue(const GemmArgs& p, const GemmLayer& L, int tile, int m0, int mrows, int wcols,
@@ -346,29 +352,62 @@ __device__ void gemm_epilogue(const GemmArgs& p, const GemmLayer& L, int tile, i
                                                              : (long long)m * p.ldo + n0 + co] = Elem<T>::from_f(h);
             }
         }
-    } else if (EPI == EPI_ARGMAX) {
+    } else if (EPI == EPI_ARGMAX || EPI == EPI_LSE) {
+        // element-parallel: a row's wcols columns are spread over LPR consecutive lanes
+        // (EPT consecutive columns each), all rows of the tile at once; the lanes of a row
+        // combine with xor shuffles (a fixed order)
+        constexpr int LPR = 8;
+        const int ept = wcols / LPR;
         const int n0 = tile * wcols;
         const int G = p.gamma;
-        for (int row = wv; row < mrows; row += nwaves) {
+        const int sub = threadIdx.x % LPR;
+        for (int row = threadIdx.x / LPR; row < ((mrows + 15) & ~15); row += nthreads_epi(blockDim.x, LPR)) {
             const int m = m0 + row;
+            const bool live = row < mrows;
             const int b = m / G, jj = m % G;
-            unsigned long long best = 0ull;
-            for (int c = lane; c < wcols; c += 64) {
-                const int n = n0 + c;
-                if (n < p.N) {
-                    const float v = Ct[row * wcols + c];
-                    const unsigned long long key = pack_argmax(v, (uint32_t)n);
-                    best = key > best ? key : best;
-                    if (p.dbg_logits && jj >= p.dbg_first)
-                        p.dbg_logits[((long long)b * (G - p.dbg_first) + (jj - p.dbg_first)) * p.N + n] = v;
+            const bool dbg = live && p.dbg_logits && jj >= p.dbg_first;
+            if (EPI == EPI_ARGMAX) {
+                unsigned long long best = 0ull;
+                for (int e = 0; e < ept; ++e) {
+                    const int c = sub * ept + e, n = n0 + c;
+                    if (live && n < p.N) {
+                        const float v = Ct[row * wcols + c];
+                        const unsigned long long key = pack_argmax(v, (uint32_t)n);
+                        best = key > best ? key : best;
+                        if (dbg) p.dbg_logits[((long long)b * (G - p.dbg_first) + (jj - p.dbg_first)) * p.N + n] = v;
+                    }
                 }
-            }
 #pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) {
-                const unsigned long long other = __shfl_xor(best, o, WAVE);
-                best = other > best ? other : best;
+                for (int o = 1; o < LPR; o <<= 1) {
+                    const unsigned long long other = __shfl_xor(best, o, WAVE);
+                    best = other > best ? other : best;
+                }
+                if (live && sub == 0) p.amax[(long long)tile * p.M + m] = best;
+            } else {
+                // the tile's largest logit mx and sum of exp(logit - mx); the lane holding
+                // the row's label column stores its logit
+                const int lab = (live && jj >= 1) ? p.labels[b * (G - 1) + jj - 1] : -1;
+                float mx = -INFINITY;
+                for (int e = 0; e < ept; ++e) {
+                    const int c = sub * ept + e, n = n0 + c;
+                    if (live && n < p.N) {
+                        const float v = Ct[row * wcols + c];
+                        mx = fmaxf(mx, v);
+                        if (n == lab) p.lab_logit[m] = v;
+                        if (dbg) p.dbg_logits[((long long)b * (G - p.dbg_first) + (jj - p.dbg_first)) * p.N + n] = v;
+                    }
+                }
+#pragma unroll
+                for (int o = 1; o < LPR; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, WAVE));
+                float se = 0.f;
+                for (int e = 0; e < ept; ++e) {
+                    const int c = sub * ept + e;
+                    if (live && n0 + c < p.N) se += __expf(Ct[row * wcols + c] - mx);
+                }
+#pragma unroll
+                for (int o = 1; o < LPR; o <<= 1) se += __shfl_xor(se, o, WAVE);
+                if (live && sub == 0) p.lse[(long long)tile * p.M + m] = make_float2(mx, se);
             }
-            if (lane == 0) p.amax[(long long)tile * p.M + m] = best;
         }
     }
 }
@@ -422,6 +461,95 @@ __global__ __launch_bounds__(256) void argmax_finish_kernel(const unsigned long 
             __threadfence();
             draft[i] = (int)unpack_argmax_index(atomicMax(best + i, 0ull));
         }
+    }
+}
+
+}  // namespace dflash
+
+namespace dflash {
+
+// ---- block loss: cross-entropy of the mask rows against their labels, weighted per
+// block position ("DFlash" technical summary, section 2.3, loss weighting: the weight of
+// block position k is exp(-(k - 1) / gamma), early positions count more).
+//
+// Stage 1.  lse is [n_tiles][M] (max logit, sum of exp(logit - max)) per LM-head tile.
+// Workgroup (s, rb) folds slice s of n_slices of the tiles for the 64 rows rb*64 ..
+// +63 (one row per lane; wave w takes tiles s0 + w, s0 + w + 4, ... in ascending
+// order, so every read is 64 consecutive pairs) and writes part[s][m]: the four waves
+// are combined through LDS in wave order.  Deterministic: fixed orders throughout.
+__device__ __forceinline__ float2 lse_fold(float2 acc, float2 t) {
+    if (t.x == -INFINITY) return acc;
+    if (acc.x == -INFINITY) return t;
+    const float mx = fmaxf(acc.x, t.x);
+    return make_float2(mx, acc.y * __expf(acc.x - mx) + t.y * __expf(t.x - mx));
+}
+
+__global__ __launch_bounds__(256) void lse_slices_kernel(const float2* __restrict__ lse, int n_tiles, int n_slices,
+                                                         int M, float2* __restrict__ part) {
+    __shared__ float2 red[4][64];
+    const int s = blockIdx.x;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int m = blockIdx.y * 64 + lane;
+    const int per = (n_tiles + n_slices - 1) / n_slices;
+    const int t0 = s * per, t1 = min(n_tiles, t0 + per);
+    float2 acc = make_float2(-INFINITY, 0.f);
+    if (m < M)
+        for (int t = t0 + w; t < t1; t += 4) acc = lse_fold(acc, lse[(long long)t * M + m]);
+    red[w][lane] = acc;
+    __syncthreads();
+    if (threadIdx.x < 64 && m < M) {
+        float2 x = red[0][lane];
+        for (int k = 1; k < 4; ++k) x = lse_fold(x, red[k][lane]);
+        part[(long long)s * M + m] = x;
+    }
+}
+
+// Stage 2 (one workgroup of BLOCK_LOSS_THREADS threads, one wavefront per row at a
+// time).  Row m = b*gamma + j with j >= 1: the lanes fold the slices s = lane, lane +
+// 64, ... in ascending order and an xor-shuffle tree combines the lanes; LSE - logit
+// of the label is the row's CE; row_loss[b][j-1] = CE (nullable); loss[0] = sum_b
+// sum_j w_j CE / (batch * sum_j w_j) with w_j = exp(-(j - 1) / gamma), each wave
+// summing its rows in ascending order and the waves summed in wave order.  A label
+// outside [0, vocab) sets STATUS_BAD_TOKEN and makes its row (and the total) NaN.
+constexpr int BLOCK_LOSS_THREADS = 1024;
+
+__global__ __launch_bounds__(BLOCK_LOSS_THREADS) void block_loss_kernel(
+    const float2* __restrict__ part, int n_slices, int M, int gamma, const int* __restrict__ labels,
+    const float* __restrict__ lab_logit, int vocab, float* __restrict__ loss, float* __restrict__ row_loss,
+    unsigned* status) {
+    constexpr int NW = BLOCK_LOSS_THREADS / 64;
+    __shared__ float red[NW];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int G = gamma;
+    float acc = 0.f;
+    for (int m = wv; m < M; m += NW) {
+        const int b = m / G, j = m % G;
+        if (j == 0) continue;
+        const int lab = labels[b * (G - 1) + j - 1];
+        float ce;
+        if (lab < 0 || lab >= vocab) {
+            if (lane == 0) atomicOr(status, STATUS_BAD_TOKEN);
+            ce = __int_as_float(0x7fc00000);
+        } else {
+            float2 x = make_float2(-INFINITY, 0.f);
+            for (int sl = lane; sl < n_slices; sl += 64) x = lse_fold(x, part[(long long)sl * M + m]);
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const float2 y = make_float2(__shfl_xor(x.x, o, WAVE), __shfl_xor(x.y, o, WAVE));
+                x = lse_fold(x, y);
+            }
+            ce = x.x + logf(x.y) - lab_logit[m];
+        }
+        if (lane == 0 && row_loss) row_loss[b * (G - 1) + j - 1] = ce;
+        acc += expf(-(float)(j - 1) / (float)G) * ce;
+    }
+    if (lane == 0) red[wv] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float tot = 0.f, wsum = 0.f;
+        for (int k = 0; k < NW; ++k) tot += red[k];
+        for (int j = 1; j < G; ++j) wsum += expf(-(float)(j - 1) / (float)G);
+        loss[0] = tot / ((float)(M / G) * wsum);
     }
 }
 

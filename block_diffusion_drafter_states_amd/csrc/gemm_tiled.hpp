@@ -116,6 +116,52 @@ __device__ __forceinline__ void tg_epilogue(const GemmArgs& p, const GemmLayer& 
                         reinterpret_cast<T*>(p.out_t)[(long long)m * p.ldo + n] = Elem<T>::from_f(h);
                     }
                 }
+    } else if constexpr (EPI == EPI_LSE) {
+        // per row: largest logit and sum of exp(logit - max) over this wave's columns (16
+        // lanes: xor shuffles), then over the two wn waves through LDS; the lane holding
+        // the row's label column stores its logit
+        float2* redl = reinterpret_cast<float2*>(smem);
+        const int G = p.gamma;
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int mr = wm * 64 + a * 16 + 4 * g + v;
+                const int m = m0 + mr;
+                const int bb = m / G, jj = m % G;
+                const int lab = (m < p.M && jj >= 1) ? p.labels[bb * (G - 1) + jj - 1] : -1;
+                float mx = -INFINITY;
+#pragma unroll
+                for (int b = 0; b < WN; ++b) {
+                    const int n = tile * BN + wn * (BN / 2) + b * 16 + r;
+                    if (m < p.M && n < p.N) {
+                        const float x = acc[a][b][v];
+                        mx = fmaxf(mx, x);
+                        if (n == lab) p.lab_logit[m] = x;
+                        if (p.dbg_logits && jj >= p.dbg_first)
+                            p.dbg_logits[((long long)bb * (G - p.dbg_first) + (jj - p.dbg_first)) * p.N + n] = x;
+                    }
+                }
+#pragma unroll
+                for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, WAVE));
+                float se = 0.f;
+#pragma unroll
+                for (int b = 0; b < WN; ++b) {
+                    const int n = tile * BN + wn * (BN / 2) + b * 16 + r;
+                    if (m < p.M && n < p.N) se += __expf(acc[a][b][v] - mx);
+                }
+#pragma unroll
+                for (int o = 1; o < 16; o <<= 1) se += __shfl_xor(se, o, WAVE);
+                if (r == 0) redl[wn * TG_BM + mr] = make_float2(mx, se);
+            }
+        __syncthreads();
+        if (threadIdx.x < TG_BM && m0 + (int)threadIdx.x < p.M) {
+            const float2 x0 = redl[threadIdx.x], x1 = redl[TG_BM + threadIdx.x];
+            const float mx = fmaxf(x0.x, x1.x);
+            const float se = (x0.x == -INFINITY ? 0.f : x0.y * __expf(x0.x - mx)) +
+                             (x1.x == -INFINITY ? 0.f : x1.y * __expf(x1.x - mx));
+            p.lse[(long long)tile * p.M + m0 + threadIdx.x] = make_float2(mx, se);
+        }
     } else {    // EPI_ARGMAX
         unsigned long long* redu = reinterpret_cast<unsigned long long*>(smem);
         const int G = p.gamma;

@@ -257,6 +257,27 @@ int dflash_choose_gamma(const int32_t *tau, const int32_t *gamma_used, int32_t n
                         int32_t gamma_min, int32_t gamma_max, double prior_p, double prior_weight,
                         int32_t *gamma_out, double *p_out);
 
+/* Training objective of the drafter (summary section 2.3, loss weighting):
+ * the drafter's forward pass exactly as dflash_draft_block (same anchor, mask
+ * rows and context), then, for each mask row j = 1 .. gamma-1 of sequence b,
+ * the cross-entropy CE[b][j] = logsumexp(logits) - logit[label] against
+ * labels[b][j-1] (the target's token at block position j), weighted by block
+ * position: w_j = exp(-(j - 1) / gamma), so early positions count most;
+ *   loss[0] = sum_b sum_j w_j CE[b][j] / (batch * sum_j w_j).
+ *   labels      int32 [batch][gamma-1], each in [0, vocab)
+ *   loss        fp32 [1]
+ *   row_loss    nullable fp32 [batch][gamma-1]: CE[b][j]
+ *   dbg_logits  nullable fp32 [batch][gamma-1][V]: logits of the mask rows
+ * The block's K/V are not written, len is not changed.  A label outside
+ * [0, vocab) sets DFLASH_STATUS_BAD_TOKEN and makes its row's CE and loss NaN.
+ * Sums run in fixed orders: the result is deterministic.  Forward only (no
+ * gradients).  Workspace: dflash_workspace_bytes(cfg, batch, 0); argument
+ * errors as for dflash_draft_block. */
+int dflash_block_loss(const dflash_config *cfg, const dflash_weights *w, const dflash_kv *kv,
+                      int32_t batch, int32_t gamma, const int32_t *anchor, const int32_t *labels,
+                      float *loss, float *row_loss, float *dbg_logits,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
 /* Human-readable name of a dflash_status value (static string). */
 const char *dflash_status_str(int status);
 
