@@ -252,6 +252,57 @@ def block_loss_leg(args, dfl, cfg, gen, torch):
           flush=True)
 
 
+def input_fusion_leg(args, dfl, cfg, gen, torch):
+    """Cost of the two ways to condition the drafter on the target's context features, each
+    followed by the drafting pass: KV injection (the fused feature through every layer's W_k /
+    W_v) and input fusion (the fused feature as the input of the whole layer stack, causal over
+    the new rows).  Same inputs; the context is held at its configured length."""
+    import numpy as np
+    B, gamma = args.batch, cfg.gamma
+    cfg = cfg.with_(batch=B)
+    lengths = gen.context_lengths(cfg)
+    cap = (int(lengths.max()) + 2 * cfg.gamma_max + 63) // 64 * 64
+    W = gen.weights(cfg)
+    model = dfl.Model(cfg, W, device="cuda", max_batch=B, kv_capacity=cap)
+    cache = dfl.Cache(model)
+    Kc, Vc = gen.context_kv(cfg, lengths, int(lengths.max()), tag="bench.ctx")
+    cache.set_context(Kc, Vc, lengths)
+    ws = dfl.Workspace(model, B, gamma)
+    len0 = torch.as_tensor(np.asarray(lengths, dtype=np.int32), device="cuda")
+    feat = dfl.to_device(gen.features(cfg, B, gamma, tag="bench.if.feat"), "cuda")
+    n_rows = 6                                   # about the planted mean accept length
+    n_new = torch.full((B,), n_rows, dtype=torch.int32, device="cuda")
+    anchor = torch.as_tensor(gen.tokens(cfg, "bench.if.anchor", (B,)), device="cuda")
+    draft = torch.zeros((B, gamma - 1), dtype=torch.int32, device="cuda")
+
+    def timed(inject):
+        def step():
+            cache.len.copy_(len0)
+            inject(model, cache, feat, n_new, ws)
+            dfl.draft_block(model, cache, gamma, anchor, draft, ws)
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        assert int(cache.status.item()) == 0
+        return e0.elapsed_time(e1) * 1000.0 / args.steps
+
+    us_kv = timed(dfl.inject_kv)
+    us_if = timed(dfl.inject_kv_input_fusion)
+    print(json.dumps({"metric": "conditioning + drafting time, input fusion vs KV injection", "value": round(us_if, 1),
+                      "unit": "us", "higher_is_better": False, "steps": args.steps, "warmup": args.warmup,
+                      "dtype": cfg.dtype, "kv_injection_us": round(us_kv, 1), "input_fusion_us": round(us_if, 1),
+                      "ratio": round(us_if / us_kv, 3), "new_context_rows": n_rows,
+                      "config": {"workload": f"{cfg.name}: {SHAPES.get(cfg.name, cfg.name)}, batch {B}, gamma {gamma}, "
+                                             f"context {int(lengths.mean())}", "batch": B, "gamma": gamma}}),
+          flush=True)
+
+
 def target_verify(args, dfl, cfg, gen, torch):
     """The verifying target's forward over one block: a Qwen3-8B-shaped target (the drafter's
     layer recipe, 36 layers, untied LM head) checks anchor + gamma-1 drafts at context C, keeping
@@ -341,6 +392,8 @@ def main():
                     help="time the injection of a whole context's feature rows instead of the cycle")
     ap.add_argument("--target", action="store_true",
                     help="time the verifying target's forward over one block (36-layer target of the config's shape)")
+    ap.add_argument("--input-fusion", action="store_true",
+                    help="time input-fusion conditioning + drafting beside KV injection + drafting")
     ap.add_argument("--loss", action="store_true",
                     help="time the drafter's position-weighted block cross-entropy beside the drafting pass")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -388,6 +441,9 @@ def main():
         return
     if args.loss:
         block_loss_leg(args, dfl, cfg, gen, torch)
+        return
+    if args.input_fusion:
+        input_fusion_leg(args, dfl, cfg, gen, torch)
         return
     B = args.batch
     cfg = cfg.with_(batch=B)

@@ -198,6 +198,24 @@ def inject_kv(model: Model, cache: Cache, feat, n_new, ws: Workspace, batch: Opt
                                  _stream_ptr(stream)), "dflash_inject_kv")
 
 
+def inject_kv_input_fusion(model: Model, cache: Cache, feat, n_new, ws: Workspace, batch: Optional[int] = None,
+                           stream=None) -> None:
+    """Input-fusion conditioning (cost comparison with inject_kv): feat [batch][rows][F][H] storage,
+    rows <= gamma_max; every draft layer runs over the fused rows and keeps their K/V; len += n_new."""
+    torch = _torch()
+    batch = feat.shape[0] if batch is None else batch
+    rows = feat.shape[1]
+    _need(feat, "feat", model.storage_dtype, (None, rows, model.cfg.n_feat, model.cfg.hidden))
+    if batch > feat.shape[0]:
+        raise ValueError(f"feat holds {feat.shape[0]} sequences, batch is {batch}")
+    _need(n_new, "n_new", torch.int32, (None,))
+    if n_new.shape[0] < batch:
+        raise ValueError(f"n_new holds {n_new.shape[0]} entries, batch is {batch}")
+    check(lib().dflash_inject_kv_input_fusion(ctypes.byref(model.c), ctypes.byref(model.w), ctypes.byref(cache.s),
+                                              batch, feat.data_ptr(), rows, n_new.data_ptr(), ws.ptr(), ws.nbytes,
+                                              _stream_ptr(stream)), "dflash_inject_kv_input_fusion")
+
+
 def draft_block(model: Model, cache: Cache, gamma: int, anchor, draft, ws: Workspace, dbg_hidden=None,
                 dbg_logits=None, stream=None) -> None:
     """anchor: device int32 [batch]; draft: device int32 [batch][gamma-1] (output)."""

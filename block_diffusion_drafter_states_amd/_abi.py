@@ -27,7 +27,7 @@ STATUS_BAD_COUNT = 4
 
 EXPORTED = ("dflash_workspace_bytes", "dflash_inject_kv", "dflash_draft_block", "dflash_verify",
             "dflash_inject_kv_traced", "dflash_draft_block_traced", "dflash_target_forward", "dflash_advance_len",
-            "dflash_choose_gamma", "dflash_block_loss", "dflash_status_str")
+            "dflash_choose_gamma", "dflash_block_loss", "dflash_inject_kv_input_fusion", "dflash_status_str")
 
 
 class dflash_config(ctypes.Structure):
@@ -100,6 +100,8 @@ def lib(path: str = LIB_PATH) -> ctypes.CDLL:
     L.dflash_choose_gamma.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_double, ctypes.c_double,
                                       ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_double)]
+    L.dflash_inject_kv_input_fusion.restype = ctypes.c_int
+    L.dflash_inject_kv_input_fusion.argtypes = L.dflash_inject_kv.argtypes
     L.dflash_block_loss.restype = ctypes.c_int
     L.dflash_block_loss.argtypes = [P(dflash_config), P(dflash_weights), P(dflash_kv), ctypes.c_int32,
                                     ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,

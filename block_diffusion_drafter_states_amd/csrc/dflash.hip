@@ -505,6 +505,10 @@ struct PassMode {
     const int* labels;      // nullable: [batch][gamma-1] labels of the mask rows -> block loss instead of drafts
     float* loss;            // with labels: [1] weighted mean cross-entropy
     float* row_loss;        // with labels: nullable [batch][gamma-1] cross-entropy per mask row
+    const float* x_in;      // nullable: fp32 [batch*gamma][H] input rows instead of token embeddings
+    const float* ssq_in;    // with x_in: [n_ssq_in][batch*gamma] per-tile sums of squares of x_in
+    int n_ssq_in;
+    int no_head;            // stop after the last decoder layer (no final norm, LM head or argmax)
 };
 
 constexpr PassMode DRAFT_PASS = {nullptr, 0, 0, nullptr, 0, nullptr, 1};
@@ -535,11 +539,19 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
     const int qkv_ld = (s.nq + 2 * s.nkv) * s.D;
     int rc;
 
-    tr.begin("embed_norm");
-    hipLaunchKernelGGL((embed_norm_kernel<T>), dim3(M), dim3(256), 0, st, static_cast<const T*>(w->embed), anchor,
-                       md.tokens, s.mask, s.V, gamma, s.H, static_cast<const T*>(w->layers[0].in_norm), s.eps, x,
-                       static_cast<T*>(nbuf), kv->status, fin_best, fin_count, n_draft, afrag);
-    tr.end();
+    if (md.x_in) {      // input rows given (fp32): they start the residual stream
+        const long long n = (long long)M * s.H;
+        const unsigned blocks = (unsigned)std::min<long long>(1024, (n + 255) / 256);
+        tr.begin("copy_input");
+        hipLaunchKernelGGL(copy_f32_kernel, dim3(blocks), dim3(256), 0, st, md.x_in, x, n);
+        tr.end();
+    } else {
+        tr.begin("embed_norm");
+        hipLaunchKernelGGL((embed_norm_kernel<T>), dim3(M), dim3(256), 0, st, static_cast<const T*>(w->embed),
+                           anchor, md.tokens, s.mask, s.V, gamma, s.H, static_cast<const T*>(w->layers[0].in_norm),
+                           s.eps, x, static_cast<T*>(nbuf), kv->status, fin_best, fin_count, n_draft, afrag);
+        tr.end();
+    }
     if (hipGetLastError() != hipSuccess) return DFLASH_ELAUNCH;
     int n_ssq = 0;      // per-tile partial sums of squares of x (written by o / down)
 
@@ -550,7 +562,10 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
         const dflash_layer_weights& lw = w->layers[l];
         {   // raw q | k | v of the block (three weight tensors, one launch)
             GemmArgs a = gemm_base(s, pl.qkv, M, s.H);
-            if (l == 0) {       // the embedding kernel normalised the rows already
+            if (l == 0 && md.x_in) {
+                if ((rc = set_norm_a<T>(a, s, x, M, md.ssq_in, md.n_ssq_in, lw.in_norm, nbuf, afrag, st, tr)))
+                    return rc;
+            } else if (l == 0) {       // the embedding kernel normalised the rows already
                 a.a = nbuf;
                 a.lda = s.H;
                 a.a_frag = afrag;
@@ -686,6 +701,7 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
         tr.end();
         if (hipGetLastError() != hipSuccess) return DFLASH_ELAUNCH;
     }
+    if (md.no_head) return DFLASH_OK;
     {   // final norm -> LM head -> per-tile argmax (or log-sum-exp and label logits)
         const bool loss = md.labels != nullptr;
         const GemmPlan plm = loss ? plan_gemm(s, EPI_LSE, s.V, s.H, M, 1) : pl.lm;
@@ -726,6 +742,54 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
     const int n_slices = std::max(1, std::min(pl.lm.n_tiles, 256 / row_blocks));
     hipLaunchKernelGGL(argmax_finish_kernel, dim3(n_slices, row_blocks), dim3(256), 0, st, amax, pl.lm.n_tiles,
                        n_slices, M, gamma, md.first_row, fin_best, fin_count, draft);
+    tr.end();
+    return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_ELAUNCH;
+}
+
+// Input-fusion conditioning (the alternative the summary's KV injection is compared with,
+// section 2.2 and the ablations of section 4): the fused feature of each new context row is
+// the drafter's input at that position; every draft layer runs over the rows (causal among
+// them, attending to the cached context) and keeps its own K/V rows.  All rows_stride rows
+// of a sequence are computed and written at len .. len + rows_stride - 1; len then advances
+// by n_new[b], so rows past n_new[b] are overwritten by later ones.
+template <typename T>
+int run_inject_input_fusion(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int batch,
+                            const void* feat, int rows, const int* n_new, void* ws, const Layout& lay,
+                            hipStream_t st, Tracer& tr) {
+    char* wsb = static_cast<char*>(ws);
+    const InjectPlans pl = inject_plans(s, batch, rows);
+    const int M = batch * rows;
+    float* c = reinterpret_cast<float*>(wsb + lay.c);
+    float* ssq_c = reinterpret_cast<float*>(wsb + lay.ssq_c);
+    int rc;
+    {   // c = W_fuse . concat(feat), with per-tile sums of squares for the first layer's norm
+        GemmArgs a = gemm_base(s, pl.fuse, M, s.F * s.H);
+        a.a = feat;
+        a.lda = (long long)s.F * s.H;
+        a.N = s.H;
+        a.seg_end[0] = a.seg_end[1] = a.seg_end[2] = s.H;
+        a.layer[0].w[0] = w->w_fuse;
+        a.out = c;
+        a.ldo = s.H;
+        a.residual = 0;
+        a.ssq_out = ssq_c;
+        a.ssq_out_ld = M;
+        if ((rc = gemm_dispatch<T>(a, pl.fuse, st, tr, "fuse"))) return rc;
+    }
+    if (pl.fuse.n_tiles > lay.ssq_c_tiles) return DFLASH_EUNSUPPORTED;
+    PassMode md = DRAFT_PASS;
+    md.causal = 1;
+    md.write_kv = 1;
+    md.first_row = 0;
+    md.x_in = c;
+    md.ssq_in = ssq_c;
+    md.n_ssq_in = pl.fuse.n_tiles;
+    md.no_head = 1;
+    if ((rc = run_draft<T>(s, w, kv, batch, rows, nullptr, nullptr, nullptr, nullptr, ws, lay, st, tr, md)))
+        return rc;
+    tr.begin("advance_len");
+    hipLaunchKernelGGL(advance_len_kernel, dim3(1), dim3(64), 0, st, kv->len, n_new, batch, s.cap, rows, rows,
+                       kv->status);
     tr.end();
     return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_ELAUNCH;
 }
@@ -803,6 +867,25 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, const 
                                      workspace_bytes, stream, nullptr);
 }
 
+int dflash_inject_kv_input_fusion(const dflash_config* cfg, const dflash_weights* w, const dflash_kv* kv,
+                                  int32_t batch, const void* feat, int32_t rows_stride, const int32_t* n_new,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+    Shape s;
+    int rc = make_shape(cfg, s);
+    if (rc) return rc;
+    if (!w || !kv || !feat || !n_new || !kv->k || !kv->v || !kv->len || !kv->status) return DFLASH_EINVAL;
+    if (!weights_ok(s, w)) return DFLASH_EINVAL;
+    if (batch < 1 || batch > s.Bmax || rows_stride < 1 || rows_stride > s.gmax) return DFLASH_EINVAL;
+    if (w->rope_rows < s.cap + s.gmax) return DFLASH_EINVAL;
+    if (!workspace) return DFLASH_EWORKSPACE;
+    const Layout lay = make_layout(s, batch, rows_stride);
+    if (workspace_bytes < lay.inject_end) return DFLASH_EWORKSPACE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    Tracer tr{nullptr, st};
+    return s.bf16 ? run_inject_input_fusion<bf16_t>(s, w, kv, batch, feat, rows_stride, n_new, workspace, lay, st, tr)
+                  : run_inject_input_fusion<float>(s, w, kv, batch, feat, rows_stride, n_new, workspace, lay, st, tr);
+}
+
 int dflash_block_loss(const dflash_config* cfg, const dflash_weights* w, const dflash_kv* kv, int32_t batch,
                       int32_t gamma, const int32_t* anchor, const int32_t* labels, float* loss, float* row_loss,
                       float* dbg_logits, void* workspace, size_t workspace_bytes, void* stream) {
@@ -865,7 +948,7 @@ int dflash_target_forward(const dflash_config* cfg, const dflash_weights* w, con
 int dflash_advance_len(const dflash_kv* kv, int32_t batch, int32_t kv_capacity, const int32_t* n, void* stream) {
     if (!kv || !kv->len || !kv->status || !n || batch < 1 || kv_capacity < 1) return DFLASH_EINVAL;
     hipLaunchKernelGGL(advance_len_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), kv->len, n, batch,
-                       kv_capacity, kv->status);
+                       kv_capacity, kv_capacity, 0, kv->status);
     return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_ELAUNCH;
 }
 

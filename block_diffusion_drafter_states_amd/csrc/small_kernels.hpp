@@ -261,12 +261,14 @@ __global__ __launch_bounds__(256) void tap_kernel(const float* __restrict__ x, l
 
 // len[b] += n[b] after a verification (n = accepted length) or a chunk of a prompt;
 // a count outside 0 .. cap - len sets a status bit and leaves len.
+// len[b] += n[b] when 0 <= n[b] <= max_n and len[b] + max(n[b], need) <= cap (need: rows
+// the same call wrote from len[b] on, which must all have fitted); else a status bit.
 __global__ __launch_bounds__(64) void advance_len_kernel(int* __restrict__ len, const int* __restrict__ n, int batch,
-                                                         int cap, unsigned* status) {
+                                                         int cap, int max_n, int need, unsigned* status) {
     for (int b = threadIdx.x; b < batch; b += 64) {
         const int l = len[b], k = n[b];
-        if (k < 0 || l < 0) atomicOr(status, STATUS_BAD_COUNT);
-        else if (l + k > cap) atomicOr(status, STATUS_KV_OVERFLOW);
+        if (k < 0 || k > max_n || l < 0) atomicOr(status, STATUS_BAD_COUNT);
+        else if (l + (k > need ? k : need) > cap) atomicOr(status, STATUS_KV_OVERFLOW);
         else len[b] = l + k;
     }
 }

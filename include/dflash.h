@@ -257,6 +257,28 @@ int dflash_choose_gamma(const int32_t *tau, const int32_t *gamma_used, int32_t n
                         int32_t gamma_min, int32_t gamma_max, double prior_p, double prior_weight,
                         int32_t *gamma_out, double *p_out);
 
+/* Input-fusion conditioning: the alternative that the summary's KV injection
+ * is measured against (section 2.2, KV-injection bullet: features fused only at
+ * the input layer are diluted with depth; section 4 ablations).  Cost
+ * comparison only.  For every sequence b: c_i = W_fuse . concat(feat[b][i])
+ * (as in dflash_inject_kv) is the drafter's input hidden state at position
+ * len[b] + i, for i < rows_stride; every draft layer runs over these rows with
+ * the drafter's recipe (input RMSNorm, q/k head RMSNorm + RoPE, attention to
+ * the cached context and causally to the rows before it, W_o, SwiGLU MLP) and
+ * keeps each row's k and v at its position in that layer's cache.  Then
+ * len[b] += n_new[b]: rows at or past n_new[b] are computed but overwritten
+ * later.  The cache must hold len[b] + rows_stride rows (else
+ * DFLASH_STATUS_KV_OVERFLOW and nothing is written for b); n_new[b] outside
+ * [0, rows_stride] sets DFLASH_STATUS_BAD_COUNT and leaves len[b].
+ * dflash_draft_block then drafts from the cache as usual.
+ *   feat     [batch][rows_stride][F][H] in the storage dtype
+ *   n_new    device int32 [batch]
+ * 1 <= rows_stride <= gamma_max; workspace: dflash_workspace_bytes(cfg, batch,
+ * rows_stride). */
+int dflash_inject_kv_input_fusion(const dflash_config *cfg, const dflash_weights *w, const dflash_kv *kv,
+                                  int32_t batch, const void *feat, int32_t rows_stride, const int32_t *n_new,
+                                  void *workspace, size_t workspace_bytes, void *stream);
+
 /* Training objective of the drafter (summary section 2.3, loss weighting):
  * the drafter's forward pass exactly as dflash_draft_block (same anchor, mask
  * rows and context), then, for each mask row j = 1 .. gamma-1 of sequence b,
