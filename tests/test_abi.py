@@ -153,6 +153,46 @@ def test_draft_host_errors():
     assert call(c=_cfg(n_q_heads=3)) == DFLASH_EUNSUPPORTED
 
 
+def test_block_loss_host_errors():
+    L = _lib()
+    c, w, kv = _cfg(), _weights(), _kv()
+    ws_need = L.dflash_workspace_bytes(ctypes.byref(c), 1, 0)
+    call = lambda **k: L.dflash_block_loss(ctypes.byref(k.get("c", c)), ctypes.byref(k.get("w", w)), ctypes.byref(kv),
+                                           k.get("batch", 1), k.get("gamma", 8), k.get("anchor", FAKE),
+                                           k.get("labels", FAKE), k.get("loss", FAKE), None, None,
+                                           k.get("ws", FAKE), k.get("wsb", ws_need), None)
+    assert call(gamma=1) == DFLASH_EINVAL
+    assert call(gamma=9) == DFLASH_EINVAL           # > gamma_max
+    assert call(batch=0) == DFLASH_EINVAL
+    assert call(anchor=None) == DFLASH_EINVAL
+    assert call(labels=None) == DFLASH_EINVAL
+    assert call(loss=None) == DFLASH_EINVAL
+    assert call(w=_weights(null_field="w_down")) == DFLASH_EINVAL
+    assert call(ws=None) == DFLASH_EWORKSPACE
+    assert call(wsb=ws_need - 256) == DFLASH_EWORKSPACE
+    assert call(c=_cfg(head_dim=32)) == DFLASH_EUNSUPPORTED
+
+
+def test_input_fusion_host_errors():
+    L = _lib()
+    c, w, kv = _cfg(), _weights(), _kv()
+    ws_need = L.dflash_workspace_bytes(ctypes.byref(c), 1, 8)
+    call = lambda **k: L.dflash_inject_kv_input_fusion(
+        ctypes.byref(k.get("c", c)), ctypes.byref(k.get("w", w)), ctypes.byref(k.get("kv", kv)), k.get("batch", 1),
+        k.get("feat", FAKE), k.get("rows", 8), k.get("n_new", FAKE), k.get("ws", FAKE), k.get("wsb", ws_need), None)
+    assert call(batch=0) == DFLASH_EINVAL
+    assert call(batch=2) == DFLASH_EINVAL
+    assert call(rows=0) == DFLASH_EINVAL
+    assert call(rows=9) == DFLASH_EINVAL            # more rows than gamma_max
+    assert call(feat=None) == DFLASH_EINVAL
+    assert call(n_new=None) == DFLASH_EINVAL
+    assert call(kv=dflash_kv(k=FAKE, v=FAKE, len=None, status=FAKE)) == DFLASH_EINVAL
+    assert call(w=_weights(null_field="wq")) == DFLASH_EINVAL
+    assert call(ws=None) == DFLASH_EWORKSPACE
+    assert call(wsb=ws_need - 1) == DFLASH_EWORKSPACE
+    assert call(c=_cfg(head_dim=32)) == DFLASH_EUNSUPPORTED
+
+
 def test_verify_host_errors():
     L = _lib()
     assert L.dflash_verify(0, 4, FAKE, FAKE, FAKE, FAKE, FAKE, None) == DFLASH_EINVAL
