@@ -84,6 +84,12 @@ int make_shape(const dflash_config* c, Shape& s) {
     // build, first loads) and its partial write; below four per CU the GPU idles.
     int ch = 2048;
     while (ch > 256 && (long long)s.Bmax * s.nkv * cdiv(s.cap, ch) < 1024) ch >>= 1;
+    // 128-key chunks when even those fit one round of workgroups (one per CU): shorter
+    // chunks shorten every workgroup (measured: Qwen3-4B shape, context 1024, batch 1:
+    // attention 88 -> 70 us per cycle; at context 4096 the 272 workgroups of 128-key
+    // chunks would need two rounds, 91 -> 119 us)
+    const long long nqs_max = cdiv(cdiv(s.group * s.gmax, 16), ATT_MAX_TILES);
+    if (ch == 256 && (1 + cdiv(s.cap, 128)) * (long long)s.nkv * nqs_max * s.Bmax <= 256) ch = 128;
     s.chunk = ch;
     s.nch_max = 1 + cdiv(s.cap, ch);
     if (s.nch_max > MERGE_MAX_CHUNKS) return DFLASH_EUNSUPPORTED;
