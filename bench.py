@@ -135,8 +135,9 @@ def algorithmic_bytes(cfg, B, C_mean, tau_mean):
     return parts, sum(parts.values())
 
 
-def cpu_oracle_baseline(cfg, W, K, V, lengths, feats, anchors, plant_k, gamma, budget_s):
-    """The oracle (fp64 numpy) on a bounded sample of the same workload."""
+def cpu_oracle_baseline(cfg, W, K, V, lengths, feats, anchors, plant_k, gammas, budget_s):
+    """The oracle (fp64 numpy) on a bounded sample of the same workload (block size of cycle n:
+    gammas[n % len(gammas)])."""
     import numpy as np
     from threadpoolctl import threadpool_info
     from oracle import dflash as O
@@ -157,7 +158,7 @@ def cpu_oracle_baseline(cfg, W, K, V, lengths, feats, anchors, plant_k, gamma, b
             kv.len[b] = lengths[b]
             f = O.decode_storage(feats[n % len(feats)][b, : tau[b]])
             O.inject(m, kv, b, f)
-            d = O.draft(m, kv, b, anchor[b], gamma)
+            d = O.draft(m, kv, b, anchor[b], gammas[n % len(gammas)])
             y = gen.planted_targets(cfg, d[None, :], np.array([plant_k[n % len(plant_k)][b]]), tag=f"cpu.{n}.{b}")[0]
             t, _, nxt = O.verify(d, y)
             tau[b], anchor[b] = t, nxt
@@ -447,7 +448,10 @@ def main():
         return
     B = args.batch
     cfg = cfg.with_(batch=B)
-    gamma = cfg.gamma
+    gamma = cfg.gamma_max
+    # block size of cycle i (a configuration with several block sizes cycles through them)
+    gseq = list(cfg.gammas) if cfg.gammas else [cfg.gamma]
+    gam = lambda i: gseq[i % len(gseq)]
     lengths = gen.context_lengths(cfg)
     cap = (int(lengths.max()) + 2 * cfg.gamma_max + 63) // 64 * 64
     dev = "cuda"
@@ -466,14 +470,14 @@ def main():
     NP = 8
     feats_host = [gen.features(cfg, B, gamma, tag=f"bench.feat.{i}") for i in range(NP)]
     feats = [dfl.to_device(f, dev) for f in feats_host]
-    plant_k = [gen.planted_accept(cfg, (B,), gamma, tag=f"bench.k.{i}") for i in range(K_steps)]
+    plant_k = [gen.planted_accept(cfg, (B,), gam(i), tag=f"bench.k.{i}") for i in range(K_steps)]
     anchor0 = gen.anchors(cfg, B, tag="bench.anchor")
     len_base = torch.as_tensor(lengths, dtype=torch.int32, device=dev)
     acc = torch.zeros((K_steps + 1, B), dtype=torch.int32, device=dev)      # accept_len per cycle
     nxt = torch.zeros((K_steps + 1, B), dtype=torch.int32, device=dev)      # next anchor per cycle
-    drafts = torch.zeros((K_steps, B, gamma - 1), dtype=torch.int32, device=dev)
-    ytgt = torch.zeros((K_steps, B, gamma), dtype=torch.int32, device=dev)
-    committed = torch.zeros((B, gamma), dtype=torch.int32, device=dev)
+    drafts = [torch.zeros((B, gam(i) - 1), dtype=torch.int32, device=dev) for i in range(K_steps)]
+    ytgt = [torch.zeros((B, gam(i)), dtype=torch.int32, device=dev) for i in range(K_steps)]
+    committed = {g: torch.zeros((B, g), dtype=torch.int32, device=dev) for g in gseq}
     tau0 = torch.as_tensor(plant_k[-1] + 1, dtype=torch.int32, device=dev)
 
     def reset():
@@ -482,19 +486,20 @@ def main():
 
     def cycle(i, trace=None):
         cache.len[:B].copy_(len_base)
+        g = gam(i)
         if trace is None:
             dfl.inject_kv(model, cache, feats[i % NP], acc[i], ws)
-            dfl.draft_block(model, cache, gamma, nxt[i], drafts[i], ws)
+            dfl.draft_block(model, cache, g, nxt[i], drafts[i], ws)
         else:
             _abi.check(dfl.lib().dflash_inject_kv_traced(
                 ctypes.byref(model.c), ctypes.byref(model.w), ctypes.byref(cache.s), B, feats[i % NP].data_ptr(),
                 gamma, acc[i].data_ptr(), ws.ptr(), ws.nbytes, dfl._stream_ptr(None), ctypes.byref(trace[0])),
                 "inject_traced")
             _abi.check(dfl.lib().dflash_draft_block_traced(
-                ctypes.byref(model.c), ctypes.byref(model.w), ctypes.byref(cache.s), B, gamma, nxt[i].data_ptr(),
+                ctypes.byref(model.c), ctypes.byref(model.w), ctypes.byref(cache.s), B, g, nxt[i].data_ptr(),
                 drafts[i].data_ptr(), None, None, ws.ptr(), ws.nbytes, dfl._stream_ptr(None),
                 ctypes.byref(trace[1])), "draft_traced")
-        dfl.verify(drafts[i], ytgt[i], acc[i + 1], committed, nxt[i + 1])
+        dfl.verify(drafts[i], ytgt[i], acc[i + 1], committed[g], nxt[i + 1])
 
     # ---- planning pass (untimed): record drafts, plant target tokens
     t1 = time.time()
@@ -502,10 +507,10 @@ def main():
     for i in range(K_steps):
         cache.len[:B].copy_(len_base)
         dfl.inject_kv(model, cache, feats[i % NP], acc[i], ws)
-        dfl.draft_block(model, cache, gamma, nxt[i], drafts[i], ws)
+        dfl.draft_block(model, cache, gam(i), nxt[i], drafts[i], ws)
         d = drafts[i].cpu().numpy()
         ytgt[i].copy_(torch.as_tensor(gen.planted_targets(cfg, d, plant_k[i], tag=f"bench.y.{i}")))
-        dfl.verify(drafts[i], ytgt[i], acc[i + 1], committed, nxt[i + 1])
+        dfl.verify(drafts[i], ytgt[i], acc[i + 1], committed[gam(i)], nxt[i + 1])
     torch.cuda.synchronize()
     status = int(cache.status.item())
     assert status == 0, f"device status {status}"
@@ -573,7 +578,8 @@ def main():
     kern_us = {nm: round(1000.0 * sum(v) / NT, 2) for nm, v in kern.items()}     # per cycle (all launches)
     lm = kern["lm_head_argmax"]
     lm_avg_ms = sum(lm) / len(lm)
-    lm_bytes = cfg.vocab * cfg.hidden * cfg.elem_bytes + B * gamma * cfg.hidden * cfg.elem_bytes   # W_lm + normalised rows
+    g_mean = float(np.mean([gam(i) for i in range(K_steps)]))
+    lm_bytes = int(cfg.vocab * cfg.hidden * cfg.elem_bytes + B * g_mean * cfg.hidden * cfg.elem_bytes)  # W_lm + rows
     lm_gbs = lm_bytes / (lm_avg_ms * 1e-3) / 1e9
     log(f"lm_head_argmax {lm_avg_ms * 1000:.1f} us -> {lm_gbs:.0f} GB/s; per-cycle kernel us {kern_us}")
 
@@ -593,10 +599,10 @@ def main():
         "data": "synthetic (seeded random-init drafter weights, N(0,1) target features and context K/V, "
                 "planted target tokens)",
         "config": {"workload": f"{cfg.name}: {SHAPES.get(cfg.name, cfg.name)}, {cfg.n_layers} layers, batch {B}, "
-                               f"gamma {gamma}, context {int(lengths.mean())}",
-                   "batch": B, "gamma": gamma, "context": int(lengths.mean()), "hidden": cfg.hidden,
-                   "layers": cfg.n_layers, "vocab": cfg.vocab, "parallelism": "single GPU"},
-        "draft_tokens_per_s": round(cps * B * (gamma - 1), 1),
+                               f"gamma {'/'.join(str(g) for g in gseq)}, context {int(lengths.mean())}",
+                   "batch": B, "gamma": gseq[0] if len(gseq) == 1 else gseq, "context": int(lengths.mean()),
+                   "hidden": cfg.hidden, "layers": cfg.n_layers, "vocab": cfg.vocab, "parallelism": "single GPU"},
+        "draft_tokens_per_s": round(cps * B * (g_mean - 1), 1),
         "committed_tokens_per_s": round(cps * B * tau_mean, 1),
         "planted_mean_accept_len": round(tau_mean, 3),
         "bytes_per_cycle": int(bytes_cycle),
@@ -612,7 +618,7 @@ def main():
     if B > 1:
         # contraction throughput (the dense-MFMA regime of large batches): the cycle's GEMM flops
         # over the whole cycle and over the projection launches alone
-        gf = gemm_flops(cfg, B, gamma, tau_mean)
+        gf = gemm_flops(cfg, B, g_mean, tau_mean)
         gemm_us = sum(v for k, v in kern_us.items() if k in GEMM_LAUNCHES)
         peak = MFMA_PEAK_TFLOPS[cfg.dtype]
         result["mfma"] = {"gemm_gflop_per_cycle": round(gf / 1e9, 1), "peak_tflops": peak,
@@ -621,7 +627,7 @@ def main():
                           "gemm_us_per_cycle": round(gemm_us, 1)}
     if not args.no_cpu_baseline:
         Kh, Vh = gen.context_kv(cfg, lengths, cap, tag="bench.ctx")
-        result["cpu_baseline"] = cpu_oracle_baseline(cfg, W, Kh, Vh, lengths, feats_host, anchor0, plant_k, gamma,
+        result["cpu_baseline"] = cpu_oracle_baseline(cfg, W, Kh, Vh, lengths, feats_host, anchor0, plant_k, gseq,
                                                      args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
