@@ -242,11 +242,14 @@ def block_loss_leg(args, dfl, cfg, gen, torch):
         return e0.elapsed_time(e1) * 1000.0 / args.steps
 
     us_loss = timed(lambda: dfl.block_loss(model, cache, gamma, anchor, labels, loss, ws))
+    dz = torch.empty((B, gamma - 1, cfg.vocab), dtype=torch.float32, device="cuda")
+    us_grad = timed(lambda: dfl.block_loss(model, cache, gamma, anchor, labels, loss, ws, dlogits=dz))
     us_draft = timed(lambda: dfl.draft_block(model, cache, gamma, anchor, draft, ws))
     assert int(cache.status.item()) == 0 and math.isfinite(float(loss.item()))
     print(json.dumps({"metric": "block loss evaluations/s", "value": round(1e6 / us_loss, 2), "unit": "blocks-batches/s",
                       "higher_is_better": True, "steps": args.steps, "warmup": args.warmup, "dtype": cfg.dtype,
-                      "us_per_call": round(us_loss, 1), "draft_block_us_per_call": round(us_draft, 1),
+                      "us_per_call": round(us_loss, 1), "with_dlogits_us_per_call": round(us_grad, 1),
+                      "draft_block_us_per_call": round(us_draft, 1),
                       "loss": float(loss.item()),
                       "config": {"workload": f"{cfg.name}: {SHAPES.get(cfg.name, cfg.name)}, batch {B}, gamma {gamma}, "
                                              f"context {int(lengths.mean())}", "batch": B, "gamma": gamma}}),

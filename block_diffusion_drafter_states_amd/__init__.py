@@ -235,9 +235,10 @@ def draft_block(model: Model, cache: Cache, gamma: int, anchor, draft, ws: Works
 
 
 def block_loss(model: Model, cache: Cache, gamma: int, anchor, labels, loss, ws: Workspace, row_loss=None,
-               dbg_logits=None, stream=None) -> None:
+               dbg_logits=None, stream=None, dlogits=None) -> None:
     """The drafter's weighted block cross-entropy: anchor int32 [B], labels int32 [B][gamma-1]
-    -> loss fp32 [1] (weights exp(-(j-1)/gamma) on mask row j), row_loss fp32 [B][gamma-1]."""
+    -> loss fp32 [1] (weights exp(-(j-1)/gamma) on mask row j), row_loss fp32 [B][gamma-1],
+    dlogits fp32 [B][gamma-1][V] (gradient of the loss w.r.t. the mask rows' logits)."""
     torch = _torch()
     batch = anchor.shape[0]
     _need(anchor, "anchor", torch.int32, (batch,))
@@ -247,9 +248,12 @@ def block_loss(model: Model, cache: Cache, gamma: int, anchor, labels, loss, ws:
         _need(row_loss, "row_loss", torch.float32, (batch, gamma - 1))
     if dbg_logits is not None:
         _need(dbg_logits, "dbg_logits", torch.float32, (batch, gamma - 1, model.cfg.vocab))
+    if dlogits is not None:
+        _need(dlogits, "dlogits", torch.float32, (batch, gamma - 1, model.cfg.vocab))
     check(lib().dflash_block_loss(ctypes.byref(model.c), ctypes.byref(model.w), ctypes.byref(cache.s), batch,
                                   gamma, anchor.data_ptr(), labels.data_ptr(), loss.data_ptr(),
                                   None if row_loss is None else row_loss.data_ptr(),
+                                  None if dlogits is None else dlogits.data_ptr(),
                                   None if dbg_logits is None else dbg_logits.data_ptr(),
                                   ws.ptr(), ws.nbytes, _stream_ptr(stream)), "dflash_block_loss")
 

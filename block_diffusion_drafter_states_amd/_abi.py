@@ -105,8 +105,8 @@ def lib(path: str = LIB_PATH) -> ctypes.CDLL:
     L.dflash_block_loss.restype = ctypes.c_int
     L.dflash_block_loss.argtypes = [P(dflash_config), P(dflash_weights), P(dflash_kv), ctypes.c_int32,
                                     ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
-                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
-                                    ctypes.c_void_p]
+                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_size_t, ctypes.c_void_p]
     L.dflash_status_str.restype = ctypes.c_char_p
     L.dflash_status_str.argtypes = [ctypes.c_int]
     _LIB = L

@@ -251,7 +251,8 @@ DraftPlans draft_plans(const Shape& s, int M) {
 // is per-call scratch: no state survives a call.
 struct Layout {
     // draft
-    size_t x, ssq_x, qkv, opart, mlpart, obuf, hbuf, amax, fin_best, fin_count, nbuf, lse_part, lab, draft_end;
+    size_t x, ssq_x, qkv, opart, mlpart, obuf, hbuf, amax, fin_best, fin_count, nbuf, lse_part, lab, lse_row,
+        draft_end;
     int ssq_x_tiles, amax_tiles;
     // inject
     size_t c, ssq_c, cnorm, kvraw, lensnap, inject_end;
@@ -282,6 +283,7 @@ Layout make_layout(const Shape& s, int batch, int rows) {
     l.nbuf = take(Mp * s.H * s.esize);                        // RMSNorm-ed rows (GEMM A operand)
     l.lse_part = take((size_t)LSE_MAX_SLICES * M * 8);        // block loss: per-slice (max, sum exp)
     l.lab = take(M * 4);                                      // block loss: the label's logit per row
+    l.lse_row = take(M * 4);                                  // block loss: log-sum-exp per row (gradient)
     l.draft_end = off;
     l.c = l.ssq_c = l.cnorm = l.kvraw = l.lensnap = 0;
     l.ssq_c_tiles = 0;
@@ -511,6 +513,7 @@ struct PassMode {
     const int* labels;      // nullable: [batch][gamma-1] labels of the mask rows -> block loss instead of drafts
     float* loss;            // with labels: [1] weighted mean cross-entropy
     float* row_loss;        // with labels: nullable [batch][gamma-1] cross-entropy per mask row
+    float* dlogits;         // with labels: nullable [batch][gamma-1][V] gradient of the loss w.r.t. the logits
     const float* x_in;      // nullable: fp32 [batch*gamma][H] input rows instead of token embeddings
     const float* ssq_in;    // with x_in: [n_ssq_in][batch*gamma] per-tile sums of squares of x_in
     int n_ssq_in;
@@ -719,7 +722,7 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
         a.layer[0].w[0] = w->lm_head;
         a.gamma = gamma;
         a.amax = amax;
-        a.dbg_logits = dbg_logits;
+        a.dbg_logits = (loss && !dbg_logits) ? md.dlogits : dbg_logits;   // the gradient needs the logits
         a.dbg_first = md.first_row;
         if (loss) {
             a.lse = reinterpret_cast<float2*>(amax);     // the same [n_tiles][M] 8-byte slots
@@ -738,10 +741,20 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
         tr.end();
         if (hipGetLastError() != hipSuccess) return DFLASH_ELAUNCH;
         tr.begin("block_loss");
+        float* lse_row = reinterpret_cast<float*>(wsb + lay.lse_row);
         hipLaunchKernelGGL(block_loss_kernel, dim3(1), dim3(BLOCK_LOSS_THREADS), 0, st, part, n_slices, M, gamma,
                            md.labels, reinterpret_cast<const float*>(wsb + lay.lab), s.V, md.loss, md.row_loss,
-                           kv->status);
+                           md.dlogits ? lse_row : nullptr, kv->status);
         tr.end();
+        if (hipGetLastError() != hipSuccess) return DFLASH_ELAUNCH;
+        if (md.dlogits) {
+            // rows x vocabulary slices of 256 ids, at most 64 slices per row (strided beyond)
+            const dim3 grid((unsigned)std::min(64, cdiv(s.V, 256)), (unsigned)(batch * (gamma - 1)));
+            tr.begin("block_loss_grad");
+            hipLaunchKernelGGL(block_loss_grad_kernel, grid, dim3(256), 0, st,
+                               dbg_logits ? dbg_logits : md.dlogits, md.dlogits, lse_row, md.labels, batch, gamma, s.V);
+            tr.end();
+        }
         return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_ELAUNCH;
     }
     tr.begin("argmax_finish");
@@ -894,7 +907,7 @@ int dflash_inject_kv_input_fusion(const dflash_config* cfg, const dflash_weights
 
 int dflash_block_loss(const dflash_config* cfg, const dflash_weights* w, const dflash_kv* kv, int32_t batch,
                       int32_t gamma, const int32_t* anchor, const int32_t* labels, float* loss, float* row_loss,
-                      float* dbg_logits, void* workspace, size_t workspace_bytes, void* stream) {
+                      float* dlogits, float* dbg_logits, void* workspace, size_t workspace_bytes, void* stream) {
     Shape s;
     int rc = make_shape(cfg, s);
     if (rc) return rc;
@@ -911,6 +924,7 @@ int dflash_block_loss(const dflash_config* cfg, const dflash_weights* w, const d
     md.labels = labels;
     md.loss = loss;
     md.row_loss = row_loss;
+    md.dlogits = dlogits;
     return s.bf16 ? run_draft<bf16_t>(s, w, kv, batch, gamma, anchor, nullptr, nullptr, dbg_logits, workspace, lay,
                                       st, tr, md)
                   : run_draft<float>(s, w, kv, batch, gamma, anchor, nullptr, nullptr, dbg_logits, workspace, lay,

@@ -505,7 +505,7 @@ __global__ __launch_bounds__(256) void lse_slices_kernel(const float2* __restric
 }
 
 // Stage 2 (one workgroup of BLOCK_LOSS_THREADS threads, one wavefront per row at a
-// time).  Row m = b*gamma + j with j >= 1: the lanes fold the slices s = lane, lane +
+// time; lse_out [M], nullable, receives each mask row's log-sum-exp).  Row m = b*gamma + j with j >= 1: the lanes fold the slices s = lane, lane +
 // 64, ... in ascending order and an xor-shuffle tree combines the lanes; LSE - logit
 // of the label is the row's CE; row_loss[b][j-1] = CE (nullable); loss[0] = sum_b
 // sum_j w_j CE / (batch * sum_j w_j) with w_j = exp(-(j - 1) / gamma), each wave
@@ -516,7 +516,7 @@ constexpr int BLOCK_LOSS_THREADS = 1024;
 __global__ __launch_bounds__(BLOCK_LOSS_THREADS) void block_loss_kernel(
     const float2* __restrict__ part, int n_slices, int M, int gamma, const int* __restrict__ labels,
     const float* __restrict__ lab_logit, int vocab, float* __restrict__ loss, float* __restrict__ row_loss,
-    unsigned* status) {
+    float* __restrict__ lse_out, unsigned* status) {
     constexpr int NW = BLOCK_LOSS_THREADS / 64;
     __shared__ float red[NW];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -538,7 +538,9 @@ __global__ __launch_bounds__(BLOCK_LOSS_THREADS) void block_loss_kernel(
                 const float2 y = make_float2(__shfl_xor(x.x, o, WAVE), __shfl_xor(x.y, o, WAVE));
                 x = lse_fold(x, y);
             }
-            ce = x.x + logf(x.y) - lab_logit[m];
+            const float lse = x.x + logf(x.y);
+            if (lse_out && lane == 0) lse_out[m] = lse;
+            ce = lse - lab_logit[m];
         }
         if (lane == 0 && row_loss) row_loss[b * (G - 1) + j - 1] = ce;
         acc += expf(-(float)(j - 1) / (float)G) * ce;
@@ -550,6 +552,30 @@ __global__ __launch_bounds__(BLOCK_LOSS_THREADS) void block_loss_kernel(
         for (int k = 0; k < NW; ++k) tot += red[k];
         for (int j = 1; j < G; ++j) wsum += expf(-(float)(j - 1) / (float)G);
         loss[0] = tot / ((float)(M / G) * wsum);
+    }
+}
+
+// Gradient of the block loss with respect to the mask rows' logits:
+//   dL/dz[b][j][v] = w_j / (batch * sum_j w_j) * (exp(z[b][j][v] - LSE[b][j]) - [v == label[b][j]])
+// z and dz are fp32 [batch][gamma-1][vocab] and may be the same buffer (in place).
+// blockIdx.y is the mask row (b, j); the x blocks stride over its vocabulary, consecutive
+// threads on consecutive ids.  A row whose label is outside [0, vocab) gets NaN.
+__global__ __launch_bounds__(256) void block_loss_grad_kernel(const float* z, float* dz, const float* __restrict__ lse,
+                                                              const int* __restrict__ labels, int batch, int gamma,
+                                                              int vocab) {
+    const int row = blockIdx.y;                          // b * (gamma - 1) + j - 1
+    const int b = row / (gamma - 1), j = row % (gamma - 1) + 1;
+    float wsum = 0.f;
+    for (int k = 1; k < gamma; ++k) wsum += expf(-(float)(k - 1) / (float)gamma);
+    const float c = expf(-(float)(j - 1) / (float)gamma) / ((float)batch * wsum);
+    const int lab = labels[row];
+    const bool bad = lab < 0 || lab >= vocab;
+    const float l = lse[b * gamma + j];
+    const float* zr = z + (long long)row * vocab;
+    float* dr = dz + (long long)row * vocab;
+    for (int v = blockIdx.x * blockDim.x + threadIdx.x; v < vocab; v += gridDim.x * blockDim.x) {
+        const float p = __expf(zr[v] - l);
+        dr[v] = bad ? __int_as_float(0x7fc00000) : c * (p - (v == lab ? 1.f : 0.f));
     }
 }
 

@@ -289,15 +289,19 @@ int dflash_inject_kv_input_fusion(const dflash_config *cfg, const dflash_weights
  *   labels      int32 [batch][gamma-1], each in [0, vocab)
  *   loss        fp32 [1]
  *   row_loss    nullable fp32 [batch][gamma-1]: CE[b][j]
+ *   dlogits     nullable fp32 [batch][gamma-1][V]: d loss / d logits =
+ *               w_j / (batch * sum_j w_j) * (softmax(logits)[v] - [v == label]);
+ *               when dbg_logits is NULL the logits are first written here and
+ *               then replaced by the gradient
  *   dbg_logits  nullable fp32 [batch][gamma-1][V]: logits of the mask rows
  * The block's K/V are not written, len is not changed.  A label outside
  * [0, vocab) sets DFLASH_STATUS_BAD_TOKEN and makes its row's CE and loss NaN.
- * Sums run in fixed orders: the result is deterministic.  Forward only (no
- * gradients).  Workspace: dflash_workspace_bytes(cfg, batch, 0); argument
+ * Sums run in fixed orders: the result is deterministic.  The gradient stops
+ * at the logits (no backward pass through the drafter).  Workspace: dflash_workspace_bytes(cfg, batch, 0); argument
  * errors as for dflash_draft_block. */
 int dflash_block_loss(const dflash_config *cfg, const dflash_weights *w, const dflash_kv *kv,
                       int32_t batch, int32_t gamma, const int32_t *anchor, const int32_t *labels,
-                      float *loss, float *row_loss, float *dbg_logits,
+                      float *loss, float *row_loss, float *dlogits, float *dbg_logits,
                       void *workspace, size_t workspace_bytes, void *stream);
 
 /* Human-readable name of a dflash_status value (static string). */

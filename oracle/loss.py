@@ -63,3 +63,18 @@ def block_loss(m: DraftModel, kv: KVCache, anchors: Sequence[int], labels: np.nd
         zs.append(z)
     ce = np.stack(ces)
     return weighted_block_loss(ce), ce, np.stack(zs)
+
+
+def block_loss_grad(z: np.ndarray, labels: np.ndarray) -> np.ndarray:
+    """Gradient of ``weighted_block_loss(CE(z, labels))`` with respect to the logits
+    z [B][gamma-1][V]: row (b, j) contributes w_j / (B * sum_j w_j) * CE[b][j], and the
+    derivative of a row's cross-entropy is softmax(z[b][j]) minus the one-hot label."""
+    z = np.asarray(z, dtype=np.float64)
+    B, R, V = z.shape
+    w = position_weights(R + 1)
+    p = np.exp(z - z.max(axis=-1, keepdims=True))
+    p /= p.sum(axis=-1, keepdims=True)
+    onehot = np.zeros_like(p)
+    lab = np.asarray(labels, dtype=np.int64)
+    np.put_along_axis(onehot, lab[..., None], 1.0, axis=-1)
+    return (w[None, :, None] / (B * w.sum())) * (p - onehot)

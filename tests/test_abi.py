@@ -159,7 +159,7 @@ def test_block_loss_host_errors():
     ws_need = L.dflash_workspace_bytes(ctypes.byref(c), 1, 0)
     call = lambda **k: L.dflash_block_loss(ctypes.byref(k.get("c", c)), ctypes.byref(k.get("w", w)), ctypes.byref(kv),
                                            k.get("batch", 1), k.get("gamma", 8), k.get("anchor", FAKE),
-                                           k.get("labels", FAKE), k.get("loss", FAKE), None, None,
+                                           k.get("labels", FAKE), k.get("loss", FAKE), None, None, None,
                                            k.get("ws", FAKE), k.get("wsb", ws_need), None)
     assert call(gamma=1) == DFLASH_EINVAL
     assert call(gamma=9) == DFLASH_EINVAL           # > gamma_max

@@ -55,11 +55,26 @@ def _loss_case(cfg, batch, lengths, gamma, tag):
     assert e_z < tol(cfg) and e_ce < tol(cfg) and e_L < tol(cfg)
     # the device's own reduction of its row losses, in fp64, agrees closely
     assert abs(got_L - OL.weighted_block_loss(got_ce)) <= 1e-5 * abs(got_L)
-    # determinism: a second call gives the same bits
+    # determinism: a second call gives the same bits; with the gradient, written in place
+    # over the logits (no dbg_logits) and next to separate logits, both against the oracle
     loss2 = torch.full((1,), float("nan"), dtype=torch.float32, device="cuda")
-    P.dfl.block_loss(P.model, P.cache, gamma, P.dev_i32(anchors), P.dev_i32(labels), loss2, P.ws)
+    g_in = torch.full((batch, gamma - 1, cfg.vocab), float("nan"), dtype=torch.float32, device="cuda")
+    P.dfl.block_loss(P.model, P.cache, gamma, P.dev_i32(anchors), P.dev_i32(labels), loss2, P.ws, dlogits=g_in)
+    lg2 = torch.full_like(g_in, float("nan"))
+    g_sep = torch.full_like(g_in, float("nan"))
+    P.dfl.block_loss(P.model, P.cache, gamma, P.dev_i32(anchors), P.dev_i32(labels), loss2, P.ws,
+                     dbg_logits=lg2, dlogits=g_sep)
     torch.cuda.synchronize()
     assert float(loss2.item()) == got_L
+    g_ref = OL.block_loss_grad(z_ref, labels)
+    g_in, g_sep = g_in.cpu().numpy(), g_sep.cpu().numpy()
+    e_g = rel_err(g_in, g_ref)
+    log(f"  dlogits rel={e_g:.2e}")
+    assert np.isfinite(g_in).all() and e_g < tol(cfg)
+    np.testing.assert_array_equal(g_in, g_sep)
+    np.testing.assert_array_equal(lg2.cpu().numpy(), got_z)
+    # softmax minus one-hot: every row's gradient sums to ~0
+    assert np.abs(g_in.astype(np.float64).sum(axis=-1)).max() < 1e-5
     return P, anchors, labels
 
 

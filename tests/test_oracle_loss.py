@@ -97,3 +97,21 @@ def test_block_loss_uses_the_draft_forward_logits():
     _, ce_w, _ = OL.block_loss(m, kv, anchors, worst, 8)
     assert np.all(ce_w >= math.log(cfg.vocab))
     assert L == pytest.approx(OL.weighted_block_loss(ce), rel=1e-15)
+
+
+def test_gradient_equals_torch_autograd():
+    """d L / d logits against torch autograd through F.cross_entropy (library routines)."""
+    rng = np.random.default_rng(4)
+    B, R, V = 3, 7, 50
+    z = rng.normal(size=(B, R, V)) * 2.0
+    lab = rng.integers(0, V, size=(B, R))
+    zt = torch.tensor(z, requires_grad=True)
+    ce = F.cross_entropy(zt.reshape(-1, V), torch.from_numpy(lab).reshape(-1), reduction="none").reshape(B, R)
+    w = torch.from_numpy(OL.position_weights(R + 1))
+    L = (ce * w[None, :]).sum() / (B * w.sum())
+    L.backward()
+    g = OL.block_loss_grad(z, lab)
+    np.testing.assert_allclose(g, zt.grad.numpy(), rtol=1e-12, atol=1e-15)
+    assert float(L) == pytest.approx(OL.weighted_block_loss(OL.cross_entropy_rows(z.reshape(-1, V), lab.reshape(-1)).reshape(B, R)), rel=1e-13)
+    # every row's gradient sums to zero (softmax minus one-hot)
+    np.testing.assert_allclose(g.sum(axis=-1), 0.0, atol=1e-15)
