@@ -112,6 +112,6 @@ def test_gradient_equals_torch_autograd():
     L.backward()
     g = OL.block_loss_grad(z, lab)
     np.testing.assert_allclose(g, zt.grad.numpy(), rtol=1e-12, atol=1e-15)
-    assert float(L) == pytest.approx(OL.weighted_block_loss(OL.cross_entropy_rows(z.reshape(-1, V), lab.reshape(-1)).reshape(B, R)), rel=1e-13)
+    assert L.item() == pytest.approx(OL.weighted_block_loss(OL.cross_entropy_rows(z.reshape(-1, V), lab.reshape(-1)).reshape(B, R)), rel=1e-13)
     # every row's gradient sums to zero (softmax minus one-hot)
     np.testing.assert_allclose(g.sum(axis=-1), 0.0, atol=1e-15)
