@@ -49,6 +49,11 @@ design notes of this repository):
   R12 accept length = accepted drafts + 1 bonus token.
   R14 the block's own K/V are not kept in the cache.
 
+Parity unpinned: R3-R7, R9, R10 and the weight initialisation are conventions the
+pages do not fix.  The functions that implement them are pinned (library routines,
+closed forms, brute force), but which convention is the pages' one is not: an
+independent oracle choosing differently would disagree there.
+
 Precision contract: numbers are carried in ``dtype`` (fp64 by default).  For
 bf16 configurations ``rho`` rounds to the nearest bf16 (ties to even) exactly
 at the points the GPU path must also round: every GEMM input (A operand), the

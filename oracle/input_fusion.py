@@ -19,6 +19,10 @@ reading that the rest supports, used here:
     so the block pass (``draft``) reads per-layer context K/V exactly as after KV
     injection; len advances by the number of rows.
 
+Parity unpinned: that this is the pages' input-fusion drafter is a reading (they give no
+formula); the computation itself is pinned (a torch causal-attention composite, layer 0
+equal to KV injection, causality, chunking).
+
 With one layer the two conditionings coincide (layer 0's K/V are the projections
 of c in both); from the second layer on, input fusion's K/V come from hidden states
 that passed through the layers below.

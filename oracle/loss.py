@@ -18,6 +18,9 @@ Readings where the pages are silent:
     a normalisation that leaves the direction of every gradient unchanged;
   * CE[b][j] = logsumexp(z[b][j]) - z[b][j][label] with the logits z of the
     drafter's forward pass exactly as drafting computes them (``draft``).
+
+Parity unpinned: the normalisation of the batch loss and the mapping of block position k
+to mask row j are readings; the weights, the cross-entropy and the gradient are pinned.
 """
 from __future__ import annotations
 
