@@ -9,7 +9,8 @@ is compared.
 
 Two draft sources: the GPU drafter itself (random weights: drafts mostly rejected), and
 planted drafts (the oracle's greedy continuation with seeded corruptions), which make the
-loop take partial acceptances of every length."""
+loop take partial acceptances of every length.  With ``policy`` the block size of every
+cycle is chosen by dflash_choose_gamma from the accept lengths so far and a cost table."""
 import numpy as np
 import pytest
 
@@ -25,7 +26,7 @@ pytestmark = pytest.mark.gpu
 NEAR_TIE = 1e-3          # fp32 storage: logit errors are ~1e-6 of the logits' scale
 
 
-def _spec_loop(cfg, batch, prompt_len, gamma, n_tokens, mode, n_target_layers=4, seed=5):
+def _spec_loop(cfg, batch, prompt_len, gamma, n_tokens, mode, n_target_layers=4, seed=5, policy=None):
     import torch
     import block_diffusion_drafter_states_amd as dfl
     dev = "cuda"
@@ -64,14 +65,18 @@ def _spec_loop(cfg, batch, prompt_len, gamma, n_tokens, mode, n_target_layers=4,
     out = [[int(t)] for t in anchor.cpu().numpy()]
 
     rng = np.random.default_rng(seed)
-    d = torch.empty((batch, gamma - 1), dtype=torch.int32, device=dev)
-    y = torch.empty((batch, gamma), dtype=torch.int32, device=dev)
-    feat = torch.empty((batch, gamma, F, H), dtype=target.storage_dtype, device=dev)
     tau = torch.empty((batch,), dtype=torch.int32, device=dev)
-    committed = torch.empty((batch, gamma), dtype=torch.int32, device=dev)
     nxt = torch.empty((batch,), dtype=torch.int32, device=dev)
-    taus = []
+    taus, used = [], []
+    hist_t, hist_g = [], []
     while min(len(o) for o in out) < n_tokens:
+        if policy is not None:             # block size of this cycle from the accept lengths so far
+            gamma, _ = dfl.choose_gamma(hist_t[-64:], hist_g[-64:], policy, 2, gmax)
+        used.append(gamma)
+        d = torch.empty((batch, gamma - 1), dtype=torch.int32, device=dev)
+        y = torch.empty((batch, gamma), dtype=torch.int32, device=dev)
+        feat = torch.empty((batch, gamma, F, H), dtype=target.storage_dtype, device=dev)
+        committed = torch.empty((batch, gamma), dtype=torch.int32, device=dev)
         if mode == "drafter":
             dfl.draft_block(drafter, dcache, gamma, anchor, d, ws_d)
         else:
@@ -95,8 +100,10 @@ def _spec_loop(cfg, batch, prompt_len, gamma, n_tokens, mode, n_target_layers=4,
         for b in range(batch):
             out[b].extend(int(v) for v in c_h[b, :t_h[b]])
         taus.append([int(v) for v in t_h])
+        hist_t.extend(int(v) for v in t_h)
+        hist_g.extend([gamma] * batch)
     assert list(tcache.len.cpu().numpy()[:batch]) == list(dcache.len.cpu().numpy()[:batch])
-    log(f"  cycles {len(taus)} accept lengths {taus}")
+    log(f"  cycles {len(taus)} block sizes {used} accept lengths {taus}")
 
     for b in range(batch):
         got, ref = out[b][:n_tokens], refs[b][:n_tokens]
@@ -107,7 +114,7 @@ def _spec_loop(cfg, batch, prompt_len, gamma, n_tokens, mode, n_target_layers=4,
         gap = float(top2_gap(logits[-1]))
         log(f"  seq {b}: first difference at token {i} (oracle top-2 gap {gap:.3e})")
         assert gap < NEAR_TIE, f"sequence {b} differs from greedy decoding at token {i}"
-    return taus
+    return (taus, used) if policy is not None else taus
 
 
 def test_spec_loop_gpu_drafter_is_lossless():
@@ -118,3 +125,14 @@ def test_spec_loop_planted_partial_acceptances_is_lossless():
     taus = _spec_loop(synth.get_config("C1"), 2, 13, 8, 48, "planted")
     flat = [t for row in taus for t in row]
     assert max(flat) > 1 and min(flat) < 8        # partial acceptances actually happened
+
+
+def test_spec_loop_with_block_size_policy_is_lossless():
+    """Block size per cycle from dflash_choose_gamma with a cost table affine in the block size,
+    steep enough that the choice follows the acceptance estimate (6 at p = 0.8, 5 at 0.75, 4 at
+    0.7): the loop changes its block size and stays lossless."""
+    cfg = synth.get_config("C1")
+    cost = [0.0, 0.0] + [300.0 + 50.0 * g for g in range(2, cfg.gamma_max + 1)]
+    taus, used = _spec_loop(cfg, 2, 13, 8, 56, "planted", seed=9, policy=cost)
+    assert len(set(used)) > 1            # the policy moved the block size
+    assert all(2 <= g <= cfg.gamma_max for g in used)
