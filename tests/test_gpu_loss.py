@@ -105,3 +105,46 @@ def test_block_loss_bad_label_sets_status_and_nan():
     assert P.status() & P.dfl._abi.STATUS_BAD_TOKEN
     assert math.isnan(float(loss.item())) and math.isnan(r[1, 3])
     assert np.isfinite(np.delete(r.ravel(), 1 * 7 + 3)).all()
+
+
+def test_block_loss_on_randomly_anchored_blocks_of_a_target_decode():
+    """The training objective as the summary's section 2.3 sets it up: a frozen (tiny,
+    random-init) target decodes a response; anchors are drawn uniformly from the response;
+    each block's context is the target's tapped hidden states before its anchor (injected),
+    its labels the target's own tokens after the anchor.  GPU loss, row losses and gradient
+    against the oracle on the same blocks."""
+    import torch
+    from oracle.tiny_target import TinyTarget, greedy
+    cfg = synth.get_config("C1")
+    B, G = 3, cfg.gamma
+    cap = gen.kv_capacity(cfg, 64)
+    P = Pair(cfg, B, cap, 64)
+    tt = TinyTarget(cfg, P.om)
+    prompt = [int(t) for t in gen.tokens(cfg, "loss.anchors.prompt", (9,))]
+    seq = prompt + greedy(tt, prompt, 40)
+    _, hiddens = tt.forward(seq)
+    feats = tt.storage_features(hiddens)                          # [n][F][H], what injection reads
+    rng = gen.rng(cfg, "loss.anchors.draw")
+    anchors_pos = [int(a) for a in rng.integers(len(prompt), len(seq) - G + 1, size=B)]
+    log(f"case random anchors at {anchors_pos} of a {len(seq)}-token sequence")
+    rows = max(anchors_pos)
+    feat = np.zeros((B, rows) + feats.shape[1:], dtype=np.float64)
+    for b, a in enumerate(anchors_pos):
+        feat[b, :a] = feats[:a]
+    P.inject(feat.astype(np.float32), np.array(anchors_pos, dtype=np.int32))
+    torch.cuda.synchronize()
+    assert P.status() == 0 and list(P.cache.len.cpu().numpy()[:B]) == anchors_pos
+    anchors = np.array([seq[a] for a in anchors_pos], dtype=np.int32)
+    labels = np.array([seq[a + 1:a + G] for a in anchors_pos], dtype=np.int32)
+    loss = torch.zeros((1,), dtype=torch.float32, device="cuda")
+    row = torch.zeros((B, G - 1), dtype=torch.float32, device="cuda")
+    dz = torch.zeros((B, G - 1, cfg.vocab), dtype=torch.float32, device="cuda")
+    P.dfl.block_loss(P.model, P.cache, G, P.dev_i32(anchors), P.dev_i32(labels), loss, P.ws, row, dlogits=dz)
+    torch.cuda.synchronize()
+    L_ref, ce_ref, z_ref = OL.block_loss(P.om, P.okv, anchors, labels, G)
+    e_L = abs(float(loss.item()) - L_ref) / abs(L_ref)
+    e_ce = rel_err(row.cpu().numpy(), ce_ref)
+    e_g = rel_err(dz.cpu().numpy(), OL.block_loss_grad(z_ref, labels))
+    log(f"  loss gpu={float(loss.item()):.6f} oracle={L_ref:.6f} rel={e_L:.2e}; row CE rel={e_ce:.2e}; dlogits rel={e_g:.2e}")
+    assert P.status() == 0
+    assert e_L < tol(cfg) and e_ce < tol(cfg) and e_g < tol(cfg)
