@@ -10,6 +10,7 @@
 #include "attention.hpp"
 #include "gemm.hpp"
 #include "gemm_tiled.hpp"
+#include "loss.hpp"
 #include "small_kernels.hpp"
 
 using namespace dflash;
