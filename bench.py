@@ -174,6 +174,43 @@ def cpu_oracle_baseline(cfg, W, K, V, lengths, feats, anchors, plant_k, gammas, 
 GEMM_LAUNCHES = ("fuse", "inject_kv", "qkv_proj", "o_proj", "gate_up", "down_proj", "lm_head_argmax")
 
 
+def measured_peaks(torch):
+    """What plain probe kernels reach on this GPU (libdflash_probe.so): the HBM read rate of a
+    grid-stride streaming kernel over 4 GiB (median of 5) and the bf16 MFMA rate of independent
+    16x16x32 MFMA chains on every SIMD (median of 5)."""
+    lib = ctypes.CDLL(os.path.join(HERE, "block_diffusion_drafter_states_amd", "libdflash_probe.so"))
+    lib.dflash_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint, ctypes.c_void_p,
+                                      ctypes.c_int, ctypes.c_void_p]
+    lib.dflash_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    stream = torch.cuda.current_stream().cuda_stream
+    nbytes = 4 << 30
+    buf = torch.zeros(nbytes // 4, dtype=torch.int32, device="cuda")
+    blocks = 256 * 16
+    sink = torch.zeros(blocks, dtype=torch.int32, device="cuda")
+    fsink = torch.zeros(blocks, dtype=torch.float32, device="cuda")
+
+    def time_ms(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        if fn() != 0:
+            raise RuntimeError("probe launch failed")
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    read = lambda: lib.dflash_probe_read(buf.data_ptr(), nbytes, 0x9E3779B9, sink.data_ptr(), blocks, stream)
+    time_ms(read)
+    gbs = nbytes / (statistics.median(time_ms(read) for _ in range(5)) * 1e-3) / 1e9
+    iters, mblocks = 2000, 256 * 8
+    mfma = lambda: lib.dflash_probe_mfma(iters, mblocks, fsink.data_ptr(), stream)
+    time_ms(mfma)
+    flops = mblocks * 4 * iters * 8 * 16384.0
+    tflops = flops / (statistics.median(time_ms(mfma) for _ in range(5)) * 1e-3) / 1e12
+    del buf
+    torch.cuda.empty_cache()
+    return {"read_GBs": round(gbs, 1), "mfma_bf16_TFLOPs": round(tflops, 1)}
+
+
 def prefill(args, dfl, cfg, gen, torch):
     """Injection of a whole prompt's feature rows (C3: 4096 positions) into an empty cache:
     the fusion and every layer's W_k | W_v over all rows, an MFMA-bound contraction."""
@@ -618,6 +655,10 @@ def main():
                      "avg_launch_us": round(lm_avg_ms * 1000, 2)},
         "kernels_us_per_cycle": kern_us,
     }
+    # plain probe kernels on the same GPU: a grid-stride read (a floor for the attainable read
+    # rate: the LM head's direct-to-LDS stream is faster) and an independent-MFMA loop
+    peaks = measured_peaks(torch)
+    result["probes"] = peaks
     if B > 1:
         # contraction throughput (the dense-MFMA regime of large batches): the cycle's GEMM flops
         # over the whole cycle and over the projection launches alone
@@ -627,7 +668,9 @@ def main():
         result["mfma"] = {"gemm_gflop_per_cycle": round(gf / 1e9, 1), "peak_tflops": peak,
                           "frac_whole_cycle": round(gf * cps / 1e12 / peak, 4),
                           "frac_gemm_launches": round(gf / (gemm_us * 1e-6) / 1e12 / peak, 4),
-                          "gemm_us_per_cycle": round(gemm_us, 1)}
+                          "gemm_us_per_cycle": round(gemm_us, 1),
+                          "frac_gemm_launches_of_mfma_probe": round(
+                              gf / (gemm_us * 1e-6) / 1e12 / peaks["mfma_bf16_TFLOPs"], 4)}
     if not args.no_cpu_baseline:
         Kh, Vh = gen.context_kv(cfg, lengths, cap, tag="bench.ctx")
         result["cpu_baseline"] = cpu_oracle_baseline(cfg, W, Kh, Vh, lengths, feats_host, anchor0, plant_k, gseq,

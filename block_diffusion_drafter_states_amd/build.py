@@ -25,9 +25,11 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> str:
-    src = os.path.join(CSRC, "dflash.hip")
-    tmp = OUT + ".tmp"
+PROBE_OUT = os.path.join(HERE, "libdflash_probe.so")
+
+
+def _compile(src: str, out: str, verbose: bool) -> None:
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-shared", "-fPIC",
            # packed fp32 VALU forms are kept out of the generated code
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -38,8 +40,14 @@ def build(verbose: bool = False) -> str:
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed building libdflash.so")
-    os.replace(tmp, OUT)
+        raise RuntimeError(f"hipcc failed building {os.path.basename(out)}")
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """libdflash.so (the C ABI) and libdflash_probe.so (the benchmark's bandwidth / MFMA probes)."""
+    _compile(os.path.join(CSRC, "dflash.hip"), OUT, verbose)
+    _compile(os.path.join(CSRC, "probe.hip"), PROBE_OUT, verbose)
     return OUT
 
 
