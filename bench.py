@@ -182,6 +182,7 @@ def measured_peaks(torch):
     lib.dflash_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint, ctypes.c_void_p,
                                       ctypes.c_int, ctypes.c_void_p]
     lib.dflash_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.dflash_probe_mfma32.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     stream = torch.cuda.current_stream().cuda_stream
     nbytes = 4 << 30
     buf = torch.zeros(nbytes // 4, dtype=torch.int32, device="cuda")
@@ -206,9 +207,14 @@ def measured_peaks(torch):
     time_ms(mfma)
     flops = mblocks * 4 * iters * 8 * 16384.0
     tflops = flops / (statistics.median(time_ms(mfma) for _ in range(5)) * 1e-3) / 1e12
+    mfma32 = lambda: lib.dflash_probe_mfma32(iters, mblocks, fsink.data_ptr(), stream)
+    time_ms(mfma32)
+    flops32 = mblocks * 4 * iters * 4 * 32768.0
+    tflops32 = flops32 / (statistics.median(time_ms(mfma32) for _ in range(5)) * 1e-3) / 1e12
     del buf
     torch.cuda.empty_cache()
-    return {"read_GBs": round(gbs, 1), "mfma_bf16_TFLOPs": round(tflops, 1)}
+    return {"read_GBs": round(gbs, 1), "mfma_bf16_TFLOPs": round(tflops, 1),
+            "mfma32_bf16_TFLOPs": round(tflops32, 1)}
 
 
 def prefill(args, dfl, cfg, gen, torch):

@@ -54,6 +54,31 @@ __global__ __launch_bounds__(256) void mfma_probe_kernel(int iters, float* __res
     if (threadIdx.x == 0) sink[blockIdx.x] = s;
 }
 
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+
+// The same with v_mfma_f32_32x32x16_bf16 (32 x 32 x 16 x 2 flops per instruction), NACC32
+// independent 32 x 32 accumulators per wave.
+constexpr int NACC32 = 4;
+
+__global__ __launch_bounds__(256) void mfma32_probe_kernel(int iters, float* __restrict__ sink) {
+    bf16x8_t a, b;
+    for (int j = 0; j < 8; ++j) {
+        a[j] = (short)(0x3f80 + (threadIdx.x & 7));
+        b[j] = (short)(0x3f80 - (threadIdx.x & 3));
+    }
+    f32x16_t acc[NACC32];
+    for (int k = 0; k < NACC32; ++k)
+        for (int e = 0; e < 16; ++e) acc[k][e] = 0.f;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int k = 0; k < NACC32; ++k) acc[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[k], 0, 0, 0);
+    }
+    float s = 0.f;
+    for (int k = 0; k < NACC32; ++k)
+        for (int e = 0; e < 16; ++e) s += acc[k][e];
+    if (threadIdx.x == 0) sink[blockIdx.x] = s;
+}
+
 }  // namespace
 
 extern "C" {
@@ -73,6 +98,14 @@ int dflash_probe_read(const void* buf, size_t bytes, unsigned key, unsigned* sin
 int dflash_probe_mfma(int iters, int blocks, float* sink, void* stream) {
     if (!sink || blocks < 1 || iters < 1) return -1;
     hipLaunchKernelGGL(mfma_probe_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream), iters, sink);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// As dflash_probe_mfma with 32 x 32 x 16 MFMAs: flops issued blocks * 4 * iters * 4 * 32768.
+int dflash_probe_mfma32(int iters, int blocks, float* sink, void* stream) {
+    if (!sink || blocks < 1 || iters < 1) return -1;
+    hipLaunchKernelGGL(mfma32_probe_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream), iters,
+                       sink);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
