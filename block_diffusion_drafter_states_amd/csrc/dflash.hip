@@ -5,7 +5,6 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
-#include <type_traits>
 
 #include "../../include/dflash.h"
 #include "attention.hpp"
@@ -327,16 +326,8 @@ template <typename T, int EPI, int BN>
 int launch_gemm_tiled(const GemmArgs& a, const GemmPlan& p, hipStream_t st, Tracer& tr, const char* name) {
     dim3 grid(cdiv(p.n_tiles, 8) * 8, p.mgroups, p.layers);   // the kernel maps blocks XCD-aware
     tr.begin(name);
-    // bf16 store / argmax / log-sum-exp blocks on the 32x32x16 MFMA form (twice the matrix-core
-    // rate of 16x16x32 on gfx950); SwiGLU and fp32 on the 16x16 forms
-    constexpr bool MF32 = std::is_same<T, bf16_t>::value && EPI != EPI_SWIGLU;
-    if constexpr (MF32) {
-        if (p.kb == 128) hipLaunchKernelGGL((gemm_tiled32_kernel<EPI, BN, 128>), grid, dim3(TG_THREADS), p.lds, st, a);
-        else hipLaunchKernelGGL((gemm_tiled32_kernel<EPI, BN, 256>), grid, dim3(TG_THREADS), p.lds, st, a);
-    } else {
-        if (p.kb == 128) hipLaunchKernelGGL((gemm_tiled_kernel<T, EPI, BN, 128>), grid, dim3(TG_THREADS), p.lds, st, a);
-        else hipLaunchKernelGGL((gemm_tiled_kernel<T, EPI, BN, 256>), grid, dim3(TG_THREADS), p.lds, st, a);
-    }
+    if (p.kb == 128) hipLaunchKernelGGL((gemm_tiled_kernel<T, EPI, BN, 128>), grid, dim3(TG_THREADS), p.lds, st, a);
+    else hipLaunchKernelGGL((gemm_tiled_kernel<T, EPI, BN, 256>), grid, dim3(TG_THREADS), p.lds, st, a);
     const bool ok = hipGetLastError() == hipSuccess;
     tr.end();
     return ok ? DFLASH_OK : DFLASH_ELAUNCH;

@@ -309,249 +309,3 @@ __global__ __launch_bounds__(TG_THREADS) void gemm_tiled_kernel(const GemmArgs p
 
 
 }  // namespace dflash
-
-namespace dflash {
-
-// ---------------------------------------------------------------------------------------------
-// The same contraction on v_mfma_f32_32x32x16_bf16 (bf16 only; store, argmax and log-sum-exp
-// epilogues).  On gfx950 that form sustains about twice the matrix-core rate of the
-// 16x16x32 one.  Staging (A and W through the same LDS stages and swizzle) is unchanged; a
-// wave's 64 x BN/2 block is 2 x BN/64 fragments of 32 x 32.  Operand fragments: lane l holds
-// row l % 32 of 32 rows, elements 8 (l / 32) .. +7 of a 16-element k step.  Accumulator:
-// element v of lane l is row 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32.
-
-// 16 bytes (8 bf16) of row `row` (0..31 of a 32-row fragment whose first 16-row LDS tile is
-// `tile`), k piece `piece` (16-byte chunk index within the KB-byte row)
-template <int KB>
-__device__ __forceinline__ u32x4_t tg32_piece(const unsigned char* tile, int row, int piece) {
-    const unsigned char* t = tile + (row >> 4) * (16 * KB);
-    const int rho = row & 15;
-    return *reinterpret_cast<const u32x4_t*>(t + rho * KB + ((piece ^ tg_swz<KB>(rho)) << 4));
-}
-
-template <int EPI, int BN>
-__device__ __forceinline__ void tg32_epilogue(const GemmArgs& p, const GemmLayer& L, f32x16_t (&acc)[2][BN / 64],
-                                              int tile, int m0, int wm, int wn, unsigned char* smem) {
-    constexpr int WN = BN / 64;
-    const int lane = threadIdx.x & 63, h = lane >> 5, c = lane & 31;
-    if constexpr (EPI == EPI_STORE) {
-        float* red = reinterpret_cast<float*>(smem);
-        float* const outp = L.out ? L.out : p.out;
-        const int ncol0 = tile * BN + wn * (BN / 2);
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int mr = wm * 64 + a * 32 + 8 * (v >> 2) + 4 * h + (v & 3);   // row within the workgroup
-                const int m = m0 + mr;
-                float ss = 0.f;
-#pragma unroll
-                for (int b = 0; b < WN; ++b) {
-                    const int n = ncol0 + b * 32 + c;
-                    float x = acc[a][b][v];
-                    if (m < p.M && n < p.N) {
-                        float* o = outp + (long long)m * p.ldo + n;
-                        if (p.residual) x += *o;
-                        *o = x;
-                    } else {
-                        x = 0.f;
-                    }
-                    ss += x * x;
-                }
-                // the 32 lanes of a half hold the row's columns: fixed xor order
-#pragma unroll
-                for (int o = 1; o < 32; o <<= 1) ss += __shfl_xor(ss, o, WAVE);
-                if (c == 0) red[wn * TG_BM + mr] = ss;
-            }
-        __syncthreads();
-        if (p.ssq_out && threadIdx.x < TG_BM && m0 + (int)threadIdx.x < p.M)
-            p.ssq_out[(long long)tile * p.ssq_out_ld + m0 + threadIdx.x] = red[threadIdx.x] + red[TG_BM + threadIdx.x];
-    } else if constexpr (EPI == EPI_ARGMAX) {
-        unsigned long long* redu = reinterpret_cast<unsigned long long*>(smem);
-        const int G = p.gamma;
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int mr = wm * 64 + a * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-                const int m = m0 + mr;
-                unsigned long long best = 0ull;
-#pragma unroll
-                for (int b = 0; b < WN; ++b) {
-                    const int n = tile * BN + wn * (BN / 2) + b * 32 + c;
-                    if (m < p.M && n < p.N) {
-                        const float x = acc[a][b][v];
-                        const unsigned long long key = pack_argmax(x, (uint32_t)n);
-                        best = key > best ? key : best;
-                        const int bb = m / G, jj = m % G;
-                        if (p.dbg_logits && jj >= p.dbg_first)
-                            p.dbg_logits[((long long)bb * (G - p.dbg_first) + (jj - p.dbg_first)) * p.N + n] = x;
-                    }
-                }
-#pragma unroll
-                for (int o = 1; o < 32; o <<= 1) {
-                    const unsigned long long other = __shfl_xor(best, o, WAVE);
-                    best = other > best ? other : best;
-                }
-                if (c == 0) redu[wn * TG_BM + mr] = best;
-            }
-        __syncthreads();
-        if (threadIdx.x < TG_BM && m0 + (int)threadIdx.x < p.M) {
-            const unsigned long long x0 = redu[threadIdx.x], x1 = redu[TG_BM + threadIdx.x];
-            p.amax[(long long)tile * p.M + m0 + threadIdx.x] = x0 > x1 ? x0 : x1;
-        }
-    } else {    // EPI_LSE
-        float2* redl = reinterpret_cast<float2*>(smem);
-        const int G = p.gamma;
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int mr = wm * 64 + a * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-                const int m = m0 + mr;
-                const int bb = m / G, jj = m % G;
-                const int lab = (m < p.M && jj >= 1) ? p.labels[bb * (G - 1) + jj - 1] : -1;
-                float mx = -INFINITY;
-#pragma unroll
-                for (int b = 0; b < WN; ++b) {
-                    const int n = tile * BN + wn * (BN / 2) + b * 32 + c;
-                    if (m < p.M && n < p.N) {
-                        const float x = acc[a][b][v];
-                        mx = fmaxf(mx, x);
-                        if (n == lab) p.lab_logit[m] = x;
-                        if (p.dbg_logits && jj >= p.dbg_first)
-                            p.dbg_logits[((long long)bb * (G - p.dbg_first) + (jj - p.dbg_first)) * p.N + n] = x;
-                    }
-                }
-#pragma unroll
-                for (int o = 1; o < 32; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, WAVE));
-                float se = 0.f;
-#pragma unroll
-                for (int b = 0; b < WN; ++b) {
-                    const int n = tile * BN + wn * (BN / 2) + b * 32 + c;
-                    if (m < p.M && n < p.N) se += __expf(acc[a][b][v] - mx);
-                }
-#pragma unroll
-                for (int o = 1; o < 32; o <<= 1) se += __shfl_xor(se, o, WAVE);
-                if (c == 0) redl[wn * TG_BM + mr] = make_float2(mx, se);
-            }
-        __syncthreads();
-        if (threadIdx.x < TG_BM && m0 + (int)threadIdx.x < p.M) {
-            const float2 x0 = redl[threadIdx.x], x1 = redl[TG_BM + threadIdx.x];
-            const float mx = fmaxf(x0.x, x1.x);
-            const float se = (x0.x == -INFINITY ? 0.f : x0.y * __expf(x0.x - mx)) +
-                             (x1.x == -INFINITY ? 0.f : x1.y * __expf(x1.x - mx));
-            p.lse[(long long)tile * p.M + m0 + threadIdx.x] = make_float2(mx, se);
-        }
-    }
-}
-
-template <int EPI, int BN, int KB>
-__global__ __launch_bounds__(TG_THREADS) void gemm_tiled32_kernel(const GemmArgs p) {
-    static_assert(BN == 128 || BN == 64, "tile width");
-    static_assert(EPI == EPI_STORE || EPI == EPI_ARGMAX || EPI == EPI_LSE, "epilogues of the 32x32 form");
-    static_assert(KB == 256 || KB == 128, "stage row bytes");
-    using T = bf16_t;
-    constexpr int STEP = Elem<T>::STEP * KB / 256;          // elements of a row per stage
-    constexpr int WN = BN / 64;                             // 32-column fragments per wave
-    constexpr int LPR = KB / 16;
-    constexpr int RPI = 64 / LPR;
-    constexpr int IPT = 16 / RPI;
-    constexpr int TILEB = 16 * KB;
-    constexpr int KS16 = KB / 32;                           // 16-element k steps per stage
-    constexpr int NI = (TG_BM + BN) / 16 * IPT;
-    constexpr int NIW = NI / 4;
-    constexpr int STAGE = tg_stage_bytes(BN, KB);
-    extern __shared__ __align__(16) unsigned char smem[];
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, h = lane >> 5, c = lane & 31;
-    const int wm = wv >> 1, wn = wv & 1;
-
-    // ---- workgroup -> (weight block, M-block): the M-blocks of a weight block share an XCD
-    const int mgroups = gridDim.y;
-    const int wlin = blockIdx.x + blockIdx.y * gridDim.x;
-    const int xcd = wlin & 7, wslot = wlin >> 3;
-    const int tile = (wslot / mgroups) * 8 + xcd;
-    const int m0 = (wslot % mgroups) * TG_BM;
-    if (tile >= p.n_tiles) return;                          // whole workgroup, before any barrier
-    const int layer = blockIdx.z;
-    const GemmLayer& L = p.layer[layer];
-    const int K = p.K;
-    const int nsteps = K / STEP;
-
-    // ---- load plan (as gemm_tiled_kernel)
-    const int lq = lane / LPR, lc = lane % LPR;
-    const void* abase = L.a ? L.a : p.a;
-    const char* src[NIW];
-    uint32_t dst[NIW];
-    const uint32_t lds0 = lds_offset(smem);
-    const int wv_u = __builtin_amdgcn_readfirstlane(wv);
-#pragma unroll
-    for (int u = 0; u < NIW; ++u) {
-        const int j = u * 4 + wv_u;
-        const int t = j / IPT, i = j % IPT;
-        const int rho = i * RPI + lq;
-        const T* rowp;
-        if (t < 8) {
-            int m = m0 + t * 16 + rho;
-            m = m < p.M ? m : p.M - 1;
-            rowp = reinterpret_cast<const T*>(abase) + (long long)m * p.lda;
-        } else {
-            const int nt = t - 8;
-            const int n0 = min(tile * BN + nt * 16, p.N - 1);
-            const int sg = n0 < p.seg_end[0] ? 0 : (n0 < p.seg_end[1] ? 1 : 2);
-            const int lo = sg == 0 ? 0 : (sg == 1 ? p.seg_end[0] : p.seg_end[1]);
-            const T* base = reinterpret_cast<const T*>(sg == 0 ? L.w[0] : (sg == 1 ? L.w[1] : L.w[2]));
-            int row = n0 - lo + rho;
-            const int rows = (sg == 0 ? p.seg_end[0] : (sg == 1 ? p.seg_end[1] : p.seg_end[2])) - lo;
-            row = min(row, rows - 1);
-            rowp = base + (long long)row * K;
-        }
-        src[u] = reinterpret_cast<const char*>(rowp) + ((lc ^ tg_swz<KB>(rho)) * 16);
-        dst[u] = (uint32_t)(t * TILEB + i * 1024);
-    }
-    auto issue = [&](int stage, int step) {
-#pragma unroll
-        for (int u = 0; u < NIW; ++u) dma_b128(src[u] + (size_t)step * KB, lds0 + stage * STAGE + dst[u]);
-    };
-
-    f32x16_t acc[2][WN];
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < WN; ++b)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
-
-    issue(0, 0);
-    if (nsteps > 1) issue(1, 1);
-    for (int s = 0; s < nsteps; ++s) {
-        if (s + 1 < nsteps) vm_wait<NIW>();
-        else vm_wait<0>();
-        __syncthreads();
-        const unsigned char* st = smem + (s & 1) * STAGE;
-        // every fragment of the stage first (k step k: piece 2k + h), then the MFMAs
-        u32x4_t af[2][KS16], bf[WN][KS16];
-#pragma unroll
-        for (int k = 0; k < KS16; ++k) {
-#pragma unroll
-            for (int a = 0; a < 2; ++a) af[a][k] = tg32_piece<KB>(st + (wm * 4 + a * 2) * TILEB, c, 2 * k + h);
-#pragma unroll
-            for (int b = 0; b < WN; ++b)
-                bf[b][k] = tg32_piece<KB>(st + (8 + wn * (BN / 32) + b * 2) * TILEB, c, 2 * k + h);
-        }
-#pragma unroll
-        for (int k = 0; k < KS16; ++k)
-#pragma unroll
-            for (int a = 0; a < 2; ++a)
-#pragma unroll
-                for (int b = 0; b < WN; ++b)
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(af[a][k]), as_bf16x8(bf[b][k]),
-                                                                         acc[a][b], 0, 0, 0);
-        __syncthreads();
-        if (s + 2 < nsteps) issue(s & 1, s + 2);
-    }
-
-    tg32_epilogue<EPI, BN>(p, L, acc, tile, m0, wm, wn, smem);
-}
-
-}  // namespace dflash
