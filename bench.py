@@ -104,6 +104,7 @@ SHAPES = {"tiny_f32": "tiny fp32 drafter", "qwen3_4b_drafter": "Qwen3-4B-shaped 
           "qwen3_8b_drafter": "Qwen3-8B-shaped drafter", "llama31_8b_drafter_b32": "LLaMA-3.1-8B-shaped drafter",
           "coder30b_drafter_longctx": "Qwen3-Coder-30B-drafter-shaped (GQA 8)"}
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}     # dense, MI355X published
+N_CU, CLOCK_HZ = 256, 2.4e9                           # MI355X compute units and peak engine clock
 
 
 def gemm_flops(cfg, B, gamma, tau_mean):
@@ -176,13 +177,15 @@ GEMM_LAUNCHES = ("fuse", "inject_kv", "qkv_proj", "o_proj", "gate_up", "down_pro
 
 def measured_peaks(torch):
     """What plain probe kernels reach on this GPU (libdflash_probe.so): the HBM read rate of a
-    grid-stride streaming kernel over 4 GiB (median of 5) and the bf16 MFMA rate of independent
-    16x16x32 MFMA chains on every SIMD (median of 5)."""
+    grid-stride streaming kernel over 4 GiB, the bf16 MFMA rate of independent 16x16x32 and
+    32x32x16 MFMA chains on every SIMD, and the LDS read rate of conflict-free 16-byte reads
+    (each the median of 5)."""
     lib = ctypes.CDLL(os.path.join(HERE, "block_diffusion_drafter_states_amd", "libdflash_probe.so"))
     lib.dflash_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint, ctypes.c_void_p,
                                       ctypes.c_int, ctypes.c_void_p]
     lib.dflash_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     lib.dflash_probe_mfma32.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.dflash_probe_lds.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_uint, ctypes.c_void_p, ctypes.c_void_p]
     stream = torch.cuda.current_stream().cuda_stream
     nbytes = 4 << 30
     buf = torch.zeros(nbytes // 4, dtype=torch.int32, device="cuda")
@@ -211,10 +214,16 @@ def measured_peaks(torch):
     time_ms(mfma32)
     flops32 = mblocks * 4 * iters * 4 * 32768.0
     tflops32 = flops32 / (statistics.median(time_ms(mfma32) for _ in range(5)) * 1e-3) / 1e12
+    lds_iters, lblocks = 8000, 256 * 4                   # 32 KB of LDS each: four per CU
+    lds = lambda: lib.dflash_probe_lds(lds_iters, lblocks, 0x9E3779B9, sink.data_ptr(), stream)
+    time_ms(lds)
+    lds_bytes = lblocks * 256 * lds_iters * 64.0
+    lds_tbs = lds_bytes / (statistics.median(time_ms(lds) for _ in range(5)) * 1e-3) / 1e12
     del buf
     torch.cuda.empty_cache()
     return {"read_GBs": round(gbs, 1), "mfma_bf16_TFLOPs": round(tflops, 1),
-            "mfma32_bf16_TFLOPs": round(tflops32, 1)}
+            "mfma32_bf16_TFLOPs": round(tflops32, 1), "lds_read_TBs": round(lds_tbs, 2),
+            "lds_bytes_per_clk_per_cu": round(lds_tbs * 1e12 / (N_CU * CLOCK_HZ), 1)}
 
 
 def prefill(args, dfl, cfg, gen, torch):

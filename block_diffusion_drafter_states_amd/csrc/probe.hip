@@ -79,6 +79,36 @@ __global__ __launch_bounds__(256) void mfma32_probe_kernel(int iters, float* __r
     if (threadIdx.x == 0) sink[blockIdx.x] = s;
 }
 
+// LDS read rate: each workgroup fills 32 KB of LDS, then every thread reads 16-byte
+// vectors from it, four per iteration, consecutive lanes at consecutive vectors (no bank
+// conflicts); the XOR of everything read decides a store into sink[blockIdx.x] that the
+// key rules out in practice.  Four VALU operations per vector read: at 64 lanes over 4
+// cycles per SIMD that caps the probe at 256 bytes per clock per CU, so a result near that
+// figure means "at least", below it the LDS is what limits.
+constexpr int LDS_VEC = 2048;
+
+__global__ __launch_bounds__(256) void lds_probe_kernel(int iters, unsigned key, unsigned* __restrict__ sink) {
+    __shared__ uint4 tile[LDS_VEC];
+    for (int i = threadIdx.x; i < LDS_VEC; i += 256) tile[i] = make_uint4(i, i * 3u, i * 5u, i * 7u + blockIdx.x);
+    __syncthreads();
+    uint4 acc = make_uint4(0u, 0u, 0u, 0u);
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint4 v = tile[(threadIdx.x + (it * 4 + u) * 256) & (LDS_VEC - 1)];
+            acc.x ^= v.x;
+            acc.y ^= v.y;
+            acc.z ^= v.z;
+            acc.w ^= v.w;
+        }
+        // the addresses repeat every two iterations: keep the compiler from merging the
+        // reads of equal addresses (which would cancel in the XOR)
+        asm volatile("" ::: "memory");
+    }
+    const unsigned a = acc.x ^ acc.y ^ acc.z ^ acc.w;
+    if (a == key) sink[blockIdx.x] = a;
+}
+
 }  // namespace
 
 extern "C" {
@@ -105,6 +135,15 @@ int dflash_probe_mfma(int iters, int blocks, float* sink, void* stream) {
 int dflash_probe_mfma32(int iters, int blocks, float* sink, void* stream) {
     if (!sink || blocks < 1 || iters < 1) return -1;
     hipLaunchKernelGGL(mfma32_probe_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream), iters,
+                       sink);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// `blocks` workgroups of 256 threads, each thread `iters` x 4 LDS reads of 16 bytes: bytes
+// read blocks * 256 * iters * 64; sink: device, `blocks` entries.
+int dflash_probe_lds(int iters, int blocks, unsigned key, unsigned* sink, void* stream) {
+    if (!sink || blocks < 1 || iters < 1) return -1;
+    hipLaunchKernelGGL(lds_probe_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream), iters, key,
                        sink);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }

@@ -269,3 +269,25 @@ def test_draft_check_flags_wrong_ids():
     assert m["argmax_self_mismatch"] == 0 and m["logits_rel"] > G.tol(cfg)
     with pytest.raises(AssertionError):
         G.assert_draft(cfg, m)
+
+
+def test_probe_library_exports_and_rejects_bad_arguments():
+    """libdflash_probe.so (the benchmark's measured ceilings) exports the four probes the
+    benchmark loads, and each returns -1 for invalid arguments before any launch."""
+    path = os.path.join(os.path.dirname(_abi.LIB_PATH), "libdflash_probe.so")
+    if not os.path.exists(path):
+        pytest.skip("libdflash_probe.so not built (run __graft_entry__.build())")
+    P = ctypes.CDLL(path)
+    out = os.popen(f"nm -D --defined-only {path}").read()
+    for name in ("dflash_probe_read", "dflash_probe_mfma", "dflash_probe_mfma32", "dflash_probe_lds"):
+        assert re.search(rf"\bT {name}\b", out), name
+    P.dflash_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint, ctypes.c_void_p, ctypes.c_int,
+                                    ctypes.c_void_p]
+    P.dflash_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    P.dflash_probe_mfma32.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    P.dflash_probe_lds.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_uint, ctypes.c_void_p, ctypes.c_void_p]
+    assert P.dflash_probe_read(None, 16, 0, None, 1, None) == -1
+    assert P.dflash_probe_read(None, 15, 0, None, 1, None) == -1
+    assert P.dflash_probe_mfma(1, 1, None, None) == -1
+    assert P.dflash_probe_mfma32(0, 1, None, None) == -1
+    assert P.dflash_probe_lds(1, 1, 0, None, None) == -1
