@@ -178,14 +178,15 @@ GEMM_LAUNCHES = ("fuse", "inject_kv", "qkv_proj", "o_proj", "gate_up", "down_pro
 def measured_peaks(torch):
     """What plain probe kernels reach on this GPU (libdflash_probe.so): the HBM read rate of a
     grid-stride streaming kernel over 4 GiB, the bf16 MFMA rate of independent 16x16x32 and
-    32x32x16 MFMA chains on every SIMD, and the LDS read rate of conflict-free 16-byte reads
-    (each the median of 5)."""
+    32x32x16 MFMA chains on every SIMD, the LDS read rate of conflict-free 16-byte reads, and the
+    direct-to-LDS load rate from L2 and from HBM (each the median of 5)."""
     lib = ctypes.CDLL(os.path.join(HERE, "block_diffusion_drafter_states_amd", "libdflash_probe.so"))
     lib.dflash_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint, ctypes.c_void_p,
                                       ctypes.c_int, ctypes.c_void_p]
     lib.dflash_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     lib.dflash_probe_mfma32.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     lib.dflash_probe_lds.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_uint, ctypes.c_void_p, ctypes.c_void_p]
+    lib.dflash_probe_dma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     stream = torch.cuda.current_stream().cuda_stream
     nbytes = 4 << 30
     buf = torch.zeros(nbytes // 4, dtype=torch.int32, device="cuda")
@@ -219,11 +220,23 @@ def measured_peaks(torch):
     time_ms(lds)
     lds_bytes = lblocks * 256 * lds_iters * 64.0
     lds_tbs = lds_bytes / (statistics.median(time_ms(lds) for _ in range(5)) * 1e-3) / 1e12
+    # direct-to-LDS loads (the GEMMs' staging path): from a 4 MiB buffer that stays in L2, and
+    # once through the 4 GiB buffer (HBM); two workgroups (64 KB of LDS each) per CU
+    dblocks = 256 * 2
+    dma_l2 = lambda: lib.dflash_probe_dma(buf.data_ptr(), 4096, 4000, dblocks, stream)
+    time_ms(dma_l2)
+    dma_l2_tbs = dblocks * 4 * 4000 * 1024.0 / (statistics.median(time_ms(dma_l2) for _ in range(5)) * 1e-3) / 1e12
+    dma_hbm_iters = (nbytes // 1024) // (dblocks * 4)
+    dma_hbm = lambda: lib.dflash_probe_dma(buf.data_ptr(), nbytes // 1024, dma_hbm_iters, dblocks, stream)
+    time_ms(dma_hbm)
+    dma_hbm_gbs = dblocks * 4 * dma_hbm_iters * 1024.0 / (statistics.median(time_ms(dma_hbm) for _ in range(5)) * 1e-3) / 1e9
     del buf
     torch.cuda.empty_cache()
     return {"read_GBs": round(gbs, 1), "mfma_bf16_TFLOPs": round(tflops, 1),
             "mfma32_bf16_TFLOPs": round(tflops32, 1), "lds_read_TBs": round(lds_tbs, 2),
-            "lds_bytes_per_clk_per_cu": round(lds_tbs * 1e12 / (N_CU * CLOCK_HZ), 1)}
+            "lds_bytes_per_clk_per_cu": round(lds_tbs * 1e12 / (N_CU * CLOCK_HZ), 1),
+            "dma_l2_TBs": round(dma_l2_tbs, 2), "dma_l2_bytes_per_clk_per_cu": round(dma_l2_tbs * 1e12 / (N_CU * CLOCK_HZ), 1),
+            "dma_hbm_GBs": round(dma_hbm_gbs, 1)}
 
 
 def prefill(args, dfl, cfg, gen, torch):

@@ -109,6 +109,29 @@ __global__ __launch_bounds__(256) void lds_probe_kernel(int iters, unsigned key,
     if (a == key) sink[blockIdx.x] = a;
 }
 
+// Direct-to-LDS load rate: every wave streams 1 KB per instruction (global_load_lds_dwordx4,
+// 16 bytes per lane) from a buffer of n_chunks 1 KB chunks (grid-stride over the waves) into a
+// ring of 16 LDS slots of its own, at most 9 instructions in flight per wave (a slot is
+// rewritten 16 instructions later, after its load has completed).  Nothing reads the LDS.
+constexpr int DMA_SLOTS = 16;
+
+__global__ __launch_bounds__(256) void dma_probe_kernel(const unsigned char* __restrict__ src, int n_chunks,
+                                                        int iters) {
+    __shared__ __align__(1024) unsigned char ring[4][DMA_SLOTS][1024];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const long long waves = (long long)gridDim.x * 4;
+    const long long w0 = (long long)blockIdx.x * 4 + wave;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)&ring[wave][0][0];
+    for (int it = 0; it < iters; ++it) {
+        const long long chunk = (w0 + (long long)it * waves) & (n_chunks - 1);   // n_chunks: a power of two
+        const unsigned char* g = src + chunk * 1024 + lane * 16;
+        const uint32_t lds = lds0 + (uint32_t)(it % DMA_SLOTS) * 1024u;
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(lds) : "memory", "m0");
+        asm volatile("s_waitcnt vmcnt(8)" : : : "memory");
+    }
+    asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+}
+
 }  // namespace
 
 extern "C" {
@@ -145,6 +168,15 @@ int dflash_probe_lds(int iters, int blocks, unsigned key, unsigned* sink, void* 
     if (!sink || blocks < 1 || iters < 1) return -1;
     hipLaunchKernelGGL(lds_probe_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream), iters, key,
                        sink);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// `blocks` workgroups of 4 waves, each wave `iters` direct-to-LDS loads of 1 KB from the first
+// n_chunks KB (a power of two) of the device buffer `buf`: bytes loaded blocks * 4 * iters * 1024.
+int dflash_probe_dma(const void* buf, int n_chunks, int iters, int blocks, void* stream) {
+    if (!buf || n_chunks < 1 || (n_chunks & (n_chunks - 1)) || iters < 1 || blocks < 1) return -1;
+    hipLaunchKernelGGL(dma_probe_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const unsigned char*>(buf), n_chunks, iters);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
