@@ -186,7 +186,8 @@ def measured_peaks(torch):
     lib.dflash_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     lib.dflash_probe_mfma32.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     lib.dflash_probe_lds.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_uint, ctypes.c_void_p, ctypes.c_void_p]
-    lib.dflash_probe_dma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.dflash_probe_dma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_void_p]
     stream = torch.cuda.current_stream().cuda_stream
     nbytes = 4 << 30
     buf = torch.zeros(nbytes // 4, dtype=torch.int32, device="cuda")
@@ -223,11 +224,13 @@ def measured_peaks(torch):
     # direct-to-LDS loads (the GEMMs' staging path): from a 4 MiB buffer that stays in L2, and
     # once through the 4 GiB buffer (HBM); two workgroups (64 KB of LDS each) per CU
     dblocks = 256 * 2
-    dma_l2 = lambda: lib.dflash_probe_dma(buf.data_ptr(), 4096, 4000, dblocks, stream)
-    time_ms(dma_l2)
-    dma_l2_tbs = dblocks * 4 * 4000 * 1024.0 / (statistics.median(time_ms(dma_l2) for _ in range(5)) * 1e-3) / 1e12
+    def dma_l2_tbs_at(depth):       # at most depth + 1 loads of 1 KB in flight per wave
+        fn = lambda: lib.dflash_probe_dma(buf.data_ptr(), 4096, 4000, dblocks, depth, stream)
+        time_ms(fn)
+        return dblocks * 4 * 4000 * 1024.0 / (statistics.median(time_ms(fn) for _ in range(5)) * 1e-3) / 1e12
+    dma_l2_tbs, dma_l2_deep_tbs = dma_l2_tbs_at(8), dma_l2_tbs_at(14)
     dma_hbm_iters = (nbytes // 1024) // (dblocks * 4)
-    dma_hbm = lambda: lib.dflash_probe_dma(buf.data_ptr(), nbytes // 1024, dma_hbm_iters, dblocks, stream)
+    dma_hbm = lambda: lib.dflash_probe_dma(buf.data_ptr(), nbytes // 1024, dma_hbm_iters, dblocks, 8, stream)
     time_ms(dma_hbm)
     dma_hbm_gbs = dblocks * 4 * dma_hbm_iters * 1024.0 / (statistics.median(time_ms(dma_hbm) for _ in range(5)) * 1e-3) / 1e9
     del buf
@@ -236,6 +239,7 @@ def measured_peaks(torch):
             "mfma32_bf16_TFLOPs": round(tflops32, 1), "lds_read_TBs": round(lds_tbs, 2),
             "lds_bytes_per_clk_per_cu": round(lds_tbs * 1e12 / (N_CU * CLOCK_HZ), 1),
             "dma_l2_TBs": round(dma_l2_tbs, 2), "dma_l2_bytes_per_clk_per_cu": round(dma_l2_tbs * 1e12 / (N_CU * CLOCK_HZ), 1),
+            "dma_l2_deep_TBs": round(dma_l2_deep_tbs, 2),
             "dma_hbm_GBs": round(dma_hbm_gbs, 1)}
 
 

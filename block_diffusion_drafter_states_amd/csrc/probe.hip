@@ -111,12 +111,14 @@ __global__ __launch_bounds__(256) void lds_probe_kernel(int iters, unsigned key,
 
 // Direct-to-LDS load rate: every wave streams 1 KB per instruction (global_load_lds_dwordx4,
 // 16 bytes per lane) from a buffer of n_chunks 1 KB chunks (grid-stride over the waves) into a
-// ring of 16 LDS slots of its own, at most 9 instructions in flight per wave (a slot is
+// ring of 16 LDS slots of its own, at most DEPTH + 1 instructions in flight per wave (a slot is
 // rewritten 16 instructions later, after its load has completed).  Nothing reads the LDS.
 constexpr int DMA_SLOTS = 16;
 
+template <int DEPTH>
 __global__ __launch_bounds__(256) void dma_probe_kernel(const unsigned char* __restrict__ src, int n_chunks,
                                                         int iters) {
+    static_assert(DEPTH + 1 < DMA_SLOTS, "a slot is rewritten only after its load has completed");
     __shared__ __align__(1024) unsigned char ring[4][DMA_SLOTS][1024];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const long long waves = (long long)gridDim.x * 4;
@@ -127,7 +129,7 @@ __global__ __launch_bounds__(256) void dma_probe_kernel(const unsigned char* __r
         const unsigned char* g = src + chunk * 1024 + lane * 16;
         const uint32_t lds = lds0 + (uint32_t)(it % DMA_SLOTS) * 1024u;
         asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(lds) : "memory", "m0");
-        asm volatile("s_waitcnt vmcnt(8)" : : : "memory");
+        asm volatile("s_waitcnt vmcnt(%0)" : : "n"(DEPTH) : "memory");
     }
     asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
 }
@@ -172,11 +174,15 @@ int dflash_probe_lds(int iters, int blocks, unsigned key, unsigned* sink, void* 
 }
 
 // `blocks` workgroups of 4 waves, each wave `iters` direct-to-LDS loads of 1 KB from the first
-// n_chunks KB (a power of two) of the device buffer `buf`: bytes loaded blocks * 4 * iters * 1024.
-int dflash_probe_dma(const void* buf, int n_chunks, int iters, int blocks, void* stream) {
+// n_chunks KB (a power of two) of the device buffer `buf`, at most depth + 1 in flight per wave
+// (depth 8 or 14): bytes loaded blocks * 4 * iters * 1024.
+int dflash_probe_dma(const void* buf, int n_chunks, int iters, int blocks, int depth, void* stream) {
     if (!buf || n_chunks < 1 || (n_chunks & (n_chunks - 1)) || iters < 1 || blocks < 1) return -1;
-    hipLaunchKernelGGL(dma_probe_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
-                       static_cast<const unsigned char*>(buf), n_chunks, iters);
+    if (depth != 8 && depth != 14) return -1;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    const unsigned char* src = static_cast<const unsigned char*>(buf);
+    if (depth == 8) hipLaunchKernelGGL(dma_probe_kernel<8>, dim3(blocks), dim3(256), 0, st, src, n_chunks, iters);
+    else hipLaunchKernelGGL(dma_probe_kernel<14>, dim3(blocks), dim3(256), 0, st, src, n_chunks, iters);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -291,6 +291,8 @@ def test_probe_library_exports_and_rejects_bad_arguments():
     assert P.dflash_probe_mfma(1, 1, None, None) == -1
     assert P.dflash_probe_mfma32(0, 1, None, None) == -1
     assert P.dflash_probe_lds(1, 1, 0, None, None) == -1
-    P.dflash_probe_dma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
-    assert P.dflash_probe_dma(None, 4096, 1, 1, None) == -1
-    assert P.dflash_probe_dma(ctypes.c_void_p(16), 3000, 1, 1, None) == -1      # not a power of two: no launch
+    P.dflash_probe_dma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_void_p]
+    assert P.dflash_probe_dma(None, 4096, 1, 1, 8, None) == -1
+    assert P.dflash_probe_dma(ctypes.c_void_p(16), 3000, 1, 1, 8, None) == -1   # not a power of two: no launch
+    assert P.dflash_probe_dma(ctypes.c_void_p(16), 4096, 1, 1, 9, None) == -1   # unsupported depth: no launch
