@@ -188,6 +188,8 @@ def measured_peaks(torch):
     lib.dflash_probe_lds.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_uint, ctypes.c_void_p, ctypes.c_void_p]
     lib.dflash_probe_dma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                      ctypes.c_void_p]
+    lib.dflash_probe_dma_issue.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+                                           ctypes.c_void_p]
     stream = torch.cuda.current_stream().cuda_stream
     nbytes = 4 << 30
     buf = torch.zeros(nbytes // 4, dtype=torch.int32, device="cuda")
@@ -233,6 +235,14 @@ def measured_peaks(torch):
     dma_hbm = lambda: lib.dflash_probe_dma(buf.data_ptr(), nbytes // 1024, dma_hbm_iters, dblocks, 8, stream)
     time_ms(dma_hbm)
     dma_hbm_gbs = dblocks * 4 * dma_hbm_iters * 1024.0 / (statistics.median(time_ms(dma_hbm) for _ in range(5)) * 1e-3) / 1e9
+    # shader-clock cycles a wave spends issuing 16 direct-to-LDS loads of 1 KB (one GEMM stage's
+    # worth), alone and with two workgroups on every CU; the 4 MiB source is warmed into L2 first
+    issue = {}
+    for nb in (1, dblocks):
+        cyc = torch.zeros(nb * 8, dtype=torch.int64, device="cuda")
+        for _ in range(3):
+            time_ms(lambda: lib.dflash_probe_dma_issue(buf.data_ptr(), 4096, cyc.data_ptr(), nb, stream))
+        issue[nb] = statistics.median(cyc.view(-1, 2)[:, 0].tolist())
     del buf
     torch.cuda.empty_cache()
     return {"read_GBs": round(gbs, 1), "mfma_bf16_TFLOPs": round(tflops, 1),
@@ -240,6 +250,7 @@ def measured_peaks(torch):
             "lds_bytes_per_clk_per_cu": round(lds_tbs * 1e12 / (N_CU * CLOCK_HZ), 1),
             "dma_l2_TBs": round(dma_l2_tbs, 2), "dma_l2_bytes_per_clk_per_cu": round(dma_l2_tbs * 1e12 / (N_CU * CLOCK_HZ), 1),
             "dma_l2_deep_TBs": round(dma_l2_deep_tbs, 2),
+            "dma_issue_cycles_16kb_alone": issue[1], "dma_issue_cycles_16kb_2wg_per_cu": issue[dblocks],
             "dma_hbm_GBs": round(dma_hbm_gbs, 1)}
 
 

@@ -134,6 +134,33 @@ __global__ __launch_bounds__(256) void dma_probe_kernel(const unsigned char* __r
     asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
 }
 
+// Issue cost of direct-to-LDS loads: every wave issues 16 loads of 1 KB (one GEMM stage's worth
+// per wave) into its own LDS slots, reading the shader clock before and after the issue loop and
+// after the loads have completed; lane 0 stores (issue cycles, issue + completion cycles) for
+// its wave in out[2w], out[2w + 1].
+__global__ __launch_bounds__(256) void dma_issue_probe_kernel(const unsigned char* __restrict__ src, int n_chunks,
+                                                              long long* __restrict__ out) {
+    __shared__ __align__(1024) unsigned char ring[4][DMA_SLOTS][1024];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const long long w0 = (long long)blockIdx.x * 4 + wave;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)&ring[wave][0][0];
+    const long long t0 = clock64();
+#pragma unroll
+    for (int it = 0; it < DMA_SLOTS; ++it) {
+        const long long chunk = (w0 * DMA_SLOTS + it) & (n_chunks - 1);
+        const unsigned char* g = src + chunk * 1024 + lane * 16;
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                     : : "v"(g), "s"(lds0 + (uint32_t)it * 1024u) : "memory", "m0");
+    }
+    const long long t1 = clock64();
+    asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+    const long long t2 = clock64();
+    if (lane == 0) {
+        out[w0 * 2] = t1 - t0;
+        out[w0 * 2 + 1] = t2 - t0;
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -183,6 +210,16 @@ int dflash_probe_dma(const void* buf, int n_chunks, int iters, int blocks, int d
     const unsigned char* src = static_cast<const unsigned char*>(buf);
     if (depth == 8) hipLaunchKernelGGL(dma_probe_kernel<8>, dim3(blocks), dim3(256), 0, st, src, n_chunks, iters);
     else hipLaunchKernelGGL(dma_probe_kernel<14>, dim3(blocks), dim3(256), 0, st, src, n_chunks, iters);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// `blocks` workgroups of 4 waves, each wave 16 direct-to-LDS loads of 1 KB from the first n_chunks
+// KB (a power of two) of `buf`; out: device, 8 * blocks int64 (per wave: issue cycles, issue +
+// completion cycles, shader clock).
+int dflash_probe_dma_issue(const void* buf, int n_chunks, long long* out, int blocks, void* stream) {
+    if (!buf || !out || n_chunks < 1 || (n_chunks & (n_chunks - 1)) || blocks < 1) return -1;
+    hipLaunchKernelGGL(dma_issue_probe_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const unsigned char*>(buf), n_chunks, out);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -272,14 +272,15 @@ def test_draft_check_flags_wrong_ids():
 
 
 def test_probe_library_exports_and_rejects_bad_arguments():
-    """libdflash_probe.so (the benchmark's measured ceilings) exports the five probes the
+    """libdflash_probe.so (the benchmark's measured ceilings) exports the six probes the
     benchmark loads, and each returns -1 for invalid arguments before any launch."""
     path = os.path.join(os.path.dirname(_abi.LIB_PATH), "libdflash_probe.so")
     if not os.path.exists(path):
         pytest.skip("libdflash_probe.so not built (run __graft_entry__.build())")
     P = ctypes.CDLL(path)
     out = os.popen(f"nm -D --defined-only {path}").read()
-    for name in ("dflash_probe_read", "dflash_probe_mfma", "dflash_probe_mfma32", "dflash_probe_lds", "dflash_probe_dma"):
+    for name in ("dflash_probe_read", "dflash_probe_mfma", "dflash_probe_mfma32", "dflash_probe_lds", "dflash_probe_dma",
+                 "dflash_probe_dma_issue"):
         assert re.search(rf"\bT {name}\b", out), name
     P.dflash_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint, ctypes.c_void_p, ctypes.c_int,
                                     ctypes.c_void_p]
@@ -296,3 +297,5 @@ def test_probe_library_exports_and_rejects_bad_arguments():
     assert P.dflash_probe_dma(None, 4096, 1, 1, 8, None) == -1
     assert P.dflash_probe_dma(ctypes.c_void_p(16), 3000, 1, 1, 8, None) == -1   # not a power of two: no launch
     assert P.dflash_probe_dma(ctypes.c_void_p(16), 4096, 1, 1, 9, None) == -1   # unsupported depth: no launch
+    P.dflash_probe_dma_issue.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    assert P.dflash_probe_dma_issue(ctypes.c_void_p(16), 4096, None, 1, None) == -1
