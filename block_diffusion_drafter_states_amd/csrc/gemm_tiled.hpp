@@ -296,12 +296,20 @@ __global__ __launch_bounds__(TG_THREADS) void gemm_tiled_kernel(const GemmArgs p
         for (int a = 0; a < 4; ++a) tg_frag<KB>(af[a], st + (wm * 4 + a) * TILEB, r, g);
 #pragma unroll
         for (int b = 0; b < WN; ++b) tg_frag<KB>(bf[b], st + (8 + wn * WN + b) * TILEB, r, g);
+        __syncthreads();    // every wave holds the stage in registers: it can be refilled
+        // the refill (step s + 2) is issued a quarter at a time between the MFMA groups: issuing
+        // a direct-to-LDS load holds the wave, so the matrix core works through it
+        const bool refill = s + 2 < nsteps;
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
+        for (int a = 0; a < 4; ++a) {
+            if (refill) {
+#pragma unroll
+                for (int u = a * NIW / 4; u < (a + 1) * NIW / 4; ++u)
+                    dma_b128(src[u] + (size_t)(s + 2) * KB, lds0 + (s & 1) * STAGE + dst[u]);
+            }
 #pragma unroll
             for (int b = 0; b < WN; ++b) tg_mfma<T, CH>(acc[a][b], af[a], bf[b]);
-        __syncthreads();    // every wave has read the stage before it is refilled
-        if (s + 2 < nsteps) issue(s & 1, s + 2);
+        }
     }
 
     tg_epilogue<T, EPI, BN>(p, L, acc, tile, m0, wm, wn, smem);
