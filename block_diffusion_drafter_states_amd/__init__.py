@@ -298,7 +298,7 @@ def advance_len(model: Model, cache: Cache, n, batch: Optional[int] = None, stre
     torch = _torch()
     _need(n, "n", torch.int32, (None,))
     batch = n.shape[0] if batch is None else batch
-    check(lib().dflash_advance_len(ctypes.byref(cache.s), batch, model.c.kv_capacity, n.data_ptr(),
+    check(lib().dflash_advance_len(ctypes.byref(model.c), ctypes.byref(cache.s), batch, n.data_ptr(),
                                    _stream_ptr(stream)), "dflash_advance_len")
 
 

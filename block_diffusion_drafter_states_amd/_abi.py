@@ -10,7 +10,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libdflash.so")
+# DFLASH_LIB_PATH selects another build of the same sources (the host-sanitized one of the
+# host-only tests); by default the in-tree library.
+LIB_PATH = os.environ.get("DFLASH_LIB_PATH") or os.path.join(HERE, "libdflash.so")
 
 DFLASH_OK = 0
 DFLASH_EINVAL = -1
@@ -27,7 +29,8 @@ STATUS_BAD_COUNT = 4
 
 EXPORTED = ("dflash_workspace_bytes", "dflash_inject_kv", "dflash_draft_block", "dflash_verify",
             "dflash_inject_kv_traced", "dflash_draft_block_traced", "dflash_target_forward", "dflash_advance_len",
-            "dflash_choose_gamma", "dflash_block_loss", "dflash_inject_kv_input_fusion", "dflash_status_str")
+            "dflash_choose_gamma", "dflash_block_loss", "dflash_inject_kv_input_fusion", "dflash_audit_workspace",
+            "dflash_status_str")
 
 
 class dflash_config(ctypes.Structure):
@@ -95,7 +98,11 @@ def lib(path: str = LIB_PATH) -> ctypes.CDLL:
                                         ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                                         ctypes.c_size_t, ctypes.c_void_p]
     L.dflash_advance_len.restype = ctypes.c_int
-    L.dflash_advance_len.argtypes = [P(dflash_kv), ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    L.dflash_advance_len.argtypes = [P(dflash_config), P(dflash_kv), ctypes.c_int32, ctypes.c_void_p,
+                                     ctypes.c_void_p]
+    L.dflash_audit_workspace.restype = ctypes.c_int
+    L.dflash_audit_workspace.argtypes = [P(dflash_config), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                         P(ctypes.c_int32), P(ctypes.c_int32), P(ctypes.c_int32)]
     L.dflash_choose_gamma.restype = ctypes.c_int
     L.dflash_choose_gamma.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_double, ctypes.c_double,

@@ -426,6 +426,12 @@ __global__ __launch_bounds__(64 * ATT_MAX_WAVES) void attn_partial_kernel(const 
     extern __shared__ __align__(16) unsigned char smem[];
     const int c = blockIdx.x, h = blockIdx.y / a.nqs, qs = blockIdx.y % a.nqs, b = blockIdx.z;
     int len = a.len[b];
+    // a length outside the cache, or a block past the RoPE table, is reported (the reads
+    // below are clamped into bounds; the drafts of that sequence are then meaningless)
+    if (c == 0 && blockIdx.y == 0 && threadIdx.x == 0 && a.kwrite == nullptr) {
+        if (len < 0) atomicOr(a.status, STATUS_BAD_COUNT);
+        else if (len > a.cap || len + a.gamma > a.rope_rows) atomicOr(a.status, STATUS_KV_OVERFLOW);
+    }
     len = len < 0 ? 0 : (len > a.cap ? a.cap : len);
     const int nch = 1 + (len + a.chunk - 1) / a.chunk;
     if (c >= nch) return;

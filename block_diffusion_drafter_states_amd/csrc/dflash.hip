@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <vector>
 
 #include "../../include/dflash.h"
 #include "attention.hpp"
@@ -23,12 +24,44 @@ constexpr size_t GEMM_MAX_LDS = 160 * 1024 - 4096;   // dynamic LDS per workgrou
 
 inline size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
-// Records caller-provided events around each launch (see dflash_trace).
+// Host-only audit of a call's workspace writes (dflash_audit_workspace).  Nothing is launched:
+// each launch site reports, for every workspace buffer its kernel writes, the byte range that
+// the kernel's indexing reaches with the launch's arguments and grid, and each range must lie
+// inside the one region of the layout it starts in.
+struct Audit {
+    struct Region {
+        size_t off, bytes;
+    };
+    uintptr_t base = 0;             // stand-in address of the workspace (never dereferenced)
+    std::vector<Region> regions;
+    int launches = 0, writes = 0, violations = 0;
+    void write(const void* p, size_t bytes) {
+        ++writes;
+        const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+        if (bytes == 0) return;
+        if (a < base) {
+            ++violations;
+            return;
+        }
+        const size_t off = a - base;
+        for (const Region& r : regions)
+            if (off >= r.off && off < r.off + r.bytes) {
+                if (off + bytes > r.off + r.bytes) ++violations;
+                return;
+            }
+        ++violations;   // starts in no region (padding, or past the workspace)
+    }
+};
+
+// Records caller-provided events around each launch (see dflash_trace); with `au` set the
+// launches are only audited, not made.
 struct Tracer {
     dflash_trace* t;
     hipStream_t st;
     int i = 0;
+    Audit* au = nullptr;
     void begin(const char* name) {
+        if (au) ++au->launches;
         if (t && i < t->capacity) {
             if (t->names) t->names[i] = name;
             if (t->events && t->events[2 * i]) (void)hipEventRecord(static_cast<hipEvent_t>(t->events[2 * i]), st);
@@ -43,6 +76,33 @@ struct Tracer {
 };
 inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 inline int pad16(int m) { return cdiv(m, 16) * 16; }
+
+// A launch through the tracer: made, or (audit) only counted.
+#define DFL_LAUNCH(tr, ...)                                  \
+    do {                                                     \
+        if (!(tr).au) hipLaunchKernelGGL(__VA_ARGS__);       \
+    } while (0)
+inline bool launched(const Tracer& tr) { return tr.au || hipGetLastError() == hipSuccess; }
+
+// Write extents (bytes from the buffer's start) of the two activation layouts: plain rows
+// (rows x cols elements, ld apart) and the weight-streaming GEMM's fragment order
+// (afrag_offset over M rows x K columns; the largest offset lies in the last 16-row tile
+// and the last 256-byte step, which are searched exhaustively).
+inline size_t span_rows(long long rows, long long ld, long long cols, int esize) {
+    return rows > 0 && cols > 0 ? (size_t)(((rows - 1) * ld + cols) * esize) : 0;
+}
+template <typename T>
+size_t span_afrag(int M, int K) {
+    constexpr int S = 256 / (int)sizeof(T);
+    long long mx = -1;
+    for (int m = std::max(0, M - 16); m < M; ++m)
+        for (int k = std::max(0, K - S); k < K; ++k) mx = std::max(mx, afrag_offset<T>(m, k, K));
+    return (size_t)(mx + 1) * sizeof(T);
+}
+template <typename T>
+size_t span_act(int frag, int M, int cols, long long ld) {
+    return frag ? span_afrag<T>(M, cols) : span_rows(M, ld, cols, (int)sizeof(T));
+}
 
 constexpr int MAX_GAMMA = 16;     // block rows: one 16-row MFMA tile per (sequence, q head)
 constexpr int LSE_MAX_SLICES = 256; // block loss: slices of the LM-head tiles folded per row in stage 1
@@ -216,9 +276,18 @@ void launch_attention_q(const AttnArgs& a, const AttnPlan& ap, dim3 grid, hipStr
 }
 
 template <typename T>
-int launch_attention(const AttnArgs& a, const AttnPlan& ap, int nch_max, int nkv, int batch, hipStream_t st) {
+int launch_attention(const AttnArgs& a, const AttnPlan& ap, int nch_max, int nkv, int batch, hipStream_t st,
+                     Tracer& tr) {
     const dim3 grid(nch_max, nkv * ap.nqs, batch);
     if (ap.ring != 4 && ap.ring != 8) return DFLASH_EINVAL;
+    if (ap.qtw != 1 && ap.qtw != 2 && ap.qtw != 4 && ap.qtw != 8) return DFLASH_EINVAL;
+    if (tr.au) {    // partial (m, l, O) of every (b, h, chunk) and query row R < group * gamma <= rpad
+        const long long rows = (long long)a.group * a.gamma;
+        const long long last = (((long long)(batch - 1) * nkv + nkv - 1) * nch_max + nch_max - 1) * a.rpad + rows;
+        tr.au->write(a.opart, (size_t)(last * (256 / sizeof(T)) * 4));
+        tr.au->write(a.mlpart, (size_t)(last * 2 * 4));
+        return rows <= a.rpad ? DFLASH_OK : DFLASH_EUNSUPPORTED;
+    }
     switch (ap.qtw) {
         case 1: launch_attention_q<T, 1>(a, ap, grid, st); break;
         case 2: launch_attention_q<T, 2>(a, ap, grid, st); break;
@@ -258,12 +327,18 @@ struct Layout {
     // inject
     size_t c, ssq_c, cnorm, kvraw, lensnap, inject_end;
     int ssq_c_tiles;
+    std::vector<Audit::Region> regions;     // every carved buffer: offset and requested bytes
 };
 
 Layout make_layout(const Shape& s, int batch, int rows) {
     Layout l;
     size_t off = 0;
-    auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        l.regions.push_back({o, bytes});
+        off = align_up(off + bytes);
+        return o;
+    };
     const size_t M = (size_t)batch * s.gmax;
     // tile counts from the weight-streaming plans, which have the most tiles (the tiled
     // plans of a call with many rows use fewer), so any call's plans fit
@@ -306,8 +381,8 @@ int launch_gemm(const GemmArgs& a, const GemmPlan& p, hipStream_t st, Tracer& tr
     constexpr int P = gemm_ring_depth(MT, NTW);
     dim3 grid(p.n_tiles, p.mgroups, p.layers);
     tr.begin(name);
-    hipLaunchKernelGGL((gemm_kernel<T, EPI, MT, NTW, P>), grid, dim3(64 * p.ns * p.ks), p.lds, st, a);
-    const bool ok = hipGetLastError() == hipSuccess;
+    DFL_LAUNCH(tr, (gemm_kernel<T, EPI, MT, NTW, P>), grid, dim3(64 * p.ns * p.ks), p.lds, st, a);
+    const bool ok = launched(tr);
     tr.end();
     return ok ? DFLASH_OK : DFLASH_ELAUNCH;
 }
@@ -326,15 +401,35 @@ template <typename T, int EPI, int BN>
 int launch_gemm_tiled(const GemmArgs& a, const GemmPlan& p, hipStream_t st, Tracer& tr, const char* name) {
     dim3 grid(cdiv(p.n_tiles, 8) * 8, p.mgroups, p.layers);   // the kernel maps blocks XCD-aware
     tr.begin(name);
-    if (p.kb == 128) hipLaunchKernelGGL((gemm_tiled_kernel<T, EPI, BN, 128>), grid, dim3(TG_THREADS), p.lds, st, a);
-    else hipLaunchKernelGGL((gemm_tiled_kernel<T, EPI, BN, 256>), grid, dim3(TG_THREADS), p.lds, st, a);
-    const bool ok = hipGetLastError() == hipSuccess;
+    if (p.kb == 128) DFL_LAUNCH(tr, (gemm_tiled_kernel<T, EPI, BN, 128>), grid, dim3(TG_THREADS), p.lds, st, a);
+    else DFL_LAUNCH(tr, (gemm_tiled_kernel<T, EPI, BN, 256>), grid, dim3(TG_THREADS), p.lds, st, a);
+    const bool ok = launched(tr);
     tr.end();
     return ok ? DFLASH_OK : DFLASH_ELAUNCH;
 }
 
+// Workspace writes of a GEMM launch (both kernels): per layer the store output (rows < M,
+// columns < N), the per-tile sums of squares [tile < n_tiles][m < M], the SwiGLU output,
+// the per-tile argmax / log-sum-exp slots [tile < n_tiles][m < M] and the label logits.
+template <typename T>
+void audit_gemm(const GemmArgs& a, const GemmPlan& p, Audit& au) {
+    for (int z = 0; z < p.layers; ++z) {
+        const GemmLayer& L = a.layer[z];
+        if (p.epi == EPI_STORE) au.write(L.out ? L.out : a.out, span_rows(a.M, a.ldo, a.N, 4));
+    }
+    if (p.epi == EPI_STORE && a.ssq_out) au.write(a.ssq_out, span_rows(p.n_tiles, a.ssq_out_ld, a.M, 4));
+    if (p.epi == EPI_SWIGLU) au.write(a.out_t, span_act<T>(a.out_frag, a.M, a.N, a.ldo));
+    if (p.epi == EPI_ARGMAX) au.write(a.amax, span_rows(p.n_tiles, a.M, a.M, 8));
+    if (p.epi == EPI_LSE) {
+        au.write(a.lse, span_rows(p.n_tiles, a.M, a.M, 8));
+        au.write(a.lab_logit, (size_t)a.M * 4);
+    }
+}
+
 template <typename T>
 int gemm_dispatch(const GemmArgs& a, const GemmPlan& p, hipStream_t st, Tracer& tr, const char* name) {
+    if (p.layers < 1 || p.layers > MAX_LAYERS || a.M < 1) return DFLASH_EINVAL;
+    if (tr.au) audit_gemm<T>(a, p, *tr.au);
     if (p.tiled) {
         if (a.a_frag || a.out_frag) return DFLASH_EINVAL;     // the tiled kernel reads and writes plain rows
         for (int k = 0; k < 2; ++k)     // a 16-row weight tile never straddles two segments
@@ -403,13 +498,14 @@ int set_norm_a(GemmArgs& a, const Shape& s, const float* x, int M, const float* 
     NormWeights nw{};
     nw.w[0] = w;
     tr.begin("rmsnorm");
-    hipLaunchKernelGGL((rmsnorm_rows_kernel<T>), dim3(M, cdiv(s.H, 1024), 1), dim3(256), 0, st, x, s.H, ssq, n_ssq, M,
-                       nw, s.H, s.eps, static_cast<T*>(nbuf), s.H, 0LL, nullptr, nullptr, 0, afrag);
+    if (tr.au) tr.au->write(nbuf, span_act<T>(afrag, M, s.H, s.H));
+    DFL_LAUNCH(tr, (rmsnorm_rows_kernel<T>), dim3(M, cdiv(s.H, 1024), 1), dim3(256), 0, st, x, s.H, ssq, n_ssq, M,
+               nw, s.H, s.eps, static_cast<T*>(nbuf), s.H, 0LL, nullptr, nullptr, 0, afrag);
     tr.end();
     a.a = nbuf;
     a.lda = s.H;
     a.a_frag = afrag;
-    return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_ELAUNCH;
+    return launched(tr) ? DFLASH_OK : DFLASH_ELAUNCH;
 }
 
 template <typename T>
@@ -418,11 +514,14 @@ int run_inject(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int
     char* wsb = static_cast<char*>(ws);
     const InjectPlans pl = inject_plans(s, batch, rows);
     const int M = batch * rows;
+    if ((long long)batch * cdiv(rows, KV_ROWS) > 65535) return DFLASH_EUNSUPPORTED;   // kv_finish grid
     float* c = reinterpret_cast<float*>(wsb + lay.c);
     float* ssq_c = reinterpret_cast<float*>(wsb + lay.ssq_c);
     float* kvraw = reinterpret_cast<float*>(wsb + lay.kvraw);
     int* lensnap = reinterpret_cast<int*>(wsb + lay.lensnap);
     int rc;
+    // the layout was carved from these plans' tile counts; checked before anything is launched
+    if (pl.fuse.n_tiles > lay.ssq_c_tiles) return DFLASH_EUNSUPPORTED;
     {   // stage 1: c = W_fuse . concat(feat)
         GemmArgs a = gemm_base(s, pl.fuse, M, s.F * s.H);
         a.a = feat;
@@ -438,7 +537,6 @@ int run_inject(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int
         if ((rc = gemm_dispatch<T>(a, pl.fuse, st, tr, "fuse"))) return rc;
     }
     {   // stage 2: every layer's RMSNorm -> W_k | W_v (one launch for all layers)
-        if (pl.fuse.n_tiles > lay.ssq_c_tiles) return DFLASH_EUNSUPPORTED;
         GemmArgs a = gemm_base(s, pl.kv, M, s.H);
         NormWeights nw{};   // one normalised copy of c per layer (each layer has its own scale)
         for (int l = 0; l < s.L; ++l) nw.w[l] = w->layers[l].in_norm;
@@ -446,11 +544,14 @@ int run_inject(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int
         const int afrag = M < TILED_MIN_ROWS ? 1 : 0;       // fragment order for the weight-streaming GEMM
         const size_t cn_layer = (size_t)pad16(M) * s.H;    // whole 16-row tiles per layer
         tr.begin("rmsnorm");
-        hipLaunchKernelGGL((rmsnorm_rows_kernel<T>), dim3(M, cdiv(s.H, 1024), s.L), dim3(256), 0, st, c, s.H, ssq_c,
-                           pl.fuse.n_tiles, M, nw, s.H, s.eps, cn, s.H, (long long)cn_layer, kv->len, lensnap, batch,
-                           afrag);
+        if (tr.au) {
+            tr.au->write(cn, (size_t)(s.L - 1) * cn_layer * sizeof(T) + span_act<T>(afrag, M, s.H, s.H));
+            tr.au->write(lensnap, (size_t)batch * 4);
+        }
+        DFL_LAUNCH(tr, (rmsnorm_rows_kernel<T>), dim3(M, cdiv(s.H, 1024), s.L), dim3(256), 0, st, c, s.H, ssq_c,
+                   pl.fuse.n_tiles, M, nw, s.H, s.eps, cn, s.H, (long long)cn_layer, kv->len, lensnap, batch, afrag);
         tr.end();
-        if (hipGetLastError() != hipSuccess) return DFLASH_ELAUNCH;
+        if (!launched(tr)) return DFLASH_ELAUNCH;
         const int ld = 2 * s.nkv * s.D;
         a.lda = s.H;
         a.N = ld;
@@ -492,10 +593,9 @@ int run_inject(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int
         a.status = kv->status;
         tr.begin("kv_finish");
         const int rb_n = cdiv(rows, KV_ROWS);
-        if ((long long)batch * rb_n > 65535) return DFLASH_EUNSUPPORTED;
-        hipLaunchKernelGGL((kv_finish_kernel<T>), dim3(2 * s.nkv, s.L, batch * rb_n), dim3(256), 0, st, a, rb_n);
+        DFL_LAUNCH(tr, (kv_finish_kernel<T>), dim3(2 * s.nkv, s.L, batch * rb_n), dim3(256), 0, st, a, rb_n);
         tr.end();
-        if (hipGetLastError() != hipSuccess) return DFLASH_ELAUNCH;
+        if (!launched(tr)) return DFLASH_ELAUNCH;
     }
     return DFLASH_OK;
 }
@@ -530,8 +630,10 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
     char* wsb = static_cast<char*>(ws);
     const int M = batch * gamma;
     const DraftPlans pl = draft_plans(s, M);
+    // the workspace was carved for other plans: checked before anything is launched
     if (pl.lm.n_tiles > lay.amax_tiles || std::max(pl.o.n_tiles, pl.down.n_tiles) > lay.ssq_x_tiles)
-        return DFLASH_EUNSUPPORTED;   // the workspace was carved for other plans
+        return DFLASH_EUNSUPPORTED;
+    if (md.labels && plan_gemm(s, EPI_LSE, s.V, s.H, M, 1).n_tiles != pl.lm.n_tiles) return DFLASH_EUNSUPPORTED;
     float* x = reinterpret_cast<float*>(wsb + lay.x);
     float* ssq_x = reinterpret_cast<float*>(wsb + lay.ssq_x);
     float* qkv = reinterpret_cast<float*>(wsb + lay.qkv);
@@ -553,16 +655,23 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
         const long long n = (long long)M * s.H;
         const unsigned blocks = (unsigned)std::min<long long>(1024, (n + 255) / 256);
         tr.begin("copy_input");
-        hipLaunchKernelGGL(copy_f32_kernel, dim3(blocks), dim3(256), 0, st, md.x_in, x, n);
+        if (tr.au) tr.au->write(x, (size_t)n * 4);
+        DFL_LAUNCH(tr, copy_f32_kernel, dim3(blocks), dim3(256), 0, st, md.x_in, x, n);
         tr.end();
     } else {
         tr.begin("embed_norm");
-        hipLaunchKernelGGL((embed_norm_kernel<T>), dim3(M), dim3(256), 0, st, static_cast<const T*>(w->embed),
+        if (tr.au) {
+            tr.au->write(x, span_rows(M, s.H, s.H, 4));
+            tr.au->write(nbuf, span_act<T>(afrag, M, s.H, s.H));
+            tr.au->write(fin_best, (size_t)n_draft * 8);
+            tr.au->write(fin_count, (size_t)n_draft * 4);
+        }
+        DFL_LAUNCH(tr, (embed_norm_kernel<T>), dim3(M), dim3(256), 0, st, static_cast<const T*>(w->embed),
                            anchor, md.tokens, s.mask, s.V, gamma, s.H, static_cast<const T*>(w->layers[0].in_norm),
                            s.eps, x, static_cast<T*>(nbuf), kv->status, fin_best, fin_count, n_draft, afrag);
         tr.end();
     }
-    if (hipGetLastError() != hipSuccess) return DFLASH_ELAUNCH;
+    if (!launched(tr)) return DFLASH_ELAUNCH;
     int n_ssq = 0;      // per-tile partial sums of squares of x (written by o / down)
 
     const AttnPlan ap = plan_attn(s, gamma, batch);
@@ -626,7 +735,7 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
             a.status = kv->status;
             a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)s.D));
             tr.begin("attention");
-            rc = launch_attention<T>(a, ap, s.nch_max, s.nkv, batch, st);
+            rc = launch_attention<T>(a, ap, s.nch_max, s.nkv, batch, st, tr);
             tr.end();
             if (rc) return rc;
             MergeArgs mgr;
@@ -644,9 +753,10 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
             mgr.head_dim = s.D;
             mgr.out_frag = afrag;
             tr.begin("attn_merge");
-            hipLaunchKernelGGL((attn_merge_kernel<T>), dim3(M, s.nq), dim3(64), 0, st, mgr);
+            if (tr.au) tr.au->write(obuf, span_act<T>(afrag, M, s.nq * s.D, s.nq * s.D));
+            DFL_LAUNCH(tr, (attn_merge_kernel<T>), dim3(M, s.nq), dim3(64), 0, st, mgr);
             tr.end();
-            if (hipGetLastError() != hipSuccess) return DFLASH_ELAUNCH;
+            if (!launched(tr)) return DFLASH_ELAUNCH;
         }
         {   // x += W_o o
             GemmArgs a = gemm_base(s, pl.o, M, s.nq * s.D);
@@ -697,25 +807,24 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
             const long long n = (long long)M * s.H;
             const unsigned blocks = (unsigned)std::min<long long>(2048, (n + 255) / 256);
             tr.begin("tap");
-            hipLaunchKernelGGL((tap_kernel<T>), dim3(blocks), dim3(256), 0, st, x, n, s.H, md.n_taps, f,
-                               static_cast<T*>(md.feat));
+            DFL_LAUNCH(tr, (tap_kernel<T>), dim3(blocks), dim3(256), 0, st, x, n, s.H, md.n_taps, f,
+                       static_cast<T*>(md.feat));
             tr.end();
-            if (hipGetLastError() != hipSuccess) return DFLASH_ELAUNCH;
+            if (!launched(tr)) return DFLASH_ELAUNCH;
         }
     }
     if (dbg_hidden) {
         const long long n = (long long)M * s.H;
         const unsigned blocks = (unsigned)std::min<long long>(1024, (n + 255) / 256);
         tr.begin("copy_hidden");
-        hipLaunchKernelGGL(copy_f32_kernel, dim3(blocks), dim3(256), 0, st, x, dbg_hidden, n);
+        DFL_LAUNCH(tr, copy_f32_kernel, dim3(blocks), dim3(256), 0, st, x, dbg_hidden, n);
         tr.end();
-        if (hipGetLastError() != hipSuccess) return DFLASH_ELAUNCH;
+        if (!launched(tr)) return DFLASH_ELAUNCH;
     }
     if (md.no_head) return DFLASH_OK;
     {   // final norm -> LM head -> per-tile argmax (or log-sum-exp and label logits)
         const bool loss = md.labels != nullptr;
-        const GemmPlan plm = loss ? plan_gemm(s, EPI_LSE, s.V, s.H, M, 1) : pl.lm;
-        if (plm.n_tiles != pl.lm.n_tiles) return DFLASH_EUNSUPPORTED;   // same geometry as the argmax plan
+        const GemmPlan plm = loss ? plan_gemm(s, EPI_LSE, s.V, s.H, M, 1) : pl.lm;   // same tiles (checked above)
         GemmArgs a = gemm_base(s, plm, M, s.H);
         if ((rc = set_norm_a<T>(a, s, x, M, ssq_x, n_ssq, w->final_norm, nbuf, afrag, st, tr))) return rc;
         a.N = s.V;
@@ -737,33 +846,39 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
         const int n_slices = std::max(1, std::min({pl.lm.n_tiles, 256 / row_blocks, LSE_MAX_SLICES}));
         float2* part = reinterpret_cast<float2*>(wsb + lay.lse_part);
         tr.begin("lse_slices");
-        hipLaunchKernelGGL(lse_slices_kernel, dim3(n_slices, row_blocks), dim3(256), 0, st,
-                           reinterpret_cast<const float2*>(amax), pl.lm.n_tiles, n_slices, M, part);
+        if (tr.au) tr.au->write(part, span_rows(n_slices, M, M, 8));
+        DFL_LAUNCH(tr, lse_slices_kernel, dim3(n_slices, row_blocks), dim3(256), 0, st,
+                   reinterpret_cast<const float2*>(amax), pl.lm.n_tiles, n_slices, M, part);
         tr.end();
-        if (hipGetLastError() != hipSuccess) return DFLASH_ELAUNCH;
+        if (!launched(tr)) return DFLASH_ELAUNCH;
         tr.begin("block_loss");
         float* lse_row = reinterpret_cast<float*>(wsb + lay.lse_row);
-        hipLaunchKernelGGL(block_loss_kernel, dim3(1), dim3(BLOCK_LOSS_THREADS), 0, st, part, n_slices, M, gamma,
+        if (tr.au && md.dlogits) tr.au->write(lse_row, (size_t)M * 4);
+        DFL_LAUNCH(tr, block_loss_kernel, dim3(1), dim3(BLOCK_LOSS_THREADS), 0, st, part, n_slices, M, gamma,
                            md.labels, reinterpret_cast<const float*>(wsb + lay.lab), s.V, md.loss, md.row_loss,
                            md.dlogits ? lse_row : nullptr, kv->status);
         tr.end();
-        if (hipGetLastError() != hipSuccess) return DFLASH_ELAUNCH;
+        if (!launched(tr)) return DFLASH_ELAUNCH;
         if (md.dlogits) {
             // rows x vocabulary slices of 256 ids, at most 64 slices per row (strided beyond)
             const dim3 grid((unsigned)std::min(64, cdiv(s.V, 256)), (unsigned)(batch * (gamma - 1)));
             tr.begin("block_loss_grad");
-            hipLaunchKernelGGL(block_loss_grad_kernel, grid, dim3(256), 0, st,
+            DFL_LAUNCH(tr, block_loss_grad_kernel, grid, dim3(256), 0, st,
                                dbg_logits ? dbg_logits : md.dlogits, md.dlogits, lse_row, md.labels, batch, gamma, s.V);
             tr.end();
         }
-        return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_ELAUNCH;
+        return launched(tr) ? DFLASH_OK : DFLASH_ELAUNCH;
     }
     tr.begin("argmax_finish");
     const int n_slices = std::max(1, std::min(pl.lm.n_tiles, 256 / row_blocks));
-    hipLaunchKernelGGL(argmax_finish_kernel, dim3(n_slices, row_blocks), dim3(256), 0, st, amax, pl.lm.n_tiles,
-                       n_slices, M, gamma, md.first_row, fin_best, fin_count, draft);
+    if (tr.au) {    // per draft row i = (m / gamma) * (gamma - first) + m % gamma - first < n_draft
+        tr.au->write(fin_best, (size_t)n_draft * 8);
+        tr.au->write(fin_count, (size_t)n_draft * 4);
+    }
+    DFL_LAUNCH(tr, argmax_finish_kernel, dim3(n_slices, row_blocks), dim3(256), 0, st, amax, pl.lm.n_tiles,
+               n_slices, M, gamma, md.first_row, fin_best, fin_count, draft);
     tr.end();
-    return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_ELAUNCH;
+    return launched(tr) ? DFLASH_OK : DFLASH_ELAUNCH;
 }
 
 // Input-fusion conditioning (the alternative the summary's KV injection is compared with,
@@ -782,6 +897,7 @@ int run_inject_input_fusion(const Shape& s, const dflash_weights* w, const dflas
     float* c = reinterpret_cast<float*>(wsb + lay.c);
     float* ssq_c = reinterpret_cast<float*>(wsb + lay.ssq_c);
     int rc;
+    if (pl.fuse.n_tiles > lay.ssq_c_tiles) return DFLASH_EUNSUPPORTED;   // before anything is launched
     {   // c = W_fuse . concat(feat), with per-tile sums of squares for the first layer's norm
         GemmArgs a = gemm_base(s, pl.fuse, M, s.F * s.H);
         a.a = feat;
@@ -796,7 +912,6 @@ int run_inject_input_fusion(const Shape& s, const dflash_weights* w, const dflas
         a.ssq_out_ld = M;
         if ((rc = gemm_dispatch<T>(a, pl.fuse, st, tr, "fuse"))) return rc;
     }
-    if (pl.fuse.n_tiles > lay.ssq_c_tiles) return DFLASH_EUNSUPPORTED;
     PassMode md = DRAFT_PASS;
     md.causal = 1;
     md.write_kv = 1;
@@ -808,10 +923,9 @@ int run_inject_input_fusion(const Shape& s, const dflash_weights* w, const dflas
     if ((rc = run_draft<T>(s, w, kv, batch, rows, nullptr, nullptr, nullptr, nullptr, ws, lay, st, tr, md)))
         return rc;
     tr.begin("advance_len");
-    hipLaunchKernelGGL(advance_len_kernel, dim3(1), dim3(64), 0, st, kv->len, n_new, batch, s.cap, rows, rows,
-                       kv->status);
+    DFL_LAUNCH(tr, advance_len_kernel, dim3(1), dim3(64), 0, st, kv->len, n_new, batch, s.cap, rows, rows, kv->status);
     tr.end();
-    return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_ELAUNCH;
+    return launched(tr) ? DFLASH_OK : DFLASH_ELAUNCH;
 }
 
 }  // namespace
@@ -966,10 +1080,13 @@ int dflash_target_forward(const dflash_config* cfg, const dflash_weights* w, con
                                      md);
 }
 
-int dflash_advance_len(const dflash_kv* kv, int32_t batch, int32_t kv_capacity, const int32_t* n, void* stream) {
-    if (!kv || !kv->len || !kv->status || !n || batch < 1 || kv_capacity < 1) return DFLASH_EINVAL;
+int dflash_advance_len(const dflash_config* cfg, const dflash_kv* kv, int32_t batch, const int32_t* n, void* stream) {
+    Shape s;
+    const int rc = make_shape(cfg, s);
+    if (rc) return rc;
+    if (!kv || !kv->len || !kv->status || !n || batch < 1 || batch > s.Bmax) return DFLASH_EINVAL;
     hipLaunchKernelGGL(advance_len_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), kv->len, n, batch,
-                       kv_capacity, kv_capacity, 0, kv->status);
+                       s.cap, s.cap, 0, kv->status);
     return hipGetLastError() == hipSuccess ? DFLASH_OK : DFLASH_ELAUNCH;
 }
 
@@ -1009,6 +1126,64 @@ int dflash_choose_gamma(const int32_t* tau, const int32_t* gamma_used, int32_t n
     *gamma_out = best;
     if (p_out) *p_out = p;
     return DFLASH_OK;
+}
+
+int dflash_audit_workspace(const dflash_config* cfg, int32_t batch, int32_t gamma, int32_t rows_stride,
+                           int32_t* launches, int32_t* writes, int32_t* violations) {
+    Shape s;
+    int rc = make_shape(cfg, s);
+    if (rc) return rc;
+    if (!launches || !writes || !violations) return DFLASH_EINVAL;
+    if (batch < 1 || batch > s.Bmax || gamma < 2 || gamma > s.gmax || rows_stride < 1) return DFLASH_EINVAL;
+    if (s.L > MAX_LAYERS) return DFLASH_EUNSUPPORTED;
+    // stand-in device addresses: the audit never dereferences them and launches nothing
+    const void* fake = reinterpret_cast<const void*>(uintptr_t(1) << 40);
+    int32_t* ifake = reinterpret_cast<int32_t*>(uintptr_t(1) << 41);
+    float* ffake = reinterpret_cast<float*>(uintptr_t(1) << 42);
+    std::vector<dflash_layer_weights> lw(s.L);
+    for (dflash_layer_weights& x : lw) x = {fake, fake, fake, fake, fake, fake, fake, fake, fake, fake, fake};
+    const dflash_weights w = {fake, fake, fake, fake, ffake, ffake, s.cap + s.gmax, lw.data()};
+    const dflash_kv kv = {const_cast<void*>(fake), const_cast<void*>(fake), ifake,
+                          reinterpret_cast<uint32_t*>(ifake)};
+    Audit au;
+    au.base = uintptr_t(1) << 44;
+    void* ws = reinterpret_cast<void*>(au.base);
+    auto run = [&](int rows, auto&& body) {
+        const Layout lay = make_layout(s, batch, rows);
+        au.regions = lay.regions;
+        Tracer tr{nullptr, nullptr};
+        tr.au = &au;
+        return body(lay, tr);
+    };
+    const int taps[1] = {1};
+    const int if_rows = std::min<int>(rows_stride, s.gmax);
+    PassMode loss = DRAFT_PASS;
+    loss.labels = ifake;
+    loss.loss = ffake;
+    loss.row_loss = ffake;
+    loss.dlogits = ffake;
+    const PassMode target = {ifake, 1, 1, taps, 1, const_cast<void*>(fake), 0};
+    rc = run(rows_stride, [&](const Layout& lay, Tracer& tr) {
+        return s.bf16 ? run_inject<bf16_t>(s, &w, &kv, batch, fake, rows_stride, ifake, ws, lay, nullptr, tr)
+                      : run_inject<float>(s, &w, &kv, batch, fake, rows_stride, ifake, ws, lay, nullptr, tr);
+    });
+    if (!rc) rc = run(if_rows, [&](const Layout& lay, Tracer& tr) {
+        return s.bf16 ? run_inject_input_fusion<bf16_t>(s, &w, &kv, batch, fake, if_rows, ifake, ws, lay, nullptr, tr)
+                      : run_inject_input_fusion<float>(s, &w, &kv, batch, fake, if_rows, ifake, ws, lay, nullptr, tr);
+    });
+    for (const PassMode* md : {&DRAFT_PASS, (const PassMode*)&loss, &target}) {
+        if (rc) break;
+        rc = run(0, [&](const Layout& lay, Tracer& tr) {
+            return s.bf16 ? run_draft<bf16_t>(s, &w, &kv, batch, gamma, ifake, ifake, ffake, ffake, ws, lay, nullptr,
+                                              tr, *md)
+                          : run_draft<float>(s, &w, &kv, batch, gamma, ifake, ifake, ffake, ffake, ws, lay, nullptr,
+                                             tr, *md);
+        });
+    }
+    *launches = au.launches;
+    *writes = au.writes;
+    *violations = au.violations;
+    return rc;
 }
 
 const char* dflash_status_str(int status) {

@@ -79,88 +79,6 @@ __global__ __launch_bounds__(256) void mfma32_probe_kernel(int iters, float* __r
     if (threadIdx.x == 0) sink[blockIdx.x] = s;
 }
 
-// LDS read rate: each workgroup fills 32 KB of LDS, then every thread reads 16-byte
-// vectors from it, four per iteration, consecutive lanes at consecutive vectors (no bank
-// conflicts); the XOR of everything read decides a store into sink[blockIdx.x] that the
-// key rules out in practice.  Four VALU operations per vector read: at 64 lanes over 4
-// cycles per SIMD that caps the probe at 256 bytes per clock per CU, so a result near that
-// figure means "at least", below it the LDS is what limits.
-constexpr int LDS_VEC = 2048;
-
-__global__ __launch_bounds__(256) void lds_probe_kernel(int iters, unsigned key, unsigned* __restrict__ sink) {
-    __shared__ uint4 tile[LDS_VEC];
-    for (int i = threadIdx.x; i < LDS_VEC; i += 256) tile[i] = make_uint4(i, i * 3u, i * 5u, i * 7u + blockIdx.x);
-    __syncthreads();
-    uint4 acc = make_uint4(0u, 0u, 0u, 0u);
-    for (int it = 0; it < iters; ++it) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const uint4 v = tile[(threadIdx.x + (it * 4 + u) * 256) & (LDS_VEC - 1)];
-            acc.x ^= v.x;
-            acc.y ^= v.y;
-            acc.z ^= v.z;
-            acc.w ^= v.w;
-        }
-        // the addresses repeat every two iterations: keep the compiler from merging the
-        // reads of equal addresses (which would cancel in the XOR)
-        asm volatile("" ::: "memory");
-    }
-    const unsigned a = acc.x ^ acc.y ^ acc.z ^ acc.w;
-    if (a == key) sink[blockIdx.x] = a;
-}
-
-// Direct-to-LDS load rate: every wave streams 1 KB per instruction (global_load_lds_dwordx4,
-// 16 bytes per lane) from a buffer of n_chunks 1 KB chunks (grid-stride over the waves) into a
-// ring of 16 LDS slots of its own, at most DEPTH + 1 instructions in flight per wave (a slot is
-// rewritten 16 instructions later, after its load has completed).  Nothing reads the LDS.
-constexpr int DMA_SLOTS = 16;
-
-template <int DEPTH>
-__global__ __launch_bounds__(256) void dma_probe_kernel(const unsigned char* __restrict__ src, int n_chunks,
-                                                        int iters) {
-    static_assert(DEPTH + 1 < DMA_SLOTS, "a slot is rewritten only after its load has completed");
-    __shared__ __align__(1024) unsigned char ring[4][DMA_SLOTS][1024];
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const long long waves = (long long)gridDim.x * 4;
-    const long long w0 = (long long)blockIdx.x * 4 + wave;
-    const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)&ring[wave][0][0];
-    for (int it = 0; it < iters; ++it) {
-        const long long chunk = (w0 + (long long)it * waves) & (n_chunks - 1);   // n_chunks: a power of two
-        const unsigned char* g = src + chunk * 1024 + lane * 16;
-        const uint32_t lds = lds0 + (uint32_t)(it % DMA_SLOTS) * 1024u;
-        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(lds) : "memory", "m0");
-        asm volatile("s_waitcnt vmcnt(%0)" : : "n"(DEPTH) : "memory");
-    }
-    asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
-}
-
-// Issue cost of direct-to-LDS loads: every wave issues 16 loads of 1 KB (one GEMM stage's worth
-// per wave) into its own LDS slots, reading the shader clock before and after the issue loop and
-// after the loads have completed; lane 0 stores (issue cycles, issue + completion cycles) for
-// its wave in out[2w], out[2w + 1].
-__global__ __launch_bounds__(256) void dma_issue_probe_kernel(const unsigned char* __restrict__ src, int n_chunks,
-                                                              long long* __restrict__ out) {
-    __shared__ __align__(1024) unsigned char ring[4][DMA_SLOTS][1024];
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const long long w0 = (long long)blockIdx.x * 4 + wave;
-    const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)&ring[wave][0][0];
-    const long long t0 = clock64();
-#pragma unroll
-    for (int it = 0; it < DMA_SLOTS; ++it) {
-        const long long chunk = (w0 * DMA_SLOTS + it) & (n_chunks - 1);
-        const unsigned char* g = src + chunk * 1024 + lane * 16;
-        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                     : : "v"(g), "s"(lds0 + (uint32_t)it * 1024u) : "memory", "m0");
-    }
-    const long long t1 = clock64();
-    asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
-    const long long t2 = clock64();
-    if (lane == 0) {
-        out[w0 * 2] = t1 - t0;
-        out[w0 * 2 + 1] = t2 - t0;
-    }
-}
-
 }  // namespace
 
 extern "C" {
@@ -188,38 +106,6 @@ int dflash_probe_mfma32(int iters, int blocks, float* sink, void* stream) {
     if (!sink || blocks < 1 || iters < 1) return -1;
     hipLaunchKernelGGL(mfma32_probe_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream), iters,
                        sink);
-    return hipGetLastError() == hipSuccess ? 0 : -1;
-}
-
-// `blocks` workgroups of 256 threads, each thread `iters` x 4 LDS reads of 16 bytes: bytes
-// read blocks * 256 * iters * 64; sink: device, `blocks` entries.
-int dflash_probe_lds(int iters, int blocks, unsigned key, unsigned* sink, void* stream) {
-    if (!sink || blocks < 1 || iters < 1) return -1;
-    hipLaunchKernelGGL(lds_probe_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream), iters, key,
-                       sink);
-    return hipGetLastError() == hipSuccess ? 0 : -1;
-}
-
-// `blocks` workgroups of 4 waves, each wave `iters` direct-to-LDS loads of 1 KB from the first
-// n_chunks KB (a power of two) of the device buffer `buf`, at most depth + 1 in flight per wave
-// (depth 8 or 14): bytes loaded blocks * 4 * iters * 1024.
-int dflash_probe_dma(const void* buf, int n_chunks, int iters, int blocks, int depth, void* stream) {
-    if (!buf || n_chunks < 1 || (n_chunks & (n_chunks - 1)) || iters < 1 || blocks < 1) return -1;
-    if (depth != 8 && depth != 14) return -1;
-    const hipStream_t st = static_cast<hipStream_t>(stream);
-    const unsigned char* src = static_cast<const unsigned char*>(buf);
-    if (depth == 8) hipLaunchKernelGGL(dma_probe_kernel<8>, dim3(blocks), dim3(256), 0, st, src, n_chunks, iters);
-    else hipLaunchKernelGGL(dma_probe_kernel<14>, dim3(blocks), dim3(256), 0, st, src, n_chunks, iters);
-    return hipGetLastError() == hipSuccess ? 0 : -1;
-}
-
-// `blocks` workgroups of 4 waves, each wave 16 direct-to-LDS loads of 1 KB from the first n_chunks
-// KB (a power of two) of `buf`; out: device, 8 * blocks int64 (per wave: issue cycles, issue +
-// completion cycles, shader clock).
-int dflash_probe_dma_issue(const void* buf, int n_chunks, long long* out, int blocks, void* stream) {
-    if (!buf || !out || n_chunks < 1 || (n_chunks & (n_chunks - 1)) || blocks < 1) return -1;
-    hipLaunchKernelGGL(dma_issue_probe_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
-                       static_cast<const unsigned char*>(buf), n_chunks, out);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

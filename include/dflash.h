@@ -218,7 +218,7 @@ int dflash_draft_block_traced(const dflash_config *cfg, const dflash_weights *w,
  *   feat  nullable, storage dtype [batch][rows][n_taps][H]: the residual stream
  *         after decoder layer taps[f] (1-based), the layout dflash_inject_kv reads;
  *   dbg_logits nullable fp32 [batch][rows][V].
- * len is not changed: after dflash_verify, dflash_advance_len(kv, batch, cap,
+ * len is not changed: after dflash_verify, dflash_advance_len(cfg, kv, batch,
  * accept_len) keeps the accepted rows (later rows are overwritten next time);
  * a prompt is processed in chunks of at most gamma_max rows, each followed by
  * dflash_advance_len with n = rows.  w->w_fuse is not used (may be NULL).
@@ -232,9 +232,12 @@ int dflash_target_forward(const dflash_config *cfg, const dflash_weights *w, con
                           void *workspace, size_t workspace_bytes, void *stream);
 
 /* len[b] += n[b] for b < batch (n device int32 [batch], e.g. dflash_verify's
- * accept_len); a count that is negative or would pass kv_capacity sets
- * DFLASH_STATUS_BAD_COUNT / DFLASH_STATUS_KV_OVERFLOW and leaves len[b]. */
-int dflash_advance_len(const dflash_kv *kv, int32_t batch, int32_t kv_capacity, const int32_t *n, void *stream);
+ * accept_len); the capacity is cfg->kv_capacity, the one the cache was sized
+ * with.  A count that is negative or would pass kv_capacity sets
+ * DFLASH_STATUS_BAD_COUNT / DFLASH_STATUS_KV_OVERFLOW and leaves len[b].
+ * 1 <= batch <= max_batch. */
+int dflash_advance_len(const dflash_config *cfg, const dflash_kv *kv, int32_t batch, const int32_t *n,
+                       void *stream);
 
 /* Block size for the next cycle (summary section 4, ablations: a drafter trained
  * on 16-token blocks also drafts smaller ones at inference; picking the size per
@@ -303,6 +306,23 @@ int dflash_block_loss(const dflash_config *cfg, const dflash_weights *w, const d
                       int32_t batch, int32_t gamma, const int32_t *anchor, const int32_t *labels,
                       float *loss, float *row_loss, float *dlogits, float *dbg_logits,
                       void *workspace, size_t workspace_bytes, void *stream);
+
+/* Host-only self-check of the launch plans (no GPU work, no device memory
+ * touched, usable on a machine without a GPU).  Runs the launch sequences of
+ * dflash_inject_kv (rows_stride rows per sequence), dflash_inject_kv_input_fusion
+ * (min(rows_stride, gamma_max) rows), dflash_draft_block, dflash_block_loss
+ * (with its gradient) and dflash_target_forward (one tap), each for `batch`
+ * sequences and block size `gamma`, with stand-in pointers and without launching
+ * anything.  For every launch it takes the byte range of each workspace buffer
+ * that the kernel writes, computed from that launch's arguments and grid the way
+ * the kernel indexes, and checks that the range lies inside the region of the
+ * workspace layout (the one dflash_workspace_bytes() sizes) where it starts.
+ *   launches, writes, violations  [host] out: launches audited, write ranges
+ *                                 checked, ranges leaving their region (0 = all
+ *                                 inside)
+ * Returns DFLASH_OK, or the status the audited calls return for this shape. */
+int dflash_audit_workspace(const dflash_config *cfg, int32_t batch, int32_t gamma, int32_t rows_stride,
+                           int32_t *launches, int32_t *writes, int32_t *violations);
 
 /* Human-readable name of a dflash_status value (static string). */
 const char *dflash_status_str(int status);

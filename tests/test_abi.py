@@ -272,30 +272,35 @@ def test_draft_check_flags_wrong_ids():
 
 
 def test_probe_library_exports_and_rejects_bad_arguments():
-    """libdflash_probe.so (the benchmark's measured ceilings) exports the six probes the
-    benchmark loads, and each returns -1 for invalid arguments before any launch."""
+    """libdflash_probe.so (the benchmark's measured ceilings, `bench.py --probes`) exports the
+    HBM-read and the two MFMA probes, and each returns -1 for invalid arguments before any launch."""
     path = os.path.join(os.path.dirname(_abi.LIB_PATH), "libdflash_probe.so")
     if not os.path.exists(path):
         pytest.skip("libdflash_probe.so not built (run __graft_entry__.build())")
     P = ctypes.CDLL(path)
     out = os.popen(f"nm -D --defined-only {path}").read()
-    for name in ("dflash_probe_read", "dflash_probe_mfma", "dflash_probe_mfma32", "dflash_probe_lds", "dflash_probe_dma",
-                 "dflash_probe_dma_issue"):
-        assert re.search(rf"\bT {name}\b", out), name
+    names = sorted(re.findall(r"\bT (dflash_probe_[a-z0-9_]+)\b", out))
+    assert names == ["dflash_probe_mfma", "dflash_probe_mfma32", "dflash_probe_read"]
     P.dflash_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint, ctypes.c_void_p, ctypes.c_int,
                                     ctypes.c_void_p]
     P.dflash_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     P.dflash_probe_mfma32.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
-    P.dflash_probe_lds.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_uint, ctypes.c_void_p, ctypes.c_void_p]
     assert P.dflash_probe_read(None, 16, 0, None, 1, None) == -1
     assert P.dflash_probe_read(None, 15, 0, None, 1, None) == -1
     assert P.dflash_probe_mfma(1, 1, None, None) == -1
     assert P.dflash_probe_mfma32(0, 1, None, None) == -1
-    assert P.dflash_probe_lds(1, 1, 0, None, None) == -1
-    P.dflash_probe_dma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                   ctypes.c_void_p]
-    assert P.dflash_probe_dma(None, 4096, 1, 1, 8, None) == -1
-    assert P.dflash_probe_dma(ctypes.c_void_p(16), 3000, 1, 1, 8, None) == -1   # not a power of two: no launch
-    assert P.dflash_probe_dma(ctypes.c_void_p(16), 4096, 1, 1, 9, None) == -1   # unsupported depth: no launch
-    P.dflash_probe_dma_issue.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
-    assert P.dflash_probe_dma_issue(ctypes.c_void_p(16), 4096, None, 1, None) == -1
+
+
+def test_advance_len_host_errors():
+    """The capacity comes from the configuration (the one the cache was sized with), so the
+    call validates the configuration and the batch against it."""
+    L = _lib()
+    c, kv = _cfg(), _kv()
+    call = lambda **k: L.dflash_advance_len(ctypes.byref(k.get("c", c)), ctypes.byref(k.get("kv", kv)),
+                                            k.get("batch", 1), k.get("n", FAKE), None)
+    assert call(batch=0) == DFLASH_EINVAL
+    assert call(batch=2) == DFLASH_EINVAL            # max_batch 1
+    assert call(n=None) == DFLASH_EINVAL
+    assert call(kv=dflash_kv(k=FAKE, v=FAKE, len=None, status=FAKE)) == DFLASH_EINVAL
+    assert call(c=_cfg(kv_capacity=100)) == DFLASH_EUNSUPPORTED
+    assert L.dflash_advance_len(None, ctypes.byref(kv), 1, FAKE, None) == DFLASH_EINVAL
