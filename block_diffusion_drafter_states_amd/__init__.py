@@ -234,6 +234,25 @@ def draft_block(model: Model, cache: Cache, gamma: int, anchor, draft, ws: Works
                                    ws.ptr(), ws.nbytes, _stream_ptr(stream)), "dflash_draft_block")
 
 
+def draft_block_noalloc(model: Model, cache: Cache, gamma: int, anchor, draft, dbg_hidden=None, dbg_logits=None,
+                        stream=None) -> None:
+    """draft_block without a workspace: the library's fixed per-GPU scratch is used instead
+    (dflash_draft_block_noalloc; calls that may overlap on one GPU race)."""
+    torch = _torch()
+    batch = anchor.shape[0]
+    _need(anchor, "anchor", torch.int32, (batch,))
+    _need(draft, "draft", torch.int32, (batch, gamma - 1))
+    if dbg_hidden is not None:
+        _need(dbg_hidden, "dbg_hidden", torch.float32, (batch, gamma, model.cfg.hidden))
+    if dbg_logits is not None:
+        _need(dbg_logits, "dbg_logits", torch.float32, (batch, gamma - 1, model.cfg.vocab))
+    check(lib().dflash_draft_block_noalloc(ctypes.byref(model.c), ctypes.byref(model.w), ctypes.byref(cache.s),
+                                           batch, gamma, anchor.data_ptr(), draft.data_ptr(),
+                                           None if dbg_hidden is None else dbg_hidden.data_ptr(),
+                                           None if dbg_logits is None else dbg_logits.data_ptr(),
+                                           _stream_ptr(stream)), "dflash_draft_block_noalloc")
+
+
 def block_loss(model: Model, cache: Cache, gamma: int, anchor, labels, loss, ws: Workspace, row_loss=None,
                dbg_logits=None, stream=None, dlogits=None) -> None:
     """The drafter's weighted block cross-entropy: anchor int32 [B], labels int32 [B][gamma-1]

@@ -19,6 +19,7 @@ DFLASH_EINVAL = -1
 DFLASH_EUNSUPPORTED = -2
 DFLASH_EWORKSPACE = -3
 DFLASH_ELAUNCH = -4
+DFLASH_ESCRATCH = -5
 
 DFLASH_F32 = 0
 DFLASH_BF16 = 1
@@ -30,7 +31,7 @@ STATUS_BAD_COUNT = 4
 EXPORTED = ("dflash_workspace_bytes", "dflash_inject_kv", "dflash_draft_block", "dflash_verify",
             "dflash_inject_kv_traced", "dflash_draft_block_traced", "dflash_target_forward", "dflash_advance_len",
             "dflash_choose_gamma", "dflash_block_loss", "dflash_inject_kv_input_fusion", "dflash_audit_workspace",
-            "dflash_status_str")
+            "dflash_draft_block_noalloc", "dflash_noalloc_scratch_bytes", "dflash_status_str")
 
 
 class dflash_config(ctypes.Structure):
@@ -100,6 +101,12 @@ def lib(path: str = LIB_PATH) -> ctypes.CDLL:
     L.dflash_advance_len.restype = ctypes.c_int
     L.dflash_advance_len.argtypes = [P(dflash_config), P(dflash_kv), ctypes.c_int32, ctypes.c_void_p,
                                      ctypes.c_void_p]
+    L.dflash_draft_block_noalloc.restype = ctypes.c_int
+    L.dflash_draft_block_noalloc.argtypes = [P(dflash_config), P(dflash_weights), P(dflash_kv), ctypes.c_int32,
+                                             ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_void_p, ctypes.c_void_p]
+    L.dflash_noalloc_scratch_bytes.restype = ctypes.c_size_t
+    L.dflash_noalloc_scratch_bytes.argtypes = []
     L.dflash_audit_workspace.restype = ctypes.c_int
     L.dflash_audit_workspace.argtypes = [P(dflash_config), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                          P(ctypes.c_int32), P(ctypes.c_int32), P(ctypes.c_int32)]

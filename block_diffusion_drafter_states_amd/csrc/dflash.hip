@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "../../include/dflash.h"
@@ -15,6 +16,10 @@
 #include "small_kernels.hpp"
 
 using namespace dflash;
+
+// Fixed scratch of dflash_draft_block_noalloc (see below): file scope, one copy per GPU.
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -928,6 +933,30 @@ int run_inject_input_fusion(const Shape& s, const dflash_weights* w, const dflas
     return launched(tr) ? DFLASH_OK : DFLASH_ELAUNCH;
 }
 
+// ---- fixed scratch for dflash_draft_block_noalloc (callers that cannot allocate) -------------
+// One array per GPU, in the library's code object: the loader places it in each device's
+// memory, where it stays until the process ends.  In host code `scratch` only names the
+// symbol; its device address is looked up once per device (hipGetSymbolAddress, with that
+// device current) and that address is what the kernels receive.
+constexpr int NOALLOC_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[NOALLOC_MAX_DEVICES] = {};
+
+// Device address of the current device's scratch array (looked up on the first call there).
+int scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return DFLASH_ELAUNCH;
+    if (dev < 0 || dev >= NOALLOC_MAX_DEVICES) return DFLASH_EUNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_addr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DFLASH_ELAUNCH;
+        g_scratch_addr[dev] = p;
+    }
+    *out = g_scratch_addr[dev];
+    return DFLASH_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -999,6 +1028,29 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, const 
                        void* workspace, size_t workspace_bytes, void* stream) {
     return dflash_draft_block_traced(cfg, w, kv, batch, gamma, anchor, draft, dbg_hidden, dbg_logits, workspace,
                                      workspace_bytes, stream, nullptr);
+}
+
+size_t dflash_noalloc_scratch_bytes(void) { return NOALLOC_SCRATCH_BYTES; }
+
+int dflash_draft_block_noalloc(const dflash_config* cfg, const dflash_weights* w, const dflash_kv* kv, int32_t batch,
+                               int32_t gamma, const int32_t* anchor, int32_t* draft, float* dbg_hidden,
+                               float* dbg_logits, void* stream) {
+    Shape s;
+    int rc = make_shape(cfg, s);
+    if (rc) return rc;
+    if (!w || !kv || !anchor || !draft || !kv->k || !kv->v || !kv->len || !kv->status) return DFLASH_EINVAL;
+    if (!weights_ok(s, w)) return DFLASH_EINVAL;
+    if (batch < 1 || batch > s.Bmax || gamma < 2 || gamma > s.gmax) return DFLASH_EINVAL;
+    if (w->rope_rows < s.cap + s.gmax) return DFLASH_EINVAL;
+    // the layout of this call (batch sequences), not of max_batch: it must fit the array
+    const Layout lay = make_layout(s, batch, 0);
+    if (lay.draft_end > NOALLOC_SCRATCH_BYTES) return DFLASH_ESCRATCH;
+    void* ws = nullptr;
+    if ((rc = scratch_address(&ws))) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    Tracer tr{nullptr, st};
+    return s.bf16 ? run_draft<bf16_t>(s, w, kv, batch, gamma, anchor, draft, dbg_hidden, dbg_logits, ws, lay, st, tr)
+                  : run_draft<float>(s, w, kv, batch, gamma, anchor, draft, dbg_hidden, dbg_logits, ws, lay, st, tr);
 }
 
 int dflash_inject_kv_input_fusion(const dflash_config* cfg, const dflash_weights* w, const dflash_kv* kv,
@@ -1193,6 +1245,9 @@ const char* dflash_status_str(int status) {
         case DFLASH_EUNSUPPORTED: return "DFLASH_EUNSUPPORTED: shape or dtype not supported";
         case DFLASH_EWORKSPACE: return "DFLASH_EWORKSPACE: workspace missing or too small";
         case DFLASH_ELAUNCH: return "DFLASH_ELAUNCH: kernel launch failed";
+        case DFLASH_ESCRATCH:
+            return "DFLASH_ESCRATCH: the call needs more scratch than the library's fixed array "
+                   "(dflash_noalloc_scratch_bytes); use the workspace entry point";
     }
     return "unknown dflash status";
 }

@@ -66,7 +66,8 @@ typedef enum {
     DFLASH_EINVAL = -1,        /* NULL pointer or size out of range */
     DFLASH_EUNSUPPORTED = -2,  /* shape or dtype this build does not handle */
     DFLASH_EWORKSPACE = -3,    /* workspace NULL or smaller than dflash_workspace_bytes() */
-    DFLASH_ELAUNCH = -4        /* the HIP runtime rejected a launch */
+    DFLASH_ELAUNCH = -4,       /* the HIP runtime rejected a launch */
+    DFLASH_ESCRATCH = -5       /* dflash_draft_block_noalloc: the call needs more than the fixed scratch */
 } dflash_status;
 
 typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
@@ -180,6 +181,26 @@ int dflash_draft_block(const dflash_config *cfg, const dflash_weights *w, const 
  * 2 <= gamma <= 1024, batch >= 1.  Exact integer work. */
 int dflash_verify(int32_t batch, int32_t gamma, const int32_t *draft, const int32_t *target,
                   int32_t *accept_len, int32_t *committed, int32_t *next_anchor, void *stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * call as dflash_draft_block, with the same arguments except the workspace,
+ * which is a fixed array inside the library instead - one per GPU, of
+ * dflash_noalloc_scratch_bytes() bytes (64 MiB), placed in each device's
+ * memory when the library is loaded and held until the process ends.  Neither
+ * call allocates or frees anything (the array's device address is looked up
+ * once per device, on the first call made with that device current, which
+ * must be the device of `stream`).  Every call on a GPU uses that GPU's one
+ * array: calls that may overlap on one GPU (other streams, other host threads)
+ * race and must be ordered by the caller.  Nothing in the array needs to start
+ * at zero (each call writes what it later reads).  Results are the same as
+ * dflash_draft_block's, bit for bit.  A call whose workspace
+ * (dflash_workspace_bytes(cfg, batch, 0)) exceeds the array returns
+ * DFLASH_ESCRATCH and enqueues nothing; other errors as for dflash_draft_block. */
+size_t dflash_noalloc_scratch_bytes(void);
+int dflash_draft_block_noalloc(const dflash_config *cfg, const dflash_weights *w, const dflash_kv *kv,
+                               int32_t batch, int32_t gamma, const int32_t *anchor, int32_t *draft,
+                               float *dbg_hidden, float *dbg_logits, void *stream);
 
 /* Tracing (optional per-launch timing).  The caller creates hipEvents and
  * passes their handles; the *_traced variants record events[2*i] before and
