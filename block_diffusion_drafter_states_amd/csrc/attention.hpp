@@ -21,7 +21,7 @@
 //    whose result leaves every lane with output columns of the same query as its
 //    scores, so the online-softmax rescaling needs no data exchange;
 //  * online softmax in base 2 (log2(e)/sqrt(D) folded into the scale); for
-//    bf16 the PV product takes P rounded to bf16.
+//    bf16 the PV product takes P as a sum of two bf16 parts (about 16 bits).
 // Chunk 0's workgroup first builds the block's keys (k RMSNorm + RoPE) and
 // values (rounded, transposed) in LDS; for a verifying target it also copies
 // them into the cache at positions len .. len + gamma - 1 (len is not changed).  The KG waves of a tile merge through
@@ -90,16 +90,22 @@ __device__ __forceinline__ void vfrag_mask(VFrag<float>& v, int valid) {
     }
 }
 
-// P of one lane (8 consecutive keys of one query) as the MFMA B operand: bf16
-// (the rounding of P is the one deviation the precision contract allows in the
-// attention product; V is bf16-exact already), or fp32 for fp32 storage.
+// P of one lane (8 consecutive keys of one query) as the MFMA B operand.  bf16
+// storage: P = hi + lo with hi = bf16(P) and lo = bf16(P - hi), two MFMAs against the
+// same (bf16-exact) V, so the product keeps ~16 significant bits of P: the softmax
+// weights are not rounded to bf16 (the precision contract rounds o, not P).  fp32
+// storage: P as is.
 template <typename T> struct PFrag;
-template <> struct PFrag<bf16_t> { u32x4_t q; };
+template <> struct PFrag<bf16_t> { u32x4_t hi, lo; };
 template <> struct PFrag<float> { float p[8]; };
 
 __device__ __forceinline__ void make_pfrag(PFrag<bf16_t>& f, const float (&p)[8]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) f.q[j] = pack2_bf16(p[2 * j], p[2 * j + 1]);
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t h = pack2_bf16(p[2 * j], p[2 * j + 1]);
+        f.hi[j] = h;
+        f.lo[j] = pack2_bf16(p[2 * j] - __uint_as_float(h << 16), p[2 * j + 1] - __uint_as_float(h & 0xFFFF0000u));
+    }
 }
 
 __device__ __forceinline__ void make_pfrag(PFrag<float>& f, const float (&p)[8]) {
@@ -109,7 +115,8 @@ __device__ __forceinline__ void make_pfrag(PFrag<float>& f, const float (&p)[8])
 
 // acc[d][q] += V^T(16 d, 8 keys of this lane group) . P^T(8 keys, q)
 __device__ __forceinline__ void pv_mfma(f32x4_t& acc, const PFrag<bf16_t>& p, const VFrag<bf16_t>& v) {
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(v.q), as_bf16x8(p.q), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(v.q), as_bf16x8(p.hi), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(v.q), as_bf16x8(p.lo), acc, 0, 0, 0);
 }
 
 __device__ __forceinline__ void pv_mfma(f32x4_t& acc, const PFrag<float>& p, const VFrag<float>& v) {
@@ -375,18 +382,21 @@ __device__ __forceinline__ void stage_issue(uint32_t stage, const T* kc, const T
     }
 }
 
-// Geometry, by the number QTW of query tiles per workgroup (1, 2, 4 or 8) and the
-// ring size RING (stages of 16 KB per workgroup): KG waves per tile split the
-// chunk's keys (8 waves in all, 4 for QTW 1); every key group owns a ring of
-// RING / KG stages in LDS.  RING 8 (128 KB) holds a whole 256-key chunk, for
-// launches with fewer workgroups than CUs; RING 4 (64 KB) for launches with many
-// (measured 2-4% faster there).  Chunk 0 builds the block's keys and values in the
-// first stage; afterwards the key-group merge reuses the space with one slot
-// (O^T, m, l of a wave) per sending wave.
+// Geometry, by the number QTW of query tiles per workgroup (1, 2, 4 or 8), the ring
+// size RING (stages of 16 KB per workgroup) and the number KG of waves per tile that
+// split the chunk's keys (8 waves in all, 4 for QTW 1 and for the four-wave layout
+// QTW 4 / KG 1); every key group owns a ring of RING / KG stages in LDS.  RING 8
+// (128 KB) holds a whole 256-key chunk, for launches with fewer workgroups than CUs;
+// RING 4 (64 KB) for launches with many (measured 2-4% faster there) and for the
+// four-wave layout with 128-key chunks, where the ring holds the whole chunk and two
+// workgroups share a CU.  Chunk 0 builds the block's keys and values in the first
+// stage; afterwards the key-group merge reuses the space with one slot (O^T, m, l of
+// a wave) per sending wave.
 constexpr int ATT_MAX_TILES = 8;
 constexpr int ATT_MAX_WAVES = 8;
-template <int QTW, int RING> struct AttGeom {
-    static constexpr int KG = QTW >= 8 ? 1 : (QTW == 4 ? 2 : 4);
+__host__ __device__ constexpr int att_default_kg(int qtw) { return qtw >= 8 ? 1 : (qtw == 4 ? 2 : 4); }
+template <int QTW, int RING, int KG_ = att_default_kg(QTW)> struct AttGeom {
+    static constexpr int KG = KG_;
     static constexpr int WAVES = QTW * KG;
     static constexpr int R = RING / KG;         // ring stages per key group
     static constexpr int NPW = 16 / QTW;        // loads per wave per stage
@@ -418,10 +428,10 @@ __device__ __forceinline__ void wait_stage(int later) {
     }
 }
 
-template <typename T, int QTW, int RING>
+template <typename T, int QTW, int RING, int KG_>
 __global__ __launch_bounds__(64 * ATT_MAX_WAVES) void attn_partial_kernel(const AttnArgs a) {
     constexpr int D = WaveAttn<T>::D, DT = WaveAttn<T>::DT, PER = Elem<T>::PER16;
-    using Geo = AttGeom<QTW, RING>;
+    using Geo = AttGeom<QTW, RING, KG_>;
     constexpr int KG = Geo::KG, R = Geo::R, NPW = Geo::NPW;
     extern __shared__ __align__(16) unsigned char smem[];
     const int c = blockIdx.x, h = blockIdx.y / a.nqs, qs = blockIdx.y % a.nqs, b = blockIdx.z;
@@ -695,56 +705,83 @@ struct MergeArgs {
 
 constexpr int MERGE_MAX_CHUNKS = 1024;
 constexpr int MERGE_BATCH = 16;   // chunk partials loaded together per lane
+constexpr int MERGE_WAVES = 4;    // waves per output row and q head, each over a range of chunks
 
+// Workgroup (row m = b*gamma + j, q head): wave w folds the contiguous chunk range
+// [w*per, (w+1)*per) (per = ceil(nch / 4)), loading every chunk's (m, l) and its lane's
+// DPL columns of O in one batch, so one memory latency covers a range of up to
+// MERGE_BATCH chunks; wave 0 then combines the four (max, sum, O) triples in wave order.
+// Every sum runs in a fixed order: the result is deterministic.
 template <typename T>
-__global__ __launch_bounds__(64) void attn_merge_kernel(const MergeArgs a) {
-    // blockIdx.x = row (b*gamma + j), blockIdx.y = q head; one wavefront, lane
-    // owns d = lane*DPL .. +DPL.  Chunks are summed in ascending order.
+__global__ __launch_bounds__(64 * MERGE_WAVES) void attn_merge_kernel(const MergeArgs a) {
     constexpr int D = 256 / (int)sizeof(T), DPL = D / 64;
-    __shared__ float wts[MERGE_MAX_CHUNKS];
+    __shared__ float red_ml[MERGE_WAVES][2];
+    __shared__ float red_o[MERGE_WAVES][DPL][64];
     const int m = blockIdx.x, hq_all = blockIdx.y;
     const int b = m / a.gamma, j = m % a.gamma;
     const int h = hq_all / a.group, hq = hq_all % a.group;
     const int R = hq * a.gamma + j;
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     int len = a.len[b];
     len = len < 0 ? 0 : (len > a.cap ? a.cap : len);
     const int nch = 1 + (len + a.chunk - 1) / a.chunk;
+    const int per = (nch + MERGE_WAVES - 1) / MERGE_WAVES;
+    const int c_lo = w * per, c_hi = min(nch, c_lo + per);
     const long long base = ((long long)b * a.n_kv + h) * a.nch_max;
-    float mmax = -INFINITY;
-    for (int c = lane; c < nch; c += 64) mmax = fmaxf(mmax, a.mlpart[((base + c) * a.rpad + R) * 2]);
-    mmax = wave_max(mmax);
-    float den = 0.f;
-    for (int c = lane; c < nch; c += 64) {
-        const long long row = (base + c) * a.rpad + R;
-        const float mc = a.mlpart[row * 2];
-        const float wc = (mc == -INFINITY) ? 0.f : exp2f(mc - mmax);
-        wts[c] = wc;
-        den += wc * a.mlpart[row * 2 + 1];
-    }
-    den = wave_sum(den);
-    __syncthreads();
-    const float* op = a.opart + (base * a.rpad + R) * (long long)D + lane * DPL;
-    const long long cstride = (long long)a.rpad * D;
-    float num[DPL];
+    float mw = -INFINITY, lw = 0.f, ow[DPL];
 #pragma unroll
-    for (int k = 0; k < DPL; ++k) num[k] = 0.f;
-    for (int c0 = 0; c0 < nch; c0 += MERGE_BATCH) {
-        float ov[MERGE_BATCH][DPL];
+    for (int k = 0; k < DPL; ++k) ow[k] = 0.f;
+    for (int cb = c_lo; cb < c_hi; cb += MERGE_BATCH) {
+        float mc[MERGE_BATCH], lc[MERGE_BATCH], oc[MERGE_BATCH][DPL];
 #pragma unroll
         for (int u = 0; u < MERGE_BATCH; ++u) {
-            const int c = min(c0 + u, nch - 1);
+            const int c = min(cb + u, c_hi - 1);       // past the range: re-read the last chunk, unused
+            const long long row = (base + c) * a.rpad + R;
+            mc[u] = a.mlpart[row * 2];
+            lc[u] = a.mlpart[row * 2 + 1];
 #pragma unroll
-            for (int k = 0; k < DPL; ++k) ov[u][k] = op[c * cstride + k];
+            for (int k = 0; k < DPL; ++k) oc[u][k] = a.opart[row * D + lane * DPL + k];
         }
+        float mb = mw;
+#pragma unroll
+        for (int u = 0; u < MERGE_BATCH; ++u)
+            if (cb + u < c_hi) mb = fmaxf(mb, mc[u]);
+        const float sc = (mw == -INFINITY) ? 0.f : exp2f(mw - mb);
+        lw *= sc;
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) ow[k] *= sc;
 #pragma unroll
         for (int u = 0; u < MERGE_BATCH; ++u) {
-            if (c0 + u < nch) {
-                const float wc = wts[c0 + u];
+            if (cb + u < c_hi) {
+                const float wc = (mc[u] == -INFINITY) ? 0.f : exp2f(mc[u] - mb);
+                lw += wc * lc[u];
 #pragma unroll
-                for (int k = 0; k < DPL; ++k) num[k] += wc * ov[u][k];
+                for (int k = 0; k < DPL; ++k) ow[k] += wc * oc[u][k];
             }
         }
+        mw = mb;
+    }
+    if (lane == 0) {
+        red_ml[w][0] = mw;
+        red_ml[w][1] = lw;
+    }
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) red_o[w][k][lane] = ow[k];
+    __syncthreads();
+    if (w != 0) return;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < MERGE_WAVES; ++v) mx = fmaxf(mx, red_ml[v][0]);
+    float den = 0.f, num[DPL];
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) num[k] = 0.f;
+#pragma unroll
+    for (int v = 0; v < MERGE_WAVES; ++v) {
+        const float mv = red_ml[v][0];
+        const float f = (mv == -INFINITY) ? 0.f : exp2f(mv - mx);
+        den += f * red_ml[v][1];
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) num[k] += f * red_o[v][k][lane];
     }
     T* out = reinterpret_cast<T*>(a.out);
     const int ncol = gridDim.y * D, col = hq_all * D + lane * DPL;

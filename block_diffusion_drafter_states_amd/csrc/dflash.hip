@@ -116,6 +116,7 @@ struct Shape {
     int H, nq, nkv, D, I, L, F, V, gmax, mask, Bmax, cap, esize, step, group, rpad, chunk, nch_max;
     float eps;
     bool bf16;
+    bool att_narrow;    // 128-key chunks for four-wave attention workgroups (two per CU)
 };
 
 int make_shape(const dflash_config* c, Shape& s) {
@@ -155,7 +156,19 @@ int make_shape(const dflash_config* c, Shape& s) {
     // attention 88 -> 70 us per cycle; at context 4096 the 272 workgroups of 128-key
     // chunks would need two rounds, 91 -> 119 us)
     const long long nqs_max = cdiv(cdiv(s.group * s.gmax, 16), ATT_MAX_TILES);
-    if (ch == 256 && (1 + cdiv(s.cap, 128)) * (long long)s.nkv * nqs_max * s.Bmax <= 256) ch = 128;
+    s.att_narrow = false;
+    if (ch == 256 && (1 + cdiv(s.cap, 128)) * (long long)s.nkv * nqs_max * s.Bmax <= 256) {
+        ch = 128;
+    } else if (ch == 256 && cdiv(s.group * s.gmax, 16) == 4 &&
+               (1 + cdiv(s.cap, 256)) * (long long)s.nkv * s.Bmax < 256 &&
+               (1 + cdiv(s.cap, 128)) * (long long)s.nkv * s.Bmax <= 512) {
+        // four query tiles (group 4 at block size 16) whose 256-key chunks leave CUs idle
+        // (the Qwen3-8B shape at context 4096: 144 workgroups for 256 CUs): 128-key chunks
+        // in four-wave workgroups, one wave per tile over the whole chunk, 64 KB of LDS and
+        // so two workgroups per CU - one round of 272 workgroups
+        ch = 128;
+        s.att_narrow = true;
+    }
     s.chunk = ch;
     s.nch_max = 1 + cdiv(s.cap, ch);
     if (s.nch_max > MERGE_MAX_CHUNKS) return DFLASH_EUNSUPPORTED;
@@ -255,7 +268,7 @@ GemmPlan plan_gemm(const Shape& s, int epi, int wrows, int K, int M, int layers)
 constexpr long long ATT_SMALL_RING_WGS = 512;
 
 struct AttnPlan {
-    int qtw, nqs, ring;
+    int qtw, nqs, ring, kg;
 };
 
 AttnPlan plan_attn(const Shape& s, int gamma, int batch) {
@@ -265,19 +278,31 @@ AttnPlan plan_attn(const Shape& s, int gamma, int batch) {
     while (a.qtw < qt && a.qtw < ATT_MAX_TILES) a.qtw *= 2;
     a.nqs = cdiv(qt, a.qtw);
     a.ring = (long long)s.nch_max * s.nkv * a.nqs * batch >= ATT_SMALL_RING_WGS ? 4 : 8;
+    a.kg = att_default_kg(a.qtw);
+    if (s.att_narrow && a.qtw == 4) {   // four waves, one per tile, 64 KB ring: two per CU
+        a.kg = 1;
+        a.ring = 4;
+    }
     return a;
 }
 
-template <typename T, int QTW, int RING>
+template <typename T, int QTW, int RING, int KG>
 void launch_attention_k(const AttnArgs& a, dim3 grid, hipStream_t st) {
-    hipLaunchKernelGGL((attn_partial_kernel<T, QTW, RING>), grid, dim3(64 * AttGeom<QTW, RING>::WAVES),
+    hipLaunchKernelGGL((attn_partial_kernel<T, QTW, RING, KG>), grid, dim3(64 * AttGeom<QTW, RING, KG>::WAVES),
                        attn_lds_bytes_host(RING), st, a);
 }
 
 template <typename T, int QTW>
 void launch_attention_q(const AttnArgs& a, const AttnPlan& ap, dim3 grid, hipStream_t st) {
-    if (ap.ring == 4) launch_attention_k<T, QTW, 4>(a, grid, st);
-    else launch_attention_k<T, QTW, 8>(a, grid, st);
+    constexpr int KG = att_default_kg(QTW);
+    if constexpr (QTW == 4) {
+        if (ap.kg == 1) {
+            launch_attention_k<T, QTW, 4, 1>(a, grid, st);
+            return;
+        }
+    }
+    if (ap.ring == 4) launch_attention_k<T, QTW, 4, KG>(a, grid, st);
+    else launch_attention_k<T, QTW, 8, KG>(a, grid, st);
 }
 
 template <typename T>
@@ -759,7 +784,7 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
             mgr.out_frag = afrag;
             tr.begin("attn_merge");
             if (tr.au) tr.au->write(obuf, span_act<T>(afrag, M, s.nq * s.D, s.nq * s.D));
-            DFL_LAUNCH(tr, (attn_merge_kernel<T>), dim3(M, s.nq), dim3(64), 0, st, mgr);
+            DFL_LAUNCH(tr, (attn_merge_kernel<T>), dim3(M, s.nq), dim3(64 * MERGE_WAVES), 0, st, mgr);
             tr.end();
             if (!launched(tr)) return DFLASH_ELAUNCH;
         }

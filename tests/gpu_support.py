@@ -24,6 +24,31 @@ def rel_err(got, ref) -> float:
     return float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
 
 
+def row_rel_err(got, ref) -> np.ndarray:
+    """Relative L2 error of every row (last axis): ||got - ref|| / ||ref|| per row."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    return np.linalg.norm(got - ref, axis=-1) / np.maximum(np.linalg.norm(ref, axis=-1), 1e-300)
+
+
+def row_tol(cfg) -> float:
+    """Per-row bound: the tensor bound of the configuration, applied to every single row
+    (each hidden row, each logit row, each (layer, head, position) K / V row)."""
+    return tol(cfg)
+
+
+def check_kv_rows(cfg, k_got, k_ref, v_got, v_ref, what=""):
+    """Whole-tensor and per-row relative errors of K / V rows [..][position][D]; asserts both."""
+    ek, ev = rel_err(k_got, k_ref), rel_err(v_got, v_ref)
+    rk, rv = row_rel_err(k_got, k_ref), row_rel_err(v_got, v_ref)
+    mk = float(rk.max()) if rk.size else 0.0
+    mv = float(rv.max()) if rv.size else 0.0
+    log(f"  {what}kv rel err k={ek:.3e} v={ev:.3e}; worst row k={mk:.3e} v={mv:.3e} over {rk.size} rows")
+    assert ek < tol(cfg) and ev < tol(cfg)
+    assert mk < row_tol(cfg) and mv < row_tol(cfg)
+    return {"k_rel": ek, "v_rel": ev, "k_row_max": mk, "v_row_max": mv}
+
+
 def decode(a):
     return O.decode_storage(a, np.float64)
 
@@ -99,36 +124,80 @@ class Pair:
         return int(self.cache.status.item())
 
 
-def check_draft(cfg, got, ref, gap_min=1e-2):
+def check_draft(cfg, got, ref, gap_min=1e-2, head=None):
     """Compare (draft, hidden, logits) of GPU vs oracle; returns a dict of metrics.
 
-    The argmax is taken on the GPU in fp32 over the logits it also returns, so the
-    drafted ids must be exactly the argmax (lowest index on ties) of those returned
-    logits.  Against the fp64 oracle the ids are unique only where the oracle's top-2
-    gap exceeds twice the largest logit error: no rounding within that error can then
-    flip the choice, so there the ids must match.  Elsewhere several ids are correct,
-    and the one chosen must be within that error of the oracle's maximum."""
+    Hidden states and logits: relative error of the whole tensor and of every row.
+    Draft ids are an argmax decided in floating point, checked three ways:
+      * self-consistency: the ids are exactly the argmax (lowest index on ties) of the
+        fp32 logits the GPU returns (`argmax_self_mismatch`);
+      * the LM head + argmax stage on its own (`head`: the oracle's final norm, rounding
+        and LM head applied to the GPU's final hidden rows): every row whose top-2 gap is
+        at least gap_min (1e-2) must draft that argmax (`head_strict_mismatch`).  The
+        stage's inputs are then identical on both sides, so its logits differ only by
+        summation order (~1e-5), far below the gap;
+      * end to end against the oracle's own forward: the two forwards round to bf16 at
+        the same points but decide some roundings differently (a value within float
+        noise of a bf16 midpoint), and such differences spread through later roundings
+        to about a bf16 unit in the hidden states (no implementation that sums in another
+        order than the fp64 oracle can avoid it).  Rows whose oracle gap exceeds twice the
+        largest logit difference of the call (and gap_min) must match (`wide_mismatch`);
+        elsewhere the chosen id must be within twice that difference of the oracle's
+        maximum (`not_near_optimal`).  The rows below gap_min (`band_exempt`), those
+        between gap_min and twice the difference (`band_wide`), and the ids that differ in
+        each band (`strict_mismatch` counts all differing ids at gap >= gap_min) are
+        reported."""
     d, x, z = got
     dr, xr, zr = ref
     assert np.isfinite(x).all() and np.isfinite(z).all()
     ex = rel_err(x, xr)
     ez = rel_err(z, zr)
+    rx = row_rel_err(x, xr)
+    rz = row_rel_err(z, zr)
     err = float(np.abs(z - zr).max())
     gap = top2_gap(zr)
-    sure = gap > max(gap_min, 2.0 * err)
-    mism = int(((d != dr) & sure).sum())
+    differ = d != dr
+    exempt = gap < gap_min
+    wide = (~exempt) & (gap <= 2.0 * err)
+    sure = (~exempt) & (~wide)
     self_mism = int((d != np.argmax(z, axis=-1)).sum())
     picked = np.take_along_axis(zr, d[..., None].astype(np.int64), axis=-1)[..., 0]
     not_near = int((picked < zr.max(axis=-1) - 2.0 * err).sum())
-    return {"hidden_rel": ex, "logits_rel": ez, "draft_checked": int(sure.sum()), "draft_mismatch": mism,
-            "argmax_self_mismatch": self_mism, "not_near_optimal": not_near, "logit_maxabs": err}
+    m = {"hidden_rel": ex, "logits_rel": ez, "hidden_row_max": float(rx.max()), "logits_row_max": float(rz.max()),
+         "rows": int(gap.size), "draft_checked": int(sure.sum()),
+         "strict_mismatch": int((differ & ~exempt).sum()), "wide_mismatch": int((differ & sure).sum()),
+         "band_exempt": int(exempt.sum()), "band_exempt_differ": int((differ & exempt).sum()),
+         "band_wide": int(wide.sum()), "band_wide_differ": int((differ & wide).sum()),
+         "argmax_self_mismatch": self_mism, "not_near_optimal": not_near, "logit_maxabs": err}
+    if head is not None:
+        zh = head(x)                       # oracle head on the GPU's final hidden rows
+        gh = top2_gap(zh)
+        hs = gh >= gap_min
+        m["head_logit_maxabs"] = float(np.abs(z - zh).max())
+        m["head_checked"] = int(hs.sum())
+        m["head_strict_mismatch"] = int(((d != np.argmax(zh, axis=-1)) & hs).sum())
+    return m
 
 
 def assert_draft(cfg, m) -> None:
     assert m["hidden_rel"] < tol(cfg) and m["logits_rel"] < tol(cfg)
+    assert m["hidden_row_max"] < row_tol(cfg) and m["logits_row_max"] < row_tol(cfg)
     assert m["argmax_self_mismatch"] == 0
-    assert m["draft_mismatch"] == 0 and m["not_near_optimal"] == 0
+    assert m["wide_mismatch"] == 0 and m["not_near_optimal"] == 0
     assert m["draft_checked"] > 0
+    if "head_strict_mismatch" in m:
+        assert m["head_strict_mismatch"] == 0 and m["head_checked"] > 0
+    if cfg.dtype == "f32":      # no bf16 roundings to decide differently: the strict bar end to end
+        assert m["strict_mismatch"] == 0
+
+
+def oracle_head(om):
+    """The oracle's final stage (final RMSNorm, bf16 rounding, LM head) as a function of
+    final hidden rows [B][gamma][H] (the anchor row excluded, as in drafting)."""
+    def f(x):
+        x = np.asarray(x, dtype=np.float64)
+        return O.linear(om.num.rho(O.rms_norm(x[:, 1:], om.final_norm, om.cfg.eps)), om.lm_head)
+    return f
 
 
 def run_cycle_case(cfg, batch, lengths, gammas, cap, seed_tag):
@@ -145,16 +214,20 @@ def run_cycle_case(cfg, batch, lengths, gammas, cap, seed_tag):
     assert list(P.cache.len.cpu().numpy()[:batch]) == list(lengths)
     k = decode(P.cache.read_k())
     v = decode(P.cache.read_v())
-    ek, ev = rel_err(k, P.okv.k), rel_err(v, P.okv.v)
-    log(f"  kv rel err k={ek:.3e} v={ev:.3e}")
-    assert ek < tol(cfg) and ev < tol(cfg)
+    # every written (layer, sequence, head, position) row, per row
+    rows_k = np.concatenate([k[:, b, :, :lengths[b]].reshape(-1, cfg.head_dim) for b in range(batch)])
+    rows_kr = np.concatenate([P.okv.k[:, b, :, :lengths[b]].reshape(-1, cfg.head_dim) for b in range(batch)])
+    rows_v = np.concatenate([v[:, b, :, :lengths[b]].reshape(-1, cfg.head_dim) for b in range(batch)])
+    rows_vr = np.concatenate([P.okv.v[:, b, :, :lengths[b]].reshape(-1, cfg.head_dim) for b in range(batch)])
+    check_kv_rows(cfg, rows_k, rows_kr, rows_v, rows_vr)
+    assert rel_err(k, P.okv.k) < tol(cfg) and rel_err(v, P.okv.v) < tol(cfg)
     results = []
     for ci, gamma in enumerate(gammas):
         anchors = gen.tokens(cfg, f"{seed_tag}.anchor.{ci}", (batch,))
         log(f"  draft cycle {ci} gamma={gamma}")
         got = P.draft(anchors, gamma)
         ref = P.oracle_draft(anchors, gamma)
-        m = check_draft(cfg, got, ref)
+        m = check_draft(cfg, got, ref, head=oracle_head(P.om))
         log(f"  {json.dumps(m)}")
         assert_draft(cfg, m)
         results.append(m)

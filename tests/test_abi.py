@@ -242,9 +242,9 @@ def test_binding_checks_tensor_arguments_before_calling_the_library():
 
 
 def test_draft_check_flags_wrong_ids():
-    """The GPU draft check itself: exact ids where the top-2 gap exceeds twice the
-    logit error, self-consistent argmax, near-optimal choice elsewhere; mistakes are
-    planted in the reference-side arrays on the CPU."""
+    """The GPU draft check itself: exact ids where the oracle's top-2 gap is at least 1e-2,
+    self-consistent argmax, near-optimal choice elsewhere, per-row relative errors; mistakes
+    are planted in the reference-side arrays on the CPU."""
     import numpy as np
     import gpu_support as G
     cfg = type("C", (), {"dtype": "bf16"})()
@@ -269,6 +269,36 @@ def test_draft_check_flags_wrong_ids():
     assert m["argmax_self_mismatch"] == 0 and m["logits_rel"] > G.tol(cfg)
     with pytest.raises(AssertionError):
         G.assert_draft(cfg, m)
+    # one hidden row off by 20%: the whole-tensor error stays small, the per-row bound fails
+    xb = x.copy()
+    xb[2, 3] *= 1.2
+    m = G.check_draft(cfg, (d, x, z), (np.argmax(zr, -1), xb, zr))
+    assert m["hidden_rel"] < G.tol(cfg) * 10 and m["hidden_row_max"] > G.tol(cfg)
+    with pytest.raises(AssertionError):
+        G.assert_draft(cfg, m)
+    # a row with a 5e-2 top-2 gap whose id differs is a strict mismatch, counted by band
+    zs = zr.copy()
+    zs[0, 1] = np.sort(zs[0, 1])        # ascending: the last id is the maximum
+    zs[0, 1, -2] = zs[0, 1, -1] - 5e-2
+    ds = np.argmax(zs, -1)
+    ds[0, 1] = zs.shape[-1] - 2
+    m = G.check_draft(cfg, (ds, x, zs), (np.argmax(zs, -1), x, zs))
+    assert m["strict_mismatch"] == 1 and m["wide_mismatch"] == 1 and m["band_exempt_differ"] == 0
+    with pytest.raises(AssertionError):
+        G.assert_draft(cfg, m)
+    # the LM-head stage on the GPU's own hidden rows: a differing id at gap >= 1e-2 fails
+    # even where the end-to-end comparison would allow it
+    m = G.check_draft(cfg, (d, x, z), (np.argmax(zr, -1), x, zr), head=lambda h: z)
+    assert m["head_strict_mismatch"] == 0 and m["head_checked"] > 0
+    G.assert_draft(cfg, m)
+    zh = z.copy()
+    zh[2, 4] = np.sort(zh[2, 4])
+    zh[2, 4, 0] = zh[2, 4, -1] + 1.0        # the head's argmax is now id 0 with a clear gap
+    m = G.check_draft(cfg, (d, x, z), (np.argmax(zr, -1), x, zr), head=lambda h: zh)
+    assert m["head_strict_mismatch"] == (0 if d[2, 4] == 0 else 1)
+    if d[2, 4] != 0:
+        with pytest.raises(AssertionError):
+            G.assert_draft(cfg, m)
 
 
 def test_probe_library_exports_and_rejects_bad_arguments():

@@ -11,7 +11,7 @@ import synth
 from synth import gen
 from oracle.input_fusion import inject_input_fusion
 
-from gpu_support import Pair, log, rel_err, decode, tol, check_draft, assert_draft
+from gpu_support import Pair, log, rel_err, decode, tol, check_draft, assert_draft, check_kv_rows, oracle_head
 
 pytestmark = pytest.mark.gpu
 
@@ -36,17 +36,15 @@ def _inject(P, rows, n_new, tag):
         c0, c1 = before[b], int(P.okv.len[b])
         if c1 == c0:
             continue
-        ek = rel_err(k[:, b, :, c0:c1], P.okv.k[:, b, :, c0:c1])
-        ev = rel_err(v[:, b, :, c0:c1], P.okv.v[:, b, :, c0:c1])
-        log(f"  {tag} seq {b} rows {c0}..{c1}: k={ek:.2e} v={ev:.2e}")
-        assert ek < tol(cfg) and ev < tol(cfg)
+        check_kv_rows(cfg, k[:, b, :, c0:c1], P.okv.k[:, b, :, c0:c1], v[:, b, :, c0:c1], P.okv.v[:, b, :, c0:c1],
+                      f"{tag} seq {b} rows {c0}..{c1}: ")
 
 
 def _draft(P, gamma, tag):
     anchors = gen.tokens(P.cfg, f"{tag}.anchor", (P.batch,))
     got = P.draft(anchors, gamma)
     ref = P.oracle_draft(anchors, gamma)
-    m = check_draft(P.cfg, got, ref)
+    m = check_draft(P.cfg, got, ref, head=oracle_head(P.om))
     log(f"  draft gamma={gamma}: {json.dumps(m)}")
     assert_draft(P.cfg, m)
 

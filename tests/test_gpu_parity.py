@@ -13,7 +13,7 @@ from synth import gen
 import oracle
 from oracle import dflash as O
 
-from gpu_support import Pair, log, rel_err, decode, tol, check_draft, assert_draft, run_cycle_case
+from gpu_support import Pair, log, rel_err, decode, tol, check_draft, assert_draft, run_cycle_case, oracle_head
 
 pytestmark = pytest.mark.gpu
 
@@ -60,7 +60,7 @@ def test_draft_against_synthetic_context_cache():
     log("case synthetic context mini_bf16")
     got = P.draft(anchors, 16)
     ref = P.oracle_draft(anchors, 16)
-    m = check_draft(cfg, got, ref)
+    m = check_draft(cfg, got, ref, head=oracle_head(P.om))
     log(f"  {json.dumps(m)}")
     assert_draft(cfg, m)
 

@@ -62,9 +62,13 @@ def _case(cfg, batch, prompt_len, gammas, taus, n_target_layers=4):
         ref_y = np.argmax(ref_lg, axis=-1)
         m = check_draft(cfg, (y, feat.reshape(batch, rows, -1), lg), (ref_y, ref_feat.reshape(batch, rows, -1), ref_lg))
         m["feat_rel"] = m.pop("hidden_rel")
+        m["feat_row_max"] = m.pop("hidden_row_max")
         log(f"  {tag} rows {start}..{start + rows}: {json.dumps(m)}")
         assert m["feat_rel"] < tol(cfg) and m["logits_rel"] < tol(cfg)
-        assert m["argmax_self_mismatch"] == 0 and m["draft_mismatch"] == 0 and m["not_near_optimal"] == 0
+        assert m["feat_row_max"] < tol(cfg) and m["logits_row_max"] < tol(cfg)
+        assert m["argmax_self_mismatch"] == 0 and m["wide_mismatch"] == 0 and m["not_near_optimal"] == 0
+        if cfg.dtype == "f32":
+            assert m["strict_mismatch"] == 0
 
     # the prompt, in chunks of at most gamma_max rows, each kept whole
     pos = 0
