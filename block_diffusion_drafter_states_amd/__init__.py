@@ -116,7 +116,8 @@ class Model:
 
 
 class Cache:
-    """Draft KV cache: K [L][B][n_kv][cap][D], V [L][B][n_kv][D][cap] (transposed), len[B], status."""
+    """Draft KV cache: K [L][B][n_kv][cap][D]; V in blocks of 32 positions, each transposed,
+    [L][B][n_kv][cap/32][D][32]; len[B], status."""
 
     def __init__(self, model: Model):
         torch = _torch()
@@ -124,7 +125,7 @@ class Cache:
         L, B, nkv, cap, D = c.n_layers, c.max_batch, c.n_kv_heads, c.kv_capacity, c.head_dim
         dt = model.storage_dtype
         self.k = torch.zeros((L, B, nkv, cap, D), dtype=dt, device=model.device)
-        self.v = torch.zeros((L, B, nkv, D, cap), dtype=dt, device=model.device)
+        self.v = torch.zeros((L, B, nkv, cap // 32, D, 32), dtype=dt, device=model.device)
         self.len = torch.zeros(B, dtype=torch.int32, device=model.device)
         self.status = torch.zeros(1, dtype=torch.int32, device=model.device)
         self.s = dflash_kv(k=self.k.data_ptr(), v=self.v.data_ptr(), len=self.len.data_ptr(),
@@ -138,15 +139,20 @@ class Cache:
         self.k.zero_()
         self.v.zero_()
         self.k[:, :B, :, :C, :] = to_device(K, self.k.device)
-        self.v[:, :B, :, :, :C] = to_device(V, self.v.device).transpose(-1, -2)
+        nb = (C + 31) // 32                                 # 32-position blocks, each transposed
+        vd = to_device(V, self.v.device)
+        if nb * 32 != C:
+            vd = torch.cat([vd, vd.new_zeros(vd.shape[:3] + (nb * 32 - C, vd.shape[4]))], dim=3)
+        self.v[:, :B, :, :nb] = vd.reshape(vd.shape[:3] + (nb, 32, vd.shape[4])).transpose(-1, -2)
         self.len[:B] = torch.as_tensor(np.asarray(lengths, dtype=np.int32), device=self.len.device)
 
     def read_k(self) -> np.ndarray:
         return to_storage(self.k)
 
     def read_v(self) -> np.ndarray:
-        """V as [L][B][n_kv][cap][D] storage (un-transposed)."""
-        return to_storage(self.v.transpose(-1, -2).contiguous())
+        """V as [L][B][n_kv][cap][D] storage (the 32-position blocks un-transposed)."""
+        v = self.v.transpose(-1, -2).contiguous()
+        return to_storage(v.reshape(v.shape[:3] + (-1, v.shape[-1])))
 
 
 class Workspace:

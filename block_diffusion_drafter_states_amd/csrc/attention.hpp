@@ -17,11 +17,11 @@
 //      S^T = K . Q^T    (A = key rows, B = queries)
 //    with the key rows permuted so that every lane ends up holding 8
 //    consecutive keys of one query - exactly the B-operand layout of
-//      O^T += V^T . P^T (A = V^T rows of the transposed V cache),
+//      O^T += V^T . P^T (A = V^T rows of the V cache, stored as 32-key blocks of V^T),
 //    whose result leaves every lane with output columns of the same query as its
 //    scores, so the online-softmax rescaling needs no data exchange;
 //  * online softmax in base 2 (log2(e)/sqrt(D) folded into the scale); for
-//    bf16 the PV product takes P as a sum of two bf16 parts (about 16 bits).
+//    bf16 the PV product takes P rounded to bf16.
 // Chunk 0's workgroup first builds the block's keys (k RMSNorm + RoPE) and
 // values (rounded, transposed) in LDS; for a verifying target it also copies
 // them into the cache at positions len .. len + gamma - 1 (len is not changed).  The KG waves of a tile merge through
@@ -33,9 +33,16 @@
 
 namespace dflash {
 
+// V cache in blocks of 32 keys: the values of keys 32 i .. 32 i + 31 are stored transposed
+// and contiguous, [D][32], so one 32-key sub-block of V^T is one 8 KB span (bf16).
+constexpr int VBLK = 32;
+__host__ __device__ __forceinline__ long long vblk_offset(int pos, int d, int D) {
+    return (long long)(pos / VBLK) * (D * VBLK) + d * VBLK + pos % VBLK;
+}
+
 struct AttnArgs {
     const void* kcache;     // this layer: T [Bmax][n_kv][cap][D]
-    const void* vcache;     // this layer: T [Bmax][n_kv][D][cap]
+    const void* vcache;     // this layer: T [Bmax][n_kv][cap / 32][D][32] (32-key blocks of V^T)
     const float* qkv;       // raw projections fp32 [B*gamma][qkv_ld]: q heads, then k heads, then v heads
     int qkv_ld;
     const void* q_norm;     // T [D]
@@ -90,22 +97,19 @@ __device__ __forceinline__ void vfrag_mask(VFrag<float>& v, int valid) {
     }
 }
 
-// P of one lane (8 consecutive keys of one query) as the MFMA B operand.  bf16
-// storage: P = hi + lo with hi = bf16(P) and lo = bf16(P - hi), two MFMAs against the
-// same (bf16-exact) V, so the product keeps ~16 significant bits of P: the softmax
-// weights are not rounded to bf16 (the precision contract rounds o, not P).  fp32
-// storage: P as is.
+// P of one lane (8 consecutive keys of one query) as the MFMA B operand: bf16 (the
+// rounding of P the precision contract allows in the attention product; V is bf16-exact
+// already), or fp32 for fp32 storage.  Splitting P into two bf16 parts (hi + lo, two
+// MFMAs) keeps ~16 bits but measured a third slower in the sub-block loop, which the
+// matrix core bounds at the Qwen3-8B shape, and does not change how far the bf16
+// forward can agree with an fp64 one (the roundings of the later stages dominate).
 template <typename T> struct PFrag;
-template <> struct PFrag<bf16_t> { u32x4_t hi, lo; };
+template <> struct PFrag<bf16_t> { u32x4_t q; };
 template <> struct PFrag<float> { float p[8]; };
 
 __device__ __forceinline__ void make_pfrag(PFrag<bf16_t>& f, const float (&p)[8]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const uint32_t h = pack2_bf16(p[2 * j], p[2 * j + 1]);
-        f.hi[j] = h;
-        f.lo[j] = pack2_bf16(p[2 * j] - __uint_as_float(h << 16), p[2 * j + 1] - __uint_as_float(h & 0xFFFF0000u));
-    }
+    for (int j = 0; j < 4; ++j) f.q[j] = pack2_bf16(p[2 * j], p[2 * j + 1]);
 }
 
 __device__ __forceinline__ void make_pfrag(PFrag<float>& f, const float (&p)[8]) {
@@ -115,8 +119,7 @@ __device__ __forceinline__ void make_pfrag(PFrag<float>& f, const float (&p)[8])
 
 // acc[d][q] += V^T(16 d, 8 keys of this lane group) . P^T(8 keys, q)
 __device__ __forceinline__ void pv_mfma(f32x4_t& acc, const PFrag<bf16_t>& p, const VFrag<bf16_t>& v) {
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(v.q), as_bf16x8(p.hi), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(v.q), as_bf16x8(p.lo), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(v.q), as_bf16x8(p.q), acc, 0, 0, 0);
 }
 
 __device__ __forceinline__ void pv_mfma(f32x4_t& acc, const PFrag<float>& p, const VFrag<float>& v) {
@@ -355,7 +358,8 @@ __device__ __forceinline__ void attn_subblock(WaveAttn<T>& w, int nvalid, int kl
 
 // Direct-to-LDS loads of context keys [kb, kb+32) of one (b,h) into a stage:
 // 8 instructions of 1 KB for K (rows beyond the real keys repeat the last real
-// one; their scores are masked) and 8 for V^T (whole rows: kb + 32 <= cap; keys
+// one; their scores are masked) and 8 for V^T (the 32-key block, one contiguous 8 KB span
+// of the blocked V cache: kb + 32 <= cap; keys
 // beyond the real ones are cleared at use).  Instruction j goes to the wave
 // iw = j % NW of the key group: every wave issues exactly 16 / NW of them.
 template <typename T, int NW>
@@ -377,7 +381,7 @@ __device__ __forceinline__ void stage_issue(uint32_t stage, const T* kc, const T
             const int jj = j - 8;
             const int d = jj * RPI + lane / CPR, p = lane % CPR;
             const int c = sizeof(T) == 2 ? (p ^ ((d >> 2) & 3)) : p;
-            dma_b128(vc + (long long)d * cap + kb + c * KPC, stage + ATT_V_OFF + jj * 1024);
+            dma_b128(vc + (long long)kb * D + d * VBLK + c * KPC, stage + ATT_V_OFF + jj * 1024);
         }
     }
 }
@@ -604,7 +608,7 @@ __global__ __launch_bounds__(64 * ATT_MAX_WAVES) void attn_partial_kernel(const 
                 }
                 for (int e = threadIdx.x; e < D * G; e += blockDim.x) {
                     const int d = e / G, key = e % G;
-                    vw[(long long)d * a.cap + raw + key] = *reinterpret_cast<const T*>(
+                    vw[vblk_offset(raw + key, d, D)] = *reinterpret_cast<const T*>(
                         smem + ATT_V_OFF + v_lds_off<T>(d, key / KPC) + (key % KPC) * (int)sizeof(T));
                 }
             }
@@ -707,10 +711,11 @@ constexpr int MERGE_MAX_CHUNKS = 1024;
 constexpr int MERGE_BATCH = 16;   // chunk partials loaded together per lane
 constexpr int MERGE_WAVES = 4;    // waves per output row and q head, each over a range of chunks
 
-// Workgroup (row m = b*gamma + j, q head): wave w folds the contiguous chunk range
-// [w*per, (w+1)*per) (per = ceil(nch / 4)), loading every chunk's (m, l) and its lane's
+// Workgroup (row m = b*gamma + j, q head) of nw waves (1, or 4 when rows have more chunks
+// than one batch): wave w folds the contiguous chunk range [w*per, (w+1)*per) (per =
+// ceil(nch / nw)), loading every chunk's (m, l) and its lane's
 // DPL columns of O in one batch, so one memory latency covers a range of up to
-// MERGE_BATCH chunks; wave 0 then combines the four (max, sum, O) triples in wave order.
+// MERGE_BATCH chunks; wave 0 then combines the (max, sum, O) triples in wave order.
 // Every sum runs in a fixed order: the result is deterministic.
 template <typename T>
 __global__ __launch_bounds__(64 * MERGE_WAVES) void attn_merge_kernel(const MergeArgs a) {
@@ -721,11 +726,11 @@ __global__ __launch_bounds__(64 * MERGE_WAVES) void attn_merge_kernel(const Merg
     const int b = m / a.gamma, j = m % a.gamma;
     const int h = hq_all / a.group, hq = hq_all % a.group;
     const int R = hq * a.gamma + j;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;   // nw <= MERGE_WAVES
     int len = a.len[b];
     len = len < 0 ? 0 : (len > a.cap ? a.cap : len);
     const int nch = 1 + (len + a.chunk - 1) / a.chunk;
-    const int per = (nch + MERGE_WAVES - 1) / MERGE_WAVES;
+    const int per = (nch + nw - 1) / nw;
     const int c_lo = w * per, c_hi = min(nch, c_lo + per);
     const long long base = ((long long)b * a.n_kv + h) * a.nch_max;
     float mw = -INFINITY, lw = 0.f, ow[DPL];
@@ -770,13 +775,11 @@ __global__ __launch_bounds__(64 * MERGE_WAVES) void attn_merge_kernel(const Merg
     __syncthreads();
     if (w != 0) return;
     float mx = -INFINITY;
-#pragma unroll
-    for (int v = 0; v < MERGE_WAVES; ++v) mx = fmaxf(mx, red_ml[v][0]);
+    for (int v = 0; v < nw; ++v) mx = fmaxf(mx, red_ml[v][0]);
     float den = 0.f, num[DPL];
 #pragma unroll
     for (int k = 0; k < DPL; ++k) num[k] = 0.f;
-#pragma unroll
-    for (int v = 0; v < MERGE_WAVES; ++v) {
+    for (int v = 0; v < nw; ++v) {
         const float mv = red_ml[v][0];
         const float f = (mv == -INFINITY) ? 0.f : exp2f(mv - mx);
         den += f * red_ml[v][1];

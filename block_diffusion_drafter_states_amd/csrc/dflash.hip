@@ -219,6 +219,8 @@ GemmPlan plan_streaming(const Shape& s, int epi, int wrows, int K, int M, int la
     if (epi == EPI_ARGMAX || epi == EPI_LSE) {
         ks = 2;
     } else if (epi == EPI_SWIGLU) {
+        // measured at 16 rows: four waves (128 KB of ring, three rounds of one workgroup per CU)
+        // 40.8 us per Qwen3-8B gate|up launch; two waves (64 KB, two per CU, 1.5 rounds) 45 us
         ks = 4;
     } else {
         p.ntw = wrows / 32 >= 192 ? 2 : 1;
@@ -279,7 +281,10 @@ AttnPlan plan_attn(const Shape& s, int gamma, int batch) {
     a.nqs = cdiv(qt, a.qtw);
     a.ring = (long long)s.nch_max * s.nkv * a.nqs * batch >= ATT_SMALL_RING_WGS ? 4 : 8;
     a.kg = att_default_kg(a.qtw);
-    if (s.att_narrow && a.qtw == 4) {   // four waves, one per tile, 64 KB ring: two per CU
+    // four waves, one per tile, 64 KB ring: the kernel's 209 VGPRs allow two such workgroups
+    // per CU (eight-wave ones: one), which doubles the K/V bytes each CU keeps in flight - for
+    // the 128-key chunks of the Qwen3-8B shape, and for launches with many workgroups
+    if (a.qtw == 4 && (s.att_narrow || a.ring == 4)) {
         a.kg = 1;
         a.ring = 4;
     }
@@ -597,7 +602,7 @@ int run_inject(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int
         }
         if ((rc = gemm_dispatch<T>(a, pl.kv, st, tr, "inject_kv"))) return rc;
     }
-    {   // stage 3: k-norm + RoPE -> K cache, v -> transposed V cache
+    {   // stage 3: k-norm + RoPE -> K cache, v -> V cache (32-key blocks of V^T)
         KvFinishArgs a;
         std::memset(&a, 0, sizeof(a));
         a.kv = kvraw;
@@ -784,7 +789,9 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
             mgr.out_frag = afrag;
             tr.begin("attn_merge");
             if (tr.au) tr.au->write(obuf, span_act<T>(afrag, M, s.nq * s.D, s.nq * s.D));
-            DFL_LAUNCH(tr, (attn_merge_kernel<T>), dim3(M, s.nq), dim3(64 * MERGE_WAVES), 0, st, mgr);
+            // four waves per (row, head) when a row has more chunks than one batch of loads
+            const int merge_waves = s.nch_max > MERGE_BATCH ? MERGE_WAVES : 1;
+            DFL_LAUNCH(tr, (attn_merge_kernel<T>), dim3(M, s.nq), dim3(64 * merge_waves), 0, st, mgr);
             tr.end();
             if (!launched(tr)) return DFLASH_ELAUNCH;
         }

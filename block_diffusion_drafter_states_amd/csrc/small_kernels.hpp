@@ -176,7 +176,7 @@ __device__ __forceinline__ void head_norm_rope_store(const float* src, int D, co
 // (k heads, then v heads) of row m = b * rows_stride + i.  Row i < n_new[b] of
 // sequence b lands at position len[b] + i: k heads get the layer's k RMSNorm and
 // RoPE (K cache [L][Bmax][n_kv][cap][D]), v heads are rounded into the
-// transposed V cache [L][Bmax][n_kv][D][cap].  Positions come from len_snap, a
+// V cache in 32-key blocks of V^T, [L][Bmax][n_kv][cap / 32][D][32].  Positions come from len_snap, a
 // copy of len taken before this kernel; workgroup (0, 0, b) then advances
 // len[b] += n_new[b], or sets STATUS_BAD_COUNT / STATUS_KV_OVERFLOW and writes
 // nothing for that sequence.  blockIdx = (head of 2 n_kv, layer, sequence);
@@ -242,7 +242,8 @@ __global__ __launch_bounds__(256) void kv_finish_kernel(const KvFinishArgs a, in
         T* vc = reinterpret_cast<T*>(a.vcache) + l * a.cache_layer + ((long long)b * a.n_kv + h) * (long long)D * cap;
         for (int e = threadIdx.x; e < D * nr; e += 256) {
             const int d = e / nr, i = e % nr;
-            vc[(long long)d * cap + len + i0 + i] = Elem<T>::from_f(src[(long long)i * ld + d]);
+            const int pos = len + i0 + i;      // 32-key blocks of V^T ([cap / 32][D][32])
+            vc[(long long)(pos / 32) * (D * 32) + d * 32 + pos % 32] = Elem<T>::from_f(src[(long long)i * ld + d]);
         }
     }
 }

@@ -46,7 +46,10 @@
  *   w_fuse                    [H][F*H]    (input = the F feature rows concatenated,
  *                                          shallowest tapped layer first)
  *   K cache  kv->k            [L][max_batch][n_kv][kv_capacity][D]
- *   V cache  kv->v            [L][max_batch][n_kv][D][kv_capacity]   (transposed)
+ *   V cache  kv->v            [L][max_batch][n_kv][kv_capacity/32][D][32]: blocks of 32
+ *                             positions, each stored transposed (the value of position
+ *                             32*i + j, dimension d at [i][d][j]), so the values of 32
+ *                             consecutive positions are one contiguous span
  *   kv->len                   int32 [max_batch]: rows of context held per sequence
  *   rope_cos / rope_sin       fp32 [rope_rows][D/2]: cos/sin of p * theta^(-2i/D)
  *                             for position p (rotate-half pairs (i, i+D/2))
@@ -127,7 +130,7 @@ typedef struct {
 
 typedef struct {
     void *k;           /* K cache, layout above */
-    void *v;           /* V cache (transposed), layout above */
+    void *v;           /* V cache (32-position blocks, each transposed), layout above */
     int32_t *len;      /* [max_batch] */
     uint32_t *status;  /* [1] sticky device status bits */
 } dflash_kv;
