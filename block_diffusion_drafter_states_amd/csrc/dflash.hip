@@ -177,6 +177,7 @@ int make_shape(const dflash_config* c, Shape& s) {
 
 struct GemmPlan {
     int ns, ks, kw, n_tiles, mt, mgroups, layers, ntw, epi;
+    int ring;       // weight-streaming kernel: ring depth (k-steps in flight per wave); 0 = the default
     bool tiled;     // gemm_tiled_kernel (many rows) instead of the weight-streaming kernel
     int bn;         // tiled: weight rows per workgroup (128, or 64 when that leaves CUs idle)
     int kb;         // tiled: bytes of every row per LDS stage (256; 128 for launches with many workgroups)
@@ -228,7 +229,12 @@ GemmPlan plan_streaming(const Shape& s, int epi, int wrows, int K, int M, int la
     }
     if (epi == EPI_SWIGLU) p.n_tiles = cdiv(wrows, 16);   // 16 gate + 16 up rows per workgroup
     else p.n_tiles = cdiv(wrows, p.ns * p.ntw * 16);
-    const int ring = gemm_ring_depth(p.mt, p.ntw);
+    // gate|up over one 16-row tile: a 2-stage ring (64 KB) so that two workgroups share a CU
+    // and one streams while the other starts or runs its epilogue (measured at the Qwen3-8B
+    // shape, 768 workgroups: 47 -> 39.6 us per launch; a 4-stage ring, one workgroup per
+    // CU, idles each CU between its three workgroups; HIP-event times)
+    p.ring = (epi == EPI_SWIGLU && p.mt == 1) ? 2 : 0;
+    const int ring = p.ring ? p.ring : gemm_ring_depth(p.mt, p.ntw);
     while (ks > 1 && K / s.step < 2 * ks) ks /= 2;        // at least two k-steps per wave
     while (ks > 1 && gemm_lds_bytes_host(p.ns, ks, p.mt, p.ntw, ring) > GEMM_MAX_LDS) ks /= 2;
     p.ks = ks;
@@ -414,9 +420,17 @@ Layout make_layout(const Shape& s, int batch, int rows) {
 template <typename T, int EPI, int MT, int NTW>
 int launch_gemm(const GemmArgs& a, const GemmPlan& p, hipStream_t st, Tracer& tr, const char* name) {
     constexpr int P = gemm_ring_depth(MT, NTW);
+    // the one non-default ring: gate|up over one 16-row tile, 2 stages
+    constexpr bool RING2 = EPI == EPI_SWIGLU && MT == 1;
+    if (p.ring && p.ring != P && !(RING2 && p.ring == 2)) return DFLASH_EINVAL;
     dim3 grid(p.n_tiles, p.mgroups, p.layers);
     tr.begin(name);
-    DFL_LAUNCH(tr, (gemm_kernel<T, EPI, MT, NTW, P>), grid, dim3(64 * p.ns * p.ks), p.lds, st, a);
+    if (p.ring && p.ring != P) {
+        if constexpr (RING2)
+            DFL_LAUNCH(tr, (gemm_kernel<T, EPI, MT, NTW, 2>), grid, dim3(64 * p.ns * p.ks), p.lds, st, a);
+    } else {
+        DFL_LAUNCH(tr, (gemm_kernel<T, EPI, MT, NTW, P>), grid, dim3(64 * p.ns * p.ks), p.lds, st, a);
+    }
     const bool ok = launched(tr);
     tr.end();
     return ok ? DFLASH_OK : DFLASH_ELAUNCH;
@@ -459,11 +473,32 @@ void audit_gemm(const GemmArgs& a, const GemmPlan& p, Audit& au) {
         au.write(a.lse, span_rows(p.n_tiles, a.M, a.M, 8));
         au.write(a.lab_logit, (size_t)a.M * 4);
     }
+    if (a.n_z > 0) au.write(a.zout, (size_t)(a.n_z - 1) * a.zstride * sizeof(T) + span_act<T>(1, a.M, a.N, a.N));
+    if (a.snap_n > 0) au.write(a.snap_dst, (size_t)a.snap_n * 4);
+}
+
+// An RMSNorm can be carried across a GEMM pair (the producer's store epilogue writes x * w_norm
+// in fragment order, the consumer multiplies its output rows by the norm's row factor) when
+// both are weight-streaming launches over one tile of at most 16 rows (a multiple of 4: the
+// consumer reads the sums of squares of 4 rows in one 16-byte load), the producer's store
+// epilogue has one output element per thread and the consumer's threads can hold the
+// producer's per-tile sums of squares in GEMM_RSQ loads each.
+bool fold_producer_ok(const GemmPlan& p, int M) {
+    return !p.tiled && p.mt == 1 && p.epi == EPI_STORE && M <= 16 && M % 4 == 0 &&
+           16 * p.ns * p.ntw * 16 <= 64 * p.ns * p.ks;
+}
+bool fold_consumer_ok(const GemmPlan& c, int rs_n, int M) {
+    return !c.tiled && c.mt == 1 && (c.epi == EPI_STORE || c.epi == EPI_SWIGLU) && M <= 16 && M % 4 == 0 &&
+           rs_n >= 1 && rs_n <= GEMM_RSQ * 64 * c.ns * c.ks / 4;
 }
 
 template <typename T>
 int gemm_dispatch(const GemmArgs& a, const GemmPlan& p, hipStream_t st, Tracer& tr, const char* name) {
     if (p.layers < 1 || p.layers > MAX_LAYERS || a.M < 1) return DFLASH_EINVAL;
+    if (a.rs_ssq && (!fold_consumer_ok(p, a.rs_n, a.M) || a.rs_ld % 4 || a.rs_ld < a.M || !a.a_frag))
+        return DFLASH_EINVAL;
+    if (a.n_z && (a.n_z < 0 || a.n_z > GEMM_ZMAX || !fold_producer_ok(p, a.M) || !a.zout)) return DFLASH_EINVAL;
+    if (a.snap_n && (p.tiled || p.epi != EPI_STORE || !a.snap_src || !a.snap_dst)) return DFLASH_EINVAL;
     if (tr.au) audit_gemm<T>(a, p, *tr.au);
     if (p.tiled) {
         if (a.a_frag || a.out_frag) return DFLASH_EINVAL;     // the tiled kernel reads and writes plain rows
@@ -543,6 +578,20 @@ int set_norm_a(GemmArgs& a, const Shape& s, const float* x, int M, const float* 
     return launched(tr) ? DFLASH_OK : DFLASH_ELAUNCH;
 }
 
+// A operand = the rows x * w_norm that the producing GEMM wrote into nbuf (fragment order);
+// this GEMM multiplies its output rows by the norm's row factor, from the producer's
+// per-tile sums of squares of x.
+void set_carried_norm_a(GemmArgs& a, const Shape& s, void* nbuf, const float* ssq, int n_ssq, int M) {
+    a.a = nbuf;
+    a.lda = s.H;
+    a.a_frag = 1;
+    a.rs_ssq = ssq;
+    a.rs_n = n_ssq;
+    a.rs_ld = M;
+    a.rs_k = (float)s.H;
+    a.rs_eps = s.eps;
+}
+
 template <typename T>
 int run_inject(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int batch, const void* feat,
                int rows, const int* n_new, void* ws, const Layout& lay, hipStream_t st, Tracer& tr) {
@@ -557,6 +606,11 @@ int run_inject(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int
     int rc;
     // the layout was carved from these plans' tile counts; checked before anything is launched
     if (pl.fuse.n_tiles > lay.ssq_c_tiles) return DFLASH_EUNSUPPORTED;
+    T* cn = reinterpret_cast<T*>(wsb + lay.cnorm);
+    const size_t cn_layer = (size_t)pad16(M) * s.H;    // whole 16-row tiles per layer
+    // every layer's RMSNorm carried across the GEMMs where the plans allow it: the fusion
+    // GEMM writes c * w_in,l for each layer (and the len snapshot), W_k|W_v scales its rows
+    const bool carry = s.L <= GEMM_ZMAX && fold_producer_ok(pl.fuse, M) && fold_consumer_ok(pl.kv, pl.fuse.n_tiles, M);
     {   // stage 1: c = W_fuse . concat(feat)
         GemmArgs a = gemm_base(s, pl.fuse, M, s.F * s.H);
         a.a = feat;
@@ -569,24 +623,36 @@ int run_inject(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int
         a.residual = 0;
         a.ssq_out = ssq_c;
         a.ssq_out_ld = M;
+        if (carry) {
+            a.n_z = s.L;
+            for (int l = 0; l < s.L; ++l) a.zw[l] = w->layers[l].in_norm;
+            a.zout = cn;
+            a.zstride = (long long)cn_layer;
+            a.snap_src = kv->len;
+            a.snap_dst = lensnap;
+            a.snap_n = batch;
+        }
         if ((rc = gemm_dispatch<T>(a, pl.fuse, st, tr, "fuse"))) return rc;
     }
     {   // stage 2: every layer's RMSNorm -> W_k | W_v (one launch for all layers)
         GemmArgs a = gemm_base(s, pl.kv, M, s.H);
-        NormWeights nw{};   // one normalised copy of c per layer (each layer has its own scale)
-        for (int l = 0; l < s.L; ++l) nw.w[l] = w->layers[l].in_norm;
-        T* cn = reinterpret_cast<T*>(wsb + lay.cnorm);
         const int afrag = M < TILED_MIN_ROWS ? 1 : 0;       // fragment order for the weight-streaming GEMM
-        const size_t cn_layer = (size_t)pad16(M) * s.H;    // whole 16-row tiles per layer
-        tr.begin("rmsnorm");
-        if (tr.au) {
-            tr.au->write(cn, (size_t)(s.L - 1) * cn_layer * sizeof(T) + span_act<T>(afrag, M, s.H, s.H));
-            tr.au->write(lensnap, (size_t)batch * 4);
+        if (carry) {
+            set_carried_norm_a(a, s, cn, ssq_c, pl.fuse.n_tiles, M);
+        } else {
+            NormWeights nw{};   // one normalised copy of c per layer (each layer has its own scale)
+            for (int l = 0; l < s.L; ++l) nw.w[l] = w->layers[l].in_norm;
+            tr.begin("rmsnorm");
+            if (tr.au) {
+                tr.au->write(cn, (size_t)(s.L - 1) * cn_layer * sizeof(T) + span_act<T>(afrag, M, s.H, s.H));
+                tr.au->write(lensnap, (size_t)batch * 4);
+            }
+            DFL_LAUNCH(tr, (rmsnorm_rows_kernel<T>), dim3(M, cdiv(s.H, 1024), s.L), dim3(256), 0, st, c, s.H, ssq_c,
+                       pl.fuse.n_tiles, M, nw, s.H, s.eps, cn, s.H, (long long)cn_layer, kv->len, lensnap, batch,
+                       afrag);
+            tr.end();
+            if (!launched(tr)) return DFLASH_ELAUNCH;
         }
-        DFL_LAUNCH(tr, (rmsnorm_rows_kernel<T>), dim3(M, cdiv(s.H, 1024), s.L), dim3(256), 0, st, c, s.H, ssq_c,
-                   pl.fuse.n_tiles, M, nw, s.H, s.eps, cn, s.H, (long long)cn_layer, kv->len, lensnap, batch, afrag);
-        tr.end();
-        if (!launched(tr)) return DFLASH_ELAUNCH;
         const int ld = 2 * s.nkv * s.D;
         a.lda = s.H;
         a.N = ld;
@@ -708,6 +774,11 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
     }
     if (!launched(tr)) return DFLASH_ELAUNCH;
     int n_ssq = 0;      // per-tile partial sums of squares of x (written by o / down)
+    // RMSNorm carried across the GEMMs where both plans allow it: o writes x * w_post for
+    // gate|up, down writes x * w_in of the next layer for its q|k|v, and those two scale their
+    // output rows; the final norm before the LM head keeps its own launch
+    const bool carry_mlp = fold_producer_ok(pl.o, M) && fold_consumer_ok(pl.gateup, pl.o.n_tiles, M);
+    const bool carry_attn = fold_producer_ok(pl.down, M) && fold_consumer_ok(pl.qkv, pl.down.n_tiles, M);
 
     const AttnPlan ap = plan_attn(s, gamma, batch);
     const size_t layer_elems = (size_t)s.Bmax * s.nkv * s.cap * s.D;
@@ -723,6 +794,8 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
                 a.a = nbuf;
                 a.lda = s.H;
                 a.a_frag = afrag;
+            } else if (carry_attn) {   // the previous layer's down wrote x * w_in into nbuf
+                set_carried_norm_a(a, s, nbuf, ssq_x, n_ssq, M);
             } else if ((rc = set_norm_a<T>(a, s, x, M, ssq_x, n_ssq, lw.in_norm, nbuf, afrag, st, tr))) {
                 return rc;
             }
@@ -808,12 +881,18 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
             a.residual = 1;
             a.ssq_out = ssq_x;
             a.ssq_out_ld = M;
+            if (carry_mlp) {        // gate|up's A operand: x * w_post
+                a.n_z = 1;
+                a.zw[0] = lw.post_norm;
+                a.zout = nbuf;
+            }
             if ((rc = gemm_dispatch<T>(a, pl.o, st, tr, "o_proj"))) return rc;
             n_ssq = pl.o.n_tiles;
         }
         {   // h = silu(W_gate a2) * (W_up a2)
             GemmArgs a = gemm_base(s, pl.gateup, M, s.H);
-            if ((rc = set_norm_a<T>(a, s, x, M, ssq_x, n_ssq, lw.post_norm, nbuf, afrag, st, tr))) return rc;
+            if (carry_mlp) set_carried_norm_a(a, s, nbuf, ssq_x, n_ssq, M);
+            else if ((rc = set_norm_a<T>(a, s, x, M, ssq_x, n_ssq, lw.post_norm, nbuf, afrag, st, tr))) return rc;
             a.N = s.I;
             a.seg_end[0] = a.seg_end[1] = a.seg_end[2] = s.I;
             a.layer[0].w[0] = lw.w_gate;
@@ -836,6 +915,11 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
             a.residual = 1;
             a.ssq_out = ssq_x;
             a.ssq_out_ld = M;
+            if (carry_attn && l + 1 < s.L) {     // the next layer's q|k|v A operand: x * w_in
+                a.n_z = 1;
+                a.zw[0] = w->layers[l + 1].in_norm;
+                a.zout = nbuf;
+            }
             if ((rc = gemm_dispatch<T>(a, pl.down, st, tr, "down_proj"))) return rc;
             n_ssq = pl.down.n_tiles;
         }

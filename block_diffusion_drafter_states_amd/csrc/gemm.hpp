@@ -20,6 +20,13 @@
 // rows (storage type, already normalised where the model normalises them;
 // L2-resident) are loaded into registers in the same ring slot; explicit vmcnt
 // waits (loads complete in issue order) make a slot's LDS data visible.
+//
+// RMSNorm carried across a GEMM pair.  RMSNorm(x; w) = f_m * (x ⊙ w) with one factor
+// f_m = 1 / sqrt(mean(x_m^2) + eps) per row, and a GEMM is linear in each row, so the
+// norm before a GEMM needs no launch of its own: the GEMM that produces x also stores
+// x ⊙ w (rounded, in the next GEMM's fragment order), and the next GEMM multiplies its
+// output rows by f_m, summed from the producer's per-tile sums of squares.  Only the
+// rounding point moves (x ⊙ w is rounded instead of f_m * x ⊙ w).
 #pragma once
 
 #include "common.hpp"
@@ -29,6 +36,8 @@ namespace dflash {
 enum { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_ARGMAX = 2, EPI_LSE = 3 };
 
 constexpr int MAX_LAYERS = 16;
+constexpr int GEMM_ZMAX = 8;    // norm-weighted copies a producer can write (one per consumer layer)
+constexpr int GEMM_RSQ = 4;     // 16-byte loads of sums of squares per thread (a consumer's row factors)
 
 struct GemmLayer {
     const void* a;          // nullable: this layer's A operand (overrides GemmArgs::a)
@@ -66,6 +75,24 @@ struct GemmArgs {
     float2* lse;            // EPI_LSE: [n_tiles][M] per tile (max logit, sum of exp(logit - max))
     const int* labels;      // EPI_LSE: [B][gamma-1] label ids of rows j >= 1
     float* lab_logit;       // EPI_LSE: [M] logit of row m's label (written by the tile holding it)
+    // ---- RMSNorm carried across a GEMM (weight-streaming kernel, one M-tile; see below)
+    // Consumer: the A rows are x * w_norm without their RMSNorm row factor, which is applied
+    // to the output instead: row m is multiplied by 1 / sqrt(sum_t rs_ssq[t][m] / rs_k + rs_eps)
+    // (EPI_STORE before the residual is added, EPI_SWIGLU before the activation).
+    const float* rs_ssq;    // nullable: [rs_n][rs_ld] per-tile sums of squares of x (a producer's ssq_out)
+    int rs_n, rs_ld;
+    float rs_k, rs_eps;
+    // Producer (EPI_STORE, at most one output element per thread): for z < n_z also store
+    // the new value times zw[z][column], in the storage type and in fragment order (K = N),
+    // at zout + z * zstride elements: the next GEMM's A operand for norm weight zw[z].
+    int n_z;
+    const void* zw[GEMM_ZMAX];
+    void* zout;
+    long long zstride;
+    // nullable: workgroup (0, 0, 0) copies snap_src[0 .. snap_n) to snap_dst at its end
+    const int* snap_src;
+    int* snap_dst;
+    int snap_n;
 };
 
 // Ring depth (k-steps in flight): the weights live in LDS; the registers of a
@@ -210,6 +237,9 @@ __global__ __launch_bounds__(512) void gemm_kernel(const GemmArgs p) {
         }
     };
     // all loads of ring slot q are complete once at most `later` later steps are outstanding
+    // The wait counts only the ring loads issued after the slot.  Other loads issued after
+    // it (the RMSNorm row sums and norm weights below) only make the wait stricter: with
+    // them in flight, "at most N outstanding" still implies the slot's loads have landed.
     auto wait_slot = [&](int q, int later) {
         if (later <= 0) vm_wait<0>();
         else if (P > 1 && later == 1) vm_wait<(P > 1 ? LPS : 0)>();
@@ -222,6 +252,45 @@ __global__ __launch_bounds__(512) void gemm_kernel(const GemmArgs p) {
 #pragma unroll
     for (int q = 0; q < P; ++q)
         if (q < nsteps) issue(q, q);
+
+    // RMSNorm carried across the GEMM: requested right after the first ring stages (so
+    // they do not delay the first weights) and read after the stream's last wait.
+    // Consumer (one M-tile): this thread's share of the producer's per-tile sums of squares,
+    // rows 4q .. 4q+3 of tiles j0, j0 + step, ... (out-of-range slots re-read tile 0 and
+    // are skipped when summed).  Producer: the norm weights of this thread's output element.
+    constexpr bool FOLD_RS = MT == 1 && (EPI == EPI_STORE || EPI == EPI_SWIGLU);
+    const bool rs_on = FOLD_RS && p.rs_ssq != nullptr;
+    u32x4_t rsv[GEMM_RSQ];
+#pragma unroll
+    for (int i = 0; i < GEMM_RSQ; ++i) rsv[i] = u32x4_t{0u, 0u, 0u, 0u};
+    if constexpr (FOLD_RS) {
+        if (rs_on) {
+            const int q = threadIdx.x & 3, j0 = threadIdx.x >> 2, step = blockDim.x >> 2;
+#pragma unroll
+            for (int i = 0; i < GEMM_RSQ; ++i) {
+                const int j = j0 + i * step;
+                const bool ok = j < p.rs_n && 4 * q < mrows;
+                vload_b128(rsv[i], p.rs_ssq + (ok ? (long long)j * p.rs_ld + m0 + 4 * q : 0));
+            }
+        }
+    }
+    uint32_t zg[GEMM_ZMAX];
+#pragma unroll
+    for (int z = 0; z < GEMM_ZMAX; ++z) zg[z] = 0u;
+    if constexpr (RES_EARLY) {
+        if (p.n_z > 0) {
+            const int e = threadIdx.x, n = tile * wcols + e % wcols;
+            const long long off = e < mrows * wcols && n < p.N ? n : 0;
+#pragma unroll
+            for (int z = 0; z < GEMM_ZMAX; ++z) {
+                if (z < p.n_z) {
+                    if constexpr (sizeof(T) == 2) vload_u16(zg[z], reinterpret_cast<const T*>(p.zw[z]) + off);
+                    else vload_b32(zg[z], reinterpret_cast<const T*>(p.zw[z]) + off);
+                }
+            }
+        }
+    }
+
 
     f32x4_t acc[MT][NTW];
 #pragma unroll
@@ -265,10 +334,15 @@ __global__ __launch_bounds__(512) void gemm_kernel(const GemmArgs p) {
         tie(resid_u[i]);
         resid[i] = __uint_as_float(resid_u[i]);
     }
+#pragma unroll
+    for (int i = 0; i < GEMM_RSQ; ++i) tie(rsv[i]);
+#pragma unroll
+    for (int z = 0; z < GEMM_ZMAX; ++z) tie(zg[z]);
 
     // ---- reduce the KS partial sums (fixed order) into Ct[mrows][wcols]
     float* slot = reinterpret_cast<float*>(smem);
     float* Ct = slot + (size_t)p.ns * p.ks * MT * NTW * 4 * 64;
+    __shared__ float rs_wave[16][16];                            // [wave][row] sums of squares
     {
         float* mine = slot + (size_t)wv * MT * NTW * 4 * 64;
 #pragma unroll
@@ -278,7 +352,37 @@ __global__ __launch_bounds__(512) void gemm_kernel(const GemmArgs p) {
 #pragma unroll
                 for (int v = 0; v < 4; ++v) mine[((mt * NTW + t) * 4 + v) * 64 + lane] = acc[mt][t][v];
     }
+    if constexpr (FOLD_RS) {
+        if (rs_on) {
+            // this thread's sums for rows 4q .. 4q+3 (its tiles in order), then the 16 lanes
+            // of the wave with the same q (lane bits 2..5, xor shuffles in a fixed order):
+            // lane q of every wave holds the wave's sums of rows 4q .. 4q+3
+            const int q = threadIdx.x & 3, j0 = threadIdx.x >> 2, step = blockDim.x >> 2;
+            float s4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < GEMM_RSQ; ++i) {
+                if (j0 + i * step < p.rs_n && 4 * q < mrows) {
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) s4[c] += __uint_as_float(rsv[i][c]);
+                }
+            }
+#pragma unroll
+            for (int o = 4; o < 64; o <<= 1)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) s4[c] += __shfl_xor(s4[c], o, WAVE);
+            if (lane < 4) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) rs_wave[wv][4 * lane + c] = s4[c];
+            }
+        }
+    }
     __syncthreads();
+    // the row factor of row r: the waves' sums in wave order
+    auto row_factor = [&](int r) {
+        float s = 0.f;
+        for (int w = 0; w < (int)(blockDim.x >> 6); ++w) s += rs_wave[w][r];
+        return 1.0f / sqrtf(s / p.rs_k + p.rs_eps);
+    };
     const int nthreads = blockDim.x;
     // sum of the KS partials of output element e (row-major over [mrows][wcols]), fixed order
     auto ksum = [&](int e) {
@@ -301,8 +405,24 @@ __global__ __launch_bounds__(512) void gemm_kernel(const GemmArgs p) {
             if (e < mrows * wcols && n < p.N) {
                 float* o = outp + (long long)(m0 + row) * p.ldo + n;
                 v = ksum(e);
+                if (rs_on) v *= row_factor(row);
                 if (p.residual) v += RES_EARLY ? res : *o;
                 *o = v;
+                if constexpr (RES_EARLY) {
+                    // the next GEMM's A operand(s): v * w_norm[n], rounded, in fragment order
+                    if (p.n_z > 0 && e == (int)threadIdx.x) {
+                        T* zo = reinterpret_cast<T*>(p.zout) + afrag_offset<T>(m0 + row, n, p.N);
+#pragma unroll
+                        for (int z = 0; z < GEMM_ZMAX; ++z) {
+                            if (z < p.n_z) {
+                                float wz;
+                                if constexpr (sizeof(T) == 2) wz = bf16_to_f32((bf16_t)zg[z]);
+                                else wz = __uint_as_float(zg[z]);
+                                zo[z * p.zstride] = Elem<T>::from_f(v * wz);
+                            }
+                        }
+                    }
+                }
             }
             float ss = v * v;
             for (int w = 1; w < wcols; w <<= 1) ss += __shfl_xor(ss, w, WAVE);
@@ -316,9 +436,11 @@ __global__ __launch_bounds__(512) void gemm_kernel(const GemmArgs p) {
         } else {
             for (int e0 = 0; e0 < 16 * MT * wcols; e0 += nthreads) store(e0 + threadIdx.x, 0.f);
         }
+        if (p.snap_n > 0 && tile == 0 && blockIdx.y == 0 && blockIdx.z == 0)
+            for (int i = threadIdx.x; i < p.snap_n; i += nthreads) p.snap_dst[i] = p.snap_src[i];
         return;
     }
-    for (int e = threadIdx.x; e < mrows * wcols; e += nthreads) Ct[e] = ksum(e);
+    for (int e = threadIdx.x; e < mrows * wcols; e += nthreads) Ct[e] = rs_on ? ksum(e) * row_factor(e / wcols) : ksum(e);
     __syncthreads();
     gemm_epilogue<T, EPI>(p, L, tile, m0, mrows, wcols, Ct);
 }
