@@ -134,52 +134,36 @@ __device__ __forceinline__ void pv_mfma(f32x4_t& acc, const PFrag<float>& p, con
 // same lane; the four lanes of a row (g = 0..3) are 16 lanes apart.
 //
 // RowIn holds what one lane needs to build its pieces of a normalised, rotated
-// row: the raw fp32 values, the norm scale and the cos/sin of its position.  The
-// loads are issued together as opaque loads (row_in_issue) and waited for
-// explicitly, so that they can be in flight together with the K/V stream.
+// row: the raw fp32 values, the norm scale and the cos/sin of its position.  A query
+// row's raw values are issued as opaque loads (row_in_issue_x) and waited for
+// explicitly, so that they can be in flight together with the K/V stream; its norm
+// scale and cos/sin come from rows staged once per workgroup (row_in_aux).
 template <typename T>
 struct RowIn {
     static constexpr int PER = Elem<T>::PER16, F4 = PER / 4;
-    static constexpr int LOADS = 4 * F4 + 4 + 4 * F4;
     u32x4_t x[4 * F4];               // piece i, vector h -> x[i * F4 + h]
     Frag64 w;                        // norm scale
     u32x4_t c[2 * F4], s[2 * F4];    // cos / sin for pieces 0, 1 (paired with 2, 3)
 };
 
 template <typename T>
-__device__ __forceinline__ void row_in_issue(RowIn<T>& in, const float* row, const T* wn, const float* cosr,
-                                             const float* sinr) {
+__device__ __forceinline__ void row_in_issue_x(RowIn<T>& in, const float* row) {
     constexpr int PER = RowIn<T>::PER, F4 = RowIn<T>::F4;
     const int g = (threadIdx.x & 63) >> 4;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int h = 0; h < F4; ++h) vload_b128(in.x[i * F4 + h], row + i * 4 * PER + g * PER + h * 4);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) vload_b128(in.w.q[i], wn + i * 4 * PER + g * PER);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int h = 0; h < F4; ++h) {
-            vload_b128(in.c[i * F4 + h], cosr + i * 4 * PER + g * PER + h * 4);
-            vload_b128(in.s[i * F4 + h], sinr + i * 4 * PER + g * PER + h * 4);
-        }
 }
 
 template <typename T>
-__device__ __forceinline__ void row_in_tie(RowIn<T>& in) {
+__device__ __forceinline__ void row_in_tie_x(RowIn<T>& in) {
 #pragma unroll
     for (int k = 0; k < 4 * RowIn<T>::F4; ++k) tie(in.x[k]);
-    tie(in.w);
-#pragma unroll
-    for (int k = 0; k < 2 * RowIn<T>::F4; ++k) {
-        tie(in.c[k]);
-        tie(in.s[k]);
-    }
 }
 
 // The same inputs read from rows staged in LDS (raw fp32 row, norm weight, cos and
-// sin rows), with the lane layout of row_in_issue.
+// sin rows), with the lane layout of row_in_issue_x.
 template <typename T>
 __device__ __forceinline__ void row_in_lds(RowIn<T>& in, const unsigned char* row, const unsigned char* wn,
                                            const unsigned char* cosr, const unsigned char* sinr) {
@@ -407,11 +391,66 @@ template <int QTW, int RING, int KG_ = att_default_kg(QTW)> struct AttGeom {
     static_assert(R >= 1 && RING % KG == 0, "whole stages per key group");
     static_assert((R - 1) * NPW <= 63, "vmcnt range");
 };
+// Rows every workgroup of a launch shares, staged once per workgroup after the ring: the
+// cos and sin rows of the block positions (row j = position len + j, D / 2 fp32; the
+// 16-byte chunk c of row j sits at position c ^ (j mod chunks per row), so the 16 rows of
+// one read hit different banks) and the q-norm weight (D elements).  Every wave of a
+// workgroup loading them itself costs 12 more loads per lane of a query tile (~13 MB of L2
+// reads per layer at the Qwen3-8B shape for 8.3 KB of distinct data).
+constexpr int ATT_AUX_COS = 0, ATT_AUX_SIN = 4096, ATT_AUX_QN = 8192, ATT_AUX_BYTES = 9216;
+__host__ __device__ constexpr int attn_aux_offset(int ring) {
+    return ring * ATT_STAGE_BYTES > ATT_RAW_KN + 1024 ? ring * ATT_STAGE_BYTES : ATT_RAW_KN + 1024;
+}
+
 // LDS of a workgroup: the ring, which also holds chunk 0's staged inputs (up to
-// ATT_RAW_KN + 1 KB) and the key-group merge slots (at most 4 of 8.5 KB)
-static inline size_t attn_lds_bytes_host(int ring) {
-    const size_t r = (size_t)ring * ATT_STAGE_BYTES;
-    return r > (size_t)ATT_RAW_KN + 1024 ? r : (size_t)ATT_RAW_KN + 1024;
+// ATT_RAW_KN + 1 KB) and the key-group merge slots (at most 4 of 8.5 KB), then the
+// shared rows
+static inline size_t attn_lds_bytes_host(int ring) { return (size_t)attn_aux_offset(ring) + ATT_AUX_BYTES; }
+
+// Direct-to-LDS loads of the shared rows, round-robin over the waves: the 16 cos rows, the
+// 16 sin rows (rows past the block repeat row 0's position; positions past the RoPE table
+// read its last row), the q-norm weight (the lanes past its 16 chunks repeat them into the
+// rest of its 1 KB slot).
+template <typename T>
+__device__ __forceinline__ void aux_stage_issue(uint32_t aux_lds, const float* cos_tab, const float* sin_tab,
+                                                const void* qn, int len, int G, int rope_rows, int wv, int nw) {
+    constexpr int D = 256 / (int)sizeof(T), CPR = D / 8;       // 16-byte chunks per cos row
+    constexpr int RPI = 64 / CPR, NT = 16 / RPI;                // rows per 1 KB load, loads per table
+    const int lane = threadIdx.x & 63;
+    for (int ins = wv; ins < 2 * NT + 1; ins += nw) {
+        const void* src;
+        uint32_t dst;
+        if (ins < 2 * NT) {
+            const int k = ins % NT, j = k * RPI + lane / CPR, pp = lane % CPR;
+            int pos = len + (j < G ? j : 0);
+            pos = pos < rope_rows ? pos : rope_rows - 1;
+            const int c = pp ^ (j & (CPR - 1));
+            src = (ins < NT ? cos_tab : sin_tab) + (long long)pos * (D / 2) + c * 4;
+            dst = aux_lds + (ins < NT ? ATT_AUX_COS : ATT_AUX_SIN) + k * 1024;
+        } else {
+            src = reinterpret_cast<const unsigned char*>(qn) + (lane & 15) * 16;
+            dst = aux_lds + ATT_AUX_QN;
+        }
+        dma_b128(src, dst);
+    }
+}
+
+// The norm weight and the cos / sin rows of block position j from the staged rows, with
+// the lane layout of row_in_issue_x.
+template <typename T>
+__device__ __forceinline__ void row_in_aux(RowIn<T>& in, const unsigned char* aux, int j) {
+    constexpr int PER = RowIn<T>::PER, F4 = RowIn<T>::F4, D = 16 * PER, CPR = D / 8;
+    const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) in.w.q[i] = *reinterpret_cast<const u32x4_t*>(aux + ATT_AUX_QN + (i * 4 + g) * 16);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int h = 0; h < F4; ++h) {
+            const int c = i * PER + g * (PER / 4) + h, pp = c ^ (j & (CPR - 1));
+            in.c[i * F4 + h] = *reinterpret_cast<const u32x4_t*>(aux + ATT_AUX_COS + (j * CPR + pp) * 16);
+            in.s[i * F4 + h] = *reinterpret_cast<const u32x4_t*>(aux + ATT_AUX_SIN + (j * CPR + pp) * 16);
+        }
 }
 
 // Wait until at most `later` (<= MAXL) stages of NPW loads each, issued after the
@@ -485,14 +524,14 @@ __global__ __launch_bounds__(64 * ATT_MAX_WAVES) void attn_partial_kernel(const 
     const int Rq = qt * 16 + r;
     const bool qvalid = Rq < rows;
     RowIn<T> qin;
+    const int qj = qvalid ? Rq % G : 0;                 // the query row's block position
     if (active) {
-        const int hq = qvalid ? Rq / G : 0, j = qvalid ? Rq % G : 0;
-        int pos = len + j;
-        pos = pos < a.rope_rows ? pos : a.rope_rows - 1;
-        row_in_issue<T>(qin, a.qkv + (long long)(b * G + j) * a.qkv_ld + (h * a.group + hq) * D,
-                        reinterpret_cast<const T*>(a.q_norm), a.rope_cos + (long long)pos * (D / 2),
-                        a.rope_sin + (long long)pos * (D / 2));
+        const int hq = qvalid ? Rq / G : 0;
+        row_in_issue_x<T>(qin, a.qkv + (long long)(b * G + qj) * a.qkv_ld + (h * a.group + hq) * D);
     }
+    const unsigned char* aux = smem + attn_aux_offset(RING);
+    aux_stage_issue<T>(lds_offset(smem) + (uint32_t)attn_aux_offset(RING), a.rope_cos, a.rope_sin, a.q_norm, len, G,
+                       a.rope_rows, __builtin_amdgcn_readfirstlane(wv), (int)(blockDim.x >> 6));
     if (c == 0) {
         // direct-to-LDS loads of 1 KB, round-robin over the waves: raw k rows, raw
         // v rows (fp32, D * 4 bytes each), cos and sin rows of the block positions
@@ -541,7 +580,8 @@ __global__ __launch_bounds__(64 * ATT_MAX_WAVES) void attn_partial_kernel(const 
         vm_wait<0>();                       // one latency for every input of chunk 0
         __syncthreads();                    // ... of every wave
         if (active) {
-            row_in_tie(qin);
+            row_in_tie_x(qin);
+            row_in_aux<T>(qin, aux, qj);
             norm_rope_frag<T>(w.qf, qin, a.eps);
             if (!qvalid) zero_frag64(w.qf);
         }
@@ -613,11 +653,15 @@ __global__ __launch_bounds__(64 * ATT_MAX_WAVES) void attn_partial_kernel(const 
                 }
             }
         }
-    } else if (active) {
-        wait_stage<NPW, R>(n_issued);      // the query loads came first
-        row_in_tie(qin);
-        norm_rope_frag<T>(w.qf, qin, a.eps);
-        if (!qvalid) zero_frag64(w.qf);
+    } else {
+        wait_stage<NPW, R>(n_issued);      // this wave's query row and shared-row loads came first
+        __syncthreads();                   // ... and every wave's share of the shared rows
+        if (active) {
+            row_in_tie_x(qin);
+            row_in_aux<T>(qin, aux, qj);
+            norm_rope_frag<T>(w.qf, qin, a.eps);
+            if (!qvalid) zero_frag64(w.qf);
+        }
     }
     for (int it = 0; it < n_iter; ++it) {
         const int kb = k_lo + 32 * it;
