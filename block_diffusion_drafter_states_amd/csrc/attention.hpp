@@ -52,7 +52,7 @@ struct AttnArgs {
     int rope_rows;
     float eps;
     const int* len;         // [B]
-    float* opart;           // [B][n_kv][nch_max][rpad][D]
+    void* opart;            // T [B][n_kv][nch_max][rpad][D]: unnormalised O of each chunk, storage type
     float* mlpart;          // [B][n_kv][nch_max][rpad][2]  (m in log2 units, l)
     int n_q, n_kv, cap, rpad, nch_max, chunk;   // chunk = CH context keys per chunk
     int gamma, group;       // rows = group * gamma
@@ -245,6 +245,27 @@ __device__ __forceinline__ int k_lds_off(int key, int c) { return key * 256 + ((
 template <typename T> __device__ __forceinline__ int v_lds_off(int d, int c);
 template <> __device__ __forceinline__ int v_lds_off<bf16_t>(int d, int c) { return d * 64 + ((c ^ ((d >> 2) & 3)) << 4); }
 template <> __device__ __forceinline__ int v_lds_off<float>(int d, int c) { return d * 128 + (c << 4); }
+
+// A chunk's unnormalised O in the storage type: four consecutive columns per store (8 bytes
+// in bf16, each value rounded to nearest even by the packed hardware conversion, which keeps
+// the kernel's register peak where it was), DPL consecutive columns per lane when merged.
+typedef __bf16 bf16x2_hw __attribute__((ext_vector_type(2)));
+typedef float f32x2_hw __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void store_o4(bf16_t* p, const f32x4_t& v) {
+    const f32x2_hw a = {v[0], v[1]}, b = {v[2], v[3]};
+    *reinterpret_cast<uint2*>(p) = make_uint2(__builtin_bit_cast(uint32_t, __builtin_convertvector(a, bf16x2_hw)),
+                                              __builtin_bit_cast(uint32_t, __builtin_convertvector(b, bf16x2_hw)));
+}
+__device__ __forceinline__ void store_o4(float* p, const f32x4_t& v) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+template <typename T, int DPL> __device__ __forceinline__ void load_o(float (&o)[DPL], const T* p);
+template <> __device__ __forceinline__ void load_o<bf16_t, 2>(float (&o)[2], const bf16_t* p) {
+    const uint32_t u = *reinterpret_cast<const uint32_t*>(p);
+    o[0] = __uint_as_float(u << 16);
+    o[1] = __uint_as_float(u & 0xFFFF0000u);
+}
+template <> __device__ __forceinline__ void load_o<float, 1>(float (&o)[1], const float* p) { o[0] = *p; }
 
 constexpr int ATT_STAGE_BYTES = 16384;   // K (32 x 256 B) then V^T (8 KB)
 constexpr int ATT_V_OFF = 8192;
@@ -472,7 +493,7 @@ __device__ __forceinline__ void wait_stage(int later) {
 }
 
 template <typename T, int QTW, int RING, int KG_>
-__global__ __launch_bounds__(64 * ATT_MAX_WAVES) void attn_partial_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(64 * (RING == 8 ? QTW * KG_ : ATT_MAX_WAVES)) void attn_partial_kernel(const AttnArgs a) {
     constexpr int D = WaveAttn<T>::D, DT = WaveAttn<T>::DT, PER = Elem<T>::PER16;
     using Geo = AttGeom<QTW, RING, KG_>;
     constexpr int KG = Geo::KG, R = Geo::R, NPW = Geo::NPW;
@@ -732,10 +753,9 @@ __global__ __launch_bounds__(64 * ATT_MAX_WAVES) void attn_partial_kernel(const 
         const int R = qt * 16 + r;
         if (R < rows) {
             const long long row = (((long long)b * a.n_kv + h) * a.nch_max + c) * a.rpad + R;
-            float* op = a.opart + row * D;
+            T* op = reinterpret_cast<T*>(a.opart) + row * D;
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-                *reinterpret_cast<float4*>(op + dt * 16 + g * 4) = make_float4(w.o[dt][0], w.o[dt][1], w.o[dt][2], w.o[dt][3]);
+            for (int dt = 0; dt < DT; ++dt) store_o4(op + dt * 16 + g * 4, w.o[dt]);
             if (g == 0) *reinterpret_cast<float2*>(a.mlpart + row * 2) = make_float2(mt, lt);
         }
     }
@@ -743,7 +763,7 @@ __global__ __launch_bounds__(64 * ATT_MAX_WAVES) void attn_partial_kernel(const 
 
 // o[b*gamma + j][(h*g + hq)*D + d] = rho( sum_c w_c O_c / sum_c w_c l_c ),  w_c = 2^(m_c - max m)
 struct MergeArgs {
-    const float* opart;
+    const void* opart;      // T, as AttnArgs::opart
     const float* mlpart;
     const int* len;
     void* out;              // T [B*gamma][n_q*D], or in fragment order (out_frag)
@@ -788,8 +808,7 @@ __global__ __launch_bounds__(64 * MERGE_WAVES) void attn_merge_kernel(const Merg
             const long long row = (base + c) * a.rpad + R;
             mc[u] = a.mlpart[row * 2];
             lc[u] = a.mlpart[row * 2 + 1];
-#pragma unroll
-            for (int k = 0; k < DPL; ++k) oc[u][k] = a.opart[row * D + lane * DPL + k];
+            load_o<T, DPL>(oc[u], reinterpret_cast<const T*>(a.opart) + row * D + lane * DPL);
         }
         float mb = mw;
 #pragma unroll

@@ -200,6 +200,18 @@ __device__ __forceinline__ uint32_t unpack_argmax_index(unsigned long long p) {
     return 0xFFFFFFFFu - (uint32_t)(p & 0xFFFFFFFFull);
 }
 
+// Per-tile maxima of an argmax LM-head launch: row m holds 8 runs of amax_per slots, tile t
+// in slot (t mod 8) * amax_per + t / 8.  Workgroup t of the launch runs on XCD t mod 8 (the
+// dispatcher deals workgroups round-robin over the eight XCDs, and the tiled kernel maps
+// tiles that way), so what one XCD writes of a row is one contiguous run of whole cache
+// lines in its own L2, and the finish reads a row as one contiguous span.  Slots of tiles
+// >= n_tiles (at most 7 per row) are never written.
+__host__ __device__ constexpr int amax_per(int n_tiles) { return (n_tiles + 7) >> 3; }
+__host__ __device__ constexpr long long amax_ld(int n_tiles) { return 8LL * amax_per(n_tiles); }
+__host__ __device__ constexpr long long amax_slot(int m, int tile, int n_tiles) {
+    return (long long)m * amax_ld(n_tiles) + (long long)(tile & 7) * amax_per(n_tiles) + (tile >> 3);
+}
+
 // Status bits (sticky, OR-ed into dflash_kv.status).
 constexpr uint32_t STATUS_KV_OVERFLOW = 1u;   // len + rows > kv_capacity
 constexpr uint32_t STATUS_BAD_TOKEN = 2u;     // token id outside [0, vocab)

@@ -325,7 +325,7 @@ int launch_attention(const AttnArgs& a, const AttnPlan& ap, int nch_max, int nkv
     if (tr.au) {    // partial (m, l, O) of every (b, h, chunk) and query row R < group * gamma <= rpad
         const long long rows = (long long)a.group * a.gamma;
         const long long last = (((long long)(batch - 1) * nkv + nkv - 1) * nch_max + nch_max - 1) * a.rpad + rows;
-        tr.au->write(a.opart, (size_t)(last * (256 / sizeof(T)) * 4));
+        tr.au->write(a.opart, (size_t)(last * (256 / sizeof(T)) * sizeof(T)));
         tr.au->write(a.mlpart, (size_t)(last * 2 * 4));
         return rows <= a.rpad ? DFLASH_OK : DFLASH_EUNSUPPORTED;
     }
@@ -362,7 +362,7 @@ DraftPlans draft_plans(const Shape& s, int M) {
 // is per-call scratch: no state survives a call.
 struct Layout {
     // draft
-    size_t x, ssq_x, qkv, opart, mlpart, obuf, hbuf, amax, fin_best, fin_count, nbuf, lse_part, lab, lse_row,
+    size_t x, ssq_x, qkv, opart, mlpart, obuf, hbuf, amax, nbuf, lse_part, lab, lse_row,
         draft_end;
     int ssq_x_tiles, amax_tiles;
     // inject
@@ -389,14 +389,12 @@ Layout make_layout(const Shape& s, int batch, int rows) {
     l.x = take(M * s.H * 4);
     l.ssq_x = take((size_t)l.ssq_x_tiles * M * 4);
     l.qkv = take(M * (size_t)(s.nq + 2 * s.nkv) * s.D * 4);
-    l.opart = take((size_t)batch * s.nkv * s.nch_max * s.rpad * s.D * 4);
+    l.opart = take((size_t)batch * s.nkv * s.nch_max * s.rpad * s.D * s.esize);
     l.mlpart = take((size_t)batch * s.nkv * s.nch_max * s.rpad * 2 * 4);
     const size_t Mp = pad16((int)M);                          // GEMM A operands: whole 16-row tiles
     l.obuf = take(Mp * s.nq * s.D * s.esize);
     l.hbuf = take(Mp * s.I * s.esize);
-    l.amax = take((size_t)l.amax_tiles * M * 8);
-    l.fin_best = take(M * 8);                                 // per draft row: running argmax, slices done
-    l.fin_count = take(M * 4);
+    l.amax = take((size_t)amax_ld(l.amax_tiles) * M * 8);     // per-tile maxima (amax_slot), or [tile][M] float2
     l.nbuf = take(Mp * s.H * s.esize);                        // RMSNorm-ed rows (GEMM A operand)
     l.lse_part = take((size_t)LSE_MAX_SLICES * M * 8);        // block loss: per-slice (max, sum exp)
     l.lab = take(M * 4);                                      // block loss: the label's logit per row
@@ -468,7 +466,7 @@ void audit_gemm(const GemmArgs& a, const GemmPlan& p, Audit& au) {
     }
     if (p.epi == EPI_STORE && a.ssq_out) au.write(a.ssq_out, span_rows(p.n_tiles, a.ssq_out_ld, a.M, 4));
     if (p.epi == EPI_SWIGLU) au.write(a.out_t, span_act<T>(a.out_frag, a.M, a.N, a.ldo));
-    if (p.epi == EPI_ARGMAX) au.write(a.amax, span_rows(p.n_tiles, a.M, a.M, 8));
+    if (p.epi == EPI_ARGMAX) au.write(a.amax, span_rows(a.M, amax_ld(p.n_tiles), amax_ld(p.n_tiles), 8));
     if (p.epi == EPI_LSE) {
         au.write(a.lse, span_rows(p.n_tiles, a.M, a.M, 8));
         au.write(a.lab_logit, (size_t)a.M * 4);
@@ -738,14 +736,12 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
     float* x = reinterpret_cast<float*>(wsb + lay.x);
     float* ssq_x = reinterpret_cast<float*>(wsb + lay.ssq_x);
     float* qkv = reinterpret_cast<float*>(wsb + lay.qkv);
-    float* opart = reinterpret_cast<float*>(wsb + lay.opart);
+    void* opart = wsb + lay.opart;
     float* mlpart = reinterpret_cast<float*>(wsb + lay.mlpart);
     void* obuf = wsb + lay.obuf;
     void* hbuf = wsb + lay.hbuf;
     unsigned long long* amax = reinterpret_cast<unsigned long long*>(wsb + lay.amax);
     void* nbuf = wsb + lay.nbuf;
-    unsigned long long* fin_best = reinterpret_cast<unsigned long long*>(wsb + lay.fin_best);
-    int* fin_count = reinterpret_cast<int*>(wsb + lay.fin_count);
     const int n_draft = batch * (gamma - md.first_row);
     // the weight-streaming GEMM (fewer than TILED_MIN_ROWS rows) reads A in fragment order
     const int afrag = M < TILED_MIN_ROWS ? 1 : 0;
@@ -764,12 +760,10 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
         if (tr.au) {
             tr.au->write(x, span_rows(M, s.H, s.H, 4));
             tr.au->write(nbuf, span_act<T>(afrag, M, s.H, s.H));
-            tr.au->write(fin_best, (size_t)n_draft * 8);
-            tr.au->write(fin_count, (size_t)n_draft * 4);
         }
         DFL_LAUNCH(tr, (embed_norm_kernel<T>), dim3(M), dim3(256), 0, st, static_cast<const T*>(w->embed),
                            anchor, md.tokens, s.mask, s.V, gamma, s.H, static_cast<const T*>(w->layers[0].in_norm),
-                           s.eps, x, static_cast<T*>(nbuf), kv->status, fin_best, fin_count, n_draft, afrag);
+                           s.eps, x, static_cast<T*>(nbuf), kv->status, afrag);
         tr.end();
     }
     if (!launched(tr)) return DFLASH_ELAUNCH;
@@ -990,14 +984,10 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
         }
         return launched(tr) ? DFLASH_OK : DFLASH_ELAUNCH;
     }
-    tr.begin("argmax_finish");
-    const int n_slices = std::max(1, std::min(pl.lm.n_tiles, 256 / row_blocks));
-    if (tr.au) {    // per draft row i = (m / gamma) * (gamma - first) + m % gamma - first < n_draft
-        tr.au->write(fin_best, (size_t)n_draft * 8);
-        tr.au->write(fin_count, (size_t)n_draft * 4);
-    }
-    DFL_LAUNCH(tr, argmax_finish_kernel, dim3(n_slices, row_blocks), dim3(256), 0, st, amax, pl.lm.n_tiles,
-               n_slices, M, gamma, md.first_row, fin_best, fin_count, draft);
+    if (n_draft < 1) return DFLASH_OK;
+    tr.begin("argmax_finish");      // one workgroup per draft row; writes only the ids
+    DFL_LAUNCH(tr, argmax_finish_kernel, dim3(n_draft), dim3(256), 0, st, amax, pl.lm.n_tiles, gamma, md.first_row,
+               draft);
     tr.end();
     return launched(tr) ? DFLASH_OK : DFLASH_ELAUNCH;
 }

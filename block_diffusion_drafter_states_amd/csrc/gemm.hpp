@@ -68,7 +68,7 @@ struct GemmArgs {
     int ssq_out_ld;
     void* out_t;            // EPI_SWIGLU: T [M][ldo], or in fragment order with N columns (out_frag)
     int out_frag;
-    unsigned long long* amax;   // EPI_ARGMAX: [n_tiles][M] packed (value, index) maxima
+    unsigned long long* amax;   // EPI_ARGMAX: packed (value, index) maxima per (row, tile), at amax_slot
     float* dbg_logits;      // EPI_ARGMAX: nullable [B][gamma-dbg_first][N] logits of rows j >= dbg_first
     int gamma;              // EPI_ARGMAX / EPI_LSE: rows per sequence in A (block size)
     int dbg_first;
@@ -504,7 +504,7 @@ __device__ void gemm_epilogue(const GemmArgs& p, const GemmLayer& L, int tile, i
                     const unsigned long long other = __shfl_xor(best, o, WAVE);
                     best = other > best ? other : best;
                 }
-                if (live && sub == 0) p.amax[(long long)tile * p.M + m] = best;
+                if (live && sub == 0) p.amax[amax_slot(m, tile, p.n_tiles)] = best;
             } else {
                 // the tile's largest logit mx and sum of exp(logit - mx); the lane holding
                 // the row's label column stores its logit
@@ -534,55 +534,47 @@ __device__ void gemm_epilogue(const GemmArgs& p, const GemmLayer& L, int tile, i
     }
 }
 
-// out[b][j - first] = argmax over the vocabulary tiles of row m = b*gamma + j, for
-// j >= first (first = 1: the drafts, rows after the anchor; 0: every row, a target's
-// verification).
-// amax is [n_tiles][M].  Workgroup (s, rb) takes slice s of n_slices of the tiles for
-// the 64 rows rb*64 .. rb*64+63: wave w reads tiles s0 + w, s0 + w + 4, ..., one row per
-// lane, so every read is 64 consecutive maxima (the host picks n_slices for about 256
-// workgroups, so a wave reads only a few tiles).  Per draft row i it folds its maximum
-// into best[i] with a 64-bit atomic max (order-independent, so the result is
-// deterministic) and counts itself in count[i]; the last of the row's n_slices
-// workgroups reads best[i] back with an atomic and writes the index.  best and count
-// start at zero (the embedding kernel of the same call clears them).
+// draft[i] = the vocabulary argmax of draft row i: row m = b*gamma + j with
+// i = b*(gamma - first) + j - first, j >= first (first = 1: the drafts, rows after the
+// anchor; 0: every row, a target's verification).  One workgroup per draft row reads the
+// row's tile maxima (amax_slot layout): lane l of a round takes tile u*256 + l, so a wave's
+// 64 loads fall in 8 cache lines (one per XCD run); tiles past the last one re-read the
+// last tile (a repeated value leaves a maximum unchanged), so every load is unconditional
+// and all of a lane's loads are in flight at once.  The maxima fold with the packed
+// (value, index) order — the larger value, and the lower index among equal values, so the
+// result does not depend on the order — in registers, across the wave with xor shuffles and
+// across the waves in LDS.  No atomics and no second pass: one memory round trip after the
+// launch.
+constexpr int ARGMAX_FIN_LOADS = 24;       // tiles per thread per round (6144 per workgroup)
 __global__ __launch_bounds__(256) void argmax_finish_kernel(const unsigned long long* __restrict__ amax, int n_tiles,
-                                                            int n_slices, int M, int gamma, int first,
-                                                            unsigned long long* best, int* count,
-                                                            int* __restrict__ draft) {
-    __shared__ unsigned long long red[4][64];
-    const int s = blockIdx.x;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int m = blockIdx.y * 64 + lane;
-    const int per = (n_tiles + n_slices - 1) / n_slices;
-    const int t0 = s * per, t1 = min(n_tiles, t0 + per);
-    unsigned long long v[4];
+                                                            int gamma, int first, int* __restrict__ draft) {
+    __shared__ unsigned long long red[4];
+    const int i = blockIdx.x, per_seq = gamma - first;
+    const int m = (i / per_seq) * gamma + first + i % per_seq;
+    const int per = amax_per(n_tiles);
+    const unsigned long long* row = amax + (long long)m * amax_ld(n_tiles);
+    unsigned long long best = 0ull;
+    for (int t0 = 0; t0 < n_tiles; t0 += 256 * ARGMAX_FIN_LOADS) {
+        unsigned long long v[ARGMAX_FIN_LOADS];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = 0ull;
-    if (m < M) {
-        for (int tb = t0 + w; tb < t1; tb += 16) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int t = tb + 4 * u;
-                const unsigned long long x = t < t1 ? amax[(long long)t * M + m] : 0ull;
-                v[u] = x > v[u] ? x : v[u];
-            }
+        for (int u = 0; u < ARGMAX_FIN_LOADS; ++u) {
+            const int t = min(t0 + u * 256 + (int)threadIdx.x, n_tiles - 1);
+            v[u] = row[(t & 7) * per + (t >> 3)];
         }
+#pragma unroll
+        for (int u = 0; u < ARGMAX_FIN_LOADS; ++u) best = v[u] > best ? v[u] : best;
     }
-    unsigned long long mx = v[0];
 #pragma unroll
-    for (int u = 1; u < 4; ++u) mx = v[u] > mx ? v[u] : mx;
-    red[w][lane] = mx;
+    for (int o = 1; o < 64; o <<= 1) {
+        const unsigned long long other = __shfl_xor(best, o, WAVE);
+        best = other > best ? other : best;
+    }
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = best;
     __syncthreads();
-    if (threadIdx.x < 64 && m < M && m % gamma >= first) {
-        unsigned long long x = red[0][lane];
-        for (int k = 1; k < 4; ++k) x = red[k][lane] > x ? red[k][lane] : x;
-        const int i = (m / gamma) * (gamma - first) + (m % gamma - first);
-        atomicMax(best + i, x);
-        __threadfence();
-        if (atomicAdd(count + i, 1) == n_slices - 1) {
-            __threadfence();
-            draft[i] = (int)unpack_argmax_index(atomicMax(best + i, 0ull));
-        }
+    if (threadIdx.x == 0) {
+        unsigned long long x = red[0];
+        for (int w = 1; w < 4; ++w) x = red[w] > x ? red[w] : x;
+        draft[i] = (int)unpack_argmax_index(x);
     }
 }
 

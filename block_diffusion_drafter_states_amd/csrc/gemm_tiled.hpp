@@ -194,7 +194,7 @@ __device__ __forceinline__ void tg_epilogue(const GemmArgs& p, const GemmLayer& 
         __syncthreads();
         if (threadIdx.x < TG_BM && m0 + (int)threadIdx.x < p.M) {
             const unsigned long long x0 = redu[threadIdx.x], x1 = redu[TG_BM + threadIdx.x];
-            p.amax[(long long)tile * p.M + m0 + threadIdx.x] = x0 > x1 ? x0 : x1;
+            p.amax[amax_slot(m0 + (int)threadIdx.x, tile, p.n_tiles)] = x0 > x1 ? x0 : x1;
         }
     }
 }

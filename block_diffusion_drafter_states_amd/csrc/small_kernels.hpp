@@ -17,17 +17,11 @@ __global__ __launch_bounds__(256) void embed_norm_kernel(const T* __restrict__ e
                                                          int gamma, int H,
                                                          const T* __restrict__ w_norm, float eps,
                                                          float* __restrict__ x, T* __restrict__ xn,
-                                                         unsigned* status, unsigned long long* __restrict__ fin_best,
-                                                         int* __restrict__ fin_count, int n_fin, int xn_frag) {
+                                                         unsigned* status, int xn_frag) {
     constexpr int EPC = 16 / (int)sizeof(T);                    // elements per 16-byte chunk
     constexpr int MAXC = EMBED_MAX_HIDDEN / EPC / 256;           // chunks per thread
     __shared__ float red[4];
     const int m = blockIdx.x;
-    if (m == 0)     // the LM-head argmax of this call starts from empty maxima and counts
-        for (int i = threadIdx.x; i < n_fin; i += 256) {
-            fin_best[i] = 0ull;
-            fin_count[i] = 0;
-        }
     const int b = m / gamma, j = m % gamma;
     int id = tokens ? tokens[m] : ((j == 0) ? anchor[b] : mask_id);
     if (id < 0 || id >= vocab) {

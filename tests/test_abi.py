@@ -344,16 +344,16 @@ def test_noalloc_rejects_calls_beyond_the_fixed_scratch():
     c5 = synth.get_config("C5")
     big = dflash_config(hidden=c5.hidden, n_q_heads=c5.n_q, n_kv_heads=c5.n_kv, head_dim=c5.head_dim,
                         inter=c5.inter, n_layers=c5.n_layers, n_feat=c5.n_feat, vocab=c5.vocab, gamma_max=16,
-                        mask_token_id=c5.mask_id, max_batch=4, kv_capacity=32832, rms_eps=1e-6, dtype=1)
-    assert L.dflash_workspace_bytes(ctypes.byref(big), 4, 0) > L.dflash_noalloc_scratch_bytes()
+                        mask_token_id=c5.mask_id, max_batch=12, kv_capacity=32832, rms_eps=1e-6, dtype=1)
+    assert L.dflash_workspace_bytes(ctypes.byref(big), 12, 0) > L.dflash_noalloc_scratch_bytes()
     w = _weights(c5.n_layers)
     w.rope_rows = 32832 + 16
     call = lambda **k: L.dflash_draft_block_noalloc(ctypes.byref(k.get("c", big)), ctypes.byref(k.get("w", w)),
-                                                    ctypes.byref(_kv()), k.get("batch", 4), k.get("gamma", 16),
+                                                    ctypes.byref(_kv()), k.get("batch", 12), k.get("gamma", 16),
                                                     FAKE, k.get("draft", FAKE), None, None, None)
     assert call() == _abi.DFLASH_ESCRATCH
     assert b"DFLASH_ESCRATCH" in L.dflash_status_str(_abi.DFLASH_ESCRATCH)
-    assert call(batch=5) == DFLASH_EINVAL
+    assert call(batch=13) == DFLASH_EINVAL
     assert call(gamma=17) == DFLASH_EINVAL
     assert call(draft=None) == DFLASH_EINVAL
     assert call(w=_weights(c5.n_layers, null_field="wo")) == DFLASH_EINVAL
