@@ -34,10 +34,18 @@ MR = synth.Config("ring4_bf16", "bf16", hidden=512, n_q=8, n_kv=4, head_dim=128,
 # (a partly filled tile) and 1 at gamma 3
 MT = synth.Config("long_chunks_bf16", "bf16", hidden=512, n_q=64, n_kv=16, head_dim=128, inter=1024,
                   n_layers=1, n_feat=2, vocab=1000, gamma=16, ctx=8000, batch=8, index=83)
+# a 250 000-token vocabulary: 7813 LM-head tiles of 32 rows per row at gamma 16 and 4, more than
+# the 6144 tile maxima the argmax finish reads in one round, with a partly filled last tile
+LV = synth.Config("large_vocab_bf16", "bf16", hidden=512, n_q=4, n_kv=2, head_dim=128, inter=1024,
+                  n_layers=1, n_feat=2, vocab=250000, gamma=16, ctx=200, batch=2, index=87)
 
 
 def test_batch_of_five_ragged_row_groups():
     run_cycle_case(MB, 5, [0, 1, 300, 63, 257], [16, 2, 9], gen.kv_capacity(MB, 64), "mb")
+
+
+def test_large_vocabulary_two_finish_rounds():
+    run_cycle_case(LV, 2, [0, 200], [16, 4], gen.kv_capacity(LV, 64), "lv")
 
 
 def test_many_attention_workgroups_small_rings():
