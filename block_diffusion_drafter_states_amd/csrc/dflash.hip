@@ -145,11 +145,14 @@ int make_shape(const dflash_config* c, Shape& s) {
     s.group = s.nq / s.nkv;
     if (s.group * s.gmax > 256) return DFLASH_EUNSUPPORTED;
     s.rpad = cdiv(s.group * s.gmax, 16) * 16;
-    // context keys per attention chunk: the largest power of two in 256 .. 2048 that
+    // context keys per attention chunk: the largest power of two in 256 .. 1024 that
     // still gives >= 1024 workgroups (four per CU) when the cache is full.  A workgroup
     // streams its chunk through the LDS ring, so longer chunks amortise its start (query
-    // build, first loads) and its partial write; below four per CU the GPU idles.
-    int ch = 2048;
+    // build, first loads) and its partial write; below four per CU the GPU idles.  2048-key
+    // chunks leave too few, too long workgroups for the slots of a ragged batch
+    // (LLaMA-3.1-8B shape, batch 32, contexts 512..8192: 888 workgroups with keys for 512
+    // slots; 1024-key chunks: attention 795 -> 683 us per cycle)
+    int ch = 1024;
     while (ch > 256 && (long long)s.Bmax * s.nkv * cdiv(s.cap, ch) < 1024) ch >>= 1;
     // 128-key chunks when even those fit one round of workgroups (one per CU): shorter
     // chunks shorten every workgroup (measured: Qwen3-4B shape, context 1024, batch 1:
