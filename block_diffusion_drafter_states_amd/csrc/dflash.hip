@@ -573,13 +573,13 @@ bool weights_ok(const Shape& s, const dflash_weights* w, bool need_fuse = true) 
 // order when the consumer is the weight-streaming GEMM (afrag).
 template <typename T>
 int set_norm_a(GemmArgs& a, const Shape& s, const float* x, int M, const float* ssq, int n_ssq, const void* w,
-               void* nbuf, int afrag, hipStream_t st, Tracer& tr) {
+               void* nbuf, int afrag, hipStream_t st, Tracer& tr, bool row_factor = true) {
     NormWeights nw{};
     nw.w[0] = w;
     tr.begin("rmsnorm");
     if (tr.au) tr.au->write(nbuf, span_act<T>(afrag, M, s.H, s.H));
     DFL_LAUNCH(tr, (rmsnorm_rows_kernel<T>), dim3(M, cdiv(s.H, 1024), 1), dim3(256), 0, st, x, s.H, ssq, n_ssq, M,
-               nw, s.H, s.eps, static_cast<T*>(nbuf), s.H, 0LL, nullptr, nullptr, 0, afrag);
+               nw, s.H, s.eps, static_cast<T*>(nbuf), s.H, 0LL, nullptr, nullptr, 0, afrag, row_factor ? 1 : 0);
     tr.end();
     a.a = nbuf;
     a.lda = s.H;
@@ -658,7 +658,7 @@ int run_inject(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int
             }
             DFL_LAUNCH(tr, (rmsnorm_rows_kernel<T>), dim3(M, cdiv(s.H, 1024), s.L), dim3(256), 0, st, c, s.H, ssq_c,
                        pl.fuse.n_tiles, M, nw, s.H, s.eps, cn, s.H, (long long)cn_layer, kv->len, lensnap, batch,
-                       afrag);
+                       afrag, 1);
             tr.end();
             if (!launched(tr)) return DFLASH_ELAUNCH;
         }
@@ -784,6 +784,12 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
     // output rows; the final norm before the LM head keeps its own launch
     const bool carry_mlp = fold_producer_ok(pl.o, M) && fold_consumer_ok(pl.gateup, pl.o.n_tiles, M);
     const bool carry_attn = fold_producer_ok(pl.down, M) && fold_consumer_ok(pl.qkv, pl.down.n_tiles, M);
+    // The argmax LM head reads rho(x * w_final) and leaves out the final RMSNorm's row factor,
+    // which is positive and so leaves every row's argmax where it is: the last down GEMM stores
+    // that operand where its plan allows, else the norm launch writes it without the factor.
+    // The loss head needs the true logits and keeps the whole RMSNorm.
+    const bool head_argmax = md.labels == nullptr && !md.no_head;
+    const bool carry_head = head_argmax && fold_producer_ok(pl.down, M);
 
     const AttnPlan ap = plan_attn(s, gamma, batch);
     const size_t layer_elems = (size_t)s.Bmax * s.nkv * s.cap * s.D;
@@ -924,6 +930,10 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
                 a.n_z = 1;
                 a.zw[0] = w->layers[l + 1].in_norm;
                 a.zout = nbuf;
+            } else if (carry_head && l + 1 == s.L) {     // the LM head's A operand: x * w_final
+                a.n_z = 1;
+                a.zw[0] = w->final_norm;
+                a.zout = nbuf;
             }
             if ((rc = gemm_dispatch<T>(a, pl.down, st, tr, "down_proj"))) return rc;
             n_ssq = pl.down.n_tiles;
@@ -952,7 +962,13 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
         const bool loss = md.labels != nullptr;
         const GemmPlan plm = loss ? plan_gemm(s, EPI_LSE, s.V, s.H, M, 1) : pl.lm;   // same tiles (checked above)
         GemmArgs a = gemm_base(s, plm, M, s.H);
-        if ((rc = set_norm_a<T>(a, s, x, M, ssq_x, n_ssq, w->final_norm, nbuf, afrag, st, tr))) return rc;
+        if (carry_head) {           // the last down GEMM wrote x * w_final into nbuf
+            a.a = nbuf;
+            a.lda = s.H;
+            a.a_frag = afrag;
+        } else if ((rc = set_norm_a<T>(a, s, x, M, ssq_x, n_ssq, w->final_norm, nbuf, afrag, st, tr, !head_argmax))) {
+            return rc;
+        }
         a.N = s.V;
         a.seg_end[0] = a.seg_end[1] = a.seg_end[2] = s.V;
         a.layer[0].w[0] = w->lm_head;
@@ -966,6 +982,13 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
             a.lab_logit = reinterpret_cast<float*>(wsb + lay.lab);
         }
         if ((rc = gemm_dispatch<T>(a, plm, st, tr, loss ? "lm_head_lse" : "lm_head_argmax"))) return rc;
+    }
+    if (head_argmax && dbg_logits && n_draft > 0) {   // the returned logits, with the row factor
+        tr.begin("scale_logits");
+        DFL_LAUNCH(tr, scale_logit_rows_kernel, dim3((unsigned)std::min(64, cdiv(s.V, 256)), (unsigned)n_draft),
+                   dim3(256), 0, st, dbg_logits, s.V, ssq_x, n_ssq, M, gamma, md.first_row, s.H, s.eps);
+        tr.end();
+        if (!launched(tr)) return DFLASH_ELAUNCH;
     }
     const int row_blocks = cdiv(M, 64);
     if (md.labels) {

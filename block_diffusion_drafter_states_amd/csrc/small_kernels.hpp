@@ -110,14 +110,15 @@ constexpr int NORM_MAX_PARTIALS = 512;
 
 // When len_snap is given, block 0 also copies len[0 .. n_len) there (the K/V
 // cache writes that follow read positions from the copy while len itself is
-// advanced).
+// advanced).  row_factor = 0 writes rho(x * w) without the row's factor (the input of an
+// argmax LM head: a positive factor per row leaves each row's argmax where it is).
 template <typename T>
 __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const float* __restrict__ x, int ldx,
                                                            const float* __restrict__ ssq, int n_ssq, int ssq_ld,
                                                            const NormWeights wz, int K, float eps,
                                                            T* __restrict__ out, int ldo, long long out_z,
                                                            const int* __restrict__ len, int* __restrict__ len_snap,
-                                                           int n_len, int out_frag) {
+                                                           int n_len, int out_frag, int row_factor) {
     __shared__ float red[4];
     if (len_snap && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0)
         for (int b = threadIdx.x; b < n_len; b += 256) len_snap[b] = len[b];
@@ -135,7 +136,7 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const float* __restri
     float s = wave_sum(s0 + s1);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
     __syncthreads();
-    const float rs = 1.0f / sqrtf(((red[0] + red[1]) + (red[2] + red[3])) / (float)K + eps);
+    const float rs = row_factor ? 1.0f / sqrtf(((red[0] + red[1]) + (red[2] + red[3])) / (float)K + eps) : 1.0f;
     if (has) {
         // four consecutive columns stay contiguous in fragment order (k % 4 == 0)
         T* o = out + (long long)blockIdx.z * out_z + (out_frag ? afrag_offset<T>(m, k, K) : (long long)m * ldo + k);
@@ -144,6 +145,28 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const float* __restri
         o[2] = Elem<T>::from_f(xv.z * rs * wv[2]);
         o[3] = Elem<T>::from_f(xv.w * rs * wv[3]);
     }
+}
+
+// Returned logits of an argmax LM head whose input rows were rho(x * w) without the final
+// RMSNorm's row factor: logits[i][n] *= f_m, f_m = 1 / sqrt(sum_t ssq[t][m] / K + eps), for the
+// draft rows i = b*(gamma - first) + j - first (row m = b*gamma + j, j >= first).  Workgroup
+// (s, i) takes vocabulary slice s of row i; every workgroup of a row sums the row's partial
+// sums of squares in the same order.  Only runs when the caller asks for the logits.
+__global__ __launch_bounds__(256) void scale_logit_rows_kernel(float* __restrict__ logits, int V,
+                                                               const float* __restrict__ ssq, int n_ssq, int ssq_ld,
+                                                               int gamma, int first, int K, float eps) {
+    __shared__ float red[4];
+    const int i = blockIdx.y, per_seq = gamma - first;
+    const int m = (i / per_seq) * gamma + first + i % per_seq;
+    const int t0 = threadIdx.x, t1 = threadIdx.x + 256;
+    const float s0 = t0 < n_ssq ? ssq[(long long)t0 * ssq_ld + m] : 0.f;
+    const float s1 = t1 < n_ssq ? ssq[(long long)t1 * ssq_ld + m] : 0.f;
+    const float s = wave_sum(s0 + s1);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+    __syncthreads();
+    const float f = 1.0f / sqrtf(((red[0] + red[1]) + (red[2] + red[3])) / (float)K + eps);
+    float* row = logits + (long long)i * V;
+    for (int n = blockIdx.x * 256 + threadIdx.x; n < V; n += gridDim.x * 256) row[n] *= f;
 }
 
 // Per-head RMSNorm then rotate-half RoPE of one row of D values, rounded into

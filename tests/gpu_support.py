@@ -129,11 +129,14 @@ def check_draft(cfg, got, ref, gap_min=1e-2, head=None):
 
     Hidden states and logits: relative error of the whole tensor and of every row.
     Draft ids are an argmax decided in floating point, checked three ways:
-      * self-consistency: the ids are exactly the argmax (lowest index on ties) of the
-        fp32 logits the GPU returns (`argmax_self_mismatch`);
-      * the LM head + argmax stage on its own (`head`: the oracle's final norm, rounding
-        and LM head applied to the GPU's final hidden rows): every row whose top-2 gap is
-        at least gap_min (1e-2) must draft that argmax (`head_strict_mismatch`).  The
+      * self-consistency: each id's logit in the fp32 logits the GPU returns is its row's
+        maximum (`argmax_self_mismatch`).  The argmax LM head decides on its logits before
+        the final RMSNorm's positive row factor, which the returned logits then carry; a
+        positive factor keeps every order but can round two close logits to one value, so
+        the id is a maximum of the returned row, not necessarily its lowest-index one;
+      * the LM head + argmax stage on its own (`head`: the final norm, rounding and LM head
+        of the same reading applied to the GPU's final hidden rows): every row whose top-2
+        gap is at least gap_min (1e-2) must draft that argmax (`head_strict_mismatch`).  The
         stage's inputs are then identical on both sides, so its logits differ only by
         summation order (~1e-5), far below the gap;
       * end to end against the oracle's own forward: the two forwards round to bf16 at
@@ -160,7 +163,8 @@ def check_draft(cfg, got, ref, gap_min=1e-2, head=None):
     exempt = gap < gap_min
     wide = (~exempt) & (gap <= 2.0 * err)
     sure = (~exempt) & (~wide)
-    self_mism = int((d != np.argmax(z, axis=-1)).sum())
+    picked_own = np.take_along_axis(z, d[..., None].astype(np.int64), axis=-1)[..., 0]
+    self_mism = int((picked_own != z.max(axis=-1)).sum())
     picked = np.take_along_axis(zr, d[..., None].astype(np.int64), axis=-1)[..., 0]
     not_near = int((picked < zr.max(axis=-1) - 2.0 * err).sum())
     m = {"hidden_rel": ex, "logits_rel": ez, "hidden_row_max": float(rx.max()), "logits_row_max": float(rz.max()),
@@ -192,11 +196,17 @@ def assert_draft(cfg, m) -> None:
 
 
 def oracle_head(om):
-    """The oracle's final stage (final RMSNorm, bf16 rounding, LM head) as a function of
-    final hidden rows [B][gamma][H] (the anchor row excluded, as in drafting)."""
+    """The argmax LM-head stage as a function of final hidden rows [B][gamma][H] (the anchor
+    row excluded, as in drafting), in the GPU's reading of where the final RMSNorm rounds:
+    the head's input is rho(x * w_final) and the norm's row factor f = 1 / sqrt(mean(x^2) +
+    eps) multiplies the logits, f * (rho(x * w) . W^T); the oracle's forward rounds
+    rho(f * x * w) instead.  Equal in exact arithmetic; one bf16 rounding per input either
+    way."""
     def f(x):
-        x = np.asarray(x, dtype=np.float64)
-        return O.linear(om.num.rho(O.rms_norm(x[:, 1:], om.final_norm, om.cfg.eps)), om.lm_head)
+        x = np.asarray(x, dtype=np.float64)[:, 1:]
+        w = np.asarray(om.final_norm, dtype=np.float64)
+        rf = 1.0 / np.sqrt((x * x).mean(axis=-1, keepdims=True) + om.cfg.eps)
+        return O.linear(om.num.rho(x * w), om.lm_head) * rf
     return f
 
 

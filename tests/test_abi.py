@@ -12,6 +12,7 @@ from block_diffusion_drafter_states_amd._abi import (dflash_config, dflash_kv, d
                                                      dflash_trace, DFLASH_EINVAL, DFLASH_EUNSUPPORTED,
                                                      DFLASH_EWORKSPACE)
 import synth
+from synth import gen
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "dflash.h")
@@ -239,6 +240,32 @@ def test_binding_checks_tensor_arguments_before_calling_the_library():
     with pytest.raises(TypeError, match="device tensor"):
         dfl.verify(torch.zeros((1, 7), dtype=torch.int32), torch.zeros((1, 8), dtype=torch.int32),
                    cpu_i32, torch.zeros((1, 8), dtype=torch.int32), cpu_i32)
+
+
+def test_head_composite_reading():
+    """The argmax-head composite the GPU checks compare with (rho(x * w) . W^T times the final
+    norm's row factor) against the oracle's own final stage (rho(RMSNorm(x; w)) . W^T): equal
+    to fp64 noise without rounding, within one bf16 rounding of the input with it, and the
+    same argmax wherever the top two logits are clearly apart."""
+    import numpy as np
+    import gpu_support as G
+    import oracle.dflash as O
+    for dtype in ("f32", "bf16"):
+        cfg = synth.Config(f"head_{dtype}", dtype, hidden=256, n_q=2, n_kv=1, head_dim=128 if dtype == "bf16" else 64,
+                           inter=512, n_layers=1, n_feat=2, vocab=700, gamma=8, ctx=16, batch=1, index=95)
+        om = O.DraftModel(cfg, gen.weights(cfg))
+        x = 3.0 * np.random.default_rng(7).standard_normal((2, cfg.gamma, cfg.hidden))
+        got = G.oracle_head(om)(x)
+        ref = O.linear(om.num.rho(O.rms_norm(x[:, 1:], om.final_norm, cfg.eps)), om.lm_head)
+        err = np.abs(got - ref).max() / np.abs(ref).max()
+        if dtype == "f32":      # the oracle computes in fp64 and rho rounds nothing here
+            assert err < 1e-12
+        else:
+            assert 1e-6 < err < 1e-2
+            srt = np.sort(ref, axis=-1)
+            clear = srt[..., -1] - srt[..., -2] > 20 * np.abs(got - ref).max()
+            assert clear.sum() > 0
+            assert (np.argmax(got, -1) == np.argmax(ref, -1))[clear].all()
 
 
 def test_draft_check_flags_wrong_ids():
