@@ -164,11 +164,14 @@ int dflash_inject_kv(const dflash_config *cfg, const dflash_weights *w, const df
  * ; the block's own keys/values], no mask inside the block; then the final
  * RMSNorm, the LM head and a row-wise argmax (ties -> lowest id) on the gamma-1
  * mask rows.  The block's own K/V are not written to the cache and len is not
- * changed.  Requires len[b] + gamma <= rope_rows.
+ * changed.  Requires len[b] + gamma <= rope_rows.  The argmax is taken before the final
+ * RMSNorm's row factor (positive, the same for every id of a row, so it moves no row's
+ * maximum): ties go to the lowest id among equal pre-factor logits.
  *   anchor      int32 [batch]
  *   draft       int32 [batch][gamma-1]   d_1 .. d_{gamma-1}
  *   dbg_hidden  nullable fp32 [batch][gamma][H]: final residual stream (before the final norm)
- *   dbg_logits  nullable fp32 [batch][gamma-1][V]: logits of the mask rows
+ *   dbg_logits  nullable fp32 [batch][gamma-1][V]: logits of the mask rows, with the row factor
+ *               (each draft id's logit is its row's maximum)
  * 2 <= gamma <= gamma_max, 1 <= batch <= max_batch. */
 int dflash_draft_block(const dflash_config *cfg, const dflash_weights *w, const dflash_kv *kv,
                        int32_t batch, int32_t gamma, const int32_t *anchor, int32_t *draft,
@@ -237,8 +240,9 @@ int dflash_draft_block_traced(const dflash_config *cfg, const dflash_weights *w,
  * rows - 1: writes their k (RMSNorm + RoPE) and v rows into every layer's cache
  * at those positions, attends to [cached context (len[b] rows) ; the block's
  * rows up to and including its own position], and returns
- *   y     int32 [batch][rows]: argmax (ties -> lowest id) of the logits of
- *         every row - the target's greedy token after each position;
+ *   y     int32 [batch][rows]: argmax of the logits of every row - the target's
+ *         greedy token after each position (taken as in dflash_draft_block: before the
+ *         final norm's positive row factor, ties to the lowest id);
  *   feat  nullable, storage dtype [batch][rows][n_taps][H]: the residual stream
  *         after decoder layer taps[f] (1-based), the layout dflash_inject_kv reads;
  *   dbg_logits nullable fp32 [batch][rows][V].
