@@ -382,6 +382,11 @@ struct Layout {
     std::vector<Audit::Region> regions;     // every carved buffer: offset and requested bytes
 };
 
+// Row stride of the per-tile sums of squares a store GEMM writes for the next RMSNorm: the rows
+// rounded up to 4, so that a consumer's 16-byte loads of four rows stay aligned (the padding rows
+// are loaded and never used).
+constexpr int ssq_ld(long long rows) { return (int)((rows + 3) & ~3LL); }
+
 Layout make_layout(const Shape& s, int batch, int rows) {
     Layout l;
     size_t off = 0;
@@ -398,7 +403,7 @@ Layout make_layout(const Shape& s, int batch, int rows) {
     l.ssq_x_tiles = std::max(1, std::max(dp.o.n_tiles, dp.down.n_tiles));
     l.amax_tiles = dp.lm.n_tiles;
     l.x = take(M * s.H * 4);
-    l.ssq_x = take((size_t)l.ssq_x_tiles * M * 4);
+    l.ssq_x = take((size_t)l.ssq_x_tiles * ssq_ld(M) * 4);
     l.qkv = take(M * (size_t)(s.nq + 2 * s.nkv) * s.D * 4);
     l.opart = take((size_t)batch * s.nkv * s.nch_max * s.rpad * s.D * s.esize);
     l.mlpart = take((size_t)batch * s.nkv * s.nch_max * s.rpad * 2 * 4);
@@ -417,7 +422,7 @@ Layout make_layout(const Shape& s, int batch, int rows) {
         const size_t Mi = (size_t)batch * rows;
         l.ssq_c_tiles = plan_gemm(s, EPI_STORE, s.H, s.F * s.H, std::min((int)Mi, TILED_MIN_ROWS - 1), 1).n_tiles;
         l.c = take(Mi * s.H * 4);
-        l.ssq_c = take((size_t)l.ssq_c_tiles * Mi * 4);
+        l.ssq_c = take((size_t)l.ssq_c_tiles * ssq_ld(Mi) * 4);
         l.cnorm = take((size_t)s.L * pad16((int)Mi) * s.H * s.esize);   // per-layer RMSNorm-ed rows
         l.kvraw = take((size_t)s.L * Mi * 2 * s.nkv * s.D * 4); // per-layer k | v projections
         l.lensnap = take((size_t)batch * 4);                     // len before this injection
@@ -493,11 +498,11 @@ void audit_gemm(const GemmArgs& a, const GemmPlan& p, Audit& au) {
 // epilogue has one output element per thread and the consumer's threads can hold the
 // producer's per-tile sums of squares in GEMM_RSQ loads each.
 bool fold_producer_ok(const GemmPlan& p, int M) {
-    return !p.tiled && p.mt == 1 && p.epi == EPI_STORE && M <= 16 && M % 4 == 0 &&
+    return !p.tiled && p.mt == 1 && p.epi == EPI_STORE && M <= 16 &&
            16 * p.ns * p.ntw * 16 <= 64 * p.ns * p.ks;
 }
 bool fold_consumer_ok(const GemmPlan& c, int rs_n, int M) {
-    return !c.tiled && c.mt == 1 && (c.epi == EPI_STORE || c.epi == EPI_SWIGLU) && M <= 16 && M % 4 == 0 &&
+    return !c.tiled && c.mt == 1 && (c.epi == EPI_STORE || c.epi == EPI_SWIGLU) && M <= 16 &&
            rs_n >= 1 && rs_n <= GEMM_RSQ * 64 * c.ns * c.ks / 4;
 }
 
@@ -578,7 +583,7 @@ int set_norm_a(GemmArgs& a, const Shape& s, const float* x, int M, const float* 
     nw.w[0] = w;
     tr.begin("rmsnorm");
     if (tr.au) tr.au->write(nbuf, span_act<T>(afrag, M, s.H, s.H));
-    DFL_LAUNCH(tr, (rmsnorm_rows_kernel<T>), dim3(M, cdiv(s.H, 1024), 1), dim3(256), 0, st, x, s.H, ssq, n_ssq, M,
+    DFL_LAUNCH(tr, (rmsnorm_rows_kernel<T>), dim3(M, cdiv(s.H, 1024), 1), dim3(256), 0, st, x, s.H, ssq, n_ssq, ssq_ld(M),
                nw, s.H, s.eps, static_cast<T*>(nbuf), s.H, 0LL, nullptr, nullptr, 0, afrag, row_factor ? 1 : 0);
     tr.end();
     a.a = nbuf;
@@ -596,7 +601,7 @@ void set_carried_norm_a(GemmArgs& a, const Shape& s, void* nbuf, const float* ss
     a.a_frag = 1;
     a.rs_ssq = ssq;
     a.rs_n = n_ssq;
-    a.rs_ld = M;
+    a.rs_ld = ssq_ld(M);
     a.rs_k = (float)s.H;
     a.rs_eps = s.eps;
 }
@@ -631,7 +636,7 @@ int run_inject(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int
         a.ldo = s.H;
         a.residual = 0;
         a.ssq_out = ssq_c;
-        a.ssq_out_ld = M;
+        a.ssq_out_ld = ssq_ld(M);
         if (carry) {
             a.n_z = s.L;
             for (int l = 0; l < s.L; ++l) a.zw[l] = w->layers[l].in_norm;
@@ -657,7 +662,7 @@ int run_inject(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int
                 tr.au->write(lensnap, (size_t)batch * 4);
             }
             DFL_LAUNCH(tr, (rmsnorm_rows_kernel<T>), dim3(M, cdiv(s.H, 1024), s.L), dim3(256), 0, st, c, s.H, ssq_c,
-                       pl.fuse.n_tiles, M, nw, s.H, s.eps, cn, s.H, (long long)cn_layer, kv->len, lensnap, batch,
+                       pl.fuse.n_tiles, ssq_ld(M), nw, s.H, s.eps, cn, s.H, (long long)cn_layer, kv->len, lensnap, batch,
                        afrag, 1);
             tr.end();
             if (!launched(tr)) return DFLASH_ELAUNCH;
@@ -726,7 +731,7 @@ struct PassMode {
     float* row_loss;        // with labels: nullable [batch][gamma-1] cross-entropy per mask row
     float* dlogits;         // with labels: nullable [batch][gamma-1][V] gradient of the loss w.r.t. the logits
     const float* x_in;      // nullable: fp32 [batch*gamma][H] input rows instead of token embeddings
-    const float* ssq_in;    // with x_in: [n_ssq_in][batch*gamma] per-tile sums of squares of x_in
+    const float* ssq_in;    // with x_in: [n_ssq_in][ssq_ld(batch*gamma)] per-tile sums of squares of x_in
     int n_ssq_in;
     int no_head;            // stop after the last decoder layer (no final norm, LM head or argmax)
 };
@@ -891,7 +896,7 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
             a.ldo = s.H;
             a.residual = 1;
             a.ssq_out = ssq_x;
-            a.ssq_out_ld = M;
+            a.ssq_out_ld = ssq_ld(M);
             if (carry_mlp) {        // gate|up's A operand: x * w_post
                 a.n_z = 1;
                 a.zw[0] = lw.post_norm;
@@ -925,7 +930,7 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
             a.ldo = s.H;
             a.residual = 1;
             a.ssq_out = ssq_x;
-            a.ssq_out_ld = M;
+            a.ssq_out_ld = ssq_ld(M);
             if (carry_attn && l + 1 < s.L) {     // the next layer's q|k|v A operand: x * w_in
                 a.n_z = 1;
                 a.zw[0] = w->layers[l + 1].in_norm;
@@ -986,7 +991,7 @@ int run_draft(const Shape& s, const dflash_weights* w, const dflash_kv* kv, int 
     if (head_argmax && dbg_logits && n_draft > 0) {   // the returned logits, with the row factor
         tr.begin("scale_logits");
         DFL_LAUNCH(tr, scale_logit_rows_kernel, dim3((unsigned)std::min(64, cdiv(s.V, 256)), (unsigned)n_draft),
-                   dim3(256), 0, st, dbg_logits, s.V, ssq_x, n_ssq, M, gamma, md.first_row, s.H, s.eps);
+                   dim3(256), 0, st, dbg_logits, s.V, ssq_x, n_ssq, ssq_ld(M), gamma, md.first_row, s.H, s.eps);
         tr.end();
         if (!launched(tr)) return DFLASH_ELAUNCH;
     }
@@ -1054,7 +1059,7 @@ int run_inject_input_fusion(const Shape& s, const dflash_weights* w, const dflas
         a.ldo = s.H;
         a.residual = 0;
         a.ssq_out = ssq_c;
-        a.ssq_out_ld = M;
+        a.ssq_out_ld = ssq_ld(M);
         if ((rc = gemm_dispatch<T>(a, pl.fuse, st, tr, "fuse"))) return rc;
     }
     PassMode md = DRAFT_PASS;
