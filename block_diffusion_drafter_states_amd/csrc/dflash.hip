@@ -201,13 +201,15 @@ constexpr int STREAM_ROUND_WGS = 256;
 // gate/up).  Every workgroup owns complete output columns (no cross-workgroup
 // reduction); its waves split K (ks) and rows (ns).  The A operand is always a
 // storage-type matrix (RMSNorm is applied by rmsnorm_rows_kernel first).
-// Choices follow a sweep on MI355X at 16 rows: 16-column tiles (ntw 1) with 8
-// waves along K (4 when there are >= 512 workgroups) for the 2048- and
-// 4096-row projections so that every CU streams, 32-column
-// tiles with 4 waves for wider ones, 4 waves per 16 gate + 16 up rows for
-// SwiGLU, two waves per 32 vocabulary rows for the LM head (weights read from
-// HBM, not from the last-level cache); one workgroup's LDS ring must fit the
-// 160 KB of a CU.
+// Choices follow sweeps on MI355X at 16 rows: store projections in 16-column tiles
+// (ntw 1) with 8 waves along K (128 KB of ring, one workgroup per CU) when the launch
+// has at most one workgroup per CU, else 4 waves (64 KB, two per CU, so that every
+// workgroup is resident at once: q|k|v at the Qwen3-8B shape, 384 workgroups, 88.6 ->
+// 87.4 us per cycle, at the Coder-30B drafter shape (320) 76.0 -> 59.1 us, against
+// 32-column tiles with 4 waves, 192 workgroups, one per CU); 4 waves per 16 gate + 16 up
+// rows for SwiGLU, two waves per 32 vocabulary rows for the LM head (weights read from
+// HBM, not from the last-level cache); one workgroup's LDS ring must fit the 160 KB of
+// a CU.
 GemmPlan plan_streaming(const Shape& s, int epi, int wrows, int K, int M, int layers) {
     GemmPlan p;
     p.bn = 0;
@@ -227,8 +229,8 @@ GemmPlan plan_streaming(const Shape& s, int epi, int wrows, int K, int M, int la
         // 40.8 us per Qwen3-8B gate|up launch; two waves (64 KB, two per CU, 1.5 rounds) 45 us
         ks = 4;
     } else {
-        p.ntw = wrows / 32 >= 192 ? 2 : 1;
-        ks = p.ntw == 2 ? 4 : (cdiv(wrows, 16) * layers >= 512 ? 4 : 8);
+        p.ntw = 1;
+        ks = cdiv(wrows, 16) * layers > STREAM_ROUND_WGS ? 4 : 8;
     }
     if (epi == EPI_SWIGLU) p.n_tiles = cdiv(wrows, 16);   // 16 gate + 16 up rows per workgroup
     else p.n_tiles = cdiv(wrows, p.ns * p.ntw * 16);
@@ -537,9 +539,7 @@ int gemm_dispatch(const GemmArgs& a, const GemmPlan& p, hipStream_t st, Tracer& 
     for (int k = 0; k < 2; ++k)     // a 16-row weight tile never straddles two segments
         if (a.seg_end[k] < a.N && a.seg_end[k] % 16) return DFLASH_EINVAL;
     switch (p.epi) {
-        case EPI_STORE:
-            return p.ntw == 1 ? launch_gemm_mt<T, EPI_STORE, 1>(a, p, st, tr, name)
-                              : launch_gemm_mt<T, EPI_STORE, 2>(a, p, st, tr, name);
+        case EPI_STORE: return p.ntw == 1 ? launch_gemm_mt<T, EPI_STORE, 1>(a, p, st, tr, name) : DFLASH_EINVAL;
         case EPI_SWIGLU: return launch_gemm_mt<T, EPI_SWIGLU, 2>(a, p, st, tr, name);
         case EPI_ARGMAX: return launch_gemm_mt<T, EPI_ARGMAX, 2>(a, p, st, tr, name);
         case EPI_LSE: return launch_gemm_mt<T, EPI_LSE, 2>(a, p, st, tr, name);
