@@ -14,7 +14,8 @@
 // Streaming.  Weights go from HBM straight into a per-wave LDS ring with
 // direct-to-LDS loads (global_load_lds, 16 bytes per lane): one instruction
 // fetches 4 weight rows x 256 contiguous bytes, P k-steps ahead, without
-// passing through registers.  Inside a 16-row x 256-byte ring tile, the
+// passing through registers, with the non-temporal hint (a launch reads each weight
+// byte once per 16*MT-row group).  Inside a 16-row x 256-byte ring tile, the
 // 16-byte chunk c of row rho sits at position c ^ rho, so the MFMA fragment
 // reads (lane r <- row r) hit 16 distinct bank groups.  The few activation
 // rows (storage type, already normalised where the model normalises them;
@@ -228,7 +229,7 @@ __global__ __launch_bounds__(512) void gemm_kernel(const GemmArgs p) {
         for (int t = 0; t < NTW; ++t)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                dma_b128(wsrc[t][i] + (size_t)step * 256, ring_lds + (uint32_t)((q * NTW + t) * 4096 + i * 1024));
+                dma_b128_nt(wsrc[t][i] + (size_t)step * 256, ring_lds + (uint32_t)((q * NTW + t) * 4096 + i * 1024));
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             const char* a = arow[mt] + (size_t)step * a_step;
