@@ -62,6 +62,7 @@ struct AttnArgs {
     void* kwrite;           // nullable: this layer's K cache, where the block's keys are kept at len ..
     void* vwrite;           // ... and its V^T cache (a verifying target); nothing is written when null
     unsigned* status;       // sticky error bits (with kwrite: len < 0, len + gamma beyond the cache)
+    int kv_nt;              // load the context K/V with the non-temporal hint
 };
 
 // Per-wave attention state for one query tile.
@@ -366,10 +367,11 @@ __device__ __forceinline__ void attn_subblock(WaveAttn<T>& w, int nvalid, int kl
 // one; their scores are masked) and 8 for V^T (the 32-key block, one contiguous 8 KB span
 // of the blocked V cache: kb + 32 <= cap; keys
 // beyond the real ones are cleared at use).  Instruction j goes to the wave
-// iw = j % NW of the key group: every wave issues exactly 16 / NW of them.
+// iw = j % NW of the key group: every wave issues exactly 16 / NW of them (with the
+// non-temporal hint when nt).
 template <typename T, int NW>
 __device__ __forceinline__ void stage_issue(uint32_t stage, const T* kc, const T* vc, int cap, int kb, int nvalid,
-                                            int iw) {
+                                            int iw, int nt) {
     constexpr int D = 256 / (int)sizeof(T), KPC = 16 / (int)sizeof(T);   // elements per 16 bytes
     constexpr int RB = 32 * (int)sizeof(T), CPR = RB / 16, RPI = 1024 / RB;
     const int lane = threadIdx.x & 63;
@@ -381,12 +383,14 @@ __device__ __forceinline__ void stage_issue(uint32_t stage, const T* kc, const T
             const int key = 4 * j + (lane >> 4);
             const int src = key < nvalid ? key : nvalid - 1;
             const int c = (lane & 15) ^ kswz(key);
-            dma_b128(kc + (long long)(kb + src) * D + c * KPC, stage + j * 1024);
+            if (nt) dma_b128_nt(kc + (long long)(kb + src) * D + c * KPC, stage + j * 1024);
+            else dma_b128(kc + (long long)(kb + src) * D + c * KPC, stage + j * 1024);
         } else {
             const int jj = j - 8;
             const int d = jj * RPI + lane / CPR, p = lane % CPR;
             const int c = sizeof(T) == 2 ? (p ^ ((d >> 2) & 3)) : p;
-            dma_b128(vc + (long long)kb * D + d * VBLK + c * KPC, stage + ATT_V_OFF + jj * 1024);
+            if (nt) dma_b128_nt(vc + (long long)kb * D + d * VBLK + c * KPC, stage + ATT_V_OFF + jj * 1024);
+            else dma_b128(vc + (long long)kb * D + d * VBLK + c * KPC, stage + ATT_V_OFF + jj * 1024);
         }
     }
 }
@@ -593,7 +597,7 @@ __global__ __launch_bounds__(64 * (RING == 8 ? QTW * KG_ : ATT_MAX_WAVES)) void 
     for (int st = 0; st < R; ++st) {
         const int kb = k_lo + 32 * st;
         if (kb < k_hi) {
-            stage_issue<T, QTW>(kgbuf_lds + st * ATT_STAGE_BYTES, kc, vc, a.cap, kb, min(32, k_hi - kb), tl);
+            stage_issue<T, QTW>(kgbuf_lds + st * ATT_STAGE_BYTES, kc, vc, a.cap, kb, min(32, k_hi - kb), tl, a.kv_nt);
             ++n_issued;
         }
     }
@@ -707,7 +711,8 @@ __global__ __launch_bounds__(64 * (RING == 8 ? QTW * KG_ : ATT_MAX_WAVES)) void 
             __syncthreads();
             const int kbn = kb + 32 * R;
             if (kbn < k_hi)
-                stage_issue<T, QTW>(kgbuf_lds + (it % R) * ATT_STAGE_BYTES, kc, vc, a.cap, kbn, min(32, k_hi - kbn), tl);
+                stage_issue<T, QTW>(kgbuf_lds + (it % R) * ATT_STAGE_BYTES, kc, vc, a.cap, kbn, min(32, k_hi - kbn), tl,
+                                    a.kv_nt);
         }
     }
 
