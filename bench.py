@@ -207,11 +207,13 @@ GEMM_LAUNCHES = ("fuse", "inject_kv", "qkv_proj", "o_proj", "gate_up", "down_pro
 
 def measured_peaks(torch):
     """What plain probe kernels reach on this GPU (libdflash_probe.so): the HBM read rate of a
-    grid-stride streaming kernel over 4 GiB and the bf16 MFMA rate of independent 16x16x32 and
-    32x32x16 MFMA chains on every SIMD (each the median of 5)."""
+    grid-stride streaming kernel over 4 GiB (plain loads, 16 workgroups per CU; and with the
+    non-temporal hint, eight loads in flight per thread, one workgroup per CU) and the bf16 MFMA
+    rate of independent 16x16x32 and 32x32x16 MFMA chains on every SIMD (each the median of 5)."""
     lib = ctypes.CDLL(os.path.join(HERE, "block_diffusion_drafter_states_amd", "libdflash_probe.so"))
     lib.dflash_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint, ctypes.c_void_p,
                                       ctypes.c_int, ctypes.c_void_p]
+    lib.dflash_probe_read_nt.argtypes = lib.dflash_probe_read.argtypes
     lib.dflash_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     lib.dflash_probe_mfma32.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     stream = torch.cuda.current_stream().cuda_stream
@@ -233,6 +235,9 @@ def measured_peaks(torch):
     read = lambda: lib.dflash_probe_read(buf.data_ptr(), nbytes, 0x9E3779B9, sink.data_ptr(), blocks, stream)
     time_ms(read)
     gbs = nbytes / (statistics.median(time_ms(read) for _ in range(5)) * 1e-3) / 1e9
+    read_nt = lambda: lib.dflash_probe_read_nt(buf.data_ptr(), nbytes, 0x9E3779B9, sink.data_ptr(), 256, stream)
+    time_ms(read_nt)
+    gbs_nt = nbytes / (statistics.median(time_ms(read_nt) for _ in range(5)) * 1e-3) / 1e9
     iters, mblocks = 2000, 256 * 8
     mfma = lambda: lib.dflash_probe_mfma(iters, mblocks, fsink.data_ptr(), stream)
     time_ms(mfma)
@@ -244,7 +249,7 @@ def measured_peaks(torch):
     tflops32 = flops32 / (statistics.median(time_ms(mfma32) for _ in range(5)) * 1e-3) / 1e12
     del buf
     torch.cuda.empty_cache()
-    return {"read_GBs": round(gbs, 1), "mfma_bf16_TFLOPs": round(tflops, 1),
+    return {"read_GBs": round(gbs, 1), "read_nt_GBs": round(gbs_nt, 1), "mfma_bf16_TFLOPs": round(tflops, 1),
             "mfma32_bf16_TFLOPs": round(tflops32, 1)}
 
 

@@ -32,6 +32,29 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict
     if (acc == key) sink[blockIdx.x] = acc;
 }
 
+// The same read with the non-temporal hint and eight independent loads per thread in
+// flight: on MI355X the best of the shapes measured (one workgroup per CU, 7.1-7.2 TB/s
+// over 2 GiB against ~5.5 TB/s for the plain loads above with many workgroups).
+typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(256) void read_nt_probe_kernel(const u32x4v* __restrict__ src, long long n_vec,
+                                                            unsigned key, unsigned* __restrict__ sink) {
+    const long long stride = (long long)gridDim.x * blockDim.x;
+    unsigned acc = 0u;
+    long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    for (; i + 7 * stride < n_vec; i += 8 * stride) {
+        u32x4v v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    for (; i < n_vec; i += stride) {
+        const u32x4v a = src[i];
+        acc ^= a.x ^ a.y ^ a.z ^ a.w;
+    }
+    if (acc == key) sink[blockIdx.x] = acc;
+}
+
 // Each wave runs `iters` rounds of NACC independent v_mfma_f32_16x16x32_bf16 on register
 // operands (no memory traffic in the loop); lane 0 of each workgroup stores a sum of its
 // accumulators so that the chain is kept.  16 x 16 x 32 x 2 flops per instruction.
@@ -90,6 +113,14 @@ int dflash_probe_read(const void* buf, size_t bytes, unsigned key, unsigned* sin
     if (!buf || !sink || blocks < 1 || bytes % 16) return -1;
     hipLaunchKernelGGL(read_probe_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
                        static_cast<const uint4*>(buf), (long long)(bytes / 16), key, sink);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// As dflash_probe_read with the non-temporal eight-load kernel.
+int dflash_probe_read_nt(const void* buf, size_t bytes, unsigned key, unsigned* sink, int blocks, void* stream) {
+    if (!buf || !sink || blocks < 1 || bytes % 16) return -1;
+    hipLaunchKernelGGL(read_nt_probe_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const u32x4v*>(buf), (long long)(bytes / 16), key, sink);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

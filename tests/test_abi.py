@@ -330,20 +330,23 @@ def test_draft_check_flags_wrong_ids():
 
 def test_probe_library_exports_and_rejects_bad_arguments():
     """libdflash_probe.so (the benchmark's measured ceilings, `bench.py --probes`) exports the
-    HBM-read and the two MFMA probes, and each returns -1 for invalid arguments before any launch."""
+    two HBM-read and the two MFMA probes, and each returns -1 for invalid arguments before any launch."""
     path = os.path.join(os.path.dirname(_abi.LIB_PATH), "libdflash_probe.so")
     if not os.path.exists(path):
         pytest.skip("libdflash_probe.so not built (run __graft_entry__.build())")
     P = ctypes.CDLL(path)
     out = os.popen(f"nm -D --defined-only {path}").read()
     names = sorted(re.findall(r"\bT (dflash_probe_[a-z0-9_]+)\b", out))
-    assert names == ["dflash_probe_mfma", "dflash_probe_mfma32", "dflash_probe_read"]
+    assert names == ["dflash_probe_mfma", "dflash_probe_mfma32", "dflash_probe_read", "dflash_probe_read_nt"]
     P.dflash_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint, ctypes.c_void_p, ctypes.c_int,
                                     ctypes.c_void_p]
+    P.dflash_probe_read_nt.argtypes = P.dflash_probe_read.argtypes
     P.dflash_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     P.dflash_probe_mfma32.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     assert P.dflash_probe_read(None, 16, 0, None, 1, None) == -1
     assert P.dflash_probe_read(None, 15, 0, None, 1, None) == -1
+    assert P.dflash_probe_read_nt(None, 16, 0, None, 1, None) == -1
+    assert P.dflash_probe_read_nt(None, 16, 0, None, 0, None) == -1
     assert P.dflash_probe_mfma(1, 1, None, None) == -1
     assert P.dflash_probe_mfma32(0, 1, None, None) == -1
 
