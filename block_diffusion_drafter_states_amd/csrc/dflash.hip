@@ -223,10 +223,10 @@ GemmPlan plan_streaming(const Shape& s, int epi, int wrows, int K, int M, int la
     p.ntw = 2;
     int ks;
     if (epi == EPI_ARGMAX || epi == EPI_LSE) {
-        // the argmax LM head over one 16-row tile: four waves on a 2-stage ring (64 KB, two
-        // workgroups per CU), measured at the Qwen3-8B shape with the non-temporal weight
-        // stream: 199.2 -> 179.5 us per launch (6.9 TB/s) against two waves on a 4-stage ring
-        ks = epi == EPI_ARGMAX && p.mt == 1 ? 4 : 2;
+        // the LM head over one 16-row tile: four waves on a 2-stage ring (64 KB, two workgroups
+        // per CU), measured at the Qwen3-8B shape with the non-temporal weight stream: argmax
+        // 199.2 -> 179.5 us per launch (6.9 TB/s) against two waves on a 4-stage ring
+        ks = p.mt == 1 ? 4 : 2;
     } else if (epi == EPI_SWIGLU) {
         // measured at 16 rows: four waves (128 KB of ring, three rounds of one workgroup per CU)
         // 40.8 us per Qwen3-8B gate|up launch; two waves (64 KB, two per CU, 1.5 rounds) 45 us
@@ -241,7 +241,7 @@ GemmPlan plan_streaming(const Shape& s, int epi, int wrows, int K, int M, int la
     // and one streams while the other starts or runs its epilogue (measured at the Qwen3-8B
     // shape, 768 workgroups: 47 -> 39.6 us per launch; a 4-stage ring, one workgroup per
     // CU, idles each CU between its three workgroups; HIP-event times)
-    p.ring = ((epi == EPI_SWIGLU || epi == EPI_ARGMAX) && p.mt == 1) ? 2 : 0;
+    p.ring = ((epi == EPI_SWIGLU || epi == EPI_ARGMAX || epi == EPI_LSE) && p.mt == 1) ? 2 : 0;
     const int ring = p.ring ? p.ring : gemm_ring_depth(p.mt, p.ntw);
     while (ks > 1 && K / s.step < 2 * ks) ks /= 2;        // at least two k-steps per wave
     while (ks > 1 && gemm_lds_bytes_host(p.ns, ks, p.mt, p.ntw, ring) > GEMM_MAX_LDS) ks /= 2;
@@ -439,8 +439,8 @@ Layout make_layout(const Shape& s, int batch, int rows) {
 template <typename T, int EPI, int MT, int NTW>
 int launch_gemm(const GemmArgs& a, const GemmPlan& p, hipStream_t st, Tracer& tr, const char* name) {
     constexpr int P = gemm_ring_depth(MT, NTW);
-    // the one non-default ring: gate|up and the argmax LM head over one 16-row tile, 2 stages
-    constexpr bool RING2 = (EPI == EPI_SWIGLU || EPI == EPI_ARGMAX) && MT == 1;
+    // the one non-default ring: gate|up and the LM head over one 16-row tile, 2 stages
+    constexpr bool RING2 = (EPI == EPI_SWIGLU || EPI == EPI_ARGMAX || EPI == EPI_LSE) && MT == 1;
     if (p.ring && p.ring != P && !(RING2 && p.ring == 2)) return DFLASH_EINVAL;
     dim3 grid(p.n_tiles, p.mgroups, p.layers);
     tr.begin(name);
