@@ -184,6 +184,7 @@ struct GemmPlan {
     bool tiled;     // gemm_tiled_kernel (many rows) instead of the weight-streaming kernel
     int bn;         // tiled: weight rows per workgroup (128, or 64 when that leaves CUs idle)
     int kb;         // tiled: bytes of every row per LDS stage (256; 128 for launches with many workgroups)
+    int bm;         // tiled: rows of A per workgroup (TG_BM, or 2 x TG_BM with 128-byte stages)
     size_t lds;
 };
 
@@ -214,6 +215,7 @@ GemmPlan plan_streaming(const Shape& s, int epi, int wrows, int K, int M, int la
     GemmPlan p;
     p.bn = 0;
     p.kb = 0;
+    p.bm = 0;
     p.epi = epi;
     p.layers = layers;
     p.tiled = false;
@@ -261,7 +263,8 @@ GemmPlan plan_gemm(const Shape& s, int epi, int wrows, int K, int M, int layers)
     p.kw = K;
     p.mt = 8;
     p.ntw = 0;
-    p.mgroups = cdiv(M, TG_BM);
+    p.bm = TG_BM;
+    p.mgroups = cdiv(M, p.bm);
     p.bn = 128;
     // 64-wide blocks when 128-wide ones would leave half the CUs idle (measured at 512 rows:
     // down 4096 x 14336 138 -> 90 us; q|k|v 6144 x 4096, 192 blocks, 47 -> 58 us the other way)
@@ -273,7 +276,15 @@ GemmPlan plan_gemm(const Shape& s, int epi, int wrows, int K, int M, int layers)
     // workgroups per CU on (measured at 512 rows: LM head 857 -> 636 us, gate|up
     // 182 -> 143 us; with 256 workgroups they pack onto fewer CUs and lose)
     p.kb = tiled_wgs >= 512 ? 128 : 256;
-    p.lds = tg_lds_bytes(p.bn, p.kb);
+    // 256-row blocks (eight waves, 96 KB of LDS, one workgroup per CU) for those launches:
+    // a quarter fewer bytes staged per flop and fewer loads issued per wave per k-step.
+    // Measured at 512 rows: gate|up 660.7 -> 624.5 us per cycle; the 4096-row prefill 1535.6
+    // -> 1442.6 us; not for the LM-head epilogues (argmax 540.1 -> 561.6 us)
+    if (p.kb == 128 && p.bn == 128 && M >= 2 * TG_BM && epi != EPI_ARGMAX && epi != EPI_LSE) {
+        p.bm = 2 * TG_BM;
+        p.mgroups = cdiv(M, p.bm);
+    }
+    p.lds = tg_lds_bytes(p.bm, p.bn, p.kb);
     return p;
 }
 
@@ -468,9 +479,18 @@ int launch_gemm_mt(const GemmArgs& a, const GemmPlan& p, hipStream_t st, Tracer&
 template <typename T, int EPI, int BN>
 int launch_gemm_tiled(const GemmArgs& a, const GemmPlan& p, hipStream_t st, Tracer& tr, const char* name) {
     dim3 grid(cdiv(p.n_tiles, 8) * 8, p.mgroups, p.layers);   // the kernel maps blocks XCD-aware
+    if (p.bm != TG_BM && (p.bm != 2 * TG_BM || p.kb != 128 || BN != 128)) return DFLASH_EINVAL;
+    if (p.kb != 128 && p.kb != 256) return DFLASH_EINVAL;
     tr.begin(name);
-    if (p.kb == 128) DFL_LAUNCH(tr, (gemm_tiled_kernel<T, EPI, BN, 128>), grid, dim3(TG_THREADS), p.lds, st, a);
-    else DFL_LAUNCH(tr, (gemm_tiled_kernel<T, EPI, BN, 256>), grid, dim3(TG_THREADS), p.lds, st, a);
+    if (p.bm == 2 * TG_BM) {
+        if constexpr (BN == 128)
+            DFL_LAUNCH(tr, (gemm_tiled_kernel<T, EPI, BN, 128, 2 * TG_BM>), grid, dim3(tg_threads(2 * TG_BM)), p.lds,
+                       st, a);
+    } else if (p.kb == 128) {
+        DFL_LAUNCH(tr, (gemm_tiled_kernel<T, EPI, BN, 128, TG_BM>), grid, dim3(tg_threads(TG_BM)), p.lds, st, a);
+    } else {
+        DFL_LAUNCH(tr, (gemm_tiled_kernel<T, EPI, BN, 256, TG_BM>), grid, dim3(tg_threads(TG_BM)), p.lds, st, a);
+    }
     const bool ok = launched(tr);
     tr.end();
     return ok ? DFLASH_OK : DFLASH_ELAUNCH;

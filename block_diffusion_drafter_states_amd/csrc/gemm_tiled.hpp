@@ -2,14 +2,14 @@
 // prompt's injection): out = A . W^T with the same epilogues as the weight-streaming
 // GEMM (store + residual + per-tile sums of squares, SwiGLU, argmax).
 //
-// At these sizes the product is a dense contraction: each workgroup computes a 128 x BN
-// block (128 rows of A against BN = 128 or 64 weight rows; SwiGLU: 64 gate + 64 up rows
-// of the same 64 output columns), its four waves arranged 2 x 2, each wave 64 x BN/2
-// (4 x BN/32 MFMA tiles of 16 x 16).  Both operands go HBM -> LDS with direct-to-LDS
-// loads, KB bytes of every row per stage, two stages.  KB = 256 (128 KB of LDS at
-// BN = 128: one workgroup per CU) for launches with few workgroups, KB = 128 (64 KB:
+// At these sizes the product is a dense contraction: each workgroup computes a BM x BN
+// block (BM = 128 or 256 rows of A against BN = 128 or 64 weight rows; SwiGLU: 64 gate +
+// 64 up rows of the same 64 output columns), its BM / 32 waves arranged BM / 64 x 2, each
+// wave 64 x BN/2 (4 x BN/32 MFMA tiles of 16 x 16).  Both operands go HBM -> LDS with
+// direct-to-LDS loads, KB bytes of every row per stage, two stages.  KB = 256 (128 KB of
+// LDS at 128 x 128: one workgroup per CU) for launches with few workgroups, KB = 128 (64 KB:
 // several workgroups per CU hide each other's barriers and load latency) for launches
-// with many.  Inside a 16-row tile the 16-byte chunk c of row rho sits at c ^ swz(rho)
+// with many; 256 x 128 blocks (96 KB, eight waves) for some of those.  Inside a 16-row tile the 16-byte chunk c of row rho sits at c ^ swz(rho)
 // (rho for 256-byte rows, (rho >> 1) & 7 for 128-byte rows), so the fragment reads of
 // 16 lanes (one row each) hit 16 different bank groups.
 //
@@ -23,11 +23,12 @@
 
 namespace dflash {
 
-constexpr int TG_BM = 128;                               // rows of A per workgroup
-constexpr int TG_THREADS = 256;
-// bytes per stage and of the two stages, for BN weight rows and KB bytes per row
-__host__ __device__ constexpr int tg_stage_bytes(int bn, int kb) { return (TG_BM + bn) * kb; }
-__host__ __device__ constexpr int tg_lds_bytes(int bn, int kb) { return 2 * tg_stage_bytes(bn, kb); }
+constexpr int TG_BM = 128;                               // rows of A per workgroup (or 2 x TG_BM)
+// threads of a workgroup over BM rows of A: BM / 32 waves, 2 along the weight rows
+__host__ __device__ constexpr int tg_threads(int bm) { return 2 * bm; }
+// bytes per stage and of the two stages, for BM rows of A, BN weight rows and KB bytes per row
+__host__ __device__ constexpr int tg_stage_bytes(int bm, int bn, int kb) { return (bm + bn) * kb; }
+__host__ __device__ constexpr int tg_lds_bytes(int bm, int bn, int kb) { return 2 * tg_stage_bytes(bm, bn, kb); }
 
 template <int KB> __device__ __forceinline__ int tg_swz(int rho) { return KB == 256 ? rho : ((rho >> 1) & 7); }
 
@@ -58,10 +59,10 @@ __device__ __forceinline__ void tg_mfma(f32x4_t& acc, const u32x4_t (&a)[CH], co
 // Output columns per workgroup (SwiGLU: 64 outputs from 64 gate + 64 up rows).
 __host__ __device__ constexpr int tg_cols(int epi, int bn) { return epi == EPI_SWIGLU ? bn / 2 : bn; }
 
-// Epilogues of a workgroup's 128 x BN block (the stages are no longer read).  Lane (g, r)
+// Epilogues of a workgroup's BM x BN block (the stages are no longer read).  Lane (g, r)
 // of tile (a, b) holds C[m][n] for m = m0 + wm*64 + a*16 + 4g + v, column wn*BN/2 + b*16 + r
 // of the workgroup.
-template <typename T, int EPI, int BN>
+template <typename T, int EPI, int BN, int BM>
 __device__ __forceinline__ void tg_epilogue(const GemmArgs& p, const GemmLayer& L, f32x4_t (&acc)[4][BN / 32],
                                             int tile, int m0, int wm, int wn, unsigned char* smem) {
     constexpr int WN = BN / 32;
@@ -95,11 +96,11 @@ __device__ __forceinline__ void tg_epilogue(const GemmArgs& p, const GemmLayer& 
                 ss += __shfl_xor(ss, 2, WAVE);
                 ss += __shfl_xor(ss, 4, WAVE);
                 ss += __shfl_xor(ss, 8, WAVE);
-                if (r == 0) red[wn * TG_BM + mr] = ss;
+                if (r == 0) red[wn * BM + mr] = ss;
             }
         __syncthreads();
-        if (p.ssq_out && threadIdx.x < TG_BM && m0 + (int)threadIdx.x < p.M)
-            p.ssq_out[(long long)tile * p.ssq_out_ld + m0 + threadIdx.x] = red[threadIdx.x] + red[TG_BM + threadIdx.x];
+        if (p.ssq_out && threadIdx.x < BM && m0 + (int)threadIdx.x < p.M)
+            p.ssq_out[(long long)tile * p.ssq_out_ld + m0 + threadIdx.x] = red[threadIdx.x] + red[BM + threadIdx.x];
     } else if constexpr (EPI == EPI_SWIGLU) {
         // tiles b = 0, 2: gate of output tiles 0, 1 of this wave; b = 1, 3: up
 #pragma unroll
@@ -152,11 +153,11 @@ __device__ __forceinline__ void tg_epilogue(const GemmArgs& p, const GemmLayer& 
                 }
 #pragma unroll
                 for (int o = 1; o < 16; o <<= 1) se += __shfl_xor(se, o, WAVE);
-                if (r == 0) redl[wn * TG_BM + mr] = make_float2(mx, se);
+                if (r == 0) redl[wn * BM + mr] = make_float2(mx, se);
             }
         __syncthreads();
-        if (threadIdx.x < TG_BM && m0 + (int)threadIdx.x < p.M) {
-            const float2 x0 = redl[threadIdx.x], x1 = redl[TG_BM + threadIdx.x];
+        if (threadIdx.x < BM && m0 + (int)threadIdx.x < p.M) {
+            const float2 x0 = redl[threadIdx.x], x1 = redl[BM + threadIdx.x];
             const float mx = fmaxf(x0.x, x1.x);
             const float se = (x0.x == -INFINITY ? 0.f : x0.y * __expf(x0.x - mx)) +
                              (x1.x == -INFINITY ? 0.f : x1.y * __expf(x1.x - mx));
@@ -189,23 +190,24 @@ __device__ __forceinline__ void tg_epilogue(const GemmArgs& p, const GemmLayer& 
                     const unsigned long long other = __shfl_xor(best, o, WAVE);
                     best = other > best ? other : best;
                 }
-                if (r == 0) redu[wn * TG_BM + mr] = best;
+                if (r == 0) redu[wn * BM + mr] = best;
             }
         __syncthreads();
-        if (threadIdx.x < TG_BM && m0 + (int)threadIdx.x < p.M) {
-            const unsigned long long x0 = redu[threadIdx.x], x1 = redu[TG_BM + threadIdx.x];
+        if (threadIdx.x < BM && m0 + (int)threadIdx.x < p.M) {
+            const unsigned long long x0 = redu[threadIdx.x], x1 = redu[BM + threadIdx.x];
             p.amax[amax_slot(m0 + (int)threadIdx.x, tile, p.n_tiles)] = x0 > x1 ? x0 : x1;
         }
     }
 }
 
 // BN = 128 or 64 weight rows per workgroup (64: twice the workgroups for narrow weights;
-// SwiGLU always 128).  Wave (wm, wn) computes A rows wm*64 .. +63 against W rows
-// wn*BN/2 .. +BN/2-1: 4 x WN MFMA tiles.
-template <typename T, int EPI, int BN, int KB>
-__global__ __launch_bounds__(TG_THREADS) void gemm_tiled_kernel(const GemmArgs p) {
+// SwiGLU always 128), BM = 128 or 256 rows of A (BM / 32 waves).  Wave (wm, wn) computes A
+// rows wm*64 .. +63 against W rows wn*BN/2 .. +BN/2-1: 4 x WN MFMA tiles.
+template <typename T, int EPI, int BN, int KB, int BM>
+__global__ __launch_bounds__(tg_threads(BM)) void gemm_tiled_kernel(const GemmArgs p) {
     static_assert(BN == 128 || (BN == 64 && EPI != EPI_SWIGLU), "tile width");
     static_assert(KB == 256 || KB == 128, "stage row bytes");
+    static_assert(BM == TG_BM || (BM == 2 * TG_BM && KB == 128), "rows of A per workgroup");
     constexpr int STEP = Elem<T>::STEP * KB / 256;          // elements of a row per stage
     constexpr int WN = BN / 32;                             // n-tiles per wave
     constexpr int LPR = KB / 16;                            // lanes per row in a 1 KB instruction
@@ -213,9 +215,12 @@ __global__ __launch_bounds__(TG_THREADS) void gemm_tiled_kernel(const GemmArgs p
     constexpr int IPT = 16 / RPI;                           // instructions per 16-row tile
     constexpr int TILEB = 16 * KB;                          // bytes of a 16-row tile
     constexpr int CH = KB / 64;                             // 16-byte pieces per lane and tile
-    constexpr int NI = (TG_BM + BN) / 16 * IPT;             // direct-to-LDS instructions per stage
-    constexpr int NIW = NI / 4;                             // ... per wave
-    constexpr int STAGE = tg_stage_bytes(BN, KB);
+    constexpr int NW = BM / 32;                             // waves
+    constexpr int AT = BM / 16;                             // 16-row A tiles per stage
+    constexpr int NI = (BM + BN) / 16 * IPT;                // direct-to-LDS instructions per stage
+    static_assert(NI % NW == 0, "whole instructions per wave");
+    constexpr int NIW = NI / NW;                            // ... per wave
+    constexpr int STAGE = tg_stage_bytes(BM, BN, KB);
     extern __shared__ __align__(16) unsigned char smem[];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, g = lane >> 4, r = lane & 15;
     const int wm = wv >> 1, wn = wv & 1;
@@ -225,15 +230,15 @@ __global__ __launch_bounds__(TG_THREADS) void gemm_tiled_kernel(const GemmArgs p
     const int wlin = blockIdx.x + blockIdx.y * gridDim.x;
     const int xcd = wlin & 7, wslot = wlin >> 3;
     const int tile = (wslot / mgroups) * 8 + xcd;           // gridDim.x = n_tiles rounded up to 8
-    const int m0 = (wslot % mgroups) * TG_BM;
+    const int m0 = (wslot % mgroups) * BM;
     if (tile >= p.n_tiles) return;                          // whole workgroup, before any barrier
     const int layer = blockIdx.z;
     const GemmLayer& L = p.layer[layer];
     const int K = p.K;
     const int nsteps = K / STEP;
 
-    // ---- load plan: NI direct-to-LDS instructions per stage (8 A tiles, BN / 16 W tiles,
-    // IPT per tile), instruction j by wave j % 4; each fetches RPI rows x KB bytes
+    // ---- load plan: NI direct-to-LDS instructions per stage (AT A tiles, BN / 16 W tiles,
+    // IPT per tile), instruction j by wave j % NW; each fetches RPI rows x KB bytes
     const int lq = lane / LPR, lc = lane % LPR;
     const void* abase = L.a ? L.a : p.a;
     const char* src[NIW];
@@ -242,16 +247,16 @@ __global__ __launch_bounds__(TG_THREADS) void gemm_tiled_kernel(const GemmArgs p
     const int wv_u = __builtin_amdgcn_readfirstlane(wv);
 #pragma unroll
     for (int u = 0; u < NIW; ++u) {
-        const int j = u * 4 + wv_u;                 // 0..NI-1, wave-uniform
-        const int t = j / IPT, i = j % IPT;         // tile (0..7 A, 8.. W), rows RPI*i ..
+        const int j = u * NW + wv_u;                // 0..NI-1, wave-uniform
+        const int t = j / IPT, i = j % IPT;         // tile (0..AT-1 A, AT.. W), rows RPI*i ..
         const int rho = i * RPI + lq;
         const T* rowp;
-        if (t < 8) {
+        if (t < AT) {
             int m = m0 + t * 16 + rho;
             m = m < p.M ? m : p.M - 1;              // rows past M: re-read a valid row, result discarded
             rowp = reinterpret_cast<const T*>(abase) + (long long)m * p.lda;
         } else {
-            const int nt = t - 8;
+            const int nt = t - AT;
             const T* base;
             int row, rows;
             if (EPI == EPI_SWIGLU) {                // n-tile 2c: gate tile c, 2c + 1: up tile c
@@ -295,7 +300,7 @@ __global__ __launch_bounds__(TG_THREADS) void gemm_tiled_kernel(const GemmArgs p
 #pragma unroll
         for (int a = 0; a < 4; ++a) tg_frag<KB>(af[a], st + (wm * 4 + a) * TILEB, r, g);
 #pragma unroll
-        for (int b = 0; b < WN; ++b) tg_frag<KB>(bf[b], st + (8 + wn * WN + b) * TILEB, r, g);
+        for (int b = 0; b < WN; ++b) tg_frag<KB>(bf[b], st + (AT + wn * WN + b) * TILEB, r, g);
         __syncthreads();    // every wave holds the stage in registers: it can be refilled
         // the refill (step s + 2) is issued a quarter at a time between the MFMA groups: issuing
         // a direct-to-LDS load holds the wave, so the matrix core works through it
@@ -312,7 +317,7 @@ __global__ __launch_bounds__(TG_THREADS) void gemm_tiled_kernel(const GemmArgs p
         }
     }
 
-    tg_epilogue<T, EPI, BN>(p, L, acc, tile, m0, wm, wn, smem);
+    tg_epilogue<T, EPI, BN, BM>(p, L, acc, tile, m0, wm, wn, smem);
 }
 
 
