@@ -201,16 +201,16 @@ constexpr int STREAM_ROUND_WGS = 256;
 // Geometry of one projection.  wrows = weight rows (EPI_SWIGLU: rows of each of
 // gate/up).  Every workgroup owns complete output columns (no cross-workgroup
 // reduction); its waves split K (ks) and rows (ns).  The A operand is always a
-// storage-type matrix (RMSNorm is applied by rmsnorm_rows_kernel first).
+// storage-type matrix (rows normalised by rmsnorm_rows_kernel, or x * w_norm stored by the
+// producing GEMM where the norm is carried across).
 // Choices follow sweeps on MI355X at 16 rows: store projections in 16-column tiles
 // (ntw 1) with 8 waves along K (128 KB of ring, one workgroup per CU) when the launch
 // has at most one workgroup per CU, else 4 waves (64 KB, two per CU, so that every
 // workgroup is resident at once: q|k|v at the Qwen3-8B shape, 384 workgroups, 88.6 ->
 // 87.4 us per cycle, at the Coder-30B drafter shape (320) 76.0 -> 59.1 us, against
 // 32-column tiles with 4 waves, 192 workgroups, one per CU); 4 waves per 16 gate + 16 up
-// rows for SwiGLU, two waves per 32 vocabulary rows for the LM head (weights read from
-// HBM, not from the last-level cache); one workgroup's LDS ring must fit the 160 KB of
-// a CU.
+// rows for SwiGLU; 4 waves per 32 vocabulary rows for the LM head over one 16-row tile, 2
+// over more; one workgroup's LDS ring must fit the 160 KB of a CU.
 GemmPlan plan_streaming(const Shape& s, int epi, int wrows, int K, int M, int layers) {
     GemmPlan p;
     p.bn = 0;
