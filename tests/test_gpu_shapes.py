@@ -40,8 +40,21 @@ LV = synth.Config("large_vocab_bf16", "bf16", hidden=512, n_q=4, n_kv=2, head_di
                   n_layers=1, n_feat=2, vocab=250000, gamma=16, ctx=200, batch=2, index=87)
 
 
+# 24 sequences x gamma 16 = 384 block rows with a wide SwiGLU (I 11264): the tiled gate|up
+# launch has 176 x 3 blocks of 128 rows, so it takes 256-row blocks (eight waves), two of
+# them with the second only half filled (rows 384..511 re-read row 383, results dropped);
+# at gamma 4 the 96 rows take the weight-streaming kernel
+BM = synth.Config("bm256_bf16", "bf16", hidden=512, n_q=4, n_kv=2, head_dim=128, inter=11264,
+                  n_layers=1, n_feat=2, vocab=1000, gamma=16, ctx=200, batch=24, index=88)
+
+
 def test_batch_of_five_ragged_row_groups():
     run_cycle_case(MB, 5, [0, 1, 300, 63, 257], [16, 2, 9], gen.kv_capacity(MB, 64), "mb")
+
+
+def test_tiled_256_row_blocks_ragged_last_block():
+    lengths = [int(x) for x in np.linspace(0, 200, 24)]
+    run_cycle_case(BM, 24, lengths, [16, 4], gen.kv_capacity(BM, 64), "bm")
 
 
 def test_large_vocabulary_two_finish_rounds():
