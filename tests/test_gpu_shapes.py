@@ -2,8 +2,9 @@
 groups with ragged context lengths (serving concurrency), attention launches with
 enough workgroups for the small LDS rings, GQA group 8 at a
 32k-token context with a block size that changes per cycle (long chain-of-thought
-drafting), and the Qwen3-8B-shaped drafter at full size in the launch
-configuration the benchmark times.  Same bars as the other parity tests."""
+drafting), tiled GEMMs over 256-row blocks with a half-filled last block, and the
+Qwen3-8B-shaped drafter at full size in the launch configuration the benchmark times.
+Same bars as the other parity tests."""
 import json
 
 import numpy as np
@@ -54,7 +55,14 @@ def test_batch_of_five_ragged_row_groups():
 
 def test_tiled_256_row_blocks_ragged_last_block():
     lengths = [int(x) for x in np.linspace(0, 200, 24)]
-    run_cycle_case(BM, 24, lengths, [16, 4], gen.kv_capacity(BM, 64), "bm")
+    P, _ = run_cycle_case(BM, 24, lengths, [16, 4], gen.kv_capacity(BM, 64), "bm")
+    # every sum in the eight-wave blocks runs in a fixed order: two drafts, the same bits
+    anchors = gen.tokens(BM, "bm.det", (24,))
+    log("case determinism of the 256-row tiled blocks")
+    a = P.draft(anchors, 16)
+    b = P.draft(anchors, 16)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
 
 
 def test_large_vocabulary_two_finish_rounds():
